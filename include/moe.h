@@ -1,0 +1,186 @@
+/*
+ * moe.h -- C ABI of the single-GPU mixture-of-experts layer forward pass (gfx950).
+ *
+ * One call runs the whole layer on one HIP stream:
+ *   router GEMM + softmax + top-k gating, per-group expert capacity with overflow drop,
+ *   optional random routing of the 2nd expert, dispatch into a compact expert-major
+ *   buffer, the two-layer FFN of every expert, and the gate-weighted combine back to
+ *   token order (with the residual), plus the auxiliary load-balancing loss.
+ *
+ * Sources, cited by page title and section:
+ *   [GShard]     "GShard: Scaling Giant Models with Conditional Computation and Automatic
+ *                Sharding" (reading notes)
+ *   [MegaBlocks] "04 · 路由、负载均衡与专家并行" (MegaBlocks router / parallelism chapter)
+ *   [Lec16]      "Lec16 Systems for MoE Models" (CMU 11-868 notes)
+ *
+ * Conventions for every entry point
+ *   - Tensors are dense, row-major, caller-owned DEVICE memory, 16-byte aligned.  T is
+ *     the layer dtype: fp32 (cfg.dtype = MOE_DTYPE_F32) or bf16 (MOE_DTYPE_BF16, passed
+ *     as raw 16-bit words).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  All work is enqueued
+ *     asynchronously on it; outputs are valid once the stream has been synchronised.
+ *   - The library allocates no device memory, keeps no pointer after returning and has
+ *     no global state: calls with distinct workspaces may run concurrently.
+ *   - Return value: MOE_OK (0) or a negative MOE_E* code.  All argument checks run on the
+ *     host before anything is enqueued; a call that fails them enqueues nothing and writes
+ *     nothing.  MOE_EHIP reports a launch error (hipGetLastError) after enqueueing.
+ *   - Results are bitwise deterministic for identical inputs (no floating-point atomics).
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,        /* bad cfg, NULL required pointer, pointer not 16-byte aligned */
+  MOE_EWORKSPACE = -2,    /* workspace_bytes < moe_workspace_size(cfg) */
+  MOE_EUNSUPPORTED = -3,  /* valid cfg outside the kernels' shape constraints */
+  MOE_EHIP = -4           /* a HIP launch failed */
+};
+
+enum moe_act { MOE_ACT_RELU = 0, MOE_ACT_GELU = 1 };       /* GELU: exact erf form */
+enum moe_gate_norm { MOE_NORM_NONE = 0, MOE_NORM_SUM = 1 };
+enum moe_dtype { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 };
+
+/*
+ * Layer configuration (plain old data, all int32).
+ *   n_tokens       N >= 0 tokens, split into n_groups contiguous groups of S = N/G tokens
+ *                  that route independently ([GShard] "Top-2 gating 的四个机制 / Local group
+ *                  dispatching"); N % G == 0, G >= 1.
+ *   d_model        M, d_ff H: every expert is act(x W1^T) W2^T, M -> H -> M, no biases
+ *                  ([GShard] "MoE Transformer").
+ *   n_experts      E routed experts, 1 <= E <= 256.
+ *   n_shared       Es >= 0 always-on experts added with weight 1 to every token
+ *                  ([Lec16] "共享专家 vs. 路由专家"); they take no capacity and are not in aux.
+ *   top_k          1 <= k <= min(E, 8): experts selected per token by the k largest logits,
+ *                  descending, ties to the lower expert index.
+ *   capacity       C >= 1 slots per (group, expert) ([GShard] "Expert capacity"); C >= S
+ *                  means nothing is ever dropped.
+ *   act            enum moe_act.
+ *   gate_norm      MOE_NORM_SUM: w_j = p_j / sum of the k selected p (softmax over the
+ *                  selected logits); MOE_NORM_NONE: w_j = p_j, the full softmax probability.
+ *   random_routing 1: keep the 2nd slot iff u[n] < 2 p2/(p1+p2) ([GShard] "Random routing");
+ *                  needs top_k == 2 and a non-NULL u.
+ *   residual       1: y = x + layer(x) (a fully dropped token gets y = x exactly);
+ *                  0: y = layer(x) (a fully dropped token gets 0).
+ *   dtype          enum moe_dtype.
+ * Shape constraints (MOE_EUNSUPPORTED otherwise):
+ *   bf16: M % 128 == 0 and H % 128 == 0.   fp32: M % 64 == 0 and H % 64 == 0.
+ */
+typedef struct moe_cfg {
+  int32_t n_tokens;
+  int32_t n_groups;
+  int32_t d_model;
+  int32_t d_ff;
+  int32_t n_experts;
+  int32_t n_shared;
+  int32_t top_k;
+  int32_t capacity;
+  int32_t act;
+  int32_t gate_norm;
+  int32_t random_routing;
+  int32_t residual;
+  int32_t dtype;
+} moe_cfg;
+
+/*
+ * Dispatch metadata: caller-allocated device arrays the layer fills ([MegaBlocks] section 2
+ * returns scores, expert weights and top experts; [Lec16] "MoE Kernel 优化" keeps a dense
+ * token-to-expert table).  Every pointer is required (16-byte aligned).
+ *   logits    [N, E] fp32   router logits x Wg^T (+ bg)   (moe_forward only; moe_route
+ *                           reads its logits from its own argument and ignores this one)
+ *   topk_idx  [N, k] int32  selected experts, descending logit, BEFORE capacity / random
+ *                           routing
+ *   topk_w    [N, k] fp32   combine weight of each slot; 0 where the slot is not kept
+ *                           (no renormalisation after drops)
+ *   pos       [N, k] int32  position inside the (group, expert) capacity, -1 if not kept
+ *   row       [N, k] int32  row in the compact expert-major buffer, -1 if not kept; rows
+ *                           are ordered (expert, group, position)
+ *   count     [G, E] int32  kept slots per (group, expert), <= C
+ *   offset    [E+1]  int32  first row of each expert; offset[E] = R, the kept slots
+ *   stats     [4]    int32  {R, dropped slots, fully dropped tokens, random-routing skips}
+ */
+typedef struct moe_meta {
+  float* logits;
+  int32_t* topk_idx;
+  float* topk_w;
+  int32_t* pos;
+  int32_t* row;
+  int32_t* count;
+  int32_t* offset;
+  int32_t* stats;
+} moe_meta;
+
+/* Number of stage boundaries recorded by moe_forward_timed. */
+#define MOE_N_EVENTS 7
+
+/* ABI version of the loaded library (MOE_ABI_VERSION at build time). */
+int moe_abi_version(void);
+
+/* Static, human-readable description of a moe_status code. */
+const char* moe_strerror(int code);
+
+/*
+ * Device workspace (bytes) that moe_forward / moe_route need for this cfg.  Host only.
+ * Errors: MOE_EINVAL (NULL pointer, bad cfg), MOE_EUNSUPPORTED.
+ */
+int moe_workspace_size(const moe_cfg* cfg, size_t* bytes);
+
+/*
+ * Whole layer forward ([GShard] "MoE 系统的重点是 dispatch/combine": scores -> top-k ->
+ * capacity/position -> dispatch -> experts -> combine -> residual, on one GPU).
+ *   x         [N, M] T
+ *   Wg        [E, M] T      row e = expert e's gate vector ([MegaBlocks] section 2)
+ *   bg        [E] fp32 or NULL: fixed per-expert router offsets added to the logits
+ *   W1        [E+Es, H, M] T   row n of W1[e] feeds hidden unit n; shared experts last
+ *   W2        [E+Es, M, H] T   row m of W2[e] produces output feature m
+ *   u         [N] fp32 in [0,1), required iff cfg.random_routing
+ *   y         [N, M] T      output (fp32 accumulation, one rounding to T)
+ *   aux_loss  device fp32 scalar: mean over groups of E * sum_e m_e c_e / (k S), with m_e
+ *             the group's mean softmax probability and c_e its pre-capacity top-k
+ *             selections ([GShard] "Auxiliary loss"; [MegaBlocks] "3. 负载均衡损失")
+ *   meta      dispatch metadata (above)
+ *   workspace device scratch of at least moe_workspace_size(cfg) bytes; its content on
+ *             entry is irrelevant and on exit unspecified
+ * N == 0 is valid: only count, offset, stats (zeros) and aux_loss (0) are written, and only
+ * cfg, meta->count/offset/stats, aux_loss and workspace are required (others may be NULL).
+ * Check order: cfg, then aux_loss/workspace (MOE_EINVAL), then workspace_bytes
+ * (MOE_EWORKSPACE), then meta and tensor pointers (MOE_EINVAL).
+ */
+int moe_forward(const moe_cfg* cfg, const void* x, const void* Wg, const float* bg,
+                const void* W1, const void* W2, const float* u, void* y, float* aux_loss,
+                const moe_meta* meta, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_forward, recording `events[0..MOE_N_EVENTS-1]` (caller-created hipEvent_t, passed as
+ * void*) on `stream` at the stage boundaries: before the router, after the router, after
+ * the capacity scan, after the dispatch scatter, after expert GEMM 1, after expert GEMM 2,
+ * after the combine.  Same outputs and errors as moe_forward.
+ */
+int moe_forward_timed(const moe_cfg* cfg, const void* x, const void* Wg, const float* bg,
+                      const void* W1, const void* W2, const float* u, void* y,
+                      float* aux_loss, const moe_meta* meta, void* workspace,
+                      size_t workspace_bytes, void* stream, void* const* events);
+
+/*
+ * Routing only, from caller-given logits [N, E] fp32: softmax, top-k, gate weights, random
+ * routing, capacity positions, dispatch rows and aux ([GShard] "Top-2 gating 的四个机制").
+ * Fills meta (except meta->logits, which is not touched and may be NULL) and aux_loss.
+ * bg is NOT added here: the logits are taken as final.
+ */
+int moe_route(const moe_cfg* cfg, const float* logits, const float* u, const moe_meta* meta,
+              float* aux_loss, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

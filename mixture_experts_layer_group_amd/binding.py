@@ -1,0 +1,199 @@
+"""ctypes binding of libmoe.so (include/moe.h).  Argument marshalling only.
+
+Every step of the layer runs in the HIP library; this module turns torch tensors into
+device pointers, allocates outputs and workspace with ``torch.empty`` and passes torch's
+current HIP stream.  If libmoe.so is missing it raises: there is no fallback path.
+"""
+import ctypes
+import os
+import re
+
+from .configs import CFG_FIELDS
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "moe.h")
+
+MOE_OK, MOE_EINVAL, MOE_EWORKSPACE, MOE_EUNSUPPORTED, MOE_EHIP = 0, -1, -2, -3, -4
+MOE_N_EVENTS = 7
+STAGES = ("router", "gate", "permute", "ffn1", "ffn2", "combine")
+
+
+class MoeCfg(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int32) for f in CFG_FIELDS]
+
+
+class MoeMetaC(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_void_p) for f in
+                ("logits", "topk_idx", "topk_w", "pos", "row", "count", "offset", "stats")]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code, where):
+        super().__init__(f"{where}: {moe_strerror(code)} ({code})")
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path=LIB_PATH):
+    """Load libmoe.so (cached).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run `python -m mixture_experts_layer_group_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    cfgp, metap = ctypes.POINTER(MoeCfg), ctypes.POINTER(MoeMetaC)
+    lib.moe_abi_version.restype = i32
+    lib.moe_abi_version.argtypes = []
+    lib.moe_strerror.restype = ctypes.c_char_p
+    lib.moe_strerror.argtypes = [i32]
+    lib.moe_workspace_size.restype = i32
+    lib.moe_workspace_size.argtypes = [cfgp, ctypes.POINTER(sz)]
+    fwd = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, metap, vp, sz, vp]
+    lib.moe_forward.restype = i32
+    lib.moe_forward.argtypes = fwd
+    lib.moe_forward_timed.restype = i32
+    lib.moe_forward_timed.argtypes = fwd + [ctypes.POINTER(vp)]
+    lib.moe_route.restype = i32
+    lib.moe_route.argtypes = [cfgp, vp, vp, metap, vp, vp, sz, vp]
+    _lib = lib
+    return lib
+
+
+def header_functions(path=HEADER):
+    """Names of the functions include/moe.h declares."""
+    text = open(path).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(moe_\w+)\s*\(", text, re.M)))
+
+
+def moe_abi_version():
+    return load_library().moe_abi_version()
+
+
+def moe_strerror(code):
+    return load_library().moe_strerror(int(code)).decode()
+
+
+def make_cfg(cfg):
+    """dict (configs.py style) or MoeCfg -> MoeCfg."""
+    if isinstance(cfg, MoeCfg):
+        return cfg
+    return MoeCfg(**{f: int(cfg[f]) for f in CFG_FIELDS})
+
+
+def moe_workspace_size(cfg):
+    n = ctypes.c_size_t(0)
+    rc = load_library().moe_workspace_size(ctypes.byref(make_cfg(cfg)), ctypes.byref(n))
+    if rc:
+        raise MoeError(rc, "moe_workspace_size")
+    return n.value
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+class Meta:
+    """Device tensors of the dispatch metadata (moe_meta)."""
+
+    FIELDS = ("logits", "topk_idx", "topk_w", "pos", "row", "count", "offset", "stats")
+
+    def __init__(self, **tensors):
+        for f in self.FIELDS:
+            setattr(self, f, tensors.get(f))
+
+    def as_struct(self):
+        return MoeMetaC(**{f: _ptr(getattr(self, f)) for f in self.FIELDS})
+
+    def to_numpy(self):
+        return {f: getattr(self, f).cpu().numpy() for f in self.FIELDS
+                if getattr(self, f) is not None}
+
+
+def alloc_meta(cfg, device="cuda"):
+    import torch
+    N, E, k, G = cfg["n_tokens"], cfg["n_experts"], cfg["top_k"], cfg["n_groups"]
+    i32 = dict(dtype=torch.int32, device=device)
+    return Meta(logits=torch.empty((N, E), dtype=torch.float32, device=device),
+                topk_idx=torch.empty((N, k), **i32),
+                topk_w=torch.empty((N, k), dtype=torch.float32, device=device),
+                pos=torch.empty((N, k), **i32), row=torch.empty((N, k), **i32),
+                count=torch.empty((G, E), **i32), offset=torch.empty((E + 1,), **i32),
+                stats=torch.empty((4,), **i32))
+
+
+def alloc_workspace(cfg, device="cuda"):
+    import torch
+    return torch.empty(max(1, moe_workspace_size(cfg)), dtype=torch.uint8, device=device)
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def moe_forward(cfg, x, Wg, bg, W1, W2, u, y, aux_loss, meta, workspace, stream=None):
+    """C ABI moe_forward on torch tensors (see include/moe.h for layouts)."""
+    c = make_cfg(cfg)
+    m = meta.as_struct()
+    rc = load_library().moe_forward(
+        ctypes.byref(c), _ptr(x), _ptr(Wg), _ptr(bg), _ptr(W1), _ptr(W2), _ptr(u), _ptr(y),
+        _ptr(aux_loss), ctypes.byref(m), _ptr(workspace), workspace.numel(), _stream(stream))
+    if rc:
+        raise MoeError(rc, "moe_forward")
+
+
+def moe_forward_timed(cfg, x, Wg, bg, W1, W2, u, y, aux_loss, meta, workspace, events,
+                      stream=None):
+    """moe_forward recording MOE_N_EVENTS torch.cuda.Event objects at stage boundaries."""
+    c = make_cfg(cfg)
+    m = meta.as_struct()
+    arr = (ctypes.c_void_p * MOE_N_EVENTS)(*[ev.cuda_event for ev in events])
+    rc = load_library().moe_forward_timed(
+        ctypes.byref(c), _ptr(x), _ptr(Wg), _ptr(bg), _ptr(W1), _ptr(W2), _ptr(u), _ptr(y),
+        _ptr(aux_loss), ctypes.byref(m), _ptr(workspace), workspace.numel(), _stream(stream),
+        arr)
+    if rc:
+        raise MoeError(rc, "moe_forward_timed")
+
+
+def moe_route(cfg, logits, u, meta, aux_loss, workspace, stream=None):
+    """C ABI moe_route: routing, positions, rows and aux from given fp32 logits."""
+    c = make_cfg(cfg)
+    m = meta.as_struct()
+    rc = load_library().moe_route(ctypes.byref(c), _ptr(logits), _ptr(u), ctypes.byref(m),
+                                  _ptr(aux_loss), _ptr(workspace), workspace.numel(),
+                                  _stream(stream))
+    if rc:
+        raise MoeError(rc, "moe_route")
+
+
+def torch_dtype(cfg):
+    import torch
+    return torch.bfloat16 if cfg["dtype"] == 1 else torch.float32
+
+
+def forward(cfg, x, Wg, W1, W2, bg=None, u=None, workspace=None, meta=None, y=None,
+            stream=None):
+    """Allocate outputs (torch.empty) and run moe_forward.  Returns (y, aux_loss, meta)."""
+    import torch
+    dt = torch_dtype(cfg)
+    for name, t in (("x", x), ("Wg", Wg), ("W1", W1), ("W2", W2)):
+        if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} tensor on the GPU")
+    dev = x.device
+    meta = alloc_meta(cfg, dev) if meta is None else meta
+    y = torch.empty_like(x) if y is None else y
+    aux = torch.empty((4,), dtype=torch.float32, device=dev)
+    workspace = alloc_workspace(cfg, dev) if workspace is None else workspace
+    moe_forward(cfg, x, Wg, bg, W1, W2, u, y, aux, meta, workspace, stream)
+    return y, aux[:1], meta

@@ -1,0 +1,347 @@
+// Host side of the C ABI in include/moe.h: argument checks, workspace layout, and the
+// launch sequence of the MoE layer on one stream.
+//
+//   moe_router -> moe_gate (scan, offsets) -> moe_permute -> expert GEMM 1 (+act)
+//   -> expert GEMM 2 -> moe_combine (+aux)
+//
+// Capacity is static, so every grid size is known on the host; the data-dependent parts
+// (kept rows per expert, GEMM tiles) stay on the device and nothing is copied back.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/moe.h"
+#include "moe_internal.h"
+
+namespace {
+
+using moe::kRouteTokens;
+
+struct Layout {
+  // byte offsets inside the workspace
+  size_t buf, h, hsh, osh, active, psum, sel, ahist, abase, ntot, Pg, Cg, gbase, tiles, ntiles;
+  size_t total;
+  // sizes
+  int64_t S, nbg, Rmax, rows_alloc, max_tiles;
+  int esz, BM;
+};
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int check_cfg(const moe_cfg* c) {
+  if (!c) return MOE_EINVAL;
+  if (c->n_tokens < 0 || c->n_groups < 1 || c->d_model < 1 || c->d_ff < 1) return MOE_EINVAL;
+  if (c->n_tokens % c->n_groups != 0) return MOE_EINVAL;
+  if (c->n_experts < 1 || c->n_shared < 0 || c->capacity < 1) return MOE_EINVAL;
+  if (c->top_k < 1 || c->top_k > c->n_experts) return MOE_EINVAL;
+  if (c->act != MOE_ACT_RELU && c->act != MOE_ACT_GELU) return MOE_EINVAL;
+  if (c->gate_norm != MOE_NORM_NONE && c->gate_norm != MOE_NORM_SUM) return MOE_EINVAL;
+  if (c->random_routing != 0 && c->random_routing != 1) return MOE_EINVAL;
+  if (c->random_routing && c->top_k != 2) return MOE_EINVAL;
+  if (c->residual != 0 && c->residual != 1) return MOE_EINVAL;
+  if (c->dtype != MOE_DTYPE_F32 && c->dtype != MOE_DTYPE_BF16) return MOE_EINVAL;
+  if (c->n_experts > moe::kMaxExperts || c->top_k > moe::kMaxTopK) return MOE_EUNSUPPORTED;
+  if (c->dtype == MOE_DTYPE_BF16) {
+    if (c->d_model % 128 || c->d_ff % 128) return MOE_EUNSUPPORTED;
+  } else {
+    if (c->d_model % 64 || c->d_ff % 64) return MOE_EUNSUPPORTED;
+  }
+  return MOE_OK;
+}
+
+int make_layout(const moe_cfg* c, Layout* L) {
+  const int rc = check_cfg(c);
+  if (rc) return rc;
+  const int64_t N = c->n_tokens, G = c->n_groups, M = c->d_model, H = c->d_ff;
+  const int64_t E = c->n_experts, Es = c->n_shared, k = c->top_k, C = c->capacity;
+  L->esz = c->dtype == MOE_DTYPE_BF16 ? 2 : 4;
+  L->BM = moe::gemm_block_m(c->dtype);
+  L->S = N / G;
+  L->nbg = (L->S + kRouteTokens - 1) / kRouteTokens;
+  L->Rmax = std::min<int64_t>(k * N, G * E * std::min<int64_t>(C, L->S));
+  L->rows_alloc = L->Rmax + L->BM;
+  L->max_tiles = L->Rmax / L->BM + E + 1;
+  // 32-bit index limits used by the kernels
+  const int64_t lim = (int64_t{1} << 31) - 1;
+  if (N * k > lim || N * std::max<int64_t>(M, E) > lim || L->rows_alloc * std::max(M, H) > lim ||
+      (E + Es) * M * H > lim || N * Es * H > lim || G * k * E * L->nbg > lim)
+    return MOE_EUNSUPPORTED;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  const size_t esz = static_cast<size_t>(L->esz);
+  L->buf = take(static_cast<size_t>(L->rows_alloc) * M * esz);    // dispatched rows, then o
+  L->h = take(static_cast<size_t>(L->rows_alloc) * H * esz);
+  L->hsh = take(static_cast<size_t>(N) * Es * H * esz);
+  L->osh = take(static_cast<size_t>(N) * (Es ? M : 0) * esz);
+  L->active = take(static_cast<size_t>(N) * k);
+  L->psum = take(static_cast<size_t>(G) * E * L->nbg * 8);
+  L->sel = take(static_cast<size_t>(G) * E * L->nbg * 4);
+  L->ahist = take(static_cast<size_t>(G) * k * E * L->nbg * 4);
+  L->abase = take(static_cast<size_t>(G) * k * E * L->nbg * 4);
+  L->ntot = take(static_cast<size_t>(G) * k * E * 4);
+  L->Pg = take(static_cast<size_t>(G) * E * 8);
+  L->Cg = take(static_cast<size_t>(G) * E * 4);
+  L->gbase = take(static_cast<size_t>(G) * E * 4);
+  L->tiles = take(static_cast<size_t>(L->max_tiles) * sizeof(moe::TileDesc));
+  L->ntiles = take(16);
+  L->total = off;
+  return MOE_OK;
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_meta(const moe_meta* m, bool need_logits) {
+  if (!m) return MOE_EINVAL;
+  const void* ps[] = {m->topk_idx, m->topk_w, m->pos, m->row, m->count, m->offset, m->stats};
+  for (const void* p : ps)
+    if (!p || !aligned16(p)) return MOE_EINVAL;
+  if (need_logits && (!m->logits || !aligned16(m->logits))) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+struct Run {
+  const moe_cfg* c;
+  Layout L;
+  char* ws;
+  hipStream_t s;
+};
+
+int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+void record(void* const* ev, int i, hipStream_t s) {
+  if (ev && ev[i]) hipEventRecord(static_cast<hipEvent_t>(ev[i]), s);
+}
+
+// Router (or routing from given logits) + scan + offsets + positions/scatter.
+int run_routing(const Run& r, const void* x, const void* Wg, const float* bg, const float* u,
+                const float* logits_in, const moe_meta* m, int bm, void* const* ev) {
+  const moe_cfg* c = r.c;
+  const Layout& L = r.L;
+  char* ws = r.ws;
+  moe::RouterArgs ra{};
+  ra.x = x; ra.Wg = Wg; ra.bg = bg; ra.u = u; ra.logits_in = logits_in;
+  ra.logits_out = logits_in ? nullptr : m->logits;
+  ra.topk_idx = m->topk_idx; ra.topk_w = m->topk_w;
+  ra.active = reinterpret_cast<uint8_t*>(ws + L.active);
+  ra.psum = reinterpret_cast<double*>(ws + L.psum);
+  ra.sel = reinterpret_cast<int32_t*>(ws + L.sel);
+  ra.ahist = reinterpret_cast<int32_t*>(ws + L.ahist);
+  ra.N = c->n_tokens; ra.G = c->n_groups; ra.S = static_cast<int>(L.S); ra.M = c->d_model;
+  ra.E = c->n_experts; ra.k = c->top_k; ra.norm = c->gate_norm; ra.rr = c->random_routing;
+  ra.nbg = static_cast<int>(L.nbg); ra.dtype = c->dtype;
+  record(ev, 0, r.s);
+  int rc = status_of(moe::launch_router(ra, r.s));
+  if (rc) return rc;
+  record(ev, 1, r.s);
+
+  moe::ScanArgs sa{};
+  sa.ahist = ra.ahist; sa.psum = ra.psum; sa.sel = ra.sel;
+  sa.abase = reinterpret_cast<int32_t*>(ws + L.abase);
+  sa.count = m->count;
+  sa.ntot = reinterpret_cast<int32_t*>(ws + L.ntot);
+  sa.Pg = reinterpret_cast<double*>(ws + L.Pg);
+  sa.Cg = reinterpret_cast<int32_t*>(ws + L.Cg);
+  sa.G = c->n_groups; sa.E = c->n_experts; sa.k = c->top_k; sa.C = c->capacity;
+  sa.nbg = static_cast<int>(L.nbg);
+  rc = status_of(moe::launch_gate_scan(sa, r.s));
+  if (rc) return rc;
+
+  moe::OffsetsArgs oa{};
+  oa.count = m->count; oa.ntot = sa.ntot; oa.offset = m->offset;
+  oa.gbase = reinterpret_cast<int32_t*>(ws + L.gbase);
+  oa.tiles = reinterpret_cast<moe::TileDesc*>(ws + L.tiles);
+  oa.num_tiles = reinterpret_cast<int32_t*>(ws + L.ntiles);
+  oa.stats = m->stats;
+  oa.G = c->n_groups; oa.E = c->n_experts; oa.k = c->top_k; oa.N = c->n_tokens; oa.BM = bm;
+  rc = status_of(moe::launch_offsets(oa, r.s));
+  if (rc) return rc;
+  record(ev, 2, r.s);
+
+  moe::PermuteArgs pa{};
+  pa.x = x; pa.topk_idx = m->topk_idx; pa.active = ra.active; pa.abase = sa.abase;
+  pa.gbase = oa.gbase; pa.pos = m->pos; pa.row = m->row; pa.topk_w = m->topk_w;
+  pa.stats = m->stats; pa.buf = ws + L.buf;
+  pa.N = c->n_tokens; pa.G = c->n_groups; pa.S = static_cast<int>(L.S); pa.M = c->d_model;
+  pa.E = c->n_experts; pa.k = c->top_k; pa.C = c->capacity; pa.nbg = static_cast<int>(L.nbg);
+  pa.dtype = c->dtype;
+  rc = status_of(moe::launch_permute(pa, r.s));
+  if (rc) return rc;
+  record(ev, 3, r.s);
+  return MOE_OK;
+}
+
+moe::CombineArgs combine_args(const Run& r, const void* x, void* y, float* aux,
+                              const moe_meta* m) {
+  const moe_cfg* c = r.c;
+  moe::CombineArgs ca{};
+  ca.x = x; ca.o = r.ws + r.L.buf; ca.o_sh = c->n_shared ? r.ws + r.L.osh : nullptr;
+  ca.row = m->row; ca.topk_w = m->topk_w; ca.y = y;
+  ca.Pg = reinterpret_cast<const double*>(r.ws + r.L.Pg);
+  ca.Cg = reinterpret_cast<const int32_t*>(r.ws + r.L.Cg);
+  ca.aux = aux;
+  ca.N = c->n_tokens; ca.M = c->d_model; ca.k = c->top_k; ca.residual = c->residual;
+  ca.dtype = c->dtype; ca.G = c->n_groups; ca.E = c->n_experts; ca.S = static_cast<int>(r.L.S);
+  return ca;
+}
+
+int empty_call(const moe_cfg* c, const moe_meta* m, float* aux, hipStream_t s, void* const* ev) {
+  moe::EmptyArgs ea{m->count, m->offset, m->stats, aux, c->n_groups, c->n_experts};
+  for (int i = 0; i < MOE_N_EVENTS - 1; ++i) record(ev, i, s);
+  const int rc = status_of(moe::launch_empty(ea, s));
+  record(ev, MOE_N_EVENTS - 1, s);
+  return rc;
+}
+
+int forward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* bg,
+                 const void* W1, const void* W2, const float* u, void* y, float* aux,
+                 const moe_meta* m, void* workspace, size_t wbytes, void* stream,
+                 void* const* ev) {
+  Run r;
+  r.c = c;
+  int rc = make_layout(c, &r.L);
+  if (rc) return rc;
+  if (!aux || !aligned16(aux) || !workspace || !aligned16(workspace)) return MOE_EINVAL;
+  if (wbytes < r.L.total) return MOE_EWORKSPACE;
+  if (c->n_tokens == 0) {
+    // Nothing to route: only the small outputs are written; token pointers may be NULL.
+    if (!m || !m->count || !m->offset || !m->stats) return MOE_EINVAL;
+    return empty_call(c, m, aux, static_cast<hipStream_t>(stream), ev);
+  }
+  rc = check_meta(m, true);
+  if (rc) return rc;
+  if (c->random_routing && (!u || !aligned16(u))) return MOE_EINVAL;
+  if (bg && !aligned16(bg)) return MOE_EINVAL;
+  const void* req[] = {x, Wg, W1, W2, y};
+  for (const void* p : req)
+    if (!p || !aligned16(p)) return MOE_EINVAL;
+  r.ws = static_cast<char*>(workspace);
+  r.s = static_cast<hipStream_t>(stream);
+
+  const int64_t M = c->d_model, H = c->d_ff, E = c->n_experts, Es = c->n_shared;
+  const int BM = r.L.BM;
+  rc = run_routing(r, x, Wg, bg, u, nullptr, m, BM, ev);
+  if (rc) return rc;
+
+  const Layout& L = r.L;
+  char* ws = r.ws;
+  const moe::TileDesc* tiles = reinterpret_cast<const moe::TileDesc*>(ws + L.tiles);
+  const int32_t* ntiles = reinterpret_cast<const int32_t*>(ws + L.ntiles);
+  const int a_rows = static_cast<int>(L.rows_alloc);
+
+  // GEMM 1: h = act(buf . W1_e^T) for every expert (+ shared: h_sh = act(x . W1_sh^T)).
+  moe::GemmArgs g1{};
+  g1.dtype = c->dtype;
+  g1.p0 = moe::GemmProblem{ws + L.buf, M, W1, M, H * M, M, 0, ws + L.h, H,
+                           static_cast<int>(H), static_cast<int>(M), a_rows, c->act,
+                           tiles, ntiles, static_cast<int>(L.max_tiles), 0};
+  g1.nprob = 1;
+  if (Es) {
+    const char* w1sh = static_cast<const char*>(W1) + E * H * M * L.esz;
+    g1.p1 = moe::GemmProblem{x, M, w1sh, M, 0, M, 0, ws + L.hsh, Es * H,
+                             static_cast<int>(Es * H), static_cast<int>(M), c->n_tokens,
+                             c->act, nullptr, nullptr,
+                             static_cast<int>((c->n_tokens + BM - 1) / BM), c->n_tokens};
+    g1.nprob = 2;
+  }
+  rc = status_of(moe::launch_expert_gemm(g1, r.s));
+  if (rc) return rc;
+  record(ev, 4, r.s);
+
+  // GEMM 2: o = h . W2_e^T into the dispatch buffer (+ shared: o_sh = h_sh . [W2_sh...]^T).
+  moe::GemmArgs g2{};
+  g2.dtype = c->dtype;
+  g2.p0 = moe::GemmProblem{ws + L.h, H, W2, H, M * H, H, 0, ws + L.buf, M,
+                           static_cast<int>(M), static_cast<int>(H), a_rows, -1,
+                           tiles, ntiles, static_cast<int>(L.max_tiles), 0};
+  g2.nprob = 1;
+  if (Es) {
+    const char* w2sh = static_cast<const char*>(W2) + E * M * H * L.esz;
+    g2.p1 = moe::GemmProblem{ws + L.hsh, Es * H, w2sh, H, 0, H, M * H, ws + L.osh, M,
+                             static_cast<int>(M), static_cast<int>(Es * H), c->n_tokens, -1,
+                             nullptr, nullptr,
+                             static_cast<int>((c->n_tokens + BM - 1) / BM), c->n_tokens};
+    g2.nprob = 2;
+  }
+  rc = status_of(moe::launch_expert_gemm(g2, r.s));
+  if (rc) return rc;
+  record(ev, 5, r.s);
+
+  rc = status_of(moe::launch_combine(combine_args(r, x, y, aux, m), r.s));
+  record(ev, 6, r.s);
+  return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_strerror(int code) {
+  switch (code) {
+    case MOE_OK: return "success";
+    case MOE_EINVAL: return "invalid argument (cfg, NULL or misaligned pointer)";
+    case MOE_EWORKSPACE: return "workspace too small";
+    case MOE_EUNSUPPORTED: return "shape outside the kernels' constraints";
+    case MOE_EHIP: return "HIP launch error";
+    default: return "unknown error";
+  }
+}
+
+int moe_workspace_size(const moe_cfg* cfg, size_t* bytes) {
+  if (!bytes) return MOE_EINVAL;
+  Layout L;
+  const int rc = make_layout(cfg, &L);
+  if (rc) return rc;
+  *bytes = L.total;
+  return MOE_OK;
+}
+
+int moe_forward(const moe_cfg* cfg, const void* x, const void* Wg, const float* bg,
+                const void* W1, const void* W2, const float* u, void* y, float* aux_loss,
+                const moe_meta* meta, void* workspace, size_t workspace_bytes, void* stream) {
+  return forward_impl(cfg, x, Wg, bg, W1, W2, u, y, aux_loss, meta, workspace, workspace_bytes,
+                      stream, nullptr);
+}
+
+int moe_forward_timed(const moe_cfg* cfg, const void* x, const void* Wg, const float* bg,
+                      const void* W1, const void* W2, const float* u, void* y,
+                      float* aux_loss, const moe_meta* meta, void* workspace,
+                      size_t workspace_bytes, void* stream, void* const* events) {
+  if (!events) return MOE_EINVAL;
+  return forward_impl(cfg, x, Wg, bg, W1, W2, u, y, aux_loss, meta, workspace, workspace_bytes,
+                      stream, events);
+}
+
+int moe_route(const moe_cfg* cfg, const float* logits, const float* u, const moe_meta* meta,
+              float* aux_loss, void* workspace, size_t workspace_bytes, void* stream) {
+  Run r;
+  r.c = cfg;
+  int rc = make_layout(cfg, &r.L);
+  if (rc) return rc;
+  if (!aux_loss || !aligned16(aux_loss) || !workspace || !aligned16(workspace))
+    return MOE_EINVAL;
+  if (workspace_bytes < r.L.total) return MOE_EWORKSPACE;
+  if (cfg->n_tokens == 0) {
+    if (!meta || !meta->count || !meta->offset || !meta->stats) return MOE_EINVAL;
+    return empty_call(cfg, meta, aux_loss, static_cast<hipStream_t>(stream), nullptr);
+  }
+  rc = check_meta(meta, false);
+  if (rc) return rc;
+  if (cfg->random_routing && (!u || !aligned16(u))) return MOE_EINVAL;
+  if (!logits || !aligned16(logits)) return MOE_EINVAL;
+  r.ws = static_cast<char*>(workspace);
+  r.s = static_cast<hipStream_t>(stream);
+  rc = run_routing(r, nullptr, nullptr, nullptr, u, logits, meta, r.L.BM, nullptr);
+  if (rc) return rc;
+  moe::CombineArgs ca = combine_args(r, nullptr, nullptr, aux_loss, meta);
+  return status_of(moe::launch_aux_only(ca, r.s));
+}
+
+}  // extern "C"

@@ -1,0 +1,119 @@
+// moe_combine: expert outputs back to token order, and the final aux-loss reduction.
+//
+// y_n = sum_j w_{n,j} o[row_{n,j}] + o_sh[n] + x_n (residual), in fp32 with one rounding to
+// the layer dtype, summed in that order.  [GShard] "MoE Transformer": the layer output is
+// the gate-weighted sum of the selected experts' outputs; "Capacity overflow 会跳过 expert
+// computation": a token with no kept slot leaves through the residual, so y_n = x_n
+// bit-exactly (0 + x in fp32 is x).  [Lec16] "共享专家 vs. 路由专家": the shared experts add
+// with weight 1.  Each block gathers 32 tokens; lanes move 16-byte chunks of rows.
+//
+// Block 0 also finishes the aux loss of [GShard] "Top-2 gating 的四个机制 / Auxiliary loss":
+// aux = (1/G) sum_g E/(k S) sum_e m_{g,e} c_{g,e},  m_{g,e} = P_{g,e} / S, from the per-
+// (group, expert) sums of probabilities P and selections c, in fp64 with a fixed-order
+// reduction (deterministic).
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kTok = 32;  // tokens per block
+
+__device__ void aux_final(const CombineArgs& a) {
+  __shared__ double red[4];
+  const int t = threadIdx.x;
+  double s = 0.0;
+  const int n = a.G * a.E;
+  for (int i = t; i < n; i += 256) s += a.Pg[i] * static_cast<double>(a.Cg[i]);
+  s = wave_sum(s);
+  if ((t & 63) == 0) red[t >> 6] = s;
+  __syncthreads();
+  if (t == 0) {
+    const double tot = ((red[0] + red[1]) + red[2]) + red[3];
+    const double S = static_cast<double>(a.S);
+    const double aux = static_cast<double>(a.E) * tot / (static_cast<double>(a.G) * a.k * S * S);
+    *a.aux = static_cast<float>(aux);
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+  __shared__ int rows_s[kTok][kMaxTopK];
+  __shared__ float w_s[kTok][kMaxTopK];
+  const int t = threadIdx.x;
+  const int tok0 = blockIdx.x * kTok;
+  const int nt = min(kTok, a.N - tok0);
+  const int k = a.k;
+  if (blockIdx.x == 0) aux_final(a);
+  for (int i = t; i < nt * k; i += 256) {
+    const int tl = i / k, jj = i - tl * k;
+    const size_t o = static_cast<size_t>(tok0) * k + i;
+    rows_s[tl][jj] = a.row[o];
+    w_s[tl][jj] = a.topk_w[o];
+  }
+  __syncthreads();
+
+  constexpr int EPC = DT == 1 ? 8 : 4;  // elements per 16-byte chunk
+  const int ch = a.M / EPC;
+  const size_t rowbytes = static_cast<size_t>(a.M) * (DT == 1 ? 2 : 4);
+  const char* xb = static_cast<const char*>(a.x);
+  const char* ob = static_cast<const char*>(a.o);
+  const char* sb = static_cast<const char*>(a.o_sh);
+  char* yb = static_cast<char*>(a.y);
+  for (int idx = t; idx < nt * ch; idx += 256) {
+    const int tl = idx / ch, c = idx - tl * ch;
+    const size_t n = static_cast<size_t>(tok0 + tl);
+    float acc[EPC];
+#pragma unroll
+    for (int q = 0; q < EPC; ++q) acc[q] = 0.f;
+    auto add = [&](const char* p, float wgt) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+      if (DT == 1) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] = fmaf(wgt, __uint_as_float(v[q] << 16), acc[2 * q]);
+          acc[2 * q + 1] = fmaf(wgt, __uint_as_float(v[q] & 0xffff0000u), acc[2 * q + 1]);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] = fmaf(wgt, __uint_as_float(v[q]), acc[q]);
+      }
+    };
+    for (int jj = 0; jj < k; ++jj) {
+      const int r = rows_s[tl][jj];
+      if (r >= 0) add(ob + static_cast<size_t>(r) * rowbytes + c * 16, w_s[tl][jj]);
+    }
+    if (sb) add(sb + n * rowbytes + c * 16, 1.0f);
+    if (a.residual) add(xb + n * rowbytes + c * 16, 1.0f);
+    u32x4 out;
+    if (DT == 1) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) out[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) out[q] = __float_as_uint(acc[q]);
+    }
+    *reinterpret_cast<u32x4*>(yb + n * rowbytes + c * 16) = out;
+  }
+}
+
+__global__ __launch_bounds__(256) void aux_only_kernel(CombineArgs a) { aux_final(a); }
+
+}  // namespace
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
+  const int grid = (a.N + kTok - 1) / kTok;
+  if (grid == 0) return hipSuccess;
+  if (a.dtype == 1)
+    hipLaunchKernelGGL(combine_kernel<1>, dim3(grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(combine_kernel<0>, dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_aux_only(const CombineArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(aux_only_kernel, dim3(1), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,295 @@
+// moe_expert_ffn: grouped (ragged) GEMM of the expert FFNs.
+//
+// [GShard] "MoE Transformer": every expert is a two-layer network of the dense FFN's shape,
+// here act(x W1_e^T) W2_e^T.  The dispatched rows sit expert-major in one compact buffer,
+// so each expert's rows form one contiguous GEMM; a tile list built on the device
+// (offsets_kernel) cuts them into BM-row tiles, and one launch covers every expert, with
+// no padding rows computed beyond the last partial tile of each expert and no host sync.
+// A second, dense problem (the shared experts, fused into one FFN whose hidden layer is the
+// concatenation of theirs, [11-868 #12] "機制：Transformer 各部分怎麼切") can ride in the
+// same launch.
+//
+// bf16 kernel (gfx950):
+//   * block tile BM x BN x 64, 256 threads = 2 x 2 waves, each wave (BM/2) x (BN/2) built
+//     from v_mfma_f32_32x32x16_bf16 tiles with fp32 accumulators;
+//   * A (token rows) and B (weight rows: W1 is [H, M], W2 is [M, H], so both operands are
+//     K-contiguous) staged through LDS in two buffers of 128-byte rows whose 16-byte
+//     columns are XOR-swizzled by (row & 7), so the fragment reads of 8 consecutive rows hit
+//     distinct banks; the next K chunk is fetched into registers while the current one is
+//     multiplied;
+//   * the weight fragment is the MFMA's first operand, so every lane ends up owning one
+//     token row and runs of 4 consecutive output features: the epilogue applies the
+//     activation, rounds to bf16 and writes 8 bytes per run, masking rows past the tile;
+//   * tiles are numbered so that each XCD (blocks b with equal b % 8) receives a contiguous
+//     range, and inside a range 8 m-tiles sweep the n-tiles together (L2 reuse of the
+//     weight tile across an expert's row tiles).
+// fp32 kernel: a 64 x 64 x 16 FMA tile for the fp32 layers (the fp32 MFMA and fp32 vector
+// peaks are equal on this chip).
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+
+struct Job {
+  const char* A;   // first row of the tile (bytes)
+  int64_t lda;     // bytes
+  const char* B;   // first row of the n-tile of expert e (bytes)
+  int64_t ldb;     // bytes
+  int64_t kseg;    // elements
+  int64_t segb;    // bytes between K segments of B
+  char* C;         // first row, first column of the tile (bytes)
+  int64_t ldc;     // bytes
+  int K;
+  int nrows;       // valid rows of the tile
+  int rows_left;   // rows readable from the tile's first row (clamp)
+  int act;
+};
+
+template <int BM, int BN, int ESZ>
+__device__ __forceinline__ bool decode_tile(const GemmArgs& g, Job& j) {
+  const int nt0 = g.p0.N / BN;
+  const int mt0 = g.p0.tiles ? *g.p0.num_tiles : g.p0.max_tiles;
+  const int tot0 = mt0 * nt0;
+  const int nt1 = g.nprob > 1 ? g.p1.N / BN : 0;
+  const int mt1 = g.nprob > 1 ? g.p1.max_tiles : 0;
+  const int total = tot0 + mt1 * nt1;
+  const int bid = blockIdx.x;
+  if (bid >= total) return false;
+  // Blocks are dispatched round-robin over the 8 XCDs (block b -> XCD b % 8); give every
+  // XCD a contiguous range of tiles so neighbouring tiles share its L2.
+  const int xcd = bid & 7, loc = bid >> 3, q = total >> 3, r = total & 7;
+  const int pid = xcd * q + min(xcd, r) + loc;
+  const bool second = pid >= tot0;
+  const int lp = second ? pid - tot0 : pid;
+  const int mts = second ? mt1 : mt0;
+  const int nts = second ? nt1 : nt0;
+  constexpr int GM = 8;
+  const int per_group = GM * nts;
+  const int grp = lp / per_group;
+  const int first = grp * GM;
+  const int gsz = min(mts - first, GM);
+  const int in = lp - grp * per_group;
+  const int mt = first + in % gsz;
+  const int nt = in / gsz;
+
+  const GemmProblem& P = second ? g.p1 : g.p0;
+  int e, row0, nrows;
+  if (P.tiles) {
+    const TileDesc d = P.tiles[mt];
+    e = d.expert; row0 = d.row0; nrows = d.nrows;
+  } else {
+    e = 0; row0 = mt * BM; nrows = min(BM, P.dense_rows - row0);
+  }
+  j.lda = P.lda * ESZ;
+  j.A = static_cast<const char*>(P.A) + static_cast<int64_t>(row0) * j.lda;
+  j.ldb = P.ldb * ESZ;
+  j.B = static_cast<const char*>(P.B) + (static_cast<int64_t>(e) * P.b_stride) * ESZ +
+        static_cast<int64_t>(nt) * BN * j.ldb;
+  j.kseg = P.kseg;
+  j.segb = P.seg_stride * ESZ;
+  j.ldc = P.ldc * ESZ;
+  j.C = static_cast<char*>(P.C) + static_cast<int64_t>(row0) * j.ldc +
+        static_cast<int64_t>(nt) * BN * ESZ;
+  j.K = P.K;
+  j.nrows = nrows;
+  j.rows_left = P.a_rows - row0;
+  j.act = P.act;
+  return true;
+}
+
+// Byte offset of K element kk inside a (possibly segmented) B row.
+__device__ __forceinline__ int64_t bseg_offset(const Job& j, int kk, int esz) {
+  const int64_t seg = kk / j.kseg;
+  return seg * j.segb + (kk - seg * j.kseg) * esz;
+}
+
+template <int BM, int BN>
+__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g) {
+  constexpr int WTM = BM / 2, WTN = BN / 2;   // wave tile (2 x 2 waves)
+  constexpr int TM = WTM / 32, TN = WTN / 32; // 32x32 MFMA tiles per wave
+  constexpr int ACH = BM / 32, BCH = BN / 32; // 16-byte chunks per thread per K chunk
+  constexpr int ROW = 128;                    // bytes of one LDS row (64 bf16 of K)
+  constexpr int STAGE = (BM + BN) * ROW;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
+
+  Job j;
+  if (!decode_tile<BM, BN, 2>(g, j)) return;
+
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  const int c = t & 7;                          // 16-byte column this thread loads
+  const int rsub = t >> 3;                      // row within each 32-row slab
+  const int scol = (c ^ (rsub & 7)) * 16;       // swizzled LDS column (rows r = rsub + 32 i)
+
+  const char* aptr[ACH];
+#pragma unroll
+  for (int i = 0; i < ACH; ++i) {
+    int r = rsub + 32 * i;
+    r = r < j.rows_left ? r : j.rows_left - 1;
+    aptr[i] = j.A + static_cast<int64_t>(r) * j.lda + c * 16;
+  }
+  const char* bptr = j.B + static_cast<int64_t>(rsub) * j.ldb + c * 16;
+
+  f32x16 acc[TN][TM];
+#pragma unroll
+  for (int jn = 0; jn < TN; ++jn)
+#pragma unroll
+    for (int im = 0; im < TM; ++im) acc[jn][im] = f32x16{};
+
+  u32x4 ra[ACH], rb[BCH];
+  auto gload = [&](int kt) {
+    const int64_t ka = static_cast<int64_t>(kt) * ROW;
+    const int64_t kb = bseg_offset(j, kt * 64, 2);
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) ra[i] = *reinterpret_cast<const u32x4*>(aptr[i] + ka);
+#pragma unroll
+    for (int i = 0; i < BCH; ++i)
+      rb[i] = *reinterpret_cast<const u32x4*>(bptr + static_cast<int64_t>(32 * i) * j.ldb + kb);
+  };
+  auto sstore = [&](int st) {
+    unsigned char* As = smem + st * STAGE;
+    unsigned char* Bs = As + BM * ROW;
+#pragma unroll
+    for (int i = 0; i < ACH; ++i)
+      *reinterpret_cast<u32x4*>(As + (rsub + 32 * i) * ROW + scol) = ra[i];
+#pragma unroll
+    for (int i = 0; i < BCH; ++i)
+      *reinterpret_cast<u32x4*>(Bs + (rsub + 32 * i) * ROW + scol) = rb[i];
+  };
+
+  const int KT = j.K / 64;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  const int arow = wm * WTM + (lane & 31);
+  const int brow = wn * WTN + (lane & 31);
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < KT) gload(kt + 1);
+    const unsigned char* As = smem + cur * STAGE;
+    const unsigned char* Bs = As + BM * ROW;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int phys = (((2 * s) + (lane >> 5)) ^ (lane & 7)) * 16;
+      bf16x8 af[TM], bfr[TN];
+#pragma unroll
+      for (int im = 0; im < TM; ++im)
+        af[im] = *reinterpret_cast<const bf16x8*>(As + (arow + 32 * im) * ROW + phys);
+#pragma unroll
+      for (int jn = 0; jn < TN; ++jn)
+        bfr[jn] = *reinterpret_cast<const bf16x8*>(Bs + (brow + 32 * jn) * ROW + phys);
+#pragma unroll
+      for (int jn = 0; jn < TN; ++jn)
+#pragma unroll
+        for (int im = 0; im < TM; ++im)
+          acc[jn][im] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[jn], af[im], acc[jn][im], 0, 0, 0);
+    }
+    if (kt + 1 < KT) sstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // D[feature][token]: lane owns token (lane & 31) of each token tile and features
+  // 8 (r / 4) + 4 (lane / 32) + (r % 4) of each feature tile.
+  const int act = j.act;
+#pragma unroll
+  for (int im = 0; im < TM; ++im) {
+    const int tok = wm * WTM + 32 * im + (lane & 31);
+    if (tok < j.nrows) {
+      char* crow = j.C + static_cast<int64_t>(tok) * j.ldc;
+#pragma unroll
+      for (int jn = 0; jn < TN; ++jn) {
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const int f = wn * WTN + 32 * jn + 8 * qd + 4 * (lane >> 5);
+          const float v0 = apply_act(acc[jn][im][4 * qd + 0], act);
+          const float v1 = apply_act(acc[jn][im][4 * qd + 1], act);
+          const float v2 = apply_act(acc[jn][im][4 * qd + 2], act);
+          const float v3 = apply_act(acc[jn][im][4 * qd + 3], act);
+          u32x2 pk;
+          pk[0] = pack_bf16x2(v0, v1);
+          pk[1] = pack_bf16x2(v2, v3);
+          *reinterpret_cast<u32x2*>(crow + f * 2) = pk;
+        }
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs g) {
+  constexpr int BM = 64, BN = 64, BK = 16, LDSW = 68;
+  __shared__ __attribute__((aligned(16))) float As[BK][LDSW];
+  __shared__ __attribute__((aligned(16))) float Bs[BK][LDSW];
+  Job j;
+  if (!decode_tile<BM, BN, 4>(g, j)) return;
+  const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
+  const int lr = t >> 2, lc = (t & 3) * 4;
+  const int ar = lr < j.rows_left ? lr : j.rows_left - 1;
+  const char* ap = j.A + static_cast<int64_t>(ar) * j.lda + lc * 4;
+  const char* bp = j.B + static_cast<int64_t>(lr) * j.ldb + lc * 4;
+  float acc[4][4] = {};
+  for (int kt = 0; kt < j.K / BK; ++kt) {
+    const f32x4 av = *reinterpret_cast<const f32x4*>(ap + static_cast<int64_t>(kt) * BK * 4);
+    const f32x4 bv = *reinterpret_cast<const f32x4*>(bp + bseg_offset(j, kt * BK, 4));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      As[lc + q][lr] = av[q];
+      Bs[lc + q][lr] = bv[q];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < BK; ++kk) {
+      const f32x4 a4 = *reinterpret_cast<const f32x4*>(&As[kk][ty * 4]);
+      const f32x4 b4 = *reinterpret_cast<const f32x4*>(&Bs[kk][tx * 4]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) acc[i][jj] = fmaf(a4[i], b4[jj], acc[i][jj]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = ty * 4 + i;
+    if (r < j.nrows) {
+      f32x4 o;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) o[jj] = apply_act(acc[i][jj], j.act);
+      *reinterpret_cast<f32x4*>(j.C + static_cast<int64_t>(r) * j.ldc + tx * 16) = o;
+    }
+  }
+}
+
+int grid_of(const GemmArgs& a, int BN) {
+  int64_t total = static_cast<int64_t>(a.p0.max_tiles) * (a.p0.N / BN);
+  if (a.nprob > 1) total += static_cast<int64_t>(a.p1.max_tiles) * (a.p1.N / BN);
+  return static_cast<int>(total);
+}
+
+}  // namespace
+
+int gemm_block_m(int dtype) { return dtype == 1 ? 256 : 64; }
+
+int gemm_block_n(int dtype, int n0, int n1) {
+  if (dtype != 1) return 64;
+  return (n0 % 256 == 0 && n1 % 256 == 0) ? 256 : 128;
+}
+
+hipError_t launch_expert_gemm(const GemmArgs& a, hipStream_t s) {
+  const int BN = gemm_block_n(a.dtype, a.p0.N, a.nprob > 1 ? a.p1.N : a.p0.N);
+  const int grid = grid_of(a, BN);
+  if (grid == 0) return hipSuccess;
+  if (a.dtype == 1) {
+    if (BN == 256)
+      hipLaunchKernelGGL((gemm_bf16_kernel<256, 256>), dim3(grid), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_bf16_kernel<256, 128>), dim3(grid), dim3(kThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(gemm_f32_kernel, dim3(grid), dim3(kThreads), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

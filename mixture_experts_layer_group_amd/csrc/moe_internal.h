@@ -1,0 +1,130 @@
+// Kernel argument blocks and launchers of the MoE layer (host <-> kernel interface).
+// Nothing here is part of the public C ABI (include/moe.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kRouteTokens = 64;  // tokens per router / dispatch block (one wave of lanes)
+constexpr int kMaxExperts = 256;
+constexpr int kMaxTopK = 8;
+
+// Router GEMM + softmax + top-k + gates + random routing + per-block histograms.
+// Blocks never straddle a group: block b covers tokens [g*S + bi*64, min(+64, (g+1)*S)),
+// g = b / nbg, bi = b % nbg.
+struct RouterArgs {
+  const void* x;          // [N, M] T          (unused when logits_in != nullptr)
+  const void* Wg;         // [E, M] T
+  const float* bg;        // [E] or nullptr
+  const float* u;         // [N] or nullptr
+  const float* logits_in; // [N, E]: route from these logits instead of running the GEMM
+  float* logits_out;      // [N, E] or nullptr
+  int32_t* topk_idx;      // [N, k]
+  float* topk_w;          // [N, k]  pre-drop weights (zeroed later for dropped slots)
+  uint8_t* active;        // [N, k]  slot dispatched (random routing), before capacity
+  double* psum;           // [G][E][nbg]  sum of softmax probabilities of the block's tokens
+  int32_t* sel;           // [G][E][nbg]  top-k selections of the block's tokens
+  int32_t* ahist;         // [G][k][E][nbg] active slots per rank
+  int N, G, S, M, E, k, norm, rr, nbg, dtype;
+};
+
+// Per (group, expert): exclusive scans over router blocks -> block bases of the capacity
+// positions, kept counts, active totals, and the aux partial sums.
+struct ScanArgs {
+  const int32_t* ahist;   // [G][k][E][nbg]
+  const double* psum;     // [G][E][nbg]
+  const int32_t* sel;     // [G][E][nbg]
+  int32_t* abase;         // [G][k][E][nbg]  base_j(e) + active slots in earlier blocks
+  int32_t* count;         // [G, E]  kept slots (meta)
+  int32_t* ntot;          // [G][k][E] active slots per rank
+  double* Pg;             // [G][E]  sum_n p[n, e] over the group
+  int32_t* Cg;            // [G][E]  selections over the group
+  int G, E, k, C, nbg;
+};
+
+struct TileDesc {         // one BM-row tile of one expert in the compact buffer
+  int32_t expert, row0, nrows, pad;
+};
+
+// One block: offsets, per-(group, expert) row bases, GEMM tile lists, stats.
+struct OffsetsArgs {
+  const int32_t* count;   // [G, E]
+  const int32_t* ntot;    // [G][k][E]
+  int32_t* offset;        // [E+1] (meta)
+  int32_t* gbase;         // [G, E] first row of (g, e) in the compact buffer
+  TileDesc* tiles;        // [max tiles]
+  int32_t* num_tiles;     // [1]
+  int32_t* stats;         // [4] (meta): R, dropped slots, (fully dropped: zeroed here), rr skips
+  int G, E, k, N, BM;
+};
+
+// Capacity positions, dispatch rows, dropped-weight zeroing and the row scatter of x.
+struct PermuteArgs {
+  const void* x;          // [N, M] T (nullptr: positions only)
+  const int32_t* topk_idx;
+  const uint8_t* active;
+  const int32_t* abase;
+  const int32_t* gbase;
+  int32_t* pos;           // [N, k] (meta)
+  int32_t* row;           // [N, k] (meta)
+  float* topk_w;          // [N, k] (meta): zeroed where the slot is not kept
+  int32_t* stats;         // stats[2] += fully dropped tokens of the block
+  void* buf;              // [R, M] T compact expert-major rows
+  int N, G, S, M, E, k, C, nbg, dtype;
+};
+
+// One GEMM problem of the expert FFN: C[rows, N] = act(A[rows, K] . B_e[N, K]^T).
+// B_e = B + e * b_stride; the K axis of B may be split into segments of kseg elements that
+// sit seg_stride elements apart (the shared experts' W2 blocks).
+struct GemmProblem {
+  const void* A; int64_t lda;
+  const void* B; int64_t ldb; int64_t b_stride; int64_t kseg; int64_t seg_stride;
+  void* C; int64_t ldc;
+  int N, K;
+  int a_rows;             // rows readable through A (loads clamp to a_rows - 1)
+  int act;                // -1 none, 0 ReLU, 1 GELU
+  const TileDesc* tiles;  // routed: device tile list (nullptr: dense problem)
+  const int32_t* num_tiles;
+  int max_tiles;          // routed: grid bound on the tile count; dense: ceil(rows / BM)
+  int dense_rows;         // dense problem: number of rows
+};
+
+struct GemmArgs {
+  GemmProblem p0, p1;
+  int nprob;              // 1 or 2 (p1 is always dense)
+  int dtype;
+};
+
+// Gather + gate-weighted sum + shared experts + residual, and (block 0) the final aux.
+struct CombineArgs {
+  const void* x;          // [N, M] T
+  const void* o;          // [R, M] T expert outputs in compact order
+  const void* o_sh;       // [N, M] T shared-expert sum or nullptr
+  const int32_t* row;     // [N, k]
+  const float* topk_w;    // [N, k]
+  void* y;                // [N, M] T
+  const double* Pg;       // [G][E]
+  const int32_t* Cg;      // [G][E]
+  float* aux;             // scalar
+  int N, M, k, residual, dtype, G, E, S;
+};
+
+struct EmptyArgs {         // N == 0: zero the small outputs
+  int32_t* count; int32_t* offset; int32_t* stats; float* aux; int G, E;
+};
+
+int gemm_block_m(int dtype);                           // BM of the expert GEMM tiles
+int gemm_block_n(int dtype, int n0, int n1);           // BN for problems with widths n0, n1
+
+hipError_t launch_router(const RouterArgs& a, hipStream_t s);
+hipError_t launch_gate_scan(const ScanArgs& a, hipStream_t s);
+hipError_t launch_offsets(const OffsetsArgs& a, hipStream_t s);
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+hipError_t launch_expert_gemm(const GemmArgs& a, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+hipError_t launch_aux_only(const CombineArgs& a, hipStream_t s);
+hipError_t launch_empty(const EmptyArgs& a, hipStream_t s);
+
+}  // namespace moe
