@@ -106,7 +106,28 @@ __device__ __forceinline__ int64_t bseg_offset(const Job& j, int kk, int esz) {
   return seg * j.segb + (kk - seg * j.kseg) * esz;
 }
 
-template <int BM, int BN>
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer resource over [base, base + bytes): loads past the end return 0 and stores past
+// it are dropped by the hardware.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int32_t n = bytes > 0x7fffffff ? 0x7fffffff : static_cast<int32_t>(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ u32x4 bload(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+
+template <int ACT>
+__device__ __forceinline__ float act_fn(float z) {
+  if (ACT == 0) return fmaxf(z, 0.0f);
+  if (ACT == 1) return gelu_erf(z);
+  return z;
+}
+
+template <int BM, int BN, int ACT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int WTM = BM / 2, WTN = BN / 2;   // wave tile (2 x 2 waves)
   constexpr int TM = WTM / 32, TN = WTN / 32; // 32x32 MFMA tiles per wave
@@ -124,14 +145,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g) {
   const int rsub = t >> 3;                      // row within each 32-row slab
   const int scol = (c ^ (rsub & 7)) * 16;       // swizzled LDS column (rows r = rsub + 32 i)
 
-  const char* aptr[ACH];
-#pragma unroll
-  for (int i = 0; i < ACH; ++i) {
-    int r = rsub + 32 * i;
-    r = r < j.rows_left ? r : j.rows_left - 1;
-    aptr[i] = j.A + static_cast<int64_t>(r) * j.lda + c * 16;
-  }
-  const char* bptr = j.B + static_cast<int64_t>(rsub) * j.ldb + c * 16;
+  // A: only the tile's valid rows are addressable; the rest of the BM rows load as zeros.
+  const uint32_t lda = static_cast<uint32_t>(j.lda), ldb = static_cast<uint32_t>(j.ldb);
+  const rsrc_t ra_rs = make_rsrc(j.A, static_cast<int64_t>(j.nrows) * j.lda);
+  const int nseg = (j.K + static_cast<int>(j.kseg) - 1) / static_cast<int>(j.kseg);
+  const rsrc_t rb_rs = make_rsrc(j.B, (nseg - 1) * j.segb + static_cast<int64_t>(BN) * j.ldb);
+  const uint32_t avoff = rsub * lda + c * 16;
+  const uint32_t bvoff = rsub * ldb + c * 16;
 
   f32x16 acc[TN][TM];
 #pragma unroll
@@ -139,41 +159,49 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
     for (int im = 0; im < TM; ++im) acc[jn][im] = f32x16{};
 
-  u32x4 ra[ACH], rb[BCH];
-  auto gload = [&](int kt) {
-    const int64_t ka = static_cast<int64_t>(kt) * ROW;
-    const int64_t kb = bseg_offset(j, kt * 64, 2);
+  // Two register sets of prefetched K chunks: while chunk kt is multiplied out of LDS,
+  // chunk kt+1 sits in one set (loaded one iteration earlier) and chunk kt+2 is in flight
+  // into the other, so a global load has two chunks of MFMA work to arrive.
+  u32x4 pa0[ACH], pb0[BCH], pa1[ACH], pb1[BCH];
+  auto gload = [&](u32x4 (&pa)[ACH], u32x4 (&pb)[BCH], uint32_t ka, uint32_t kb) {
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) ra[i] = *reinterpret_cast<const u32x4*>(aptr[i] + ka);
+    for (int i = 0; i < ACH; ++i) pa[i] = bload(ra_rs, avoff, ka + i * 32 * lda);
 #pragma unroll
-    for (int i = 0; i < BCH; ++i)
-      rb[i] = *reinterpret_cast<const u32x4*>(bptr + static_cast<int64_t>(32 * i) * j.ldb + kb);
+    for (int i = 0; i < BCH; ++i) pb[i] = bload(rb_rs, bvoff, kb + i * 32 * ldb);
   };
-  auto sstore = [&](int st) {
+  auto sstore = [&](const u32x4 (&pa)[ACH], const u32x4 (&pb)[BCH], int st) {
     unsigned char* As = smem + st * STAGE;
     unsigned char* Bs = As + BM * ROW;
 #pragma unroll
     for (int i = 0; i < ACH; ++i)
-      *reinterpret_cast<u32x4*>(As + (rsub + 32 * i) * ROW + scol) = ra[i];
+      *reinterpret_cast<u32x4*>(As + (rsub + 32 * i) * ROW + scol) = pa[i];
 #pragma unroll
     for (int i = 0; i < BCH; ++i)
-      *reinterpret_cast<u32x4*>(Bs + (rsub + 32 * i) * ROW + scol) = rb[i];
+      *reinterpret_cast<u32x4*>(Bs + (rsub + 32 * i) * ROW + scol) = pb[i];
   };
 
-  const int KT = j.K / 64;
-  gload(0);
-  sstore(0);
-  __syncthreads();
+  // K position of B inside its segment (elements) and the segment's byte offset.
+  int kin = 0;
+  uint32_t segoff = 0;
+  const int kseg = static_cast<int>(j.kseg);
+  const uint32_t segb = static_cast<uint32_t>(j.segb);
+  auto next_kb = [&]() -> uint32_t {
+    kin += 64;
+    const bool wrap = kin == kseg;
+    kin = wrap ? 0 : kin;
+    segoff += wrap ? segb : 0u;
+    return segoff + static_cast<uint32_t>(kin) * 2;
+  };
+
   const int arow = wm * WTM + (lane & 31);
   const int brow = wn * WTN + (lane & 31);
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
-    const unsigned char* As = smem + cur * STAGE;
+  const int sw = lane & 7;
+  auto compute = [&](int st) {
+    const unsigned char* As = smem + st * STAGE;
     const unsigned char* Bs = As + BM * ROW;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int phys = (((2 * s) + (lane >> 5)) ^ (lane & 7)) * 16;
+      const int phys = (((2 * s) + (lane >> 5)) ^ sw) * 16;
       bf16x8 af[TM], bfr[TN];
 #pragma unroll
       for (int im = 0; im < TM; ++im)
@@ -185,15 +213,38 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g) {
       for (int jn = 0; jn < TN; ++jn)
 #pragma unroll
         for (int im = 0; im < TM; ++im)
-          acc[jn][im] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[jn], af[im], acc[jn][im], 0, 0, 0);
+          acc[jn][im] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[jn], af[im], acc[jn][im],
+                                                                0, 0, 0);
     }
-    if (kt + 1 < KT) sstore(cur ^ 1);
+    // (scheduling left to the compiler)
+  };
+
+  // K is a multiple of 128 here, so the chunk count KT is even: the loop runs chunk pairs
+  // with no control flow inside, and the last pair is peeled.
+  const int KT = j.K / 64;
+  gload(pa0, pb0, 0, 0);
+  gload(pa1, pb1, ROW, next_kb());
+  sstore(pa0, pb0, 0);
+  __syncthreads();
+  for (int kt = 0; kt + 2 < KT; kt += 2) {
+    // stage 0 holds chunk kt, pa1/pb1 hold chunk kt+1; pa0/pb0 receive chunk kt+2
+    gload(pa0, pb0, static_cast<uint32_t>(kt + 2) * ROW, next_kb());
+    compute(0);
+    sstore(pa1, pb1, 1);
+    __syncthreads();
+    // stage 1 holds chunk kt+1, pa0/pb0 hold chunk kt+2; pa1/pb1 receive chunk kt+3
+    gload(pa1, pb1, static_cast<uint32_t>(kt + 3) * ROW, next_kb());
+    compute(1);
+    sstore(pa0, pb0, 0);
     __syncthreads();
   }
+  compute(0);
+  sstore(pa1, pb1, 1);
+  __syncthreads();
+  compute(1);
 
   // D[feature][token]: lane owns token (lane & 31) of each token tile and features
   // 8 (r / 4) + 4 (lane / 32) + (r % 4) of each feature tile.
-  const int act = j.act;
 #pragma unroll
   for (int im = 0; im < TM; ++im) {
     const int tok = wm * WTM + 32 * im + (lane & 31);
@@ -204,13 +255,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
           const int f = wn * WTN + 32 * jn + 8 * qd + 4 * (lane >> 5);
-          const float v0 = apply_act(acc[jn][im][4 * qd + 0], act);
-          const float v1 = apply_act(acc[jn][im][4 * qd + 1], act);
-          const float v2 = apply_act(acc[jn][im][4 * qd + 2], act);
-          const float v3 = apply_act(acc[jn][im][4 * qd + 3], act);
           u32x2 pk;
-          pk[0] = pack_bf16x2(v0, v1);
-          pk[1] = pack_bf16x2(v2, v3);
+          pk[0] = pack_bf16x2(act_fn<ACT>(acc[jn][im][4 * qd + 0]),
+                              act_fn<ACT>(acc[jn][im][4 * qd + 1]));
+          pk[1] = pack_bf16x2(act_fn<ACT>(acc[jn][im][4 * qd + 2]),
+                              act_fn<ACT>(acc[jn][im][4 * qd + 3]));
           *reinterpret_cast<u32x2*>(crow + f * 2) = pk;
         }
       }
@@ -281,11 +330,20 @@ hipError_t launch_expert_gemm(const GemmArgs& a, hipStream_t s) {
   const int BN = gemm_block_n(a.dtype, a.p0.N, a.nprob > 1 ? a.p1.N : a.p0.N);
   const int grid = grid_of(a, BN);
   if (grid == 0) return hipSuccess;
+  const int act = a.p0.act;  // both problems of one launch share the activation
   if (a.dtype == 1) {
-    if (BN == 256)
-      hipLaunchKernelGGL((gemm_bf16_kernel<256, 256>), dim3(grid), dim3(kThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL((gemm_bf16_kernel<256, 128>), dim3(grid), dim3(kThreads), 0, s, a);
+#define MOE_GEMM_LAUNCH(BNV, ACTV) \
+  hipLaunchKernelGGL((gemm_bf16_kernel<256, BNV, ACTV>), dim3(grid), dim3(kThreads), 0, s, a)
+    if (BN == 256) {
+      if (act == 0) MOE_GEMM_LAUNCH(256, 0);
+      else if (act == 1) MOE_GEMM_LAUNCH(256, 1);
+      else MOE_GEMM_LAUNCH(256, 2);
+    } else {
+      if (act == 0) MOE_GEMM_LAUNCH(128, 0);
+      else if (act == 1) MOE_GEMM_LAUNCH(128, 1);
+      else MOE_GEMM_LAUNCH(128, 2);
+    }
+#undef MOE_GEMM_LAUNCH
   } else {
     hipLaunchKernelGGL(gemm_f32_kernel, dim3(grid), dim3(kThreads), 0, s, a);
   }
