@@ -120,11 +120,47 @@ __device__ __forceinline__ u32x4 bload(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
 }
 
+// XOR pattern of the 16-byte columns of LDS row r (128-byte rows).  Among any 8 aligned
+// consecutive rows it takes 8 distinct values, and among any 16 aligned consecutive rows the
+// rows of equal parity take 8 distinct values, so a ds_read_b128 of one column from 16
+// consecutive rows touches every bank once whether the LDS serves 8 lanes per cycle from
+// 32 banks or 16 lanes from 64 banks.
+__device__ __forceinline__ int lds_swz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+
 template <int ACT>
 __device__ __forceinline__ float act_fn(float z) {
   if (ACT == 0) return fmaxf(z, 0.0f);
   if (ACT == 1) return gelu_erf(z);
   return z;
+}
+
+// Instruction order of one K chunk (a scheduling region between two barriers), given to
+// the compiler as groups: the first k-step's fragment reads, then for every MFMA one other
+// memory operation -- the next k-step's fragment reads first, global loads of the chunk
+// after next during k-steps 0-1, LDS writes of the next chunk (whose loads are the oldest
+// in flight) during k-steps 2-3.  MF = MFMAs per k-step, DR = fragment reads per k-step,
+// NL = global loads, NW = LDS writes.
+template <int MF, int DR, int NL, int NW>
+__device__ __forceinline__ void sched_chunk() {
+#pragma unroll
+  for (int i = 0; i < DR; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  int loads = NL, writes = NW;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+#pragma unroll
+    for (int m = 0; m < MF; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (s < 3 && m < DR) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      } else if (s < 2 && loads > 0) {
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        --loads;
+      } else if (s >= 2 && writes > 0) {
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+        --writes;
+      }
+    }
+  }
 }
 
 template <int BM, int BN, int ACT>
@@ -143,7 +179,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g) {
   const int wm = w >> 1, wn = w & 1;
   const int c = t & 7;                          // 16-byte column this thread loads
   const int rsub = t >> 3;                      // row within each 32-row slab
-  const int scol = (c ^ (rsub & 7)) * 16;       // swizzled LDS column (rows r = rsub + 32 i)
+  const int scol = (c ^ lds_swz(rsub)) * 16;    // swizzled LDS column (rows r = rsub + 32 i)
 
   // A: only the tile's valid rows are addressable; the rest of the BM rows load as zeros.
   const uint32_t lda = static_cast<uint32_t>(j.lda), ldb = static_cast<uint32_t>(j.ldb);
@@ -195,53 +231,69 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g) {
 
   const int arow = wm * WTM + (lane & 31);
   const int brow = wn * WTN + (lane & 31);
-  const int sw = lane & 7;
-  auto compute = [&](int st) {
+  const int sw = lds_swz(lane);
+  // One K chunk out of LDS stage st (4 MFMA k-steps), with the next step's fragments read
+  // while the current step multiplies, and (if X is given) the prefetched chunk in X written
+  // into the other stage a quarter per k-step, so the LDS writes overlap the MFMAs.
+  auto compute = [&](int st, const u32x4* xa, const u32x4* xb) {
     const unsigned char* As = smem + st * STAGE;
     const unsigned char* Bs = As + BM * ROW;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    unsigned char* Ao = smem + (st ^ 1) * STAGE;
+    unsigned char* Bo = Ao + BM * ROW;
+    bf16x8 af[2][TM], bfr[2][TN];
+    auto fread = [&](int s, int b) {
       const int phys = (((2 * s) + (lane >> 5)) ^ sw) * 16;
-      bf16x8 af[TM], bfr[TN];
 #pragma unroll
       for (int im = 0; im < TM; ++im)
-        af[im] = *reinterpret_cast<const bf16x8*>(As + (arow + 32 * im) * ROW + phys);
+        af[b][im] = *reinterpret_cast<const bf16x8*>(As + (arow + 32 * im) * ROW + phys);
 #pragma unroll
       for (int jn = 0; jn < TN; ++jn)
-        bfr[jn] = *reinterpret_cast<const bf16x8*>(Bs + (brow + 32 * jn) * ROW + phys);
+        bfr[b][jn] = *reinterpret_cast<const bf16x8*>(Bs + (brow + 32 * jn) * ROW + phys);
+    };
+    fread(0, 0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (s < 3) fread(s + 1, (s + 1) & 1);
 #pragma unroll
       for (int jn = 0; jn < TN; ++jn)
 #pragma unroll
         for (int im = 0; im < TM; ++im)
-          acc[jn][im] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[jn], af[im], acc[jn][im],
-                                                                0, 0, 0);
+          acc[jn][im] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[s & 1][jn], af[s & 1][im],
+                                                                acc[jn][im], 0, 0, 0);
+      if (xa) {
+#pragma unroll
+        for (int i = s * ACH / 4; i < (s + 1) * ACH / 4; ++i)
+          *reinterpret_cast<u32x4*>(Ao + (rsub + 32 * i) * ROW + scol) = xa[i];
+#pragma unroll
+        for (int i = s * BCH / 4; i < (s + 1) * BCH / 4; ++i)
+          *reinterpret_cast<u32x4*>(Bo + (rsub + 32 * i) * ROW + scol) = xb[i];
+      }
     }
-    // (scheduling left to the compiler)
   };
 
   // K is a multiple of 128 here, so the chunk count KT is even: the loop runs chunk pairs
-  // with no control flow inside, and the last pair is peeled.
+  // with no control flow inside, and the last pair is peeled.  Invariant at the top of a
+  // half-iteration: the current stage holds chunk c, one register set holds chunk c+1
+  // (in flight or arrived), the other set is free and receives chunk c+2.
   const int KT = j.K / 64;
   gload(pa0, pb0, 0, 0);
   gload(pa1, pb1, ROW, next_kb());
   sstore(pa0, pb0, 0);
   __syncthreads();
   for (int kt = 0; kt + 2 < KT; kt += 2) {
-    // stage 0 holds chunk kt, pa1/pb1 hold chunk kt+1; pa0/pb0 receive chunk kt+2
     gload(pa0, pb0, static_cast<uint32_t>(kt + 2) * ROW, next_kb());
-    compute(0);
-    sstore(pa1, pb1, 1);
+    compute(0, pa1, pb1);
+    sched_chunk<TM * TN, TM + TN, ACH + BCH, ACH + BCH>();
     __syncthreads();
-    // stage 1 holds chunk kt+1, pa0/pb0 hold chunk kt+2; pa1/pb1 receive chunk kt+3
     gload(pa1, pb1, static_cast<uint32_t>(kt + 3) * ROW, next_kb());
-    compute(1);
-    sstore(pa0, pb0, 0);
+    compute(1, pa0, pb0);
+    sched_chunk<TM * TN, TM + TN, ACH + BCH, ACH + BCH>();
     __syncthreads();
   }
-  compute(0);
-  sstore(pa1, pb1, 1);
+  compute(0, pa1, pb1);
+  sched_chunk<TM * TN, TM + TN, 0, ACH + BCH>();
   __syncthreads();
-  compute(1);
+  compute(1, nullptr, nullptr);
 
   // D[feature][token]: lane owns token (lane & 31) of each token tile and features
   // 8 (r / 4) + 4 (lane / 32) + (r % 4) of each feature tile.
