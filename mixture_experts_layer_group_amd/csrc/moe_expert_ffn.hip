@@ -9,20 +9,12 @@
 // concatenation of theirs, [11-868 #12] "機制：Transformer 各部分怎麼切") can ride in the
 // same launch.
 //
-// bf16 kernel (gfx950):
-//   * block tile BM x BN x 64, 256 threads = 2 x 2 waves, each wave (BM/2) x (BN/2) built
-//     from v_mfma_f32_32x32x16_bf16 tiles with fp32 accumulators;
-//   * A (token rows) and B (weight rows: W1 is [H, M], W2 is [M, H], so both operands are
-//     K-contiguous) staged through LDS in two buffers of 128-byte rows whose 16-byte
-//     columns are XOR-swizzled by (row & 7), so the fragment reads of 8 consecutive rows hit
-//     distinct banks; the next K chunk is fetched into registers while the current one is
-//     multiplied;
-//   * the weight fragment is the MFMA's first operand, so every lane ends up owning one
-//     token row and runs of 4 consecutive output features: the epilogue applies the
-//     activation, rounds to bf16 and writes 8 bytes per run, masking rows past the tile;
-//   * tiles are numbered so that each XCD (blocks b with equal b % 8) receives a contiguous
-//     range, and inside a range 8 m-tiles sweep the n-tiles together (L2 reuse of the
-//     weight tile across an expert's row tiles).
+// bf16 kernel (gfx950): 256 x {256, 128} tiles, 8 (or 4) waves, v_mfma_f32_32x32x16_bf16,
+// operands loaded global -> LDS directly (buffer_load ... lds) through two stages of 64-deep
+// K chunks, an LDS-staged epilogue with the activation fused, and an XCD-aware tile order:
+// each XCD (blocks b with equal b % 8) receives a contiguous range of tiles, inside which 8
+// m-tiles sweep the n-tiles together (L2 reuse of weight tiles across an expert's row tiles
+// and of row tiles across n-tiles).  Details at gemm_bf16_kernel.
 // fp32 kernel: a 64 x 64 x 16 FMA tile for the fp32 layers (the fp32 MFMA and fp32 vector
 // peaks are equal on this chip).
 #include "moe_device.h"
@@ -106,6 +98,13 @@ __device__ __forceinline__ int64_t bseg_offset(const Job& j, int kk, int esz) {
   return seg * j.segb + (kk - seg * j.kseg) * esz;
 }
 
+// Workgroup barrier for LDS hand-offs only: wait for this wave's LDS operations, then
+// s_barrier.  Unlike __syncthreads() it carries no global-memory fence, so global loads in
+// flight are not drained by it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 // Raw buffer resource over [base, base + bytes): loads past the end return 0 and stores past
@@ -114,10 +113,6 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
   const int32_t n = bytes > 0x7fffffff ? 0x7fffffff : static_cast<int32_t>(bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n,
                                            0x00020000);
-}
-
-__device__ __forceinline__ u32x4 bload(rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
 }
 
 // XOR pattern of the 16-byte columns of LDS row r (128-byte rows).  Among any 8 aligned
@@ -134,60 +129,91 @@ __device__ __forceinline__ float act_fn(float z) {
   return z;
 }
 
-// Instruction order of one K chunk (a scheduling region between two barriers), given to
-// the compiler as groups: the first k-step's fragment reads, then for every MFMA one other
-// memory operation -- the next k-step's fragment reads first, global loads of the chunk
-// after next during k-steps 0-1, LDS writes of the next chunk (whose loads are the oldest
-// in flight) during k-steps 2-3.  MF = MFMAs per k-step, DR = fragment reads per k-step,
-// NL = global loads, NW = LDS writes.
-template <int MF, int DR, int NL, int NW>
-__device__ __forceinline__ void sched_chunk() {
-#pragma unroll
-  for (int i = 0; i < DR; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  int loads = NL, writes = NW;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-#pragma unroll
-    for (int m = 0; m < MF; ++m) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (s < 3 && m < DR) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      } else if (s < 2 && loads > 0) {
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        --loads;
-      } else if (s >= 2 && writes > 0) {
-        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-        --writes;
-      }
-    }
-  }
+// s_waitcnt immediate for "at most n vector-memory operations outstanding" (gfx9 encoding:
+// vmcnt in bits [3:0] and [15:14]; expcnt and lgkmcnt left at their no-wait maxima).
+#define MOE_WAIT_VMCNT(n) \
+  __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// 16 bytes per lane from a raw buffer straight into LDS (lane i -> lds + 16 i).  Kept out of
+// lambdas: the host compilation pass drops the kernel's launch stub when this builtin is
+// called from inside one.
+__device__ __forceinline__ void dma16(rsrc_t r, unsigned char* lds, uint32_t voff,
+                                      uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
 }
 
-template <int BM, int BN, int ACT>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g) {
-  constexpr int WTM = BM / 2, WTN = BN / 2;   // wave tile (2 x 2 waves)
-  constexpr int TM = WTM / 32, TN = WTN / 32; // 32x32 MFMA tiles per wave
-  constexpr int ACH = BM / 32, BCH = BN / 32; // 16-byte chunks per thread per K chunk
-  constexpr int ROW = 128;                    // bytes of one LDS row (64 bf16 of K)
+// Expert GEMM tile: C[BM, BN] = act(A[BM, K] . B[BN, K]^T), bf16 in, fp32 accumulate, bf16 out.
+//  * 2 x WN waves; wave (wm, wn) owns rows [wm BM/2, +BM/2) and columns [wn BN/WN, +BN/WN) as
+//    v_mfma_f32_32x32x16_bf16 tiles (the weight fragment is the first operand, so a lane holds
+//    one token row and runs of 4 features);
+//  * K advances in chunks of 64 through two LDS stages of 128-byte rows.  Operands go from
+//    global memory straight into LDS (buffer_load ... lds, 16 bytes per lane), chunk k+1
+//    landing while chunk k is multiplied; full 128-byte lines per row keep the L2 requests
+//    whole.  Lane i of a load instruction writes LDS unit i, so the XOR column swizzle is
+//    applied on the global side: LDS unit (row r, column p) receives global column
+//    p ^ lds_swz(r);
+//  * a barrier without a global-memory fence separates the stages, so the loads in flight are
+//    never drained by it;
+//  * the epilogue applies the activation, packs bf16 and stages the tile in LDS (16-byte
+//    columns XOR (row % columns)), then writes whole rows, 16 bytes per lane.
+template <int BM, int BN, int WN, int ACT>
+__global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
+  constexpr int BK = 64, ROW = 128, NST = 2;
+  constexpr int NT = 128 * WN, NW = 2 * WN;
   constexpr int STAGE = (BM + BN) * ROW;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
+  constexpr int WTM = BM / 2, WTN = BN / WN;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  constexpr int AQ = BM * ROW / 1024 / NW, BQ = BN * ROW / 1024 / NW;  // loads per wave/chunk
+  constexpr int SMEM = NST * STAGE > BM * BN * 2 ? NST * STAGE : BM * BN * 2;
+  static_assert(AQ * NW * 1024 == BM * ROW && BQ * NW * 1024 == BN * ROW, "tile/wave split");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
 
   Job j;
   if (!decode_tile<BM, BN, 2>(g, j)) return;
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = w / WN, wn = w % WN;
 
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int wm = w >> 1, wn = w & 1;
-  const int c = t & 7;                          // 16-byte column this thread loads
-  const int rsub = t >> 3;                      // row within each 32-row slab
-  const int scol = (c ^ lds_swz(rsub)) * 16;    // swizzled LDS column (rows r = rsub + 32 i)
-
-  // A: only the tile's valid rows are addressable; the rest of the BM rows load as zeros.
   const uint32_t lda = static_cast<uint32_t>(j.lda), ldb = static_cast<uint32_t>(j.ldb);
   const rsrc_t ra_rs = make_rsrc(j.A, static_cast<int64_t>(j.nrows) * j.lda);
   const int nseg = (j.K + static_cast<int>(j.kseg) - 1) / static_cast<int>(j.kseg);
   const rsrc_t rb_rs = make_rsrc(j.B, (nseg - 1) * j.segb + static_cast<int64_t>(BN) * j.ldb);
-  const uint32_t avoff = rsub * lda + c * 16;
-  const uint32_t bvoff = rsub * ldb + c * 16;
+
+  // Load slot q of this wave fills LDS units [(w + NW q) 64, +64) of its operand: unit u is
+  // row u / 8, physical column u % 8.
+  uint32_t aoff[AQ], boff[BQ];
+#pragma unroll
+  for (int q = 0; q < AQ; ++q) {
+    const int u = (w + NW * q) * 64 + lane, r = u >> 3, c = (u & 7) ^ lds_swz(r);
+    aoff[q] = r * lda + c * 16;
+  }
+#pragma unroll
+  for (int q = 0; q < BQ; ++q) {
+    const int u = (w + NW * q) * 64 + lane, r = u >> 3, c = (u & 7) ^ lds_swz(r);
+    boff[q] = r * ldb + c * 16;
+  }
+
+  // K position of B inside its segment (elements) and the segment's byte offset.
+  int kin = 0;
+  uint32_t segoff = 0;
+  const int kseg = static_cast<int>(j.kseg);
+  const uint32_t segb = static_cast<uint32_t>(j.segb);
+  auto issue = [&](int kt, int st) {
+    unsigned char* As = smem + st * STAGE;
+    unsigned char* Bs = As + BM * ROW;
+    const uint32_t ka = static_cast<uint32_t>(kt) * ROW;
+    const uint32_t kb = segoff + static_cast<uint32_t>(kin) * 2;
+#pragma unroll
+    for (int q = 0; q < AQ; ++q) dma16(ra_rs, As + (w + NW * q) * 1024, aoff[q], ka);
+#pragma unroll
+    for (int q = 0; q < BQ; ++q) dma16(rb_rs, Bs + (w + NW * q) * 1024, boff[q], kb);
+    kin += BK;
+    const bool wrap = kin == kseg;
+    kin = wrap ? 0 : kin;
+    segoff += wrap ? segb : 0u;
+  };
 
   f32x16 acc[TN][TM];
 #pragma unroll
@@ -195,127 +221,71 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
     for (int im = 0; im < TM; ++im) acc[jn][im] = f32x16{};
 
-  // Two register sets of prefetched K chunks: while chunk kt is multiplied out of LDS,
-  // chunk kt+1 sits in one set (loaded one iteration earlier) and chunk kt+2 is in flight
-  // into the other, so a global load has two chunks of MFMA work to arrive.
-  u32x4 pa0[ACH], pb0[BCH], pa1[ACH], pb1[BCH];
-  auto gload = [&](u32x4 (&pa)[ACH], u32x4 (&pb)[BCH], uint32_t ka, uint32_t kb) {
-#pragma unroll
-    for (int i = 0; i < ACH; ++i) pa[i] = bload(ra_rs, avoff, ka + i * 32 * lda);
-#pragma unroll
-    for (int i = 0; i < BCH; ++i) pb[i] = bload(rb_rs, bvoff, kb + i * 32 * ldb);
-  };
-  auto sstore = [&](const u32x4 (&pa)[ACH], const u32x4 (&pb)[BCH], int st) {
-    unsigned char* As = smem + st * STAGE;
-    unsigned char* Bs = As + BM * ROW;
-#pragma unroll
-    for (int i = 0; i < ACH; ++i)
-      *reinterpret_cast<u32x4*>(As + (rsub + 32 * i) * ROW + scol) = pa[i];
-#pragma unroll
-    for (int i = 0; i < BCH; ++i)
-      *reinterpret_cast<u32x4*>(Bs + (rsub + 32 * i) * ROW + scol) = pb[i];
-  };
-
-  // K position of B inside its segment (elements) and the segment's byte offset.
-  int kin = 0;
-  uint32_t segoff = 0;
-  const int kseg = static_cast<int>(j.kseg);
-  const uint32_t segb = static_cast<uint32_t>(j.segb);
-  auto next_kb = [&]() -> uint32_t {
-    kin += 64;
-    const bool wrap = kin == kseg;
-    kin = wrap ? 0 : kin;
-    segoff += wrap ? segb : 0u;
-    return segoff + static_cast<uint32_t>(kin) * 2;
-  };
-
   const int arow = wm * WTM + (lane & 31);
   const int brow = wn * WTN + (lane & 31);
-  const int sw = lds_swz(lane);
-  // One K chunk out of LDS stage st (4 MFMA k-steps), with the next step's fragments read
-  // while the current step multiplies, and (if X is given) the prefetched chunk in X written
-  // into the other stage a quarter per k-step, so the LDS writes overlap the MFMAs.
-  auto compute = [&](int st, const u32x4* xa, const u32x4* xb) {
+  const int sw = lds_swz(lane & 31);
+  auto compute = [&](int st) {
     const unsigned char* As = smem + st * STAGE;
     const unsigned char* Bs = As + BM * ROW;
-    unsigned char* Ao = smem + (st ^ 1) * STAGE;
-    unsigned char* Bo = Ao + BM * ROW;
-    bf16x8 af[2][TM], bfr[2][TN];
-    auto fread = [&](int s, int b) {
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s) {
       const int phys = (((2 * s) + (lane >> 5)) ^ sw) * 16;
+      bf16x8 af[TM], bfr[TN];
 #pragma unroll
       for (int im = 0; im < TM; ++im)
-        af[b][im] = *reinterpret_cast<const bf16x8*>(As + (arow + 32 * im) * ROW + phys);
+        af[im] = *reinterpret_cast<const bf16x8*>(As + (arow + 32 * im) * ROW + phys);
 #pragma unroll
       for (int jn = 0; jn < TN; ++jn)
-        bfr[b][jn] = *reinterpret_cast<const bf16x8*>(Bs + (brow + 32 * jn) * ROW + phys);
-    };
-    fread(0, 0);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      if (s < 3) fread(s + 1, (s + 1) & 1);
+        bfr[jn] = *reinterpret_cast<const bf16x8*>(Bs + (brow + 32 * jn) * ROW + phys);
 #pragma unroll
       for (int jn = 0; jn < TN; ++jn)
 #pragma unroll
         for (int im = 0; im < TM; ++im)
-          acc[jn][im] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[s & 1][jn], af[s & 1][im],
-                                                                acc[jn][im], 0, 0, 0);
-      if (xa) {
-#pragma unroll
-        for (int i = s * ACH / 4; i < (s + 1) * ACH / 4; ++i)
-          *reinterpret_cast<u32x4*>(Ao + (rsub + 32 * i) * ROW + scol) = xa[i];
-#pragma unroll
-        for (int i = s * BCH / 4; i < (s + 1) * BCH / 4; ++i)
-          *reinterpret_cast<u32x4*>(Bo + (rsub + 32 * i) * ROW + scol) = xb[i];
-      }
+          acc[jn][im] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[jn], af[im], acc[jn][im],
+                                                                0, 0, 0);
     }
   };
 
-  // K is a multiple of 128 here, so the chunk count KT is even: the loop runs chunk pairs
-  // with no control flow inside, and the last pair is peeled.  Invariant at the top of a
-  // half-iteration: the current stage holds chunk c, one register set holds chunk c+1
-  // (in flight or arrived), the other set is free and receives chunk c+2.
-  const int KT = j.K / 64;
-  gload(pa0, pb0, 0, 0);
-  gload(pa1, pb1, ROW, next_kb());
-  sstore(pa0, pb0, 0);
-  __syncthreads();
-  for (int kt = 0; kt + 2 < KT; kt += 2) {
-    gload(pa0, pb0, static_cast<uint32_t>(kt + 2) * ROW, next_kb());
-    compute(0, pa1, pb1);
-    sched_chunk<TM * TN, TM + TN, ACH + BCH, ACH + BCH>();
-    __syncthreads();
-    gload(pa1, pb1, static_cast<uint32_t>(kt + 3) * ROW, next_kb());
-    compute(1, pa0, pb0);
-    sched_chunk<TM * TN, TM + TN, ACH + BCH, ACH + BCH>();
-    __syncthreads();
+  const int KT = j.K / BK;
+  issue(0, 0);
+  for (int kt = 0; kt + 1 < KT; ++kt) {
+    MOE_WAIT_VMCNT(0);   // this wave's part of chunk kt is in LDS
+    lds_barrier();       // ... and every wave's; stage (kt+1)&1 is no longer being read
+    issue(kt + 1, (kt + 1) & 1);
+    compute(kt & 1);
   }
-  compute(0, pa1, pb1);
-  sched_chunk<TM * TN, TM + TN, 0, ACH + BCH>();
-  __syncthreads();
-  compute(1, nullptr, nullptr);
+  MOE_WAIT_VMCNT(0);
+  lds_barrier();
+  compute((KT - 1) & 1);
 
-  // D[feature][token]: lane owns token (lane & 31) of each token tile and features
-  // 8 (r / 4) + 4 (lane / 32) + (r % 4) of each feature tile.
+  // Epilogue through LDS: D[feature][token] -> tile[token][feature] bf16 (rows of BN*2 bytes,
+  // NCH 16-byte columns XOR (row % NCH)), then whole rows to global memory.
+  constexpr int RB = BN * 2, NCH = RB / 16;
+  static_assert((NCH & (NCH - 1)) == 0, "power-of-two column count");
+  lds_barrier();
 #pragma unroll
   for (int im = 0; im < TM; ++im) {
     const int tok = wm * WTM + 32 * im + (lane & 31);
-    if (tok < j.nrows) {
-      char* crow = j.C + static_cast<int64_t>(tok) * j.ldc;
 #pragma unroll
-      for (int jn = 0; jn < TN; ++jn) {
+    for (int jn = 0; jn < TN; ++jn) {
 #pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-          const int f = wn * WTN + 32 * jn + 8 * qd + 4 * (lane >> 5);
-          u32x2 pk;
-          pk[0] = pack_bf16x2(act_fn<ACT>(acc[jn][im][4 * qd + 0]),
-                              act_fn<ACT>(acc[jn][im][4 * qd + 1]));
-          pk[1] = pack_bf16x2(act_fn<ACT>(acc[jn][im][4 * qd + 2]),
-                              act_fn<ACT>(acc[jn][im][4 * qd + 3]));
-          *reinterpret_cast<u32x2*>(crow + f * 2) = pk;
-        }
+      for (int qd = 0; qd < 4; ++qd) {
+        const int f = wn * WTN + 32 * jn + 8 * qd + 4 * (lane >> 5);
+        u32x2 pk;
+        pk[0] = pack_bf16x2(act_fn<ACT>(acc[jn][im][4 * qd + 0]),
+                            act_fn<ACT>(acc[jn][im][4 * qd + 1]));
+        pk[1] = pack_bf16x2(act_fn<ACT>(acc[jn][im][4 * qd + 2]),
+                            act_fn<ACT>(acc[jn][im][4 * qd + 3]));
+        const int ch = f >> 3, within = (f & 7) * 2;
+        *reinterpret_cast<u32x2*>(smem + tok * RB + ((ch ^ (tok & (NCH - 1))) << 4) + within) = pk;
       }
     }
+  }
+  lds_barrier();
+  for (int i = t; i < j.nrows * NCH; i += NT) {
+    const int r = i / NCH, c = i - r * NCH;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * RB + ((c ^ (r & (NCH - 1))) << 4));
+    *reinterpret_cast<u32x4*>(j.C + static_cast<int64_t>(r) * j.ldc + c * 16) = v;
   }
 }
 
@@ -384,8 +354,9 @@ hipError_t launch_expert_gemm(const GemmArgs& a, hipStream_t s) {
   if (grid == 0) return hipSuccess;
   const int act = a.p0.act;  // both problems of one launch share the activation
   if (a.dtype == 1) {
-#define MOE_GEMM_LAUNCH(BNV, ACTV) \
-  hipLaunchKernelGGL((gemm_bf16_kernel<256, BNV, ACTV>), dim3(grid), dim3(kThreads), 0, s, a)
+#define MOE_GEMM_LAUNCH(BNV, ACTV)                                                       \
+  hipLaunchKernelGGL((gemm_bf16_kernel<256, BNV, BNV / 64, ACTV>), dim3(grid),            \
+                     dim3(128 * (BNV / 64)), 0, s, a)
     if (BN == 256) {
       if (act == 0) MOE_GEMM_LAUNCH(256, 0);
       else if (act == 1) MOE_GEMM_LAUNCH(256, 1);
