@@ -9,7 +9,7 @@
 // concatenation of theirs, [11-868 #12] "機制：Transformer 各部分怎麼切") can ride in the
 // same launch.
 //
-// bf16 kernel (gfx950): 256 x {256, 128} tiles, 8 (or 4) waves, v_mfma_f32_32x32x16_bf16,
+// bf16 kernel (gfx950): 256 x 256 tiles (the last n-tile of a problem may be partial), 8 waves, v_mfma_f32_32x32x16_bf16,
 // operands loaded global -> LDS directly (buffer_load ... lds) through two stages of 64-deep
 // K chunks, an LDS-staged epilogue with the activation fused, and an XCD-aware tile order:
 // each XCD (blocks b with equal b % 8) receives a contiguous range of tiles, inside which 8
@@ -36,16 +36,17 @@ struct Job {
   int64_t ldc;     // bytes
   int K;
   int nrows;       // valid rows of the tile
+  int ncols;       // valid columns of the tile (the last n-tile of a problem may be partial)
   int rows_left;   // rows readable from the tile's first row (clamp)
   int act;
 };
 
 template <int BM, int BN, int ESZ>
 __device__ __forceinline__ bool decode_tile(const GemmArgs& g, Job& j) {
-  const int nt0 = g.p0.N / BN;
+  const int nt0 = (g.p0.N + BN - 1) / BN;
   const int mt0 = g.p0.tiles ? *g.p0.num_tiles : g.p0.max_tiles;
   const int tot0 = mt0 * nt0;
-  const int nt1 = g.nprob > 1 ? g.p1.N / BN : 0;
+  const int nt1 = g.nprob > 1 ? (g.p1.N + BN - 1) / BN : 0;
   const int mt1 = g.nprob > 1 ? g.p1.max_tiles : 0;
   const int total = tot0 + mt1 * nt1;
   const int bid = blockIdx.x;
@@ -87,6 +88,7 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& g, Job& j) {
         static_cast<int64_t>(nt) * BN * ESZ;
   j.K = P.K;
   j.nrows = nrows;
+  j.ncols = min(BN, P.N - nt * BN);
   j.rows_left = P.a_rows - row0;
   j.act = P.act;
   return true;
@@ -179,7 +181,8 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
   const uint32_t lda = static_cast<uint32_t>(j.lda), ldb = static_cast<uint32_t>(j.ldb);
   const rsrc_t ra_rs = make_rsrc(j.A, static_cast<int64_t>(j.nrows) * j.lda);
   const int nseg = (j.K + static_cast<int>(j.kseg) - 1) / static_cast<int>(j.kseg);
-  const rsrc_t rb_rs = make_rsrc(j.B, (nseg - 1) * j.segb + static_cast<int64_t>(BN) * j.ldb);
+  // Weight rows past the problem's N (a partial last n-tile) read as zeros.
+  const rsrc_t rb_rs = make_rsrc(j.B, (nseg - 1) * j.segb + static_cast<int64_t>(j.ncols) * j.ldb);
 
   // Load slot q of this wave fills LDS units [(w + NW q) 64, +64) of its operand: unit u is
   // row u / 8, physical column u % 8.
@@ -282,8 +285,10 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
     }
   }
   lds_barrier();
+  const int ncch = j.ncols / 8;   // valid 16-byte columns
   for (int i = t; i < j.nrows * NCH; i += NT) {
     const int r = i / NCH, c = i - r * NCH;
+    if (c >= ncch) continue;
     const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * RB + ((c ^ (r & (NCH - 1))) << 4));
     *reinterpret_cast<u32x4*>(j.C + static_cast<int64_t>(r) * j.ldc + c * 16) = v;
   }
@@ -334,8 +339,8 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs g) {
 }
 
 int grid_of(const GemmArgs& a, int BN) {
-  int64_t total = static_cast<int64_t>(a.p0.max_tiles) * (a.p0.N / BN);
-  if (a.nprob > 1) total += static_cast<int64_t>(a.p1.max_tiles) * (a.p1.N / BN);
+  int64_t total = static_cast<int64_t>(a.p0.max_tiles) * ((a.p0.N + BN - 1) / BN);
+  if (a.nprob > 1) total += static_cast<int64_t>(a.p1.max_tiles) * ((a.p1.N + BN - 1) / BN);
   return static_cast<int>(total);
 }
 
@@ -344,8 +349,9 @@ int grid_of(const GemmArgs& a, int BN) {
 int gemm_block_m(int dtype) { return dtype == 1 ? 256 : 64; }
 
 int gemm_block_n(int dtype, int n0, int n1) {
-  if (dtype != 1) return 64;
-  return (n0 % 256 == 0 && n1 % 256 == 0) ? 256 : 128;
+  (void)n0;
+  (void)n1;
+  return dtype == 1 ? 256 : 64;  // bf16: partial last n-tiles are masked
 }
 
 hipError_t launch_expert_gemm(const GemmArgs& a, hipStream_t s) {
@@ -357,15 +363,9 @@ hipError_t launch_expert_gemm(const GemmArgs& a, hipStream_t s) {
 #define MOE_GEMM_LAUNCH(BNV, ACTV)                                                       \
   hipLaunchKernelGGL((gemm_bf16_kernel<256, BNV, BNV / 64, ACTV>), dim3(grid),            \
                      dim3(128 * (BNV / 64)), 0, s, a)
-    if (BN == 256) {
-      if (act == 0) MOE_GEMM_LAUNCH(256, 0);
-      else if (act == 1) MOE_GEMM_LAUNCH(256, 1);
-      else MOE_GEMM_LAUNCH(256, 2);
-    } else {
-      if (act == 0) MOE_GEMM_LAUNCH(128, 0);
-      else if (act == 1) MOE_GEMM_LAUNCH(128, 1);
-      else MOE_GEMM_LAUNCH(128, 2);
-    }
+    if (act == 0) MOE_GEMM_LAUNCH(256, 0);
+    else if (act == 1) MOE_GEMM_LAUNCH(256, 1);
+    else MOE_GEMM_LAUNCH(256, 2);
 #undef MOE_GEMM_LAUNCH
   } else {
     hipLaunchKernelGGL(gemm_f32_kernel, dim3(grid), dim3(kThreads), 0, s, a);
