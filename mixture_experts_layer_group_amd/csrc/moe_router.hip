@@ -21,95 +21,159 @@
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;       // 16 waves: all of them share the per-token epilogue
+constexpr int kGemmThreads = 256;    // the GEMM phase runs on waves 0..3
+constexpr int kLanesPerToken = kThreads / kRouteTokens;
 constexpr int kRowBytes = 256;  // bytes of K per LDS row per chunk
+
+}  // namespace
+__host__ __device__ int router_lds_stage_bytes(int dt, int epad);
+namespace {
 
 __device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 7); }
 
+// LDS staging area of the fp32 path: x[64] and Wg[epad] rows of 256 bytes (it is also
+// large enough for the logits tile [64][epad + 1] floats that aliases it afterwards).
 __host__ __device__ inline int router_stage_bytes(int epad) {
-  return kRouteTokens * kRowBytes + epad * kRowBytes;  // >= lg tile [64][epad+1] floats
+  return kRouteTokens * kRowBytes + epad * kRowBytes;
 }
 
-// x[64 tokens, M] . Wg[E, M]^T -> lg[64][ls] (bf16 inputs, MFMA 32x32x16).
-__device__ void router_gemm_bf16(const RouterArgs& a, unsigned char* stage, float* lg, int ls,
-                                 int tok0, int nt, int epad) {
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int32_t n = bytes > 0x7fffffff ? 0x7fffffff : static_cast<int32_t>(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n,
+                                           0x00020000);
+}
+
+// 16 bytes per lane from a raw buffer straight into LDS (lane i -> lds + 16 i).
+__device__ __forceinline__ void dma16(rsrc_t r, unsigned char* lds, uint32_t voff,
+                                      uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
+}
+
+#define MOE_WAIT_VMCNT(n) \
+  __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// LDS layout of the bf16 router GEMM for EPAD padded experts and top-k <= 8: stages of
+// x[64] + Wg[EPAD] rows of ROWB bytes, within 160 KB together with the histograms.
+template <int EPAD>
+struct RouterPipe {
+  static constexpr int kRowB = EPAD >= 256 ? 128 : 256;
+  static constexpr int kStage = (kRouteTokens + EPAD) * kRowB;
+  static constexpr int kHist = EPAD * (1 + kMaxTopK) * 4;
+  static constexpr int kFit = (160 * 1024 - kHist) / kStage;
+  static constexpr int kStages = kFit >= 4 ? 4 : kFit;
+  static constexpr int kXq = kRouteTokens * kRowB / 1024 / 4;  // x loads per wave per chunk
+  static constexpr int kWq = EPAD * kRowB / 1024 / 4;          // Wg loads per wave per chunk
+  static_assert(kStages >= 2, "router pipeline needs two stages");
+};
+
+// XOR pattern of the 16-byte columns of row r: conflict-free fragment reads of one column
+// from 16 consecutive rows on the 64-bank LDS (16 columns per 256-byte row, or 8 per 128-byte
+// row with two rows per bank line).
+template <int ROWB>
+__device__ __forceinline__ int rswz(int r) {
+  return ROWB == 256 ? (r & 15) : (((r >> 1) & 7) ^ ((r & 1) << 2));
+}
+
+// x[64 tokens, M] . Wg[E, M]^T -> lg[64][ls] (bf16, v_mfma_f32_32x32x16_bf16, fp32 sums).
+// K is streamed in row chunks of ROWB bytes through RouterPipe::kStages LDS stages, each
+// filled by buffer_load ... lds (lane i of a wave instruction -> 16 bytes at LDS unit i), so
+// several chunks are in flight while one is multiplied.  The 16-byte columns of each row are
+// XOR-permuted (rswz, applied on the global side) so fragment reads are conflict-free.  Rows
+// of x past the block's tokens and rows of Wg past E read as zeros (buffer bounds).
+template <int EPAD>
+__device__ void router_gemm_bf16(const RouterArgs& a, unsigned char* smem, float* lg, int ls,
+                                 int tok0, int nt) {
+  using P = RouterPipe<EPAD>;
+  constexpr int NST = P::kStages, STAGE = P::kStage, XQ = P::kXq, WQ = P::kWq;
+  constexpr int ROWB = P::kRowB, CPR = ROWB / 16;
+  constexpr int NTILE = 2 * (EPAD / 32);   // 2 token tiles x EPAD/32 expert tiles
+  constexpr int TPW = (NTILE + 3) / 4;     // MFMA tiles per wave
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int E = a.E;
-  const size_t rowbytes = static_cast<size_t>(a.M) * 2;
-  const int nks = static_cast<int>(rowbytes / kRowBytes);
-  const char* xb = static_cast<const char*>(a.x);
-  const char* wb = static_cast<const char*>(a.Wg);
-  unsigned char* xs = stage;
-  unsigned char* ws = stage + kRouteTokens * kRowBytes;
-  const int ntiles = 2 * (epad / 32);     // 2 token tiles x (epad/32) expert tiles
-  const int wl = epad / 16;               // Wg 16-byte chunks per thread per K chunk
+  const uint32_t rowbytes = static_cast<uint32_t>(a.M) * 2;
+  const int nks = static_cast<int>(rowbytes / ROWB);
+  const char* xb = static_cast<const char*>(a.x) + static_cast<size_t>(tok0) * rowbytes;
+  const rsrc_t xr = make_rsrc(xb, static_cast<int64_t>(nt) * rowbytes);
+  const rsrc_t wr = make_rsrc(a.Wg, static_cast<int64_t>(E) * rowbytes);
 
-  f32x16 acc[4];
+  uint32_t xoff[XQ], woff[WQ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
-  u32x4 xr[4];
-  u32x4 wr[16];
-
-  auto load = [&](int kc) {
+  for (int q = 0; q < XQ; ++q) {
+    const int u = (w + 4 * q) * 64 + lane, r = u / CPR, c = (u % CPR) ^ rswz<ROWB>(r);
+    xoff[q] = r * rowbytes + c * 16;
+  }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = t + kThreads * i, r = idx >> 4, c = idx & 15;
-      const int rr = r < nt ? r : nt - 1;
-      xr[i] = *reinterpret_cast<const u32x4*>(xb + static_cast<size_t>(tok0 + rr) * rowbytes +
-                                              static_cast<size_t>(kc) * kRowBytes + c * 16);
-    }
+  for (int q = 0; q < WQ; ++q) {
+    const int u = (w + 4 * q) * 64 + lane, r = u / CPR, c = (u % CPR) ^ rswz<ROWB>(r);
+    woff[q] = r * rowbytes + c * 16;
+  }
+  auto issue = [&](int kc, int st) {
+    unsigned char* xs = smem + st * STAGE;
+    unsigned char* ws = xs + kRouteTokens * ROWB;
+    const uint32_t k0 = static_cast<uint32_t>(kc) * ROWB;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i < wl) {
-        const int idx = t + kThreads * i, r = idx >> 4, c = idx & 15;
-        const int re = r < E ? r : E - 1;
-        wr[i] = *reinterpret_cast<const u32x4*>(wb + static_cast<size_t>(re) * rowbytes +
-                                                static_cast<size_t>(kc) * kRowBytes + c * 16);
-      }
-    }
-  };
-  auto store = [&]() {
+    for (int q = 0; q < XQ; ++q) dma16(xr, xs + (w + 4 * q) * 1024, xoff[q], k0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = t + kThreads * i, r = idx >> 4, c = idx & 15;
-      *reinterpret_cast<u32x4*>(xs + r * kRowBytes + swz(r, c) * 16) = xr[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i < wl) {
-        const int idx = t + kThreads * i, r = idx >> 4, c = idx & 15;
-        *reinterpret_cast<u32x4*>(ws + r * kRowBytes + swz(r, c) * 16) = wr[i];
-      }
-    }
+    for (int q = 0; q < WQ; ++q) dma16(wr, ws + (w + 4 * q) * 1024, woff[q], k0);
   };
 
-  load(0);
-  for (int kc = 0; kc < nks; ++kc) {
-    store();
-    __syncthreads();
-    if (kc + 1 < nks) load(kc + 1);
+  f32x16 acc[TPW];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int c = 2 * s + (lane >> 5);
+  for (int i = 0; i < TPW; ++i) acc[i] = f32x16{};
+  const int sw = rswz<ROWB>(lane & 31);
+  auto compute = [&](int st) {
+    const unsigned char* xs = smem + st * STAGE;
+    const unsigned char* ws = xs + kRouteTokens * ROWB;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+    for (int s = 0; s < ROWB / 32; ++s) {
+      const int phys = ((2 * s + (lane >> 5)) ^ sw) * 16;
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
         const int tile = w + 4 * i;
-        if (tile < ntiles) {
+        if (tile < NTILE) {
           const int ra = (tile & 1) * 32 + (lane & 31);
           const int rb = (tile >> 1) * 32 + (lane & 31);
-          const bf16x8 av = *reinterpret_cast<const bf16x8*>(xs + ra * kRowBytes + swz(ra, c) * 16);
-          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(ws + rb * kRowBytes + swz(rb, c) * 16);
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(xs + ra * ROWB + phys);
+          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(ws + rb * ROWB + phys);
           acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[i], 0, 0, 0);
         }
       }
     }
-    __syncthreads();
+  };
+
+  // Waves 0..3 load and multiply; the other waves of the block only take part in the barriers
+  // (they issue no loads, so their vmcnt waits return at once).
+  const bool gw = w < 4;
+  const int pre = nks < NST - 1 ? nks : NST - 1;
+  if (gw)
+    for (int i = 0; i < pre; ++i) issue(i, i);
+  for (int kc = 0; kc < nks; ++kc) {
+    // chunks issued after chunk kc: min(NST - 2, nks - 1 - kc)
+    const int after = nks - 1 - kc < NST - 2 ? nks - 1 - kc : NST - 2;
+    if (after >= 2) MOE_WAIT_VMCNT(2 * (XQ + WQ));
+    else if (after == 1) MOE_WAIT_VMCNT(XQ + WQ);
+    else MOE_WAIT_VMCNT(0);
+    lds_barrier();
+    if (gw) {
+      if (kc + NST - 1 < nks) issue(kc + NST - 1, (kc + NST - 1) % NST);
+      compute(kc % NST);
+    }
   }
-  // The loop ended with a barrier, so lg (aliasing the staging area) can be written.
+  lds_barrier();  // every wave is done with the stages before lg (aliasing them) is written
+  if (!gw) return;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < TPW; ++i) {
     const int tile = w + 4 * i;
-    if (tile < ntiles) {
+    if (tile < NTILE) {
       const int col = (tile >> 1) * 32 + (lane & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -123,7 +187,7 @@ __device__ void router_gemm_bf16(const RouterArgs& a, unsigned char* stage, floa
 // Same contraction for fp32 inputs with plain FMAs: lane = token, wave = expert phase.
 __device__ void router_gemm_f32(const RouterArgs& a, unsigned char* stage, float* lg, int ls,
                                 int tok0, int nt, int epad) {
-  const int t = threadIdx.x, tl = t & 63, eg = t >> 6;
+  const int t = threadIdx.x, tl = t & 63, eg = (t >> 6) & 3;
   const int E = a.E;
   const size_t rowbytes = static_cast<size_t>(a.M) * 4;
   const int nks = static_cast<int>(rowbytes / kRowBytes);
@@ -134,50 +198,57 @@ __device__ void router_gemm_f32(const RouterArgs& a, unsigned char* stage, float
   const int wl = epad / 16;
   const int ne = epad / 4;               // experts per thread: e = eg + 4 i
 
+  const bool gt = t < kGemmThreads;  // threads 0..255 compute; the rest join the barriers
   float acc[64];
 #pragma unroll
   for (int i = 0; i < 64; ++i) acc[i] = 0.f;
 
   for (int kc = 0; kc < nks; ++kc) {
+    if (gt) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = t + kThreads * i, r = idx >> 4, c = idx & 15;
-      const int rr = r < nt ? r : nt - 1;
-      *reinterpret_cast<u32x4*>(xs + r * kRowBytes + swz(r, c) * 16) =
-          *reinterpret_cast<const u32x4*>(xb + static_cast<size_t>(tok0 + rr) * rowbytes +
-                                          static_cast<size_t>(kc) * kRowBytes + c * 16);
-    }
-    for (int i = 0; i < wl; ++i) {
-      const int idx = t + kThreads * i, r = idx >> 4, c = idx & 15;
-      const int re = r < E ? r : E - 1;
-      *reinterpret_cast<u32x4*>(ws + r * kRowBytes + swz(r, c) * 16) =
-          *reinterpret_cast<const u32x4*>(wb + static_cast<size_t>(re) * rowbytes +
-                                          static_cast<size_t>(kc) * kRowBytes + c * 16);
+      for (int i = 0; i < 4; ++i) {
+        const int idx = t + kGemmThreads * i, r = idx >> 4, c = idx & 15;
+        const int rr = r < nt ? r : nt - 1;
+        *reinterpret_cast<u32x4*>(xs + r * kRowBytes + swz(r, c) * 16) =
+            *reinterpret_cast<const u32x4*>(xb + static_cast<size_t>(tok0 + rr) * rowbytes +
+                                            static_cast<size_t>(kc) * kRowBytes + c * 16);
+      }
+      for (int i = 0; i < wl; ++i) {
+        const int idx = t + kGemmThreads * i, r = idx >> 4, c = idx & 15;
+        const int re = r < E ? r : E - 1;
+        *reinterpret_cast<u32x4*>(ws + r * kRowBytes + swz(r, c) * 16) =
+            *reinterpret_cast<const u32x4*>(wb + static_cast<size_t>(re) * rowbytes +
+                                            static_cast<size_t>(kc) * kRowBytes + c * 16);
+      }
     }
     __syncthreads();
-    for (int c = 0; c < 16; ++c) {
-      const f32x4 xv = *reinterpret_cast<const f32x4*>(xs + tl * kRowBytes + swz(tl, c) * 16);
+    if (gt) {
+      for (int c = 0; c < 16; ++c) {
+        const f32x4 xv = *reinterpret_cast<const f32x4*>(xs + tl * kRowBytes + swz(tl, c) * 16);
 #pragma unroll
-      for (int i = 0; i < 64; ++i) {
-        if (i < ne) {
-          const int e = eg + 4 * i;
-          const f32x4 wv = *reinterpret_cast<const f32x4*>(ws + e * kRowBytes + swz(e, c) * 16);
-          acc[i] = fmaf(xv[0], wv[0], acc[i]);
-          acc[i] = fmaf(xv[1], wv[1], acc[i]);
-          acc[i] = fmaf(xv[2], wv[2], acc[i]);
-          acc[i] = fmaf(xv[3], wv[3], acc[i]);
+        for (int i = 0; i < 64; ++i) {
+          if (i < ne) {
+            const int e = eg + 4 * i;
+            const f32x4 wv = *reinterpret_cast<const f32x4*>(ws + e * kRowBytes + swz(e, c) * 16);
+            acc[i] = fmaf(xv[0], wv[0], acc[i]);
+            acc[i] = fmaf(xv[1], wv[1], acc[i]);
+            acc[i] = fmaf(xv[2], wv[2], acc[i]);
+            acc[i] = fmaf(xv[3], wv[3], acc[i]);
+          }
         }
       }
     }
     __syncthreads();
   }
+  if (!gt) return;
 #pragma unroll
   for (int i = 0; i < 64; ++i)
     if (i < ne) lg[tl * ls + eg + 4 * i] = acc[i];
 }
 
-template <int DT>
-__global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a, int epad) {
+template <int DT, int EPAD>
+__global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
+  constexpr int epad = EPAD;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int t = threadIdx.x;
   const int b = blockIdx.x;
@@ -187,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a, int epad
   const int E = a.E, k = a.k;
   const int ls = epad + 1;
   float* lg = reinterpret_cast<float*>(smem);
-  int* hsel = reinterpret_cast<int*>(smem + router_stage_bytes(epad));
+  int* hsel = reinterpret_cast<int*>(smem + router_lds_stage_bytes(DT, epad));
   int* hact = hsel + epad;
   for (int i = t; i < epad * (1 + k); i += kThreads) hsel[i] = 0;
 
@@ -199,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a, int epad
     __syncthreads();
   } else {
     if (DT == 1)
-      router_gemm_bf16(a, smem, lg, ls, tok0, nt, epad);
+      router_gemm_bf16<EPAD>(a, smem, lg, ls, tok0, nt);
     else
       router_gemm_f32(a, smem, lg, ls, tok0, nt, epad);
     __syncthreads();
@@ -213,24 +284,25 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a, int epad
     __syncthreads();
   }
 
-  // ---- per token: 4 lanes (a quad) share one row of logits
-  const int tl = t >> 2, q = t & 3;
+  // ---- per token: L = 16 consecutive lanes share one row of logits
+  constexpr int L = kLanesPerToken;
+  const int tl = t / L, q = t % L;
   const bool valid = tl < nt;
   const int n = tok0 + tl;
   float* row = lg + tl * ls;
 
   float mx = -INFINITY;
-  for (int e = q; e < E; e += 4) mx = fmaxf(mx, row[e]);
-  mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+  for (int e = q; e < E; e += L) mx = fmaxf(mx, row[e]);
+#pragma unroll
+  for (int off = 1; off < L; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
   float se = 0.f;
-  for (int e = q; e < E; e += 4) se += expf(row[e] - mx);
-  se += __shfl_xor(se, 1, 64);
-  se += __shfl_xor(se, 2, 64);
+  for (int e = q; e < E; e += L) se += expf(row[e] - mx);
+#pragma unroll
+  for (int off = 1; off < L; off <<= 1) se += __shfl_xor(se, off, 64);
 
   int sel_e[kMaxTopK];
   float sel_l[kMaxTopK];
-  uint64_t taken = 0;  // bit i <-> expert q + 4 i already selected
+  uint32_t taken = 0;  // bit i <-> expert q + L i already selected (E <= 256 -> i < 16)
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) {
     sel_e[j] = 0;
@@ -239,22 +311,22 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a, int epad
       float bv = -INFINITY;
       int bix = 0x7fffffff;
       int i = 0;
-      for (int e = q; e < E; e += 4, ++i) {
-        if (!((taken >> i) & 1ull)) {
+      for (int e = q; e < E; e += L, ++i) {
+        if (!((taken >> i) & 1u)) {
           float v = row[e];
           if (v != v) v = -INFINITY;  // a NaN never wins, so bix is always a real expert
           if (v > bv || (v == bv && e < bix)) { bv = v; bix = e; }
         }
       }
 #pragma unroll
-      for (int off = 1; off <= 2; off <<= 1) {
+      for (int off = 1; off < L; off <<= 1) {
         const float ov = __shfl_xor(bv, off, 64);
         const int oi = __shfl_xor(bix, off, 64);
         if (ov > bv || (ov == bv && oi < bix)) { bv = ov; bix = oi; }
       }
       sel_e[j] = bix;
       sel_l[j] = bv;
-      if ((bix & 3) == q) taken |= 1ull << (bix >> 2);
+      if (bix % L == q) taken |= 1u << (bix / L);
     }
   }
 
@@ -273,17 +345,18 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a, int epad
     for (int j = 0; j < kMaxTopK; ++j) wgt[j] = wgt[j] / psel;
   }
   // [GShard] "Random routing": keep the 2nd slot iff u < 2 w2, w2 = 1 / (1 + exp(l1 - l2)),
-  // decided in fp64 from the two fp32 logits.
+  // decided in fp64 from the two fp32 logits (by the two lanes that use it).
   bool keep2 = true;
-  if (a.rr && valid) {
+  if (a.rr && valid && q < 2) {
     const double th = 2.0 / (1.0 + exp(static_cast<double>(sel_l[0]) - static_cast<double>(sel_l[1])));
     keep2 = static_cast<double>(a.u[n]) < th;
   }
 
   if (valid) {
+    // lane q < k writes slot q
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) {
-      if (j < k && (j & 3) == q) {
+      if (j < k && j == q) {
         const size_t o = static_cast<size_t>(n) * k + j;
         a.topk_idx[o] = sel_e[j];
         a.topk_w[o] = wgt[j];
@@ -302,15 +375,24 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a, int epad
   }
   // Softmax probabilities for the block's column sums; each lane rewrites only its own
   // entries of its own row, which no other lane reads before the barrier.
-  for (int e = q; e < E; e += 4) row[e] = valid ? expf(row[e] - mx) / se : 0.f;
+  for (int e = q; e < E; e += L) row[e] = valid ? expf(row[e] - mx) / se : 0.f;
   __syncthreads();
 
-  for (int e = t; e < E; e += kThreads) {
+  // Column sums of the probabilities: SPC consecutive lanes per expert, each summing every
+  // SPC-th row in fp64, then a fixed butterfly over those lanes (deterministic).
+  constexpr int SPC = kThreads / EPAD;
+  {
+    const int e = t / SPC, part = t % SPC;
     double s = 0.0;
-    for (int r = 0; r < nt; ++r) s += static_cast<double>(lg[r * ls + e]);
-    const size_t o = (static_cast<size_t>(g) * E + e) * a.nbg + bi;
-    a.psum[o] = s;
-    a.sel[o] = hsel[e];
+    if (e < E)
+      for (int r = part; r < nt; r += SPC) s += static_cast<double>(lg[r * ls + e]);
+#pragma unroll
+    for (int off = 1; off < SPC; off <<= 1) s += __shfl_xor(s, off, 64);
+    if (e < E && part == 0) {
+      const size_t o = (static_cast<size_t>(g) * E + e) * a.nbg + bi;
+      a.psum[o] = s;
+      a.sel[o] = hsel[e];
+    }
   }
   for (int idx = t; idx < k * E; idx += kThreads) {
     const int j = idx / E, e = idx - j * E;
@@ -318,31 +400,50 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a, int epad
   }
 }
 
+template <int DT, int EPAD>
+hipError_t launch_router_t(const RouterArgs& a, hipStream_t s, int grid) {
+  const size_t lds = router_lds_stage_bytes(DT, EPAD) + static_cast<size_t>(EPAD) * (1 + a.k) * 4;
+  static const bool attr = [] {
+    hipFuncSetAttribute(reinterpret_cast<const void*>(&router_kernel<DT, EPAD>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    return true;
+  }();
+  (void)attr;
+  hipLaunchKernelGGL((router_kernel<DT, EPAD>), dim3(grid), dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+// LDS bytes before the histograms: the bf16 pipeline stages (or the fp32 staging area),
+// never less than the logits tile [64][epad + 1] floats that aliases them.
+__host__ __device__ int router_lds_stage_bytes(int dt, int epad) {
+  int b = router_stage_bytes(epad);
+  if (dt == 1) {
+    const int rowb = epad >= 256 ? 128 : 256;
+    const int stage = (kRouteTokens + epad) * rowb;
+    const int fit = (160 * 1024 - epad * (1 + kMaxTopK) * 4) / stage;
+    b = (fit >= 4 ? 4 : fit) * stage;
+  }
+  const int lgb = kRouteTokens * (epad + 1) * 4;
+  return b > lgb ? b : lgb;
+}
 
 hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
   const int epad = (a.E + 31) / 32 * 32;
-  const size_t lds = router_stage_bytes(epad) + static_cast<size_t>(epad) * (1 + a.k) * 4;
   const int grid = a.G * a.nbg;
   if (grid == 0) return hipSuccess;
+  const int e = epad <= 32 ? 32 : epad <= 64 ? 64 : epad <= 128 ? 128 : 256;
   if (a.dtype == 1) {
-    static bool attr = false;
-    if (!attr) {
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&router_kernel<1>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-      attr = true;
-    }
-    hipLaunchKernelGGL(router_kernel<1>, dim3(grid), dim3(kThreads), lds, s, a, epad);
-  } else {
-    static bool attr = false;
-    if (!attr) {
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&router_kernel<0>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-      attr = true;
-    }
-    hipLaunchKernelGGL(router_kernel<0>, dim3(grid), dim3(kThreads), lds, s, a, epad);
+    if (e == 32) return launch_router_t<1, 32>(a, s, grid);
+    if (e == 64) return launch_router_t<1, 64>(a, s, grid);
+    if (e == 128) return launch_router_t<1, 128>(a, s, grid);
+    return launch_router_t<1, 256>(a, s, grid);
   }
-  return hipGetLastError();
+  if (e == 32) return launch_router_t<0, 32>(a, s, grid);
+  if (e == 64) return launch_router_t<0, 64>(a, s, grid);
+  if (e == 128) return launch_router_t<0, 128>(a, s, grid);
+  return launch_router_t<0, 256>(a, s, grid);
 }
 
 }  // namespace moe
