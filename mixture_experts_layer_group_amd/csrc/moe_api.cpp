@@ -1,8 +1,8 @@
 // Host side of the C ABI in include/moe.h: argument checks, workspace layout, and the
 // launch sequence of the MoE layer on one stream.
 //
-//   moe_router -> moe_gate (scan, offsets) -> moe_permute -> expert GEMM 1 (+act)
-//   -> expert GEMM 2 -> moe_combine (+aux)
+//   moe_router -> moe_gate (capacity scan) -> moe_permute (offsets, positions, scatter)
+//   -> expert GEMM 1 (+act) -> expert GEMM 2 -> moe_combine (+aux)
 //
 // Capacity is static, so every grid size is known on the host; the data-dependent parts
 // (kept rows per expert, GEMM tiles) stay on the device and nothing is copied back.
@@ -21,7 +21,7 @@ using moe::kRouteTokens;
 
 struct Layout {
   // byte offsets inside the workspace
-  size_t buf, h, hsh, osh, active, psum, sel, ahist, abase, ntot, Pg, Cg, gbase, tiles, ntiles;
+  size_t buf, h, hsh, osh, active, psum, sel, ahist, abase, ntot, Pg, Cg, tiles, ntiles;
   size_t total;
   // sizes
   int64_t S, nbg, Rmax, rows_alloc, max_tiles;
@@ -87,7 +87,6 @@ int make_layout(const moe_cfg* c, Layout* L) {
   L->ntot = take(static_cast<size_t>(G) * k * E * 4);
   L->Pg = take(static_cast<size_t>(G) * E * 8);
   L->Cg = take(static_cast<size_t>(G) * E * 4);
-  L->gbase = take(static_cast<size_t>(G) * E * 4);
   L->tiles = take(static_cast<size_t>(L->max_tiles) * sizeof(moe::TileDesc));
   L->ntiles = take(16);
   L->total = off;
@@ -149,27 +148,21 @@ int run_routing(const Run& r, const void* x, const void* Wg, const float* bg, co
   sa.Cg = reinterpret_cast<int32_t*>(ws + L.Cg);
   sa.G = c->n_groups; sa.E = c->n_experts; sa.k = c->top_k; sa.C = c->capacity;
   sa.nbg = static_cast<int>(L.nbg);
+  sa.stats = m->stats;
   rc = status_of(moe::launch_gate_scan(sa, r.s));
-  if (rc) return rc;
-
-  moe::OffsetsArgs oa{};
-  oa.count = m->count; oa.ntot = sa.ntot; oa.offset = m->offset;
-  oa.gbase = reinterpret_cast<int32_t*>(ws + L.gbase);
-  oa.tiles = reinterpret_cast<moe::TileDesc*>(ws + L.tiles);
-  oa.num_tiles = reinterpret_cast<int32_t*>(ws + L.ntiles);
-  oa.stats = m->stats;
-  oa.G = c->n_groups; oa.E = c->n_experts; oa.k = c->top_k; oa.N = c->n_tokens; oa.BM = bm;
-  rc = status_of(moe::launch_offsets(oa, r.s));
   if (rc) return rc;
   record(ev, 2, r.s);
 
   moe::PermuteArgs pa{};
   pa.x = x; pa.topk_idx = m->topk_idx; pa.active = ra.active; pa.abase = sa.abase;
-  pa.gbase = oa.gbase; pa.pos = m->pos; pa.row = m->row; pa.topk_w = m->topk_w;
+  pa.count = m->count; pa.ntot = sa.ntot; pa.offset = m->offset;
+  pa.tiles = reinterpret_cast<moe::TileDesc*>(ws + L.tiles);
+  pa.num_tiles = reinterpret_cast<int32_t*>(ws + L.ntiles);
+  pa.pos = m->pos; pa.row = m->row; pa.topk_w = m->topk_w;
   pa.stats = m->stats; pa.buf = ws + L.buf;
   pa.N = c->n_tokens; pa.G = c->n_groups; pa.S = static_cast<int>(L.S); pa.M = c->d_model;
   pa.E = c->n_experts; pa.k = c->top_k; pa.C = c->capacity; pa.nbg = static_cast<int>(L.nbg);
-  pa.dtype = c->dtype;
+  pa.dtype = c->dtype; pa.BM = bm;
   rc = status_of(moe::launch_permute(pa, r.s));
   if (rc) return rc;
   record(ev, 3, r.s);

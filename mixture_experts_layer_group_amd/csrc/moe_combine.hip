@@ -56,44 +56,68 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   constexpr int EPC = DT == 1 ? 8 : 4;  // elements per 16-byte chunk
   const int ch = a.M / EPC;
   const size_t rowbytes = static_cast<size_t>(a.M) * (DT == 1 ? 2 : 4);
-  const char* xb = static_cast<const char*>(a.x);
-  const char* ob = static_cast<const char*>(a.o);
-  const char* sb = static_cast<const char*>(a.o_sh);
-  char* yb = static_cast<char*>(a.y);
-  for (int idx = t; idx < nt * ch; idx += 256) {
-    const int tl = idx / ch, c = idx - tl * ch;
-    const size_t n = static_cast<size_t>(tok0 + tl);
-    float acc[EPC];
-#pragma unroll
-    for (int q = 0; q < EPC; ++q) acc[q] = 0.f;
-    auto add = [&](const char* p, float wgt) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(p);
-      if (DT == 1) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[2 * q] = fmaf(wgt, __uint_as_float(v[q] << 16), acc[2 * q]);
-          acc[2 * q + 1] = fmaf(wgt, __uint_as_float(v[q] & 0xffff0000u), acc[2 * q + 1]);
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[q] = fmaf(wgt, __uint_as_float(v[q]), acc[q]);
-      }
-    };
-    for (int jj = 0; jj < k; ++jj) {
-      const int r = rows_s[tl][jj];
-      if (r >= 0) add(ob + static_cast<size_t>(r) * rowbytes + c * 16, w_s[tl][jj]);
-    }
-    if (sb) add(sb + n * rowbytes + c * 16, 1.0f);
-    if (a.residual) add(xb + n * rowbytes + c * 16, 1.0f);
-    u32x4 out;
+  const char* __restrict__ xb = static_cast<const char*>(a.x);
+  const char* __restrict__ ob = static_cast<const char*>(a.o);
+  const char* __restrict__ sb = static_cast<const char*>(a.o_sh);
+  char* __restrict__ yb = static_cast<char*>(a.y);
+  auto add = [&](float (&acc)[EPC], const u32x4 v, float wgt) {
     if (DT == 1) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) out[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] = fmaf(wgt, __uint_as_float(v[q] << 16), acc[2 * q]);
+        acc[2 * q + 1] = fmaf(wgt, __uint_as_float(v[q] & 0xffff0000u), acc[2 * q + 1]);
+      }
     } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) out[q] = __float_as_uint(acc[q]);
+      for (int q = 0; q < 4; ++q) acc[q] = fmaf(wgt, __uint_as_float(v[q]), acc[q]);
     }
-    *reinterpret_cast<u32x4*>(yb + n * rowbytes + c * 16) = out;
+  };
+  // U chunks per thread per round, every load of the round issued before its stores.
+  constexpr int U = 2;
+  const int total = nt * ch;
+  for (int base = t; base < total; base += 256 * U) {
+    u32x4 vo[U][kMaxTopK], vs[U], vx[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int idx = base + u * 256;
+      if (idx < total) {
+        const int tl = idx / ch, c = idx - tl * ch;
+        const size_t n = static_cast<size_t>(tok0 + tl);
+#pragma unroll
+        for (int jj = 0; jj < kMaxTopK; ++jj) {
+          if (jj < k) {
+            const int r = rows_s[tl][jj];
+            if (r >= 0) vo[u][jj] = *reinterpret_cast<const u32x4*>(ob + static_cast<size_t>(r) * rowbytes + c * 16);
+          }
+        }
+        if (sb) vs[u] = *reinterpret_cast<const u32x4*>(sb + n * rowbytes + c * 16);
+        if (a.residual) vx[u] = *reinterpret_cast<const u32x4*>(xb + n * rowbytes + c * 16);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int idx = base + u * 256;
+      if (idx >= total) continue;
+      const int tl = idx / ch, c = idx - tl * ch;
+      const size_t n = static_cast<size_t>(tok0 + tl);
+      float acc[EPC];
+#pragma unroll
+      for (int q = 0; q < EPC; ++q) acc[q] = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < kMaxTopK; ++jj)
+        if (jj < k && rows_s[tl][jj] >= 0) add(acc, vo[u][jj], w_s[tl][jj]);
+      if (sb) add(acc, vs[u], 1.0f);
+      if (a.residual) add(acc, vx[u], 1.0f);
+      u32x4 out;
+      if (DT == 1) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) out[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) out[q] = __float_as_uint(acc[q]);
+      }
+      *reinterpret_cast<u32x4*>(yb + n * rowbytes + c * 16) = out;
+    }
   }
 }
 

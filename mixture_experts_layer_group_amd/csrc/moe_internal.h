@@ -30,7 +30,7 @@ struct RouterArgs {
   int N, G, S, M, E, k, norm, rr, nbg, dtype;
 };
 
-// Per (group, expert): exclusive scans over router blocks -> block bases of the capacity
+// Per (group, expert), one wave per rank: exclusive scans over router blocks -> block bases of the capacity
 // positions, kept counts, active totals, and the aux partial sums.
 struct ScanArgs {
   const int32_t* ahist;   // [G][k][E][nbg]
@@ -41,6 +41,7 @@ struct ScanArgs {
   int32_t* ntot;          // [G][k][E] active slots per rank
   double* Pg;             // [G][E]  sum_n p[n, e] over the group
   int32_t* Cg;            // [G][E]  selections over the group
+  int32_t* stats;         // [4] (meta): stats[2] zeroed here for the dispatch kernel's count
   int G, E, k, C, nbg;
 };
 
@@ -48,31 +49,25 @@ struct TileDesc {         // one BM-row tile of one expert in the compact buffer
   int32_t expert, row0, nrows, pad;
 };
 
-// One block: offsets, per-(group, expert) row bases, GEMM tile lists, stats.
-struct OffsetsArgs {
-  const int32_t* count;   // [G, E]
-  const int32_t* ntot;    // [G][k][E]
-  int32_t* offset;        // [E+1] (meta)
-  int32_t* gbase;         // [G, E] first row of (g, e) in the compact buffer
-  TileDesc* tiles;        // [max tiles]
-  int32_t* num_tiles;     // [1]
-  int32_t* stats;         // [4] (meta): R, dropped slots, (fully dropped: zeroed here), rr skips
-  int G, E, k, N, BM;
-};
-
-// Capacity positions, dispatch rows, dropped-weight zeroing and the row scatter of x.
+// Offsets, capacity positions, dispatch rows, dropped-weight zeroing and the row scatter
+// of x.  Every block derives its group's row bases from count; block 0 writes offset,
+// the tile list and stats[0,1,3].
 struct PermuteArgs {
   const void* x;          // [N, M] T (nullptr: positions only)
   const int32_t* topk_idx;
   const uint8_t* active;
   const int32_t* abase;
-  const int32_t* gbase;
+  const int32_t* count;   // [G, E] kept slots
+  const int32_t* ntot;    // [G][k][E] active slots per rank
+  int32_t* offset;        // [E+1] (meta)
+  TileDesc* tiles;        // [max tiles]
+  int32_t* num_tiles;     // [1]
   int32_t* pos;           // [N, k] (meta)
   int32_t* row;           // [N, k] (meta)
   float* topk_w;          // [N, k] (meta): zeroed where the slot is not kept
-  int32_t* stats;         // stats[2] += fully dropped tokens of the block
+  int32_t* stats;         // [4] (meta); stats[2] += fully dropped tokens of the block
   void* buf;              // [R, M] T compact expert-major rows
-  int N, G, S, M, E, k, C, nbg, dtype;
+  int N, G, S, M, E, k, C, nbg, dtype, BM;
 };
 
 // One GEMM problem of the expert FFN: C[rows, N] = act(A[rows, K] . B_e[N, K]^T).
@@ -120,7 +115,6 @@ int gemm_block_n(int dtype, int n0, int n1);           // BN for problems with w
 
 hipError_t launch_router(const RouterArgs& a, hipStream_t s);
 hipError_t launch_gate_scan(const ScanArgs& a, hipStream_t s);
-hipError_t launch_offsets(const OffsetsArgs& a, hipStream_t s);
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
 hipError_t launch_expert_gemm(const GemmArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);

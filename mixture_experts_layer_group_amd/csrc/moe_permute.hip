@@ -1,13 +1,19 @@
-// moe_permute: capacity positions, dispatch rows, and the row scatter of x into the compact
-// expert-major buffer.
+// moe_permute: dispatch offsets, capacity positions, dispatch rows, and the row scatter of x
+// into the compact expert-major buffer.
 //
-// One block = the 64 tokens of one router block.  For rank j, lane = token: the lanes that
-// chose the same expert and are active are found with one ballot per bit of the expert id,
-// and the count of such lanes below gives the in-block prefix; adding the block base from
-// gate_scan_kernel gives the position of [GShard] "Top-2 gating 的四个机制 / Expert
-// capacity" (kept iff < C).  The row is the (group, expert) base of offsets_kernel plus the
-// position.  A token whose slots are all lost passes through the residual ([GShard]
-// "Capacity overflow 会跳过 expert computation"), counted in stats[2].
+// One block = the 64 tokens of one router block.  Every block first derives, from the kept
+// counts per (group, expert), where its group's rows of each expert start in the compact
+// buffer: rows are laid out expert-major, in (expert, group, position) order with the
+// capacity padding squeezed out ([GShard] "Sharding 与 MoE 的交替布局": group-major tokens
+// regrouped into an expert-major buffer).  Block 0 also writes the expert offsets, the list
+// of BM-row GEMM tiles and the stats.
+//
+// For rank j, lane = token: the lanes that chose the same expert and are active are found
+// with one ballot per bit of the expert id, and the count of such lanes below gives the
+// in-block prefix; adding the block base from gate_scan_kernel gives the position of
+// [GShard] "Top-2 gating 的四个机制 / Expert capacity" (kept iff < C).  The row is the
+// (group, expert) base plus the position.  A token whose slots are all lost passes through
+// the residual ([GShard] "Capacity overflow 会跳过 expert computation"), counted in stats[2].
 //
 // The scatter then copies every kept token's row of x once per kept slot, 16 bytes per
 // lane, reading x once ([GShard] "Automatic propagation 与 manual override": dispatch as an
@@ -18,9 +24,82 @@
 namespace moe {
 namespace {
 
+// Exclusive scan of one value per thread over a 256-thread block; returns the total in *tot.
+__device__ int block_exclusive_scan(int v, int* tot, int* scratch /* [4] */) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int inc = wave_inclusive_scan(v);
+  if (lane == 63) scratch[w] = inc;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int s = scratch[i];
+    if (i < w) before += s;
+    all += s;
+  }
+  __syncthreads();
+  *tot = all;
+  return before + inc - v;
+}
+
+// Row bases of group g's experts in the compact buffer (into gbase_s), and in block 0 the
+// expert offsets, the GEMM tile list and the stats.  T threads share an expert's sum over
+// the groups (T = 256 / E rounded down to a power of two, at most 64).
+__device__ void offsets(const PermuteArgs& a, int g, int* gbase_s, int* scratch) {
+  const int t = threadIdx.x, E = a.E, G = a.G;
+  int T = 64;
+  while (T * E > 256) T >>= 1;
+  const int e = t / T, sub = t - e * T;
+  const bool lead = sub == 0 && e < E;
+  int tot = 0, pre = 0;
+  if (e < E)
+    for (int gg = sub; gg < G; gg += T) {
+      const int c = a.count[static_cast<size_t>(gg) * E + e];
+      tot += c;
+      if (gg < g) pre += c;
+    }
+  for (int o = T >> 1; o > 0; o >>= 1) {  // lanes e*T .. e*T+T-1 sit in one wave
+    tot += __shfl_xor(tot, o, 64);
+    pre += __shfl_xor(pre, o, 64);
+  }
+  int R = 0;
+  const int off = block_exclusive_scan(lead ? tot : 0, &R, scratch);
+  if (lead) gbase_s[e] = off + pre;
+  if (blockIdx.x != 0) return;
+
+  if (lead) a.offset[e] = off;
+  if (t == 0) a.offset[E] = R;
+  // GEMM tiles: expert e's rows [offset[e], offset[e] + tot) cut into BM-row pieces.
+  const int mt = lead ? (tot + a.BM - 1) / a.BM : 0;
+  int ntiles = 0;
+  const int tp = block_exclusive_scan(mt, &ntiles, scratch);
+  for (int i = 0; i < mt; ++i) {
+    TileDesc d;
+    d.expert = e;
+    d.row0 = off + i * a.BM;
+    d.nrows = min(a.BM, tot - i * a.BM);
+    d.pad = 0;
+    a.tiles[tp + i] = d;
+  }
+  if (t == 0) *a.num_tiles = ntiles;
+  // stats: R, dropped slots (active but over capacity), fully dropped tokens (stats[2],
+  // counted below by every block), random-routing skips (selected but not active).
+  int act = 0;
+  for (int i = t; i < G * a.k * E; i += 256) act += a.ntot[i];
+  int all = 0;
+  block_exclusive_scan(act, &all, scratch);
+  if (t == 0) {
+    a.stats[0] = R;
+    a.stats[1] = all - R;
+    a.stats[3] = a.N * a.k - all;
+  }
+}
+
 __global__ __launch_bounds__(256) void permute_kernel(PermuteArgs a) {
   __shared__ int rows_s[kRouteTokens][kMaxTopK];
   __shared__ int kept_any[kRouteTokens];
+  __shared__ int gbase_s[kMaxExperts];
+  __shared__ int scratch[4];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int b = blockIdx.x;
   const int g = b / a.nbg, bi = b - g * a.nbg;
@@ -28,6 +107,7 @@ __global__ __launch_bounds__(256) void permute_kernel(PermuteArgs a) {
   const int nt = min(kRouteTokens, a.S - bi * kRouteTokens);
   const int k = a.k;
   if (t < kRouteTokens) kept_any[t] = 0;
+  offsets(a, g, gbase_s, scratch);
   __syncthreads();
 
   const bool valid = lane < nt;
@@ -48,7 +128,7 @@ __global__ __launch_bounds__(256) void permute_kernel(PermuteArgs a) {
       int p = a.C;
       if (act) p = a.abase[((static_cast<size_t>(g) * k + j) * a.E + e) * a.nbg + bi] + prefix;
       const bool kept = act && p < a.C;
-      const int r = kept ? a.gbase[static_cast<size_t>(g) * a.E + e] + p : -1;
+      const int r = kept ? gbase_s[e] + p : -1;
       a.pos[o] = kept ? p : -1;
       a.row[o] = r;
       if (!kept) a.topk_w[o] = 0.f;
@@ -67,15 +147,38 @@ __global__ __launch_bounds__(256) void permute_kernel(PermuteArgs a) {
   const int esz = a.dtype == 1 ? 2 : 4;
   const int ch = a.M * esz / 16;  // 16-byte chunks per row
   const size_t rowbytes = static_cast<size_t>(a.M) * esz;
-  const char* xb = static_cast<const char*>(a.x);
-  char* bb = static_cast<char*>(a.buf);
-  for (int idx = t; idx < nt * ch; idx += 256) {
-    const int tl = idx / ch, c = idx - tl * ch;
-    if (!kept_any[tl]) continue;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(xb + static_cast<size_t>(tok0 + tl) * rowbytes + c * 16);
-    for (int j = 0; j < k; ++j) {
-      const int r = rows_s[tl][j];
-      if (r >= 0) *reinterpret_cast<u32x4*>(bb + static_cast<size_t>(r) * rowbytes + c * 16) = v;
+  const char* __restrict__ xb = static_cast<const char*>(a.x);
+  char* __restrict__ bb = static_cast<char*>(a.buf);
+  // U chunks per thread per round: all U loads are issued before any store, so U loads are
+  // in flight per lane (the stores may not be reordered above loads the compiler cannot
+  // prove disjoint from them).
+  constexpr int U = 4;
+  const int total = nt * ch;
+  for (int base = t; base < total; base += 256 * U) {
+    u32x4 v[U];
+    int tlv[U], cv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int idx = base + u * 256;
+      tlv[u] = -1;
+      if (idx < total) {
+        const int tl = idx / ch, c = idx - tl * ch;
+        if (kept_any[tl]) {
+          tlv[u] = tl;
+          cv[u] = c;
+          v[u] = *reinterpret_cast<const u32x4*>(xb + static_cast<size_t>(tok0 + tl) * rowbytes +
+                                                 c * 16);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (tlv[u] < 0) continue;
+      for (int j = 0; j < k; ++j) {
+        const int r = rows_s[tlv[u]][j];
+        if (r >= 0)
+          *reinterpret_cast<u32x4*>(bb + static_cast<size_t>(r) * rowbytes + cv[u] * 16) = v[u];
+      }
     }
   }
 }
