@@ -5,7 +5,7 @@
 // the gate-weighted sum of the selected experts' outputs; "Capacity overflow 会跳过 expert
 // computation": a token with no kept slot leaves through the residual, so y_n = x_n
 // bit-exactly (0 + x in fp32 is x).  [Lec16] "共享专家 vs. 路由专家": the shared experts add
-// with weight 1.  Each block gathers 32 tokens; lanes move 16-byte chunks of rows.
+// with weight 1.  Each block gathers 16 tokens; lanes move 16-byte chunks of rows.
 //
 // Block 0 also finishes the aux loss of [GShard] "Top-2 gating 的四个机制 / Auxiliary loss":
 // aux = (1/G) sum_g E/(k S) sum_e m_{g,e} c_{g,e},  m_{g,e} = P_{g,e} / S, from the per-
@@ -17,7 +17,7 @@
 namespace moe {
 namespace {
 
-constexpr int kTok = 32;  // tokens per block
+constexpr int kTok = 16;  // tokens per block
 
 __device__ void aux_final(const CombineArgs& a) {
   __shared__ double red[4];

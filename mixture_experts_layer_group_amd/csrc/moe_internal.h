@@ -68,6 +68,7 @@ struct PermuteArgs {
   int32_t* stats;         // [4] (meta); stats[2] += fully dropped tokens of the block
   void* buf;              // [R, M] T compact expert-major rows
   int N, G, S, M, E, k, C, nbg, dtype, BM;
+  int slices;             // column slices per router block (set by the launcher)
 };
 
 // One GEMM problem of the expert FFN: C[rows, N] = act(A[rows, K] . B_e[N, K]^T).

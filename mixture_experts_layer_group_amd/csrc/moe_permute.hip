@@ -17,7 +17,10 @@
 //
 // The scatter then copies every kept token's row of x once per kept slot, 16 bytes per
 // lane, reading x once ([GShard] "Automatic propagation 与 manual override": dispatch as an
-// index tensor plus a gather, here the transposed scatter).
+// index tensor plus a gather, here the transposed scatter).  A router block's rows are cut
+// into `slices` column slices, one block each, so that enough blocks are in flight to
+// cover HBM latency; the slices repeat the (cheap) position work and slice 0 alone writes
+// the per-slot outputs.
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -101,7 +104,8 @@ __global__ __launch_bounds__(256) void permute_kernel(PermuteArgs a) {
   __shared__ int gbase_s[kMaxExperts];
   __shared__ int scratch[4];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int b = blockIdx.x;
+  const int b = blockIdx.x / a.slices, slice = blockIdx.x - b * a.slices;
+  const bool meta = slice == 0;
   const int g = b / a.nbg, bi = b - g * a.nbg;
   const int tok0 = g * a.S + bi * kRouteTokens;
   const int nt = min(kRouteTokens, a.S - bi * kRouteTokens);
@@ -129,15 +133,17 @@ __global__ __launch_bounds__(256) void permute_kernel(PermuteArgs a) {
       if (act) p = a.abase[((static_cast<size_t>(g) * k + j) * a.E + e) * a.nbg + bi] + prefix;
       const bool kept = act && p < a.C;
       const int r = kept ? gbase_s[e] + p : -1;
-      a.pos[o] = kept ? p : -1;
-      a.row[o] = r;
-      if (!kept) a.topk_w[o] = 0.f;
+      if (meta) {
+        a.pos[o] = kept ? p : -1;
+        a.row[o] = r;
+        if (!kept) a.topk_w[o] = 0.f;
+      }
       rows_s[lane][j] = r;
       if (kept) kept_any[lane] = 1;
     }
   }
   __syncthreads();
-  if (w == 0) {
+  if (w == 0 && meta) {
     const bool dropped = valid && kept_any[lane] == 0;
     const int c = __popcll(ballot(dropped));
     if (lane == 0 && c) atomicAdd(&a.stats[2], c);
@@ -145,10 +151,13 @@ __global__ __launch_bounds__(256) void permute_kernel(PermuteArgs a) {
   if (!a.x) return;
 
   const int esz = a.dtype == 1 ? 2 : 4;
-  const int ch = a.M * esz / 16;  // 16-byte chunks per row
+  const int chr = a.M * esz / 16;  // 16-byte chunks per row
+  const int per = (chr + a.slices - 1) / a.slices;
+  const int c0 = slice * per;
+  const int ch = max(0, min(chr, c0 + per) - c0);  // chunks of this slice
   const size_t rowbytes = static_cast<size_t>(a.M) * esz;
-  const char* __restrict__ xb = static_cast<const char*>(a.x);
-  char* __restrict__ bb = static_cast<char*>(a.buf);
+  const char* __restrict__ xb = static_cast<const char*>(a.x) + c0 * 16;
+  char* __restrict__ bb = static_cast<char*>(a.buf) + c0 * 16;
   // U chunks per thread per round: all U loads are issued before any store, so U loads are
   // in flight per lane (the stores may not be reordered above loads the compiler cannot
   // prove disjoint from them).
@@ -185,10 +194,21 @@ __global__ __launch_bounds__(256) void permute_kernel(PermuteArgs a) {
 
 }  // namespace
 
-hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
-  const int grid = a.G * a.nbg;
+int permute_slices(const PermuteArgs& a) {
+  const int blocks = a.G * a.nbg;
+  const int chr = a.M * (a.dtype == 1 ? 2 : 4) / 16;
+  int slices = 1;
+  if (a.x)
+    while (blocks * slices < 2048 && chr / (2 * slices) >= 16) slices *= 2;
+  return slices;
+}
+
+hipError_t launch_permute(const PermuteArgs& a0, hipStream_t s) {
+  PermuteArgs a = a0;
+  a.slices = permute_slices(a);
+  const int64_t grid = static_cast<int64_t>(a.G) * a.nbg * a.slices;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(permute_kernel, dim3(grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(permute_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
