@@ -10,7 +10,7 @@ GShard-style layers they equal 2N/(G*E) per group, the fractional capacity of
 Sharding" (section "Top-2 gating 的四个机制 / Local group dispatching").
 """
 
-ACT_RELU, ACT_GELU = 0, 1
+ACT_RELU, ACT_GELU, ACT_SWIGLU = 0, 1, 2
 NORM_NONE, NORM_SUM = 0, 1
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
@@ -55,6 +55,14 @@ WORKLOADS = {
         gate_norm=NORM_SUM, dtype=DTYPE_BF16, zipf_s=1.2,
         desc="shared+routed bf16: 32768 tokens, M=2048, 2 shared + 64 routed experts "
              "2048->1408->2048 GELU, top-6, C=1.5*6N/64=4608, Zipf(1.2) offsets"),
+    # The gated-expert form ([Lec16] "DeepSeek V3 MoE (670B)": SwiGLU experts) on the
+    # shared+routed layer above.
+    "shared_routed_swiglu_bf16": _cfg(
+        "shared_routed_swiglu_bf16", n_tokens=32768, n_groups=1, d_model=2048, d_ff=1408,
+        n_experts=64, n_shared=2, top_k=6, capacity=4608, act=ACT_SWIGLU,
+        gate_norm=NORM_SUM, dtype=DTYPE_BF16, zipf_s=1.2,
+        desc="shared+routed SwiGLU bf16: 32768 tokens, M=2048, 2 shared + 64 routed experts "
+             "(Swish(x W1) * x W2) W3 with H=1408, top-6, C=4608, Zipf(1.2) offsets"),
 }
 
 # The workload the benchmark times by default.
@@ -83,6 +91,14 @@ SMALL = {
         "small_bare_dropless", n_tokens=520, n_groups=2, d_model=128, d_ff=256,
         n_experts=5, top_k=2, capacity=260, act=ACT_RELU, gate_norm=NORM_SUM,
         dtype=DTYPE_BF16, residual=0, seed=15),
+    "small_swiglu_shared": _cfg(
+        "small_swiglu_shared", n_tokens=1200, n_groups=2, d_model=256, d_ff=384,
+        n_experts=8, n_shared=1, top_k=2, capacity=140, act=ACT_SWIGLU,
+        gate_norm=NORM_SUM, dtype=DTYPE_BF16, zipf_s=0.8, seed=16),
+    "small_swiglu_fp32": _cfg(
+        "small_swiglu_fp32", n_tokens=500, n_groups=1, d_model=128, d_ff=192,
+        n_experts=6, n_shared=2, top_k=3, capacity=220, act=ACT_SWIGLU,
+        gate_norm=NORM_SUM, dtype=DTYPE_F32, seed=17),
 }
 
 ALL = {**WORKLOADS, **SMALL}

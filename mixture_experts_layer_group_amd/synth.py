@@ -7,7 +7,9 @@ returns, so it is the one piece of code the two sides share.
 Recipe (one ``numpy.random.default_rng(seed)`` stream, PCG64, drawn in this order):
   x   [N, M]            ~ N(0, 1)
   Wg  [E, M]            ~ N(0, 1/M)       (row e is expert e's gate vector)
-  W1  [E+Es, H, M]      ~ N(0, 1/M)       (row n of W1[e] feeds hidden unit n)
+  W1  [E+Es, H, M]      ~ N(0, 1/M)       (row n of W1[e] feeds hidden unit n;
+                                           [E+Es, 2H, M] for the gated expert, act 2:
+                                           H gate rows, then H up rows)
   W2  [E+Es, M, H]      ~ N(0, 1/H)       (row m of W2[e] feeds output feature m)
   u   [N]               ~ U[0, 1) fp32    (only when random routing is on)
   bg  [E]               = -s * ln(e + 1)  (only when zipf_s > 0: the log of a Zipf(s)
@@ -40,6 +42,11 @@ def _normal(rng, shape, std):
     return out
 
 
+def w1_rows(cfg):
+    """Rows of one expert's W1: H, or 2H (gate and up projections) for the gated expert."""
+    return 2 * cfg["d_ff"] if cfg["act"] == 2 else cfg["d_ff"]
+
+
 class Inputs:
     """Host copies of one layer's inputs.
 
@@ -58,7 +65,7 @@ class Inputs:
         raw = {
             "x": _normal(rng, (N, M), 1.0),
             "Wg": _normal(rng, (E, M), (1.0 / M) ** 0.5),
-            "W1": _normal(rng, (E + Es, H, M), (1.0 / M) ** 0.5),
+            "W1": _normal(rng, (E + Es, w1_rows(cfg), M), (1.0 / M) ** 0.5),
             "W2": _normal(rng, (E + Es, M, H), (1.0 / H) ** 0.5),
         }
         self.u = rng.random(size=N, dtype=np.float32) if cfg["random_routing"] else None

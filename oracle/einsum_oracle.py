@@ -13,11 +13,21 @@ combine weight is zero, [GShard] "Static shape 与 uneven partition"), and the o
 are combined with a second einsum.  Float64 throughout, small inputs only.
 """
 import numpy as np
-from scipy.special import erf
+from scipy.special import erf, expit
 
 
-def _act(z, act):
-    return np.maximum(z, 0.0) if act == 0 else 0.5 * z * (1.0 + erf(z / np.sqrt(2.0)))
+def _hidden(rows, W1e, act):
+    """Hidden layer of one expert.  The gated form (act 2, [Lec16] "DeepSeek V3 MoE
+    (670B)") multiplies z*sigmoid(z) of the first H projections by the last H ones;
+    the sigmoid is scipy's expit."""
+    pre = rows @ np.asarray(W1e, np.float64).T
+    if act == 0:
+        return np.maximum(pre, 0.0)
+    if act == 1:
+        return 0.5 * pre * (1.0 + erf(pre / np.sqrt(2.0)))
+    H = pre.shape[1] // 2
+    g, up = pre[:, :H], pre[:, H:]
+    return g * expit(g) * up
 
 
 def einsum_layer(cfg, x, Wg, W1, W2, bg=None, u=None, logits32=None):
@@ -74,11 +84,11 @@ def einsum_layer(cfg, x, Wg, W1, W2, bg=None, u=None, logits32=None):
     out = np.zeros_like(buf)
     for e in range(E):
         rows = buf[e].reshape(G * C, M)
-        h = _act(rows @ np.asarray(W1[e], np.float64).T, cfg["act"])
+        h = _hidden(rows, W1[e], cfg["act"])
         out[e] = (h @ np.asarray(W2[e], np.float64).T).reshape(G, C, M)
     y = np.einsum("gsec,egcm->gsm", combine, out).reshape(N, M)
     for q in range(Es):
-        h = _act(x @ np.asarray(W1[E + q], np.float64).T, cfg["act"])
+        h = _hidden(x, W1[E + q], cfg["act"])
         y = y + h @ np.asarray(W2[E + q], np.float64).T
     if cfg["residual"]:
         y = y + x

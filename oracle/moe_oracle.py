@@ -33,6 +33,11 @@ function that depends on it (and listed in the design doc):
   R-res    the layer output includes the residual: y = x + sum_j w_j FFN_e_j(x) (+ shared
            experts); a fully dropped token gets y = x.  residual=0 gives the bare layer.
   R-ffn    expert = act(x W1^T) W2^T, no biases; GELU is the exact erf form.
+  R-glu    the gated expert of [Lec16] "DeepSeek V3 MoE (670B)", (Swish(x W1) * (x W2)) W3,
+           takes Swish with beta = 1 (z * sigmoid(z), also called SiLU).  Its two input
+           projections are stacked in one weight: W1[e] is [2H, M], rows 0..H-1 the
+           Swish (gate) projection and rows H..2H-1 the linear (up) one; W2[e] [M, H]
+           holds the output projection (the formula's W3).
   R-empty  an empty batch (N = 0) routes nothing and has aux = 0.
 
 Pins: every public function here is checked by ``tests/test_oracle_pins.py`` against
@@ -236,21 +241,46 @@ def route(cfg, logits32, u=None):
 
 # --------------------------------------------------------------------------- experts
 
+ACT_SWIGLU = 2
+
+
 def activation(z, act):
     """ReLU (act 0) or exact GELU (act 1): 0.5 z (1 + erf(z / sqrt 2)) (R-ffn)."""
     z = np.asarray(z, dtype=np.float64)
     if act == 0:
         return np.maximum(z, 0.0)
-    return 0.5 * z * (1.0 + _erf(z / np.sqrt(2.0)))
+    if act == 1:
+        return 0.5 * z * (1.0 + _erf(z / np.sqrt(2.0)))
+    raise ValueError("the gated expert's activation acts on two projections (expert_ffn)")
+
+
+def swish(z):
+    """Swish with beta = 1: z * sigmoid(z), float64 (R-glu).
+
+    sigmoid(z) = 1 / (1 + exp(-z)) is evaluated from exp(-|z|), which never overflows.
+    """
+    z = np.asarray(z, dtype=np.float64)
+    t = np.exp(-np.abs(z))
+    sig = np.where(z >= 0, 1.0 / (1.0 + t), t / (1.0 + t))
+    return z * sig
 
 
 def expert_ffn(xrows, W1e, W2e, act):
-    """One expert on a batch of token rows: act(x W1e^T) W2e^T, float64, no biases.
+    """One expert on a batch of token rows, float64, no biases.
 
-    [GShard] "MoE Transformer": each expert is a two-layer network of the dense FFN's
-    shape.  W1e is [H, M] (row n feeds hidden unit n), W2e is [M, H].
+    act 0/1: act(x W1e^T) W2e^T.  [GShard] "MoE Transformer": each expert is a two-layer
+    network of the dense FFN's shape; W1e is [H, M] (row n feeds hidden unit n), W2e is
+    [M, H].
+    act 2 (gated): (Swish(x G^T) * (x U^T)) W2e^T with G = W1e[:H], U = W1e[H:] (R-glu);
+    [Lec16] "DeepSeek V3 MoE (670B)": every expert uses this SwiGLU form.
     """
-    h = activation(np.asarray(xrows, np.float64) @ np.asarray(W1e, np.float64).T, act)
+    x = np.asarray(xrows, np.float64)
+    W1e = np.asarray(W1e, np.float64)
+    if act == ACT_SWIGLU:
+        H = W1e.shape[0] // 2
+        h = swish(x @ W1e[:H].T) * (x @ W1e[H:].T)
+    else:
+        h = activation(x @ W1e.T, act)
     return h @ np.asarray(W2e, np.float64).T
 
 

@@ -16,7 +16,7 @@ import types
 
 import numpy as np
 import pytest
-from scipy.special import ndtr
+from scipy.special import expit, ndtr
 
 from mixture_experts_layer_group_amd import configs
 from oracle import einsum_oracle as eo
@@ -248,12 +248,12 @@ def check_vs_einsum(m, trials=60):
         E = 4; k = int(rng.integers(1, 3)); G = int(rng.integers(1, 3)); N = 8
         C = int(rng.integers(1, 5)); rr = int(k == 2 and t % 2)
         cfg = cfg_of(n_tokens=N, n_groups=G, n_experts=E, top_k=k, capacity=C,
-                     random_routing=rr, act=t % 2, gate_norm=int(t % 3 != 0),
+                     random_routing=rr, act=t % 3, gate_norm=int(t % 4 != 0),
                      n_shared=int(t % 5 == 0), residual=int(t % 7 != 0))
         M, H = 6, 10
         x = rng.standard_normal((N, M))
         Wg = rng.standard_normal((E, M))
-        W1 = rng.standard_normal((E + cfg["n_shared"], H, M))
+        W1 = rng.standard_normal((E + cfg["n_shared"], 2 * H if cfg["act"] == 2 else H, M))
         W2 = rng.standard_normal((E + cfg["n_shared"], M, H))
         u = rng.random(N).astype(np.float32)
         l32 = m.router_logits(x, Wg).astype(np.float32)
@@ -379,21 +379,71 @@ def check_gelu_values(m):
 
 def check_single_expert_is_dense_ffn(m):
     """E=1, k=1, C=N, norm=none => p = 1 => y = x + act(x W1^T) W2^T, a plain dense FFN
-    evaluated here with numpy matmuls on non-square weights (M=6, H=10)."""
+    evaluated here with numpy matmuls on non-square weights (M=6, H=10).  For the gated
+    expert the hidden layer is g * expit(g) * u (scipy's logistic sigmoid), g and u the
+    first and last H columns of x W1^T."""
     rng = np.random.default_rng(11)
     N, M, H = 9, 6, 10
-    x = rng.standard_normal((N, M)); W1 = rng.standard_normal((1, H, M))
-    W2 = rng.standard_normal((1, M, H)); Wg = rng.standard_normal((1, M))
-    for act in (0, 1):
+    x = rng.standard_normal((N, M)); Wg = rng.standard_normal((1, M))
+    W2 = rng.standard_normal((1, M, H))
+    for act in (0, 1, 2):
+        W1 = rng.standard_normal((1, 2 * H if act == 2 else H, M))
         cfg = cfg_of(n_tokens=N, n_experts=1, top_k=1, capacity=N, gate_norm=0, act=act,
                      d_model=M, d_ff=H)
         r = m.route(cfg, m.router_logits(x, Wg).astype(np.float32))
         np.testing.assert_array_equal(r["topk_w"], np.ones((N, 1)))
         y = m.layer_outputs(cfg, x, W1, W2, r)
         pre = np.matmul(x, np.transpose(W1[0]))
-        h = np.maximum(pre, 0) if act == 0 else pre * ndtr(pre)
+        if act == 0:
+            h = np.maximum(pre, 0)
+        elif act == 1:
+            h = pre * ndtr(pre)
+        else:
+            h = pre[:, :H] * expit(pre[:, :H]) * pre[:, H:]
         np.testing.assert_allclose(y, x + np.matmul(h, np.transpose(W2[0])), rtol=1e-12,
                                    atol=1e-12)
+
+
+def check_swish_values(m):
+    """Swish(z) = z * sigmoid(z): against scipy's expit, the odd-part identity
+    Swish(z) - Swish(-z) = z (sigmoid(z) + sigmoid(-z) = 1), Swish(0) = 0, slope 1/2 at 0,
+    and no overflow at |z| = 800."""
+    z = np.array([-800.0, -40.0, -3.0, -1.0, -1e-3, 0.0, 1e-3, 0.5, 2.0, 40.0, 800.0])
+    np.testing.assert_allclose(m.swish(z), z * expit(z), rtol=1e-14, atol=1e-300)
+    np.testing.assert_allclose(m.swish(z) - m.swish(-z), z, rtol=1e-14, atol=1e-14)
+    assert m.swish(np.array([0.0]))[0] == 0.0
+    assert abs(m.swish(np.array([1e-8]))[0] / 1e-8 - 0.5) < 1e-8
+    assert np.isfinite(m.swish(z)).all()
+
+
+def check_swiglu_gate_saturation(m):
+    """Gated expert with a gate pre-activation pinned at +-40 through a constant input
+    feature: Swish(40) = 40 in float64 (sigmoid(40) rounds to 1), so the expert is
+    40 * (x U^T) W3^T, linear in the up projection; Swish(-40) ~ -1.7e-16 turns the expert
+    off.  A swapped gate/up, a missing Swish or a missing product fails here."""
+    rng = np.random.default_rng(21)
+    N, M, H = 7, 5, 6
+    x = rng.standard_normal((N, M)); x[:, 0] = 1.0
+    U = rng.standard_normal((H, M)); W3 = rng.standard_normal((M, H))
+    for c, scale in ((40.0, 40.0), (-40.0, 0.0)):
+        G = np.zeros((H, M)); G[:, 0] = c
+        out = m.expert_ffn(x, np.concatenate([G, U]), W3, 2)
+        want = scale * np.matmul(np.matmul(x, U.T), W3.T)
+        np.testing.assert_allclose(out, want, rtol=1e-13, atol=1e-12)
+
+
+def check_swiglu_split_identity(m):
+    """The gated expert splits by hidden units too: with the gate, up and output
+    projections cut at the same hidden indices, the parts add up to the whole.  Pins the
+    H-tiling of the fused gate/up GEMM and of the shared gated experts."""
+    rng = np.random.default_rng(22)
+    N, M, H = 6, 5, 12
+    x = rng.standard_normal((N, M))
+    G = rng.standard_normal((H, M)); U = rng.standard_normal((H, M)); W3 = rng.standard_normal((M, H))
+    full = m.expert_ffn(x, np.concatenate([G, U]), W3, 2)
+    parts = sum(m.expert_ffn(x, np.concatenate([G[a:b], U[a:b]]), W3[:, a:b], 2)
+                for a, b in [(0, 4), (4, 9), (9, 12)])
+    np.testing.assert_allclose(full, parts, rtol=1e-12, atol=1e-12)
 
 
 def check_split_identity(m):
@@ -431,6 +481,7 @@ CHECKS = [check_aux_uniform_scores, check_aux_round_robin, check_aux_saturation,
           check_scan_closed_form, check_vs_einsum, check_megablocks_worked_example,
           check_gate_weights, check_random_routing, check_router_onehot_rows,
           check_gelu_values, check_single_expert_is_dense_ffn, check_split_identity,
+          check_swish_values, check_swiglu_gate_saturation, check_swiglu_split_identity,
           check_empty_batch]
 
 
@@ -456,6 +507,9 @@ def test_capacities_of_workloads():
     c = w["large_expert_bf16"]; assert c["capacity"] == c["n_tokens"]
     c = w["shared_routed_bf16"]
     assert c["capacity"] == int(1.5 * 6 * c["n_tokens"] / 64)
+    g = w["shared_routed_swiglu_bf16"]
+    assert {k: v for k, v in g.items() if k not in ("name", "act", "desc")} == \
+        {k: v for k, v in c.items() if k not in ("name", "act", "desc")}
 
 
 # ----------------------------------------------------------------------------- planted mistakes
@@ -531,6 +585,25 @@ def _gelu_tanh(z, act):
     return 0.5 * z * (1 + np.tanh(np.sqrt(2 / np.pi) * (z + 0.044715 * z ** 3)))
 
 
+def _swiglu_gate_up_swapped(xrows, W1e, W2e, act):
+    if act != 2:
+        return mo.expert_ffn(xrows, W1e, W2e, act)
+    H = W1e.shape[0] // 2
+    return mo.expert_ffn(xrows, np.concatenate([W1e[H:], W1e[:H]]), W2e, act)
+
+
+def _swiglu_no_swish(xrows, W1e, W2e, act):
+    if act != 2:
+        return mo.expert_ffn(xrows, W1e, W2e, act)
+    H = W1e.shape[0] // 2
+    x = np.asarray(xrows, np.float64)
+    return ((x @ W1e[:H].T) * (x @ W1e[H:].T)) @ np.asarray(W2e).T
+
+
+def _swish_is_sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-np.asarray(z, np.float64)))
+
+
 def _rows_group_major(idx, pos, count):
     G, E = count.shape
     N, k = idx.shape
@@ -568,7 +641,24 @@ MUTANTS = {
     "gelu_tanh_approx": dict(activation=_gelu_tanh),
     "rows_group_major": dict(dispatch_rows=_rows_group_major),
     "router_bias_reversed": dict(router_logits=_router_bias_reversed),
+    "swiglu_gate_up_swapped": dict(expert_ffn=_swiglu_gate_up_swapped),
+    "swiglu_no_swish": dict(expert_ffn=_swiglu_no_swish),
+    "swish_is_sigmoid": dict(swish=_swish_is_sigmoid),
 }
+
+
+def _expert_ffn_for(ns):
+    """expert_ffn whose activation and Swish are the (planted) ones of the namespace."""
+    def expert_ffn(xr, W1e, W2e, act):
+        x = np.asarray(xr, np.float64)
+        W1e = np.asarray(W1e, np.float64)
+        if act == 2:
+            H = W1e.shape[0] // 2
+            h = ns.swish(x @ W1e[:H].T) * (x @ W1e[H:].T)
+        else:
+            h = ns.activation(x @ W1e.T, act)
+        return h @ np.asarray(W2e).T
+    return expert_ffn
 
 
 def _layer_outputs_for(ns):
@@ -594,10 +684,10 @@ def _layer_outputs_for(ns):
 def test_planted_mistakes(name):
     """Each plausible mistake planted in a copy of the oracle fails at least one pin."""
     ns = clone(**MUTANTS[name])
-    if "expert_ffn" in MUTANTS[name] or "activation" in MUTANTS[name]:
-        if "activation" in MUTANTS[name]:
-            act_fn = ns.activation
-            ns.expert_ffn = lambda xr, a, b, act: act_fn(np.asarray(xr) @ np.asarray(a).T, act) @ np.asarray(b).T
+    planted = MUTANTS[name]
+    if "expert_ffn" in planted or "activation" in planted or "swish" in planted:
+        if "activation" in planted or "swish" in planted:
+            ns.expert_ffn = _expert_ffn_for(ns)
         ns.layer_outputs = _layer_outputs_for(ns)
     caught = []
     for check in CHECKS:
