@@ -9,8 +9,9 @@ recorded by the library at the stage boundaries (on the launch stream) give per-
 times.  Prints one JSON line.
 
 The roofline object is for the dominant kernel, the expert GEMM: algorithmic flops per
-launch (2 R M H for the routed rows, + 2 N Es H M for shared experts; R = kept rows) over
-the average launch time of its two launches per step, against the bf16 dense MFMA peak.
+launch (2 R M H for the routed rows, + 2 N Es H M for shared experts; R = kept rows; the
+gated experts' GEMM 1 does twice that) averaged over its two launches per step, over their
+average launch time, against the bf16 dense MFMA peak.
 The cpu_baseline object times the CPU oracle on a bounded sample of the same workload.
 """
 import argparse
@@ -210,14 +211,18 @@ def main():
     E, Es, k = cfg["n_experts"], cfg["n_shared"], cfg["top_k"]
     b = 2 if cfg["dtype"] == 1 else 4
 
-    # Dominant kernel: the expert GEMM (two launches per step with equal flops: GEMM 1 with
-    # the activation and GEMM 2, two instantiations of gemm_bf16_kernel).  Algorithmic work
-    # per launch: flops 2 R M H (+ 2 N Es H M); bytes = the activations read and written once
-    # plus the weights of every expert that received rows, averaged over the two launches.
+    # Dominant kernel: the expert GEMM (two launches per step: GEMM 1 with the activation and
+    # GEMM 2, two instantiations of gemm_bf16_kernel).  Algorithmic work per launch: flops
+    # 2 R M H (+ 2 N Es H M), doubled for the gated GEMM 1 (gate and up projections); bytes =
+    # the activations read and written once plus the weights of every expert that received
+    # rows; both averaged over the two launches.
     count = meta.count.cpu().numpy()
     live = int((count.sum(axis=0) > 0).sum())
-    flops_launch = 2.0 * R * M * H + 2.0 * N * Es * H * M
-    bytes_g1 = (R * M + live * H * M + R * H + (N * M + Es * H * M + N * Es * H if Es else 0)) * b
+    gl = 2 if cfg["act"] == configs.ACT_SWIGLU else 1
+    flops_g2 = 2.0 * R * M * H + 2.0 * N * Es * H * M
+    flops_launch = (gl * flops_g2 + flops_g2) / 2.0
+    bytes_g1 = (R * M + gl * live * H * M + R * H +
+                (N * M + gl * Es * H * M + N * Es * H if Es else 0)) * b
     bytes_g2 = (R * H + live * M * H + R * M + (N * Es * H + Es * M * H + N * M if Es else 0)) * b
     bytes_launch = (bytes_g1 + bytes_g2) / 2.0
     gemm_ms = (stage_avg["ffn1"] + stage_avg["ffn2"]) / 2.0
@@ -253,7 +258,7 @@ def main():
         gbps = by / (t * 1e-3) / 1e9
         hbm[name] = {"bytes": int(by), "ms": round(t, 5), "GB/s": round(gbps, 1),
                      "frac": round(gbps / PEAK_HBM_GBPS, 4)}
-    hbm["gate"] = {"ms": round(stage_avg["gate"], 5), "note": "capacity scan + offsets; latency-bound"}
+    hbm["gate"] = {"ms": round(stage_avg["gate"], 5), "note": "capacity scan; latency-bound"}
 
     # Achievable copy bandwidth in the same run (1 GiB device-to-device clone).
     src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
@@ -283,7 +288,7 @@ def main():
         "config": {"workload": args.workload, "n_tokens": N, "n_groups": cfg["n_groups"],
                    "d_model": M, "d_ff": H, "n_experts": E, "n_shared": Es, "top_k": k,
                    "capacity": cfg["capacity"], "random_routing": cfg["random_routing"],
-                   "act": ["relu", "gelu"][cfg["act"]], "parallelism": "single-gpu"},
+                   "act": ["relu", "gelu", "swiglu"][cfg["act"]], "parallelism": "single-gpu"},
         "roofline": roofline,
         "hbm": hbm,
         "copy_GBps": round(copy_gbps, 1),

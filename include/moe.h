@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2   /* 2: gated (SwiGLU) experts, MOE_ACT_SWIGLU */
 
 enum moe_status {
   MOE_OK = 0,
@@ -46,7 +46,9 @@ enum moe_status {
   MOE_EHIP = -4           /* a HIP launch failed */
 };
 
-enum moe_act { MOE_ACT_RELU = 0, MOE_ACT_GELU = 1 };       /* GELU: exact erf form */
+/* GELU: exact erf form.  SWIGLU: the gated expert (Swish(x W1) * (x W2)) W3 of [Lec16]
+ * "DeepSeek V3 MoE (670B)", Swish(z) = z sigmoid(z); weight layout at moe_forward. */
+enum moe_act { MOE_ACT_RELU = 0, MOE_ACT_GELU = 1, MOE_ACT_SWIGLU = 2 };
 enum moe_gate_norm { MOE_NORM_NONE = 0, MOE_NORM_SUM = 1 };
 enum moe_dtype { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 };
 
@@ -56,7 +58,8 @@ enum moe_dtype { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 };
  *                  that route independently ([GShard] "Top-2 gating 的四个机制 / Local group
  *                  dispatching"); N % G == 0, G >= 1.
  *   d_model        M, d_ff H: every expert is act(x W1^T) W2^T, M -> H -> M, no biases
- *                  ([GShard] "MoE Transformer").
+ *                  ([GShard] "MoE Transformer"); with MOE_ACT_SWIGLU it is
+ *                  (Swish(x G^T) * (x U^T)) W2^T, G and U the two H-row halves of W1.
  *   n_experts      E routed experts, 1 <= E <= 256.
  *   n_shared       Es >= 0 always-on experts added with weight 1 to every token
  *                  ([Lec16] "共享专家 vs. 路由专家"); they take no capacity and are not in aux.
@@ -140,8 +143,11 @@ int moe_workspace_size(const moe_cfg* cfg, size_t* bytes);
  *   x         [N, M] T
  *   Wg        [E, M] T      row e = expert e's gate vector ([MegaBlocks] section 2)
  *   bg        [E] fp32 or NULL: fixed per-expert router offsets added to the logits
- *   W1        [E+Es, H, M] T   row n of W1[e] feeds hidden unit n; shared experts last
- *   W2        [E+Es, M, H] T   row m of W2[e] produces output feature m
+ *   W1        [E+Es, H, M] T   row n of W1[e] feeds hidden unit n; shared experts last.
+ *             MOE_ACT_SWIGLU: [E+Es, 2H, M] T, rows 0..H-1 of W1[e] the Swish (gate)
+ *             projection (the formula's W1) and rows H..2H-1 the linear (up) one (its W2)
+ *   W2        [E+Es, M, H] T   row m of W2[e] produces output feature m (for
+ *             MOE_ACT_SWIGLU, the formula's W3)
  *   u         [N] fp32 in [0,1), required iff cfg.random_routing
  *   y         [N, M] T      output (fp32 accumulation, one rounding to T)
  *   aux_loss  device fp32 scalar: mean over groups of E * sum_e m_e c_e / (k S), with m_e

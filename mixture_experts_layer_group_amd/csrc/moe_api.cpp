@@ -36,7 +36,8 @@ int check_cfg(const moe_cfg* c) {
   if (c->n_tokens % c->n_groups != 0) return MOE_EINVAL;
   if (c->n_experts < 1 || c->n_shared < 0 || c->capacity < 1) return MOE_EINVAL;
   if (c->top_k < 1 || c->top_k > c->n_experts) return MOE_EINVAL;
-  if (c->act != MOE_ACT_RELU && c->act != MOE_ACT_GELU) return MOE_EINVAL;
+  if (c->act != MOE_ACT_RELU && c->act != MOE_ACT_GELU && c->act != MOE_ACT_SWIGLU)
+    return MOE_EINVAL;
   if (c->gate_norm != MOE_NORM_NONE && c->gate_norm != MOE_NORM_SUM) return MOE_EINVAL;
   if (c->random_routing != 0 && c->random_routing != 1) return MOE_EINVAL;
   if (c->random_routing && c->top_k != 2) return MOE_EINVAL;
@@ -228,18 +229,22 @@ int forward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* b
   const int a_rows = static_cast<int>(L.rows_alloc);
 
   // GEMM 1: h = act(buf . W1_e^T) for every expert (+ shared: h_sh = act(x . W1_sh^T)).
+  // Gated experts: h = Swish(buf . G_e^T) * (buf . U_e^T) from W1_e = [G_e; U_e] (2H rows).
+  const int64_t H1 = c->act == MOE_ACT_SWIGLU ? 2 * H : H;  // W1 rows per expert
   moe::GemmArgs g1{};
   g1.dtype = c->dtype;
-  g1.p0 = moe::GemmProblem{ws + L.buf, M, W1, M, H * M, M, 0, ws + L.h, H,
+  g1.p0 = moe::GemmProblem{ws + L.buf, M, W1, M, H1 * M, M, 0, ws + L.h, H,
                            static_cast<int>(H), static_cast<int>(M), a_rows, c->act,
-                           tiles, ntiles, static_cast<int>(L.max_tiles), 0};
+                           tiles, ntiles, static_cast<int>(L.max_tiles), 0,
+                           static_cast<int>(H)};
   g1.nprob = 1;
   if (Es) {
-    const char* w1sh = static_cast<const char*>(W1) + E * H * M * L.esz;
+    const char* w1sh = static_cast<const char*>(W1) + E * H1 * M * L.esz;
     g1.p1 = moe::GemmProblem{x, M, w1sh, M, 0, M, 0, ws + L.hsh, Es * H,
                              static_cast<int>(Es * H), static_cast<int>(M), c->n_tokens,
                              c->act, nullptr, nullptr,
-                             static_cast<int>((c->n_tokens + BM - 1) / BM), c->n_tokens};
+                             static_cast<int>((c->n_tokens + BM - 1) / BM), c->n_tokens,
+                             static_cast<int>(H)};
     g1.nprob = 2;
   }
   rc = status_of(moe::launch_expert_gemm(g1, r.s));
@@ -250,15 +255,15 @@ int forward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* b
   moe::GemmArgs g2{};
   g2.dtype = c->dtype;
   g2.p0 = moe::GemmProblem{ws + L.h, H, W2, H, M * H, H, 0, ws + L.buf, M,
-                           static_cast<int>(M), static_cast<int>(H), a_rows, -1,
-                           tiles, ntiles, static_cast<int>(L.max_tiles), 0};
+                           static_cast<int>(M), static_cast<int>(H), a_rows, moe::kActNone,
+                           tiles, ntiles, static_cast<int>(L.max_tiles), 0, 0};
   g2.nprob = 1;
   if (Es) {
     const char* w2sh = static_cast<const char*>(W2) + E * M * H * L.esz;
     g2.p1 = moe::GemmProblem{ws + L.hsh, Es * H, w2sh, H, 0, H, M * H, ws + L.osh, M,
-                             static_cast<int>(M), static_cast<int>(Es * H), c->n_tokens, -1,
-                             nullptr, nullptr,
-                             static_cast<int>((c->n_tokens + BM - 1) / BM), c->n_tokens};
+                             static_cast<int>(M), static_cast<int>(Es * H), c->n_tokens,
+                             moe::kActNone, nullptr, nullptr,
+                             static_cast<int>((c->n_tokens + BM - 1) / BM), c->n_tokens, 0};
     g2.nprob = 2;
   }
   rc = status_of(moe::launch_expert_gemm(g2, r.s));

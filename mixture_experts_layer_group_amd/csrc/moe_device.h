@@ -12,6 +12,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -32,6 +33,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ float gelu_erf(float z) {
   return 0.5f * z * (1.0f + erff(z * 0.70710678118654752440f));
 }
+
+// Swish with beta = 1: z * sigmoid(z) = z / (1 + exp(-z)), with the device library's expf
+// (exp(-z) = inf for very negative z gives -0).
+__device__ __forceinline__ float swish(float z) { return z / (1.0f + expf(-z)); }
 
 __device__ __forceinline__ float apply_act(float z, int act) {
   if (act == 0) return fmaxf(z, 0.0f);

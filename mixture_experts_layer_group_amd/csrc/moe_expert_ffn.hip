@@ -17,6 +17,12 @@
 // and of row tiles across n-tiles).  Details at gemm_bf16_kernel.
 // fp32 kernel: a 64 x 64 x 16 FMA tile for the fp32 layers (the fp32 MFMA and fp32 vector
 // peaks are equal on this chip).
+//
+// Gated experts ([Lec16] "DeepSeek V3 MoE (670B)": (Swish(x W1) * (x W2)) W3) run their two
+// input projections as one GEMM over the stacked weight: a tile's B rows are arranged so
+// that the lane (bf16) or thread (fp32) holding the gate pre-activation of an output also
+// holds its up pre-activation, and the epilogue writes Swish(g) * u, half as many columns
+// as the tile computed.
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -39,8 +45,10 @@ struct Job {
   int ncols;       // valid columns of the tile (the last n-tile of a problem may be partial)
   int rows_left;   // rows readable from the tile's first row (clamp)
   int act;
+  int64_t upb;     // gated problems: bytes from a gate row of B to its up row
 };
 
+// BN = output columns per tile (a gated tile computes 2 BN columns of A . B^T).
 template <int BM, int BN, int ESZ>
 __device__ __forceinline__ bool decode_tile(const GemmArgs& g, Job& j) {
   const int nt0 = (g.p0.N + BN - 1) / BN;
@@ -79,8 +87,13 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& g, Job& j) {
   j.lda = P.lda * ESZ;
   j.A = static_cast<const char*>(P.A) + static_cast<int64_t>(row0) * j.lda;
   j.ldb = P.ldb * ESZ;
+  const int c0 = nt * BN;
+  // first B row of the tile: output column c0, or for gated problems its gate row
+  const int64_t brow = P.act == kActSwiglu
+      ? static_cast<int64_t>(c0 / P.glu_h) * 2 * P.glu_h + c0 % P.glu_h : c0;
   j.B = static_cast<const char*>(P.B) + (static_cast<int64_t>(e) * P.b_stride) * ESZ +
-        static_cast<int64_t>(nt) * BN * j.ldb;
+        brow * j.ldb;
+  j.upb = static_cast<int64_t>(P.glu_h) * j.ldb;
   j.kseg = P.kseg;
   j.segb = P.seg_stride * ESZ;
   j.ldc = P.ldc * ESZ;
@@ -126,8 +139,8 @@ __device__ __forceinline__ int lds_swz(int r) { return ((r >> 1) & 7) ^ ((r & 1)
 
 template <int ACT>
 __device__ __forceinline__ float act_fn(float z) {
-  if (ACT == 0) return fmaxf(z, 0.0f);
-  if (ACT == 1) return gelu_erf(z);
+  if (ACT == kActRelu) return fmaxf(z, 0.0f);
+  if (ACT == kActGelu) return gelu_erf(z);
   return z;
 }
 
@@ -159,7 +172,11 @@ __device__ __forceinline__ void dma16(rsrc_t r, unsigned char* lds, uint32_t vof
 //  * a barrier without a global-memory fence separates the stages, so the loads in flight are
 //    never drained by it;
 //  * the epilogue applies the activation, packs bf16 and stages the tile in LDS (16-byte
-//    columns XOR (row % columns)), then writes whole rows, 16 bytes per lane.
+//    columns XOR (row % columns)), then writes whole rows, 16 bytes per lane;
+//  * gated (ACT == kActSwiglu): LDS B rows [64 s, 64 s + 32) hold the gate rows of output
+//    columns [32 s, 32 s + 32) and rows [64 s + 32, 64 s + 64) their up rows, so wave wn's two
+//    32-column MFMA blocks are the gate and up halves of the same 32 outputs, held by the
+//    same lanes in the same registers; the tile writes BN / 2 columns.
 template <int BM, int BN, int WN, int ACT>
 __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int BK = 64, ROW = 128, NST = 2;
@@ -172,8 +189,11 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
   static_assert(AQ * NW * 1024 == BM * ROW && BQ * NW * 1024 == BN * ROW, "tile/wave split");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
 
+  constexpr bool GLU = ACT == kActSwiglu;
+  constexpr int OUTN = GLU ? BN / 2 : BN;    // output columns of the tile
+  static_assert(!GLU || WN * 64 == BN, "gated tiles: every wave holds one gate/up block pair");
   Job j;
-  if (!decode_tile<BM, BN, 2>(g, j)) return;
+  if (!decode_tile<BM, OUTN, 2>(g, j)) return;
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = w / WN, wn = w % WN;
@@ -182,7 +202,8 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
   const rsrc_t ra_rs = make_rsrc(j.A, static_cast<int64_t>(j.nrows) * j.lda);
   const int nseg = (j.K + static_cast<int>(j.kseg) - 1) / static_cast<int>(j.kseg);
   // Weight rows past the problem's N (a partial last n-tile) read as zeros.
-  const rsrc_t rb_rs = make_rsrc(j.B, (nseg - 1) * j.segb + static_cast<int64_t>(j.ncols) * j.ldb);
+  const rsrc_t rb_rs = make_rsrc(j.B, (nseg - 1) * j.segb + (GLU ? j.upb : 0) +
+                                          static_cast<int64_t>(j.ncols) * j.ldb);
 
   // Load slot q of this wave fills LDS units [(w + NW q) 64, +64) of its operand: unit u is
   // row u / 8, physical column u % 8.
@@ -195,7 +216,11 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
   for (int q = 0; q < BQ; ++q) {
     const int u = (w + NW * q) * 64 + lane, r = u >> 3, c = (u & 7) ^ lds_swz(r);
-    boff[q] = r * ldb + c * 16;
+    if (GLU)   // LDS row r: output column 32 (r / 64) + r % 32, gate or up half by bit 5
+      boff[q] = ((r >> 6) * 32 + (r & 31)) * ldb + ((r >> 5) & 1) * static_cast<uint32_t>(j.upb) +
+                c * 16;
+    else
+      boff[q] = r * ldb + c * 16;
   }
 
   // K position of B inside its segment (elements) and the segment's byte offset.
@@ -261,24 +286,27 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
   lds_barrier();
   compute((KT - 1) & 1);
 
-  // Epilogue through LDS: D[feature][token] -> tile[token][feature] bf16 (rows of BN*2 bytes,
-  // NCH 16-byte columns XOR (row % NCH)), then whole rows to global memory.
-  constexpr int RB = BN * 2, NCH = RB / 16;
+  // Epilogue through LDS: D[feature][token] -> tile[token][feature] bf16 (rows of OUTN*2
+  // bytes, NCH 16-byte columns XOR (row % NCH)), then whole rows to global memory.
+  constexpr int RB = OUTN * 2, NCH = RB / 16;
+  constexpr int TNO = GLU ? TN / 2 : TN, WTNO = OUTN / WN;
   static_assert((NCH & (NCH - 1)) == 0, "power-of-two column count");
+  auto out = [&](int jo, int im, int x) {
+    if (GLU) return swish(acc[2 * jo][im][x]) * acc[2 * jo + 1][im][x];
+    return act_fn<ACT>(acc[jo][im][x]);
+  };
   lds_barrier();
 #pragma unroll
   for (int im = 0; im < TM; ++im) {
     const int tok = wm * WTM + 32 * im + (lane & 31);
 #pragma unroll
-    for (int jn = 0; jn < TN; ++jn) {
+    for (int jo = 0; jo < TNO; ++jo) {
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
-        const int f = wn * WTN + 32 * jn + 8 * qd + 4 * (lane >> 5);
+        const int f = wn * WTNO + 32 * jo + 8 * qd + 4 * (lane >> 5);
         u32x2 pk;
-        pk[0] = pack_bf16x2(act_fn<ACT>(acc[jn][im][4 * qd + 0]),
-                            act_fn<ACT>(acc[jn][im][4 * qd + 1]));
-        pk[1] = pack_bf16x2(act_fn<ACT>(acc[jn][im][4 * qd + 2]),
-                            act_fn<ACT>(acc[jn][im][4 * qd + 3]));
+        pk[0] = pack_bf16x2(out(jo, im, 4 * qd + 0), out(jo, im, 4 * qd + 1));
+        pk[1] = pack_bf16x2(out(jo, im, 4 * qd + 2), out(jo, im, 4 * qd + 3));
         const int ch = f >> 3, within = (f & 7) * 2;
         *reinterpret_cast<u32x2*>(smem + tok * RB + ((ch ^ (tok & (NCH - 1))) << 4) + within) = pk;
       }
@@ -294,17 +322,24 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
   }
 }
 
+// Thread (ty, tx) accumulates rows 4 ty + i and LDS B columns 4 tx + jj.  Gated problems:
+// LDS B column n holds output 2 (n / 4) + n % 2, its gate row for n % 4 < 2 and its up row
+// otherwise, so a thread writes Swish(acc[i][jj]) * acc[i][jj + 2] for outputs 2 tx + jj,
+// jj < 2 (32 output columns per tile).
+template <bool GLU>
 __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs g) {
   constexpr int BM = 64, BN = 64, BK = 16, LDSW = 68;
   __shared__ __attribute__((aligned(16))) float As[BK][LDSW];
   __shared__ __attribute__((aligned(16))) float Bs[BK][LDSW];
   Job j;
-  if (!decode_tile<BM, BN, 4>(g, j)) return;
+  if (!decode_tile<BM, GLU ? BN / 2 : BN, 4>(g, j)) return;
   const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
   const int lr = t >> 2, lc = (t & 3) * 4;
   const int ar = lr < j.rows_left ? lr : j.rows_left - 1;
   const char* ap = j.A + static_cast<int64_t>(ar) * j.lda + lc * 4;
-  const char* bp = j.B + static_cast<int64_t>(lr) * j.ldb + lc * 4;
+  const int64_t boffs = GLU ? (2 * (lr >> 2) + (lr & 1)) * j.ldb + ((lr >> 1) & 1) * j.upb
+                            : static_cast<int64_t>(lr) * j.ldb;
+  const char* bp = j.B + boffs + lc * 4;
   float acc[4][4] = {};
   for (int kt = 0; kt < j.K / BK; ++kt) {
     const f32x4 av = *reinterpret_cast<const f32x4*>(ap + static_cast<int64_t>(kt) * BK * 4);
@@ -329,7 +364,13 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs g) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = ty * 4 + i;
-    if (r < j.nrows) {
+    if (r >= j.nrows) continue;
+    if (GLU) {
+      f32x2 o;
+      o[0] = swish(acc[i][0]) * acc[i][2];
+      o[1] = swish(acc[i][1]) * acc[i][3];
+      *reinterpret_cast<f32x2*>(j.C + static_cast<int64_t>(r) * j.ldc + tx * 8) = o;
+    } else {
       f32x4 o;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) o[jj] = apply_act(acc[i][jj], j.act);
@@ -348,27 +389,28 @@ int grid_of(const GemmArgs& a, int BN) {
 
 int gemm_block_m(int dtype) { return dtype == 1 ? 256 : 64; }
 
-int gemm_block_n(int dtype, int n0, int n1) {
-  (void)n0;
-  (void)n1;
-  return dtype == 1 ? 256 : 64;  // bf16: partial last n-tiles are masked
+// bf16: partial last n-tiles are masked; gated tiles write half the columns they compute.
+int gemm_block_n(int dtype, int act) {
+  const int bn = dtype == 1 ? 256 : 64;
+  return act == kActSwiglu ? bn / 2 : bn;
 }
 
 hipError_t launch_expert_gemm(const GemmArgs& a, hipStream_t s) {
-  const int BN = gemm_block_n(a.dtype, a.p0.N, a.nprob > 1 ? a.p1.N : a.p0.N);
-  const int grid = grid_of(a, BN);
-  if (grid == 0) return hipSuccess;
   const int act = a.p0.act;  // both problems of one launch share the activation
+  const int grid = grid_of(a, gemm_block_n(a.dtype, act));
+  if (grid == 0) return hipSuccess;
   if (a.dtype == 1) {
-#define MOE_GEMM_LAUNCH(BNV, ACTV)                                                       \
-  hipLaunchKernelGGL((gemm_bf16_kernel<256, BNV, BNV / 64, ACTV>), dim3(grid),            \
-                     dim3(128 * (BNV / 64)), 0, s, a)
-    if (act == 0) MOE_GEMM_LAUNCH(256, 0);
-    else if (act == 1) MOE_GEMM_LAUNCH(256, 1);
-    else MOE_GEMM_LAUNCH(256, 2);
+#define MOE_GEMM_LAUNCH(ACTV) \
+  hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 4, ACTV>), dim3(grid), dim3(512), 0, s, a)
+    if (act == kActRelu) MOE_GEMM_LAUNCH(kActRelu);
+    else if (act == kActGelu) MOE_GEMM_LAUNCH(kActGelu);
+    else if (act == kActSwiglu) MOE_GEMM_LAUNCH(kActSwiglu);
+    else MOE_GEMM_LAUNCH(kActNone);
 #undef MOE_GEMM_LAUNCH
+  } else if (act == kActSwiglu) {
+    hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3(grid), dim3(kThreads), 0, s, a);
   } else {
-    hipLaunchKernelGGL(gemm_f32_kernel, dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(gemm_f32_kernel<false>, dim3(grid), dim3(kThreads), 0, s, a);
   }
   return hipGetLastError();
 }

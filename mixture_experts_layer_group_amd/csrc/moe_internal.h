@@ -71,20 +71,27 @@ struct PermuteArgs {
   int slices;             // column slices per router block (set by the launcher)
 };
 
+// Activation codes of a GEMM problem (the first three are moe_cfg's act values).
+constexpr int kActRelu = 0, kActGelu = 1, kActSwiglu = 2, kActNone = -1;
+
 // One GEMM problem of the expert FFN: C[rows, N] = act(A[rows, K] . B_e[N, K]^T).
 // B_e = B + e * b_stride; the K axis of B may be split into segments of kseg elements that
 // sit seg_stride elements apart (the shared experts' W2 blocks).
+// Gated problems (act == kActSwiglu): output column c of width N is
+// Swish(A . Bg_c) * (A . Bu_c), with gate row Bg_c = B_e row (c / glu_h) 2 glu_h + c % glu_h
+// and up row Bu_c = that row + glu_h (each expert's W1 stacks H gate rows on H up rows).
 struct GemmProblem {
   const void* A; int64_t lda;
   const void* B; int64_t ldb; int64_t b_stride; int64_t kseg; int64_t seg_stride;
   void* C; int64_t ldc;
   int N, K;
   int a_rows;             // rows readable through A (loads clamp to a_rows - 1)
-  int act;                // -1 none, 0 ReLU, 1 GELU
+  int act;                // kAct*
   const TileDesc* tiles;  // routed: device tile list (nullptr: dense problem)
   const int32_t* num_tiles;
   int max_tiles;          // routed: grid bound on the tile count; dense: ceil(rows / BM)
   int dense_rows;         // dense problem: number of rows
+  int glu_h;              // gated problems: hidden width H of one expert (else unused)
 };
 
 struct GemmArgs {
@@ -112,7 +119,7 @@ struct EmptyArgs {         // N == 0: zero the small outputs
 };
 
 int gemm_block_m(int dtype);                           // BM of the expert GEMM tiles
-int gemm_block_n(int dtype, int n0, int n1);           // BN for problems with widths n0, n1
+int gemm_block_n(int dtype, int act);                  // output columns per tile
 
 hipError_t launch_router(const RouterArgs& a, hipStream_t s);
 hipError_t launch_gate_scan(const ScanArgs& a, hipStream_t s);

@@ -63,7 +63,7 @@ BAD = [
     (dict(top_k=17, n_experts=16, random_routing=0), binding.MOE_EINVAL),
     (dict(n_experts=257, top_k=2), binding.MOE_EUNSUPPORTED),
     (dict(capacity=0), binding.MOE_EINVAL),
-    (dict(act=2), binding.MOE_EINVAL),
+    (dict(act=3), binding.MOE_EINVAL),
     (dict(gate_norm=3), binding.MOE_EINVAL),
     (dict(random_routing=1, top_k=1), binding.MOE_EINVAL),
     (dict(residual=2), binding.MOE_EINVAL),

@@ -33,7 +33,8 @@ def test_small_layer_parity(name):
 
 
 SAMPLES = {"tiny_fp32": None, "gshard_bf16": 2048, "switch_bf16": 2048,
-           "large_expert_bf16": 512, "shared_routed_bf16": 1024}
+           "large_expert_bf16": 512, "shared_routed_bf16": 1024,
+           "shared_routed_swiglu_bf16": 1024}
 
 
 @pytest.mark.parametrize("name", list(configs.WORKLOADS))
@@ -138,10 +139,12 @@ def test_empty_batch():
     assert int(meta.stats.abs().sum()) == 0 and float(aux[0]) == 0.0
 
 
-def test_single_expert_is_a_dense_ffn():
-    """E=1, k=1, C=N, norm=none: y = x + act(x W1^T) W2^T, checked against torch.matmul in
-    fp32 on the GPU (a library GEMM) rather than against the oracle."""
-    cfg = _cfg(n_tokens=700, n_experts=1, top_k=1, capacity=700, gate_norm=0, act=1,
+@pytest.mark.parametrize("act", [1, 2], ids=["gelu", "swiglu"])
+def test_single_expert_is_a_dense_ffn(act):
+    """E=1, k=1, C=N, norm=none: y = x + act(x W1^T) W2^T (gated: (silu(x G^T) * x U^T)
+    W2^T), checked against torch.matmul and torch's gelu / silu in fp32 on the GPU (library
+    routines) rather than against the oracle."""
+    cfg = _cfg(n_tokens=700, n_experts=1, top_k=1, capacity=700, gate_norm=0, act=act,
                d_model=256, d_ff=384)
     inp = synth.make_inputs(cfg)
     h = harness()
@@ -150,6 +153,11 @@ def test_single_expert_is_a_dense_ffn():
     x = dev["x"].float()
     w1 = dev["W1"][0].float().contiguous()
     w2 = dev["W2"][0].float().contiguous()
-    hid = torch.nn.functional.gelu(torch.matmul(x, w1.t().contiguous()))
+    pre = torch.matmul(x, w1.t().contiguous())
+    if act == 1:
+        hid = torch.nn.functional.gelu(pre)
+    else:
+        H = cfg["d_ff"]
+        hid = torch.nn.functional.silu(pre[:, :H]) * pre[:, H:]
     ref = (x + torch.matmul(hid, w2.t().contiguous())).cpu().numpy()
     assert h.rel_err(g["y"], ref) <= 2e-2
