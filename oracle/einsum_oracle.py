@@ -13,7 +13,7 @@ combine weight is zero, [GShard] "Static shape 与 uneven partition"), and the o
 are combined with a second einsum.  Float64 throughout, small inputs only.
 """
 import numpy as np
-from scipy.special import erf, expit
+from scipy.special import erf, expit, logsumexp
 
 
 def _hidden(rows, W1e, act):
@@ -55,7 +55,12 @@ def einsum_layer(cfg, x, Wg, W1, W2, bg=None, u=None, logits32=None):
         psel.append((probs * oh).sum(axis=1))
         remaining = np.where(oh > 0, -np.inf, remaining)
     psel = np.stack(psel, axis=1)                  # [N, k]
-    w = psel / psel.sum(axis=1, keepdims=True) if cfg["gate_norm"] else psel
+    if cfg["gate_norm"] == 2:                      # p-norm of the selected probabilities
+        P = float(cfg.get("norm_p", 1.0))
+        w = psel / np.linalg.norm(psel, ord=P, axis=1, keepdims=True) if P >= 1 else \
+            psel / (psel ** P).sum(axis=1, keepdims=True) ** (1.0 / P)
+    else:
+        w = psel / psel.sum(axis=1, keepdims=True) if cfg["gate_norm"] else psel
 
     if cfg["random_routing"]:
         l1 = (lg * onehots[0]).sum(axis=1)
@@ -102,5 +107,6 @@ def einsum_layer(cfg, x, Wg, W1, W2, bg=None, u=None, logits32=None):
         aux += E * float((m * c).sum()) / (k * S)
     aux /= G
     counts = dispatch.sum(axis=(1, 3))            # [G, E]
-    return dict(y=y, aux=aux, dispatch=dispatch, combine=combine,
+    z = float(np.mean(logsumexp(lg, axis=1) ** 2)) if N else 0.0   # router z-loss
+    return dict(y=y, aux=aux, z_loss=z, dispatch=dispatch, combine=combine,
                 count=counts.astype(np.int32), logits=lg)

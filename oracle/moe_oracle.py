@@ -38,7 +38,13 @@ function that depends on it (and listed in the design doc):
            projections are stacked in one weight: W1[e] is [2H, M], rows 0..H-1 the
            Swish (gate) projection and rows H..2H-1 the linear (up) one; W2[e] [M, H]
            holds the output projection (the formula's W3).
-  R-empty  an empty batch (N = 0) routes nothing and has aux = 0.
+  R-empty  an empty batch (N = 0) routes nothing and has aux = 0 (and z-loss 0).
+  R-pnorm  the optional p-norm renormalisation of [MegaBlocks] section 2 divides the k
+           selected probabilities by their p-norm, (sum_i p_i^P)^(1/P), P > 0 a real
+           number (P = 1 is the sum normalisation); gate_norm == 2 selects it.
+  R-z      the router z-loss of [MegaBlocks] section 2 is the mean over all N tokens of
+           logsumexp(logits_n)^2, on the fp32 logits that feed the softmax (router offsets
+           included), one number per layer whatever the grouping.
 
 Pins: every public function here is checked by ``tests/test_oracle_pins.py`` against
 closed forms, invariants, the dense one-hot formulation in ``einsum_oracle.py``, brute
@@ -89,17 +95,36 @@ def topk_experts(logits, k):
     return order[:, :k].astype(np.int32)
 
 
-def gate_weights(p, idx, gate_norm):
-    """Pre-drop combine weights of the selected experts (R-norm).
+def gate_weights(p, idx, gate_norm, norm_p=1.0):
+    """Pre-drop combine weights of the selected experts (R-norm, R-pnorm).
 
     gate_norm == 1: w_j = p_j / sum_i p_i over the k selected experts -- equal to a
     softmax over the selected logits ([Lec16] "Switch Transformer", "共享专家 vs. 路由专家")
     and to the renormalised top-k of [MegaBlocks] section 2.  gate_norm == 0: w_j = p_j.
+    gate_norm == 2: w_j = p_j / (sum_i p_i^P)^(1/P), the p-norm option of [MegaBlocks]
+    section 2 ("权重归一化"), P = norm_p.
     """
     psel = np.take_along_axis(np.asarray(p, dtype=np.float64), idx.astype(np.int64), axis=1)
-    if gate_norm:
+    if gate_norm == 1:
         return psel / psel.sum(axis=1, keepdims=True)
+    if gate_norm == 2:
+        P = float(norm_p)
+        return psel / ((psel ** P).sum(axis=1, keepdims=True) ** (1.0 / P))
     return psel
+
+
+def z_loss(logits32):
+    """Router z-loss (R-z): mean_n (log sum_e exp(l_{n,e}))^2, float64.
+
+    [MegaBlocks] section 2 ("z-loss ... mean(logsumexp(logits)²)"): it penalises large
+    router logits.  logsumexp is evaluated max-shifted.  An empty batch gives 0.
+    """
+    l = np.asarray(logits32, dtype=np.float64)
+    if l.shape[0] == 0:
+        return 0.0
+    mx = l.max(axis=1)
+    lse = mx + np.log(np.exp(l - mx[:, None]).sum(axis=1))
+    return float(np.mean(lse * lse))
 
 
 def random_routing_keep(logits32, idx, u):
@@ -217,10 +242,10 @@ def route(cfg, logits32, u=None):
         return dict(topk_idx=z, active=z.astype(bool), pos=z, row=z,
                     topk_w=np.zeros((0, k)), w_pre=np.zeros((0, k)),
                     count=np.zeros((G, E), np.int32), offset=np.zeros(E + 1, np.int32),
-                    aux=0.0, stats=np.zeros(4, np.int64), p=np.zeros((0, E)))
+                    aux=0.0, z_loss=0.0, stats=np.zeros(4, np.int64), p=np.zeros((0, E)))
     p = softmax(l32)
     idx = topk_experts(l32, k)
-    w_pre = gate_weights(p, idx, cfg["gate_norm"])
+    w_pre = gate_weights(p, idx, cfg["gate_norm"], cfg.get("norm_p", 1.0))
     active = np.ones((N, k), dtype=bool)
     if cfg["random_routing"]:
         if k != 2 or u is None:
@@ -236,7 +261,8 @@ def route(cfg, logits32, u=None):
     stats = np.array([R, n_active - R, int((~kept.any(axis=1)).sum()), N * k - n_active],
                      dtype=np.int64)
     return dict(topk_idx=idx, active=active, pos=pos, row=row, topk_w=topk_w,
-                w_pre=w_pre, count=count, offset=offset, aux=aux, stats=stats, p=p)
+                w_pre=w_pre, count=count, offset=offset, aux=aux, z_loss=z_loss(l32),
+                stats=stats, p=p)
 
 
 # --------------------------------------------------------------------------- experts
