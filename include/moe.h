@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2   /* 2: gated (SwiGLU) experts, MOE_ACT_SWIGLU */
+#define MOE_ABI_VERSION 3   /* 2: gated (SwiGLU) experts; 3: p-norm gates, router z-loss */
 
 enum moe_status {
   MOE_OK = 0,
@@ -49,7 +49,7 @@ enum moe_status {
 /* GELU: exact erf form.  SWIGLU: the gated expert (Swish(x W1) * (x W2)) W3 of [Lec16]
  * "DeepSeek V3 MoE (670B)", Swish(z) = z sigmoid(z); weight layout at moe_forward. */
 enum moe_act { MOE_ACT_RELU = 0, MOE_ACT_GELU = 1, MOE_ACT_SWIGLU = 2 };
-enum moe_gate_norm { MOE_NORM_NONE = 0, MOE_NORM_SUM = 1 };
+enum moe_gate_norm { MOE_NORM_NONE = 0, MOE_NORM_SUM = 1, MOE_NORM_P = 2 };
 enum moe_dtype { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 };
 
 /*
@@ -69,12 +69,16 @@ enum moe_dtype { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 };
  *                  means nothing is ever dropped.
  *   act            enum moe_act.
  *   gate_norm      MOE_NORM_SUM: w_j = p_j / sum of the k selected p (softmax over the
- *                  selected logits); MOE_NORM_NONE: w_j = p_j, the full softmax probability.
+ *                  selected logits); MOE_NORM_NONE: w_j = p_j, the full softmax probability;
+ *                  MOE_NORM_P: w_j = p_j / (sum_i p_i^P)^(1/P) over the k selected, P =
+ *                  norm_p ([MegaBlocks] section 2, optional p-norm of the top-k weights).
  *   random_routing 1: keep the 2nd slot iff u[n] < 2 p2/(p1+p2) ([GShard] "Random routing");
  *                  needs top_k == 2 and a non-NULL u.
  *   residual       1: y = x + layer(x) (a fully dropped token gets y = x exactly);
  *                  0: y = layer(x) (a fully dropped token gets 0).
  *   dtype          enum moe_dtype.
+ *   norm_p         P of MOE_NORM_P: finite and > 0 (MOE_EINVAL otherwise); ignored for the
+ *                  other gate_norm values.
  * Shape constraints (MOE_EUNSUPPORTED otherwise):
  *   bf16: M % 128 == 0 and H % 128 == 0.   fp32: M % 64 == 0 and H % 64 == 0.
  */
@@ -92,12 +96,13 @@ typedef struct moe_cfg {
   int32_t random_routing;
   int32_t residual;
   int32_t dtype;
+  float norm_p;
 } moe_cfg;
 
 /*
  * Dispatch metadata: caller-allocated device arrays the layer fills ([MegaBlocks] section 2
  * returns scores, expert weights and top experts; [Lec16] "MoE Kernel 优化" keeps a dense
- * token-to-expert table).  Every pointer is required (16-byte aligned).
+ * token-to-expert table).  Every pointer but z_loss is required (16-byte aligned).
  *   logits    [N, E] fp32   router logits x Wg^T (+ bg)   (moe_forward only; moe_route
  *                           reads its logits from its own argument and ignores this one)
  *   topk_idx  [N, k] int32  selected experts, descending logit, BEFORE capacity / random
@@ -110,6 +115,9 @@ typedef struct moe_cfg {
  *   count     [G, E] int32  kept slots per (group, expert), <= C
  *   offset    [E+1]  int32  first row of each expert; offset[E] = R, the kept slots
  *   stats     [4]    int32  {R, dropped slots, fully dropped tokens, random-routing skips}
+ *   z_loss    [1]    fp32   router z-loss, the mean over all N tokens of
+ *                           logsumexp(logits_n)^2 ([MegaBlocks] section 2), or NULL: not
+ *                           computed.  fp32 logsumexp per token, fp64 fixed-order mean.
  */
 typedef struct moe_meta {
   float* logits;
@@ -120,6 +128,7 @@ typedef struct moe_meta {
   int32_t* count;
   int32_t* offset;
   int32_t* stats;
+  float* z_loss;
 } moe_meta;
 
 /* Number of stage boundaries recorded by moe_forward_timed. */

@@ -19,13 +19,20 @@ MOE_N_EVENTS = 7
 STAGES = ("router", "gate", "permute", "ffn1", "ffn2", "combine")
 
 
+_FLOAT_FIELDS = ("norm_p",)
+
+
 class MoeCfg(ctypes.Structure):
-    _fields_ = [(f, ctypes.c_int32) for f in CFG_FIELDS]
+    _fields_ = [(f, ctypes.c_float if f in _FLOAT_FIELDS else ctypes.c_int32)
+                for f in CFG_FIELDS]
+
+
+META_FIELDS = ("logits", "topk_idx", "topk_w", "pos", "row", "count", "offset", "stats",
+               "z_loss")
 
 
 class MoeMetaC(ctypes.Structure):
-    _fields_ = [(f, ctypes.c_void_p) for f in
-                ("logits", "topk_idx", "topk_w", "pos", "row", "count", "offset", "stats")]
+    _fields_ = [(f, ctypes.c_void_p) for f in META_FIELDS]
 
 
 class MoeError(RuntimeError):
@@ -82,7 +89,8 @@ def make_cfg(cfg):
     """dict (configs.py style) or MoeCfg -> MoeCfg."""
     if isinstance(cfg, MoeCfg):
         return cfg
-    return MoeCfg(**{f: int(cfg[f]) for f in CFG_FIELDS})
+    return MoeCfg(**{f: float(cfg.get(f, 1.0)) if f in _FLOAT_FIELDS else int(cfg[f])
+                     for f in CFG_FIELDS})
 
 
 def moe_workspace_size(cfg):
@@ -104,7 +112,7 @@ def _ptr(t):
 class Meta:
     """Device tensors of the dispatch metadata (moe_meta)."""
 
-    FIELDS = ("logits", "topk_idx", "topk_w", "pos", "row", "count", "offset", "stats")
+    FIELDS = META_FIELDS
 
     def __init__(self, **tensors):
         for f in self.FIELDS:
@@ -127,7 +135,8 @@ def alloc_meta(cfg, device="cuda"):
                 topk_w=torch.empty((N, k), dtype=torch.float32, device=device),
                 pos=torch.empty((N, k), **i32), row=torch.empty((N, k), **i32),
                 count=torch.empty((G, E), **i32), offset=torch.empty((E + 1,), **i32),
-                stats=torch.empty((4,), **i32))
+                stats=torch.empty((4,), **i32),
+                z_loss=torch.empty((4,), dtype=torch.float32, device=device))
 
 
 def alloc_workspace(cfg, device="cuda"):

@@ -11,18 +11,18 @@ Sharding" (section "Top-2 gating 的四个机制 / Local group dispatching").
 """
 
 ACT_RELU, ACT_GELU, ACT_SWIGLU = 0, 1, 2
-NORM_NONE, NORM_SUM = 0, 1
+NORM_NONE, NORM_SUM, NORM_P = 0, 1, 2
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
 
 def _cfg(name, *, n_tokens, n_groups, d_model, d_ff, n_experts, top_k, capacity,
          act, gate_norm, dtype, n_shared=0, random_routing=0, residual=1,
-         zipf_s=0.0, seed=0, desc=""):
+         norm_p=1.0, zipf_s=0.0, seed=0, desc=""):
     return dict(name=name, n_tokens=n_tokens, n_groups=n_groups, d_model=d_model,
                 d_ff=d_ff, n_experts=n_experts, n_shared=n_shared, top_k=top_k,
                 capacity=capacity, act=act, gate_norm=gate_norm,
                 random_routing=random_routing, residual=residual, dtype=dtype,
-                zipf_s=zipf_s, seed=seed, desc=desc)
+                norm_p=norm_p, zipf_s=zipf_s, seed=seed, desc=desc)
 
 
 # The five reference workloads.
@@ -99,13 +99,21 @@ SMALL = {
         "small_swiglu_fp32", n_tokens=500, n_groups=1, d_model=128, d_ff=192,
         n_experts=6, n_shared=2, top_k=3, capacity=220, act=ACT_SWIGLU,
         gate_norm=NORM_SUM, dtype=DTYPE_F32, seed=17),
+    "small_pnorm_top4": _cfg(
+        "small_pnorm_top4", n_tokens=896, n_groups=2, d_model=256, d_ff=256,
+        n_experts=16, top_k=4, capacity=140, act=ACT_GELU, gate_norm=NORM_P, norm_p=2.0,
+        dtype=DTYPE_BF16, zipf_s=0.5, seed=18),
+    "small_pnorm_half_fp32": _cfg(
+        "small_pnorm_half_fp32", n_tokens=384, n_groups=3, d_model=64, d_ff=128,
+        n_experts=7, top_k=3, capacity=40, act=ACT_RELU, gate_norm=NORM_P, norm_p=0.5,
+        dtype=DTYPE_F32, seed=19),
 }
 
 ALL = {**WORKLOADS, **SMALL}
 
 CFG_FIELDS = ("n_tokens", "n_groups", "d_model", "d_ff", "n_experts", "n_shared",
               "top_k", "capacity", "act", "gate_norm", "random_routing", "residual",
-              "dtype")
+              "dtype", "norm_p")
 
 
 def with_overrides(cfg, **kw):

@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cfloat>
 #include <cstdint>
 #include <cstring>
 
@@ -21,7 +22,7 @@ using moe::kRouteTokens;
 
 struct Layout {
   // byte offsets inside the workspace
-  size_t buf, h, hsh, osh, active, psum, sel, ahist, abase, ntot, Pg, Cg, tiles, ntiles;
+  size_t buf, h, hsh, osh, active, psum, sel, ahist, abase, ntot, Pg, Cg, tiles, ntiles, zpart;
   size_t total;
   // sizes
   int64_t S, nbg, Rmax, rows_alloc, max_tiles;
@@ -38,7 +39,11 @@ int check_cfg(const moe_cfg* c) {
   if (c->top_k < 1 || c->top_k > c->n_experts) return MOE_EINVAL;
   if (c->act != MOE_ACT_RELU && c->act != MOE_ACT_GELU && c->act != MOE_ACT_SWIGLU)
     return MOE_EINVAL;
-  if (c->gate_norm != MOE_NORM_NONE && c->gate_norm != MOE_NORM_SUM) return MOE_EINVAL;
+  if (c->gate_norm != MOE_NORM_NONE && c->gate_norm != MOE_NORM_SUM &&
+      c->gate_norm != MOE_NORM_P)
+    return MOE_EINVAL;
+  if (c->gate_norm == MOE_NORM_P && !(c->norm_p > 0.0f && c->norm_p <= FLT_MAX))
+    return MOE_EINVAL;  // also rejects NaN and +inf
   if (c->random_routing != 0 && c->random_routing != 1) return MOE_EINVAL;
   if (c->random_routing && c->top_k != 2) return MOE_EINVAL;
   if (c->residual != 0 && c->residual != 1) return MOE_EINVAL;
@@ -90,6 +95,7 @@ int make_layout(const moe_cfg* c, Layout* L) {
   L->Cg = take(static_cast<size_t>(G) * E * 4);
   L->tiles = take(static_cast<size_t>(L->max_tiles) * sizeof(moe::TileDesc));
   L->ntiles = take(16);
+  L->zpart = take(static_cast<size_t>(G) * L->nbg * 8);
   L->total = off;
   return MOE_OK;
 }
@@ -102,6 +108,14 @@ int check_meta(const moe_meta* m, bool need_logits) {
   for (const void* p : ps)
     if (!p || !aligned16(p)) return MOE_EINVAL;
   if (need_logits && (!m->logits || !aligned16(m->logits))) return MOE_EINVAL;
+  if (m->z_loss && !aligned16(m->z_loss)) return MOE_EINVAL;  // optional output
+  return MOE_OK;
+}
+
+// N == 0: only count, offset, stats (and z_loss if requested) are written.
+int check_meta_empty(const moe_meta* m) {
+  if (!m || !m->count || !m->offset || !m->stats) return MOE_EINVAL;
+  if (m->z_loss && !aligned16(m->z_loss)) return MOE_EINVAL;
   return MOE_OK;
 }
 
@@ -132,6 +146,8 @@ int run_routing(const Run& r, const void* x, const void* Wg, const float* bg, co
   ra.psum = reinterpret_cast<double*>(ws + L.psum);
   ra.sel = reinterpret_cast<int32_t*>(ws + L.sel);
   ra.ahist = reinterpret_cast<int32_t*>(ws + L.ahist);
+  ra.zpart = reinterpret_cast<double*>(ws + L.zpart);
+  ra.norm_p = c->norm_p;
   ra.N = c->n_tokens; ra.G = c->n_groups; ra.S = static_cast<int>(L.S); ra.M = c->d_model;
   ra.E = c->n_experts; ra.k = c->top_k; ra.norm = c->gate_norm; ra.rr = c->random_routing;
   ra.nbg = static_cast<int>(L.nbg); ra.dtype = c->dtype;
@@ -179,13 +195,16 @@ moe::CombineArgs combine_args(const Run& r, const void* x, void* y, float* aux,
   ca.Pg = reinterpret_cast<const double*>(r.ws + r.L.Pg);
   ca.Cg = reinterpret_cast<const int32_t*>(r.ws + r.L.Cg);
   ca.aux = aux;
+  ca.zpart = reinterpret_cast<const double*>(r.ws + r.L.zpart);
+  ca.z_loss = m->z_loss;
+  ca.nblocks = static_cast<int>(c->n_groups * r.L.nbg);
   ca.N = c->n_tokens; ca.M = c->d_model; ca.k = c->top_k; ca.residual = c->residual;
   ca.dtype = c->dtype; ca.G = c->n_groups; ca.E = c->n_experts; ca.S = static_cast<int>(r.L.S);
   return ca;
 }
 
 int empty_call(const moe_cfg* c, const moe_meta* m, float* aux, hipStream_t s, void* const* ev) {
-  moe::EmptyArgs ea{m->count, m->offset, m->stats, aux, c->n_groups, c->n_experts};
+  moe::EmptyArgs ea{m->count, m->offset, m->stats, aux, m->z_loss, c->n_groups, c->n_experts};
   for (int i = 0; i < MOE_N_EVENTS - 1; ++i) record(ev, i, s);
   const int rc = status_of(moe::launch_empty(ea, s));
   record(ev, MOE_N_EVENTS - 1, s);
@@ -204,7 +223,8 @@ int forward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* b
   if (wbytes < r.L.total) return MOE_EWORKSPACE;
   if (c->n_tokens == 0) {
     // Nothing to route: only the small outputs are written; token pointers may be NULL.
-    if (!m || !m->count || !m->offset || !m->stats) return MOE_EINVAL;
+    rc = check_meta_empty(m);
+    if (rc) return rc;
     return empty_call(c, m, aux, static_cast<hipStream_t>(stream), ev);
   }
   rc = check_meta(m, true);
@@ -327,7 +347,8 @@ int moe_route(const moe_cfg* cfg, const float* logits, const float* u, const moe
     return MOE_EINVAL;
   if (workspace_bytes < r.L.total) return MOE_EWORKSPACE;
   if (cfg->n_tokens == 0) {
-    if (!meta || !meta->count || !meta->offset || !meta->stats) return MOE_EINVAL;
+    rc = check_meta_empty(meta);
+    if (rc) return rc;
     return empty_call(cfg, meta, aux_loss, static_cast<hipStream_t>(stream), nullptr);
   }
   rc = check_meta(meta, false);

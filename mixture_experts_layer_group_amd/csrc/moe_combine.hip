@@ -9,8 +9,9 @@
 //
 // Block 0 also finishes the aux loss of [GShard] "Top-2 gating 的四个机制 / Auxiliary loss":
 // aux = (1/G) sum_g E/(k S) sum_e m_{g,e} c_{g,e},  m_{g,e} = P_{g,e} / S, from the per-
-// (group, expert) sums of probabilities P and selections c, in fp64 with a fixed-order
-// reduction (deterministic).
+// (group, expert) sums of probabilities P and selections c, and the router z-loss of
+// [MegaBlocks] section 2, (1/N) sum_n logsumexp(logits_n)^2, from the router blocks' partial
+// sums; both in fp64 with fixed-order reductions (deterministic).
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -20,19 +21,28 @@ namespace {
 constexpr int kTok = 16;  // tokens per block
 
 __device__ void aux_final(const CombineArgs& a) {
-  __shared__ double red[4];
+  __shared__ double red[8];
   const int t = threadIdx.x;
-  double s = 0.0;
+  double s = 0.0, z = 0.0;
   const int n = a.G * a.E;
   for (int i = t; i < n; i += 256) s += a.Pg[i] * static_cast<double>(a.Cg[i]);
+  for (int i = t; i < a.nblocks; i += 256) z += a.zpart[i];
   s = wave_sum(s);
-  if ((t & 63) == 0) red[t >> 6] = s;
+  z = wave_sum(z);
+  if ((t & 63) == 0) {
+    red[t >> 6] = s;
+    red[4 + (t >> 6)] = z;
+  }
   __syncthreads();
   if (t == 0) {
     const double tot = ((red[0] + red[1]) + red[2]) + red[3];
     const double S = static_cast<double>(a.S);
     const double aux = static_cast<double>(a.E) * tot / (static_cast<double>(a.G) * a.k * S * S);
     *a.aux = static_cast<float>(aux);
+    if (a.z_loss) {
+      const double zt = ((red[4] + red[5]) + red[6]) + red[7];
+      *a.z_loss = static_cast<float>(zt / static_cast<double>(a.N));
+    }
   }
 }
 

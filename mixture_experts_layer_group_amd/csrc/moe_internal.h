@@ -27,6 +27,8 @@ struct RouterArgs {
   double* psum;           // [G][E][nbg]  sum of softmax probabilities of the block's tokens
   int32_t* sel;           // [G][E][nbg]  top-k selections of the block's tokens
   int32_t* ahist;         // [G][k][E][nbg] active slots per rank
+  double* zpart;          // [G * nbg] sum over the block's tokens of logsumexp(logits)^2
+  float norm_p;           // P of the p-norm gate normalisation (norm == 2)
   int N, G, S, M, E, k, norm, rr, nbg, dtype;
 };
 
@@ -111,11 +113,14 @@ struct CombineArgs {
   const double* Pg;       // [G][E]
   const int32_t* Cg;      // [G][E]
   float* aux;             // scalar
+  const double* zpart;    // [nblocks] router-block partial sums of logsumexp^2
+  float* z_loss;          // scalar or nullptr (not requested)
+  int nblocks;
   int N, M, k, residual, dtype, G, E, S;
 };
 
 struct EmptyArgs {         // N == 0: zero the small outputs
-  int32_t* count; int32_t* offset; int32_t* stats; float* aux; int G, E;
+  int32_t* count; int32_t* offset; int32_t* stats; float* aux; float* z_loss; int G, E;
 };
 
 int gemm_block_m(int dtype);                           // BM of the expert GEMM tiles

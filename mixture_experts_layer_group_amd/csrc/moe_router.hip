@@ -5,14 +5,17 @@
 // the balance loss, the top-k weights and the top-k expert ids.  [Lec16] "MoE Kernel 优化":
 // the gating work (softmax, top-k, dispatch bookkeeping) runs fused in one kernel.
 //
-// One block = 256 threads (4 waves) = 64 consecutive tokens of one group.
-//  1. GEMM: x[64, M] . Wg[E, M]^T, K staged through LDS in 256-byte row chunks (XOR-swizzled
-//     16-byte columns).  bf16: v_mfma_f32_32x32x16_bf16 tiles, fp32 accumulation.  fp32:
-//     plain FMA (fp32 MFMA and fp32 vector peaks are equal on this chip).
-//  2. Epilogue, 4 lanes per token: + bg, logits out, row max and sum of exp (fp32), top-k
-//     on the logits (ties to the lower expert index), gate weights, the random-routing
-//     decision in fp64, LDS histograms of selections and active slots per rank, and the
-//     per-expert column sums of the softmax probabilities (fp64) for the aux loss.
+// One block = 1024 threads (16 waves) = 64 consecutive tokens of one group.
+//  1. GEMM on waves 0..3: x[64, M] . Wg[E, M]^T.  bf16: both operands stream global -> LDS
+//     directly (buffer_load ... lds) through 3-4 stages of 256- or 128-byte row chunks
+//     (XOR-swizzled 16-byte columns) into v_mfma_f32_32x32x16_bf16 tiles, fp32
+//     accumulation.  fp32: plain FMA through an LDS staging area (fp32 MFMA and fp32
+//     vector peaks are equal on this chip).
+//  2. Epilogue, 16 lanes per token (all 16 waves): + bg, logits out, row max and sum of exp
+//     (fp32), top-k on the logits (ties to the lower expert index), gate weights (sum or
+//     p-norm), the random-routing decision in fp64, LDS histograms of selections and
+//     active slots per rank, the per-expert column sums of the softmax probabilities
+//     (fp64) for the aux loss, and the block's sum of logsumexp^2 (fp64) for the z-loss.
 #include <math.h>
 
 #include "moe_device.h"
@@ -340,10 +343,22 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
       psel += wgt[j];
     }
   }
-  if (a.norm) {
+  if (a.norm == 1) {
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) wgt[j] = wgt[j] / psel;
+  } else if (a.norm == 2) {
+    // [MegaBlocks] section 2: the selected weights divided by their p-norm
+    float sp = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+      if (j < k) sp += powf(wgt[j], a.norm_p);
+    const float den = powf(sp, 1.0f / a.norm_p);
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) wgt[j] = wgt[j] / den;
   }
+  // Router z-loss term ([MegaBlocks] section 2): logsumexp of the token's logits, kept in
+  // the spare last column of its LDS row until the block sums the squares.
+  if (q == 0) row[epad] = valid ? mx + logf(se) : 0.f;
   // [GShard] "Random routing": keep the 2nd slot iff u < 2 w2, w2 = 1 / (1 + exp(l1 - l2)),
   // decided in fp64 from the two fp32 logits (by the two lanes that use it).
   bool keep2 = true;
@@ -397,6 +412,15 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
   for (int idx = t; idx < k * E; idx += kThreads) {
     const int j = idx / E, e = idx - j * E;
     a.ahist[((static_cast<size_t>(g) * k + j) * E + e) * a.nbg + bi] = hact[j * epad + e];
+  }
+  if (t < kRouteTokens) {  // one wave: the block's sum of logsumexp^2, fp64, fixed order
+    double z = 0.0;
+    if (t < nt) {
+      const double v = lg[t * ls + epad];
+      z = v * v;
+    }
+    z = wave_sum(z);
+    if (t == 0) a.zpart[b] = z;
   }
 }
 

@@ -48,6 +48,7 @@ def run_gpu(cfg, dev, workspace=None):
     out = meta.to_numpy()
     out["y"] = y.float().cpu().numpy()
     out["aux"] = float(aux.cpu().numpy()[0])
+    out["z_loss"] = float(out["z_loss"][0])
     return out
 
 
@@ -62,7 +63,8 @@ def rr_margin(cfg, logits32, idx, u):
 
 
 def check_routing(cfg, g, ref):
-    """Bit-exact integer outputs, weights within W_TOL, aux within AUX_TOL relative."""
+    """Bit-exact integer outputs, weights within W_TOL, aux and z-loss within AUX_TOL
+    relative."""
     for f in ("topk_idx", "pos", "row", "count", "offset"):
         a, b = np.asarray(g[f]), np.asarray(ref[f]).astype(np.int64)
         assert a.shape == b.shape, (f, a.shape, b.shape)
@@ -76,6 +78,12 @@ def check_routing(cfg, g, ref):
         assert rel <= AUX_TOL, f"aux {g['aux']} vs {ref['aux']} (rel {rel})"
     else:
         assert g["aux"] == 0.0
+    if "z_loss" in g:
+        if ref["z_loss"] != 0:
+            rel = abs(g["z_loss"] - ref["z_loss"]) / abs(ref["z_loss"])
+            assert rel <= AUX_TOL, f"z_loss {g['z_loss']} vs {ref['z_loss']} (rel {rel})"
+        else:
+            assert g["z_loss"] == 0.0
 
 
 def rel_err(a, ref):
@@ -126,6 +134,7 @@ def full_check(cfg, n_sample=None, seed=None, inp=None):
     if cfg["residual"] and cfg["n_shared"] == 0 and dropped.size:
         assert (g["y"][dropped] == inp.x[dropped]).all(), "dropped tokens must pass x through"
     rep = dict(name=name, logits_err=lerr, y_err=yerr, aux=g["aux"], aux_ref=ref["aux"],
+               z_loss=g["z_loss"], z_loss_ref=ref["z_loss"],
                stats=g["stats"].tolist(), sampled=len(toks), rr_margin=margin)
     say(f"[gpu] {name}: ok {rep}")
     return rep, g, ref, inp, dev

@@ -65,6 +65,10 @@ BAD = [
     (dict(capacity=0), binding.MOE_EINVAL),
     (dict(act=3), binding.MOE_EINVAL),
     (dict(gate_norm=3), binding.MOE_EINVAL),
+    (dict(gate_norm=2, norm_p=0.0), binding.MOE_EINVAL),
+    (dict(gate_norm=2, norm_p=-1.0), binding.MOE_EINVAL),
+    (dict(gate_norm=2, norm_p=float("nan")), binding.MOE_EINVAL),
+    (dict(gate_norm=2, norm_p=float("inf")), binding.MOE_EINVAL),
     (dict(random_routing=1, top_k=1), binding.MOE_EINVAL),
     (dict(residual=2), binding.MOE_EINVAL),
     (dict(dtype=5), binding.MOE_EINVAL),
@@ -125,6 +129,7 @@ INVALID_CALLS = [
     ("null u with random routing", dict(u=None), binding.MOE_EINVAL),
     ("misaligned bg", dict(bg=FakeTensor(0x28000002)), binding.MOE_EINVAL),
     ("misaligned meta.row", dict(meta=_fake_meta(bad="row")), binding.MOE_EINVAL),
+    ("misaligned meta.z_loss", dict(meta=_fake_meta(bad="z_loss")), binding.MOE_EINVAL),
     ("null meta.logits", dict(meta=binding.Meta(**{f: FakeTensor(0x10000000 + 0x1000 * i)
                                                    for i, f in enumerate(binding.Meta.FIELDS)
                                                    if f != "logits"})), binding.MOE_EINVAL),

@@ -48,7 +48,7 @@ def test_route_from_oracle_logits():
     """Reverse direction: moe_route fed the oracle's own logits (rounded to fp32)."""
     h = harness()
     from oracle import moe_oracle as mo
-    for name in ("small_top2_rr", "small_shared_top3", "gshard_bf16"):
+    for name in ("small_top2_rr", "small_shared_top3", "small_pnorm_top4", "gshard_bf16"):
         cfg = configs.ALL[name]
         h.say(f"[gpu] moe_route {name}")
         inp = synth.make_inputs(cfg)
@@ -62,6 +62,7 @@ def test_route_from_oracle_logits():
         torch.cuda.synchronize()
         g = meta.to_numpy()
         g["aux"] = float(aux[0].cpu())
+        g["z_loss"] = float(g["z_loss"][0])
         h.check_routing(cfg, g, ref)
 
 
@@ -80,7 +81,7 @@ def test_deterministic_and_padding_never_read():
     for o in outs[1:]:
         for f in ("y", "logits", "topk_idx", "topk_w", "pos", "row", "count", "offset", "stats"):
             assert np.array_equal(o[f], outs[0][f], equal_nan=False), f
-        assert o["aux"] == outs[0]["aux"]
+        assert o["aux"] == outs[0]["aux"] and o["z_loss"] == outs[0]["z_loss"]
     assert np.isfinite(outs[0]["y"]).all()
 
 
@@ -103,6 +104,8 @@ EDGE = {
                         d_ff=192, act=1),
     "bare_layer_drops": _cfg(residual=0, capacity=20, n_experts=8, zipf_s=1.5),
     "one_token": _cfg(n_tokens=1, capacity=1),
+    "pnorm_p8_top8": _cfg(n_experts=32, top_k=8, capacity=64, gate_norm=2, norm_p=8.0,
+                          n_groups=2),
 }
 
 
@@ -130,6 +133,7 @@ def test_empty_batch():
     meta.count.fill_(7)
     meta.offset.fill_(7)
     meta.stats.fill_(7)
+    meta.z_loss.fill_(7)
     ws = binding.alloc_workspace(cfg)
     aux = torch.full((4,), 5.0, device="cuda")
     empty = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
@@ -137,6 +141,7 @@ def test_empty_batch():
     torch.cuda.synchronize()
     assert int(meta.count.abs().sum()) == 0 and int(meta.offset.abs().sum()) == 0
     assert int(meta.stats.abs().sum()) == 0 and float(aux[0]) == 0.0
+    assert float(meta.z_loss[0]) == 0.0
 
 
 @pytest.mark.parametrize("act", [1, 2], ids=["gelu", "swiglu"])
