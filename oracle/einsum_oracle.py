@@ -46,7 +46,17 @@ def einsum_layer(cfg, x, Wg, W1, W2, bg=None, u=None, logits32=None):
     # Gates: full softmax, then successive argmax with lower index winning ties.
     ex = np.exp(lg - lg.max(axis=1, keepdims=True))
     probs = ex / ex.sum(axis=1, keepdims=True)
+    D, TG = cfg.get("expert_groups", 1), cfg.get("topk_groups", 1)
     remaining = lg.copy()
+    if D > 1:
+        # group-limited routing: a group's rank counts the groups with a larger best logit
+        # (and the lower-indexed ones with an equal one); ranks below TG are allowed
+        gmax = lg.reshape(N, D, E // D).max(axis=2)                       # [N, D]
+        gt = (gmax[:, None, :] > gmax[:, :, None]).sum(axis=2)
+        eq_before = ((gmax[:, None, :] == gmax[:, :, None]) &
+                     (np.arange(D)[None, None, :] < np.arange(D)[None, :, None])).sum(axis=2)
+        ok = np.repeat((gt + eq_before) < TG, E // D, axis=1)             # [N, E]
+        remaining = np.where(ok, remaining, -np.inf)
     onehots, psel = [], []
     for _ in range(k):
         best = remaining.argmax(axis=1)           # first maximum = lowest index
@@ -55,6 +65,7 @@ def einsum_layer(cfg, x, Wg, W1, W2, bg=None, u=None, logits32=None):
         psel.append((probs * oh).sum(axis=1))
         remaining = np.where(oh > 0, -np.inf, remaining)
     psel = np.stack(psel, axis=1)                  # [N, k]
+    sel = sum(onehots)                             # [N, E] top-k selections (pre-capacity)
     if cfg["gate_norm"] == 2:                      # p-norm of the selected probabilities
         P = float(cfg.get("norm_p", 1.0))
         w = psel / np.linalg.norm(psel, ord=P, axis=1, keepdims=True) if P >= 1 else \
@@ -98,15 +109,17 @@ def einsum_layer(cfg, x, Wg, W1, W2, bg=None, u=None, logits32=None):
     if cfg["residual"]:
         y = y + x
 
-    # Aux loss from the dense masks (pre-capacity selections).
-    sel = sum(np.eye(E)[np.argsort(-lg, axis=1, kind="stable")[:, j]] for j in range(k))
-    aux = 0.0
+    # Aux and device-level losses from the dense masks (pre-capacity selections).
+    aux = dev = 0.0
     for g in range(G):
         m = probs[g * S:(g + 1) * S].mean(axis=0)
         c = sel[g * S:(g + 1) * S].sum(axis=0)
         aux += E * float((m * c).sum()) / (k * S)
+        f = E * c / (k * S)
+        dev += float((f.reshape(D, E // D).mean(axis=1) * m.reshape(D, E // D).sum(axis=1)).sum())
     aux /= G
+    dev /= G
     counts = dispatch.sum(axis=(1, 3))            # [G, E]
     z = float(np.mean(logsumexp(lg, axis=1) ** 2)) if N else 0.0   # router z-loss
-    return dict(y=y, aux=aux, z_loss=z, dispatch=dispatch, combine=combine,
+    return dict(y=y, aux=aux, z_loss=z, dev_loss=dev, dispatch=dispatch, combine=combine,
                 count=counts.astype(np.int32), logits=lg)

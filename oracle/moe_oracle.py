@@ -42,6 +42,15 @@ function that depends on it (and listed in the design doc):
   R-pnorm  the optional p-norm renormalisation of [MegaBlocks] section 2 divides the k
            selected probabilities by their p-norm, (sum_i p_i^P)^(1/P), P > 0 a real
            number (P = 1 is the sum normalisation); gate_norm == 2 selects it.
+  R-grp    group-limited routing ([Lec16] "DeepSeek V3 MoE (670B)": 8 expert groups, 4
+           "limited groups"): the E experts form D contiguous groups of E/D; a group's score
+           is the largest logit among its experts (equivalently its largest softmax score);
+           each token keeps the topk_groups best groups (ties to the lower group index)
+           and picks its top-k experts among theirs only.  D = 1 is plain top-k.
+  R-dev    the device-level balance loss of [Lec16] "DeepSeek MoE 的负载均衡" groups the
+           expert-level terms by the same D groups: per token group, sum_j f_j P_j with
+           f_j the mean over group j of f_i = E c_i / (k S) and P_j the sum over group j of
+           P_i = m_i; averaged over token groups like the aux loss.
   R-z      the router z-loss of [MegaBlocks] section 2 is the mean over all N tokens of
            logsumexp(logits_n)^2, on the fp32 logits that feed the softmax (router offsets
            included), one number per layer whatever the grouping.
@@ -93,6 +102,29 @@ def topk_experts(logits, k):
     l = np.asarray(logits, dtype=np.float64)
     order = np.argsort(-l, axis=1, kind="stable")
     return order[:, :k].astype(np.int32)
+
+
+def expert_group_mask(logits, n_expert_groups, topk_groups):
+    """Experts each token may route to under group-limited routing (R-grp), bool [N, E].
+
+    Group d holds experts [d E/D, (d+1) E/D).  Its score is the largest logit of its
+    experts; the topk_groups best groups of a token (stable order: ties to the lower group
+    index) are allowed.  With D == 1 every expert is allowed.
+    """
+    l = np.asarray(logits, dtype=np.float64)
+    N, E = l.shape
+    D = int(n_expert_groups)
+    allowed = np.ones((N, E), dtype=bool)
+    if D <= 1:
+        return allowed
+    gs = E // D
+    for n in range(N):
+        score = np.array([l[n, d * gs:(d + 1) * gs].max() for d in range(D)])
+        keep = np.argsort(-score, kind="stable")[:topk_groups]
+        allowed[n] = False
+        for d in keep:
+            allowed[n, d * gs:(d + 1) * gs] = True
+    return allowed
 
 
 def gate_weights(p, idx, gate_norm, norm_p=1.0):
@@ -228,6 +260,33 @@ def aux_loss(p, idx, n_groups, n_experts):
     return total / G
 
 
+def dev_loss(p, idx, n_groups, n_experts, n_expert_groups):
+    """Device-level balance loss (R-dev), the expert-level terms summed per expert group.
+
+    [Lec16] "DeepSeek MoE 的负载均衡": L_DevBal = sum_j f_j P_j with f_j the mean f of the
+    experts in group j and P_j the sum of their P; f_i = (E/k) * (tokens to i) / T and
+    P_i = mean routing score, as in the expert-level loss (computed per token group of S
+    tokens, then averaged over the G token groups).  An empty batch gives 0.
+    """
+    N, k = idx.shape
+    G, E, D = n_groups, n_experts, int(n_expert_groups)
+    if N == 0:
+        return 0.0
+    S = N // G
+    gs = E // D
+    total = 0.0
+    for g in range(G):
+        P = np.asarray(p[g * S:(g + 1) * S], dtype=np.float64).sum(axis=0) / S
+        cnt = np.zeros(E, dtype=np.float64)
+        for n in range(g * S, (g + 1) * S):
+            for j in range(k):
+                cnt[idx[n, j]] += 1.0
+        f = E * cnt / (k * S)
+        for d in range(D):
+            total += f[d * gs:(d + 1) * gs].mean() * P[d * gs:(d + 1) * gs].sum()
+    return total / G
+
+
 def route(cfg, logits32, u=None):
     """Routing, positions, dispatch rows and aux from given fp32 logits (no FFN).
 
@@ -242,9 +301,12 @@ def route(cfg, logits32, u=None):
         return dict(topk_idx=z, active=z.astype(bool), pos=z, row=z,
                     topk_w=np.zeros((0, k)), w_pre=np.zeros((0, k)),
                     count=np.zeros((G, E), np.int32), offset=np.zeros(E + 1, np.int32),
-                    aux=0.0, z_loss=0.0, stats=np.zeros(4, np.int64), p=np.zeros((0, E)))
+                    aux=0.0, z_loss=0.0, dev_loss=0.0, stats=np.zeros(4, np.int64),
+                    p=np.zeros((0, E)))
     p = softmax(l32)
-    idx = topk_experts(l32, k)
+    D, TG = cfg.get("expert_groups", 1), cfg.get("topk_groups", 1)
+    allowed = expert_group_mask(l32, D, TG)
+    idx = topk_experts(np.where(allowed, l32.astype(np.float64), -np.inf), k)
     w_pre = gate_weights(p, idx, cfg["gate_norm"], cfg.get("norm_p", 1.0))
     active = np.ones((N, k), dtype=bool)
     if cfg["random_routing"]:
@@ -262,7 +324,7 @@ def route(cfg, logits32, u=None):
                      dtype=np.int64)
     return dict(topk_idx=idx, active=active, pos=pos, row=row, topk_w=topk_w,
                 w_pre=w_pre, count=count, offset=offset, aux=aux, z_loss=z_loss(l32),
-                stats=stats, p=p)
+                dev_loss=dev_loss(p, idx, G, E, D), stats=stats, p=p)
 
 
 # --------------------------------------------------------------------------- experts

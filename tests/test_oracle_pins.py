@@ -43,7 +43,9 @@ def clone(**replace):
         G, C = cfg["n_groups"], cfg["capacity"]
         l32 = np.asarray(logits32, np.float32).reshape(N, E)
         p = _ns.softmax(l32)
-        idx = _ns.topk_experts(l32, k)
+        D, TG = cfg.get("expert_groups", 1), cfg.get("topk_groups", 1)
+        allowed = _ns.expert_group_mask(l32, D, TG)
+        idx = _ns.topk_experts(np.where(allowed, l32.astype(np.float64), -np.inf), k)
         w_pre = _ns.gate_weights(p, idx, cfg["gate_norm"], cfg.get("norm_p", 1.0))
         active = np.ones((N, k), bool)
         if cfg["random_routing"]:
@@ -54,7 +56,7 @@ def clone(**replace):
         return dict(topk_idx=idx, active=active, pos=pos, row=row,
                     topk_w=np.where(kept, w_pre, 0.0), w_pre=w_pre, count=count,
                     offset=offset, aux=_ns.aux_loss(p, idx, G, E),
-                    z_loss=_ns.z_loss(l32), p=p)
+                    z_loss=_ns.z_loss(l32), dev_loss=_ns.dev_loss(p, idx, G, E, D), p=p)
     if "route" not in replace:
         ns.route = route
     return ns
@@ -248,10 +250,14 @@ def check_vs_einsum(m, trials=60):
     for t in range(trials):
         E = 4; k = int(rng.integers(1, 3)); G = int(rng.integers(1, 3)); N = 8
         C = int(rng.integers(1, 5)); rr = int(k == 2 and t % 2)
+        D = [1, 2, 4][t % 3]
+        TG = int(rng.integers(1, D + 1))
+        while TG * (E // D) < k:
+            TG += 1
         cfg = cfg_of(n_tokens=N, n_groups=G, n_experts=E, top_k=k, capacity=C,
                      random_routing=rr, act=t % 3, gate_norm=[0, 1, 1, 2][t % 4],
                      n_shared=int(t % 5 == 0), residual=int(t % 7 != 0),
-                     norm_p=[0.5, 2.0, 3.0][t % 3])
+                     norm_p=[0.5, 2.0, 3.0][t % 3], expert_groups=D, topk_groups=TG)
         M, H = 6, 10
         x = rng.standard_normal((N, M))
         Wg = rng.standard_normal((E, M))
@@ -265,6 +271,7 @@ def check_vs_einsum(m, trials=60):
         np.testing.assert_allclose(y, d["y"], rtol=1e-12, atol=1e-12)
         assert abs(r["aux"] - d["aux"]) < 1e-12
         assert abs(r["z_loss"] - d["z_loss"]) <= 1e-12 * d["z_loss"]
+        assert abs(r["dev_loss"] - d["dev_loss"]) < 1e-12
         assert (r["count"] == d["count"]).all()
 
 
@@ -525,6 +532,71 @@ def check_z_loss(m):
     assert m.route(cfg, l)["z_loss"] == m.z_loss(l)
 
 
+def check_group_limited_routing(m):
+    """Group-limited routing ([Lec16] "DeepSeek V3 MoE (670B)", R-grp).  Hand example: E=8
+    in 4 pairs, one token with logits [5, 0, 0, 0, 0, 0, 4.9, 4.8]: group maxima (5, 0, 0,
+    4.9); 1 group allowed -> top-2 = (0, 1); 2 groups -> top-3 = (0, 6, 7); plain top-2 =
+    (0, 6).  Equal maxima go to the lower group.  Reductions: D = 1 or topk_groups = D is
+    plain top-k; D = E with topk_groups = k is plain top-k.  Invariant on random logits:
+    the k experts lie in at most topk_groups groups, each among the topk_groups best."""
+    l = np.array([[5, 0, 0, 0, 0, 0, 4.9, 4.8]], np.float32)
+    def sel(D, TG, k, logits=l):
+        allowed = m.expert_group_mask(logits, D, TG)
+        return m.topk_experts(np.where(allowed, logits.astype(np.float64), -np.inf), k)
+    assert sel(4, 1, 2).tolist() == [[0, 1]]
+    assert sel(4, 2, 3).tolist() == [[0, 6, 7]]
+    assert sel(1, 1, 2).tolist() == [[0, 6]]
+    eq = np.zeros((1, 8), np.float32)
+    assert m.expert_group_mask(eq, 4, 2).tolist() == [[True] * 4 + [False] * 4]
+    rng = np.random.default_rng(41)
+    N, E = 60, 16
+    lr = rng.standard_normal((N, E)).astype(np.float32)
+    plain = m.topk_experts(lr, 4)
+    np.testing.assert_array_equal(sel(4, 4, 4, lr), plain)
+    np.testing.assert_array_equal(sel(E, 4, 4, lr), plain)
+    np.testing.assert_array_equal(sel(1, 1, 4, lr), plain)
+    for D, TG, k in ((4, 2, 4), (8, 3, 5), (2, 1, 6)):
+        idx = sel(D, TG, k, lr)
+        gs = E // D
+        gmax = lr.reshape(N, D, gs).max(axis=2)
+        for n in range(N):
+            groups = set((idx[n] // gs).tolist())
+            assert len(groups) <= TG
+            best = np.sort(gmax[n])[::-1][:TG]
+            assert all(gmax[n, d] >= best[-1] for d in groups)
+    # through route(): the selection and the aux counts use the limited top-k
+    cfg = cfg_of(n_tokens=N, n_experts=E, top_k=4, capacity=N, expert_groups=4, topk_groups=2)
+    r = m.route(cfg, lr)
+    np.testing.assert_array_equal(r["topk_idx"], sel(4, 2, 4, lr))
+
+
+def check_dev_loss(m):
+    """Device-level balance loss (R-dev).  Closed forms: equal logits give 1 whatever the
+    selections (P_j = 1/D); selections spread evenly over the D groups give sum_j P_j = 1
+    whatever the scores; D = 1 gives 1; D = E gives the expert-level aux loss.  Hand
+    example (S = 2, E = 4, D = 2, k = 1): p = [[.7, .1, .1, .1], [.6, .2, .1, .1]], the
+    tokens pick experts 0 and 1: f = E c / (k S) = (2, 2, 0, 0), group means (2, 0); P =
+    (.65, .15, .1, .1), group sums (.8, .2); loss 2 * .8 = 1.6."""
+    p = np.array([[.7, .1, .1, .1], [.6, .2, .1, .1]])
+    idx = np.array([[0], [1]])
+    assert abs(m.dev_loss(p, idx, 1, 4, 2) - 1.6) < 1e-12
+    rng = np.random.default_rng(42)
+    N, E, k = 48, 8, 2
+    l = rng.standard_normal((N, E)).astype(np.float32)
+    pr = m.softmax(l)
+    idx = m.topk_experts(l, k)
+    for G in (1, 3):
+        assert abs(m.dev_loss(pr, idx, G, E, 1) - 1.0) < 1e-12
+        assert abs(m.dev_loss(pr, idx, G, E, E) - m.aux_loss(pr, idx, G, E)) < 1e-12
+        pu = m.softmax(np.zeros((N, E), np.float32))
+        for D in (2, 4):
+            assert abs(m.dev_loss(pu, idx, G, E, D) - 1.0) < 1e-12
+    # even spread over 4 groups of 2: token n picks experts 2(n % 4) and 2(n % 4) + 1
+    ev = np.stack([2 * (np.arange(N) % 4), 2 * (np.arange(N) % 4) + 1], axis=1)
+    assert abs(m.dev_loss(pr, ev, 1, E, 4) - 1.0) < 1e-12
+    assert m.route(cfg_of(n_tokens=0), np.zeros((0, 4), np.float32))["dev_loss"] == 0.0
+
+
 def check_empty_batch(m):
     r = m.route(cfg_of(n_tokens=0, n_groups=1), np.zeros((0, 4), np.float32))
     assert r["aux"] == 0.0 and r["count"].sum() == 0 and r["offset"].tolist() == [0] * 5
@@ -538,7 +610,8 @@ CHECKS = [check_aux_uniform_scores, check_aux_round_robin, check_aux_saturation,
           check_gate_weights, check_random_routing, check_router_onehot_rows,
           check_gelu_values, check_single_expert_is_dense_ffn, check_split_identity,
           check_swish_values, check_swiglu_gate_saturation, check_swiglu_split_identity,
-          check_pnorm_weights, check_z_loss, check_empty_batch]
+          check_pnorm_weights, check_z_loss, check_group_limited_routing, check_dev_loss,
+          check_empty_batch]
 
 
 @pytest.mark.parametrize("check", CHECKS, ids=[c.__name__ for c in CHECKS])
@@ -684,6 +757,35 @@ def _zloss_sum_not_mean(logits32):
     return mo.z_loss(logits32) * np.asarray(logits32).shape[0]
 
 
+def _group_score_sum(logits, n_expert_groups, topk_groups):
+    l = np.asarray(logits, np.float64)
+    N, E = l.shape
+    D = int(n_expert_groups)
+    if D <= 1:
+        return np.ones((N, E), bool)
+    gs = E // D
+    keep = np.argsort(-l.reshape(N, D, gs).sum(axis=2), axis=1, kind="stable")[:, :topk_groups]
+    return np.repeat(np.isin(np.arange(D)[None, :].repeat(N, 0), keep), gs, axis=1) if N else \
+        np.ones((0, E), bool)
+
+
+def _group_ties_high(logits, n_expert_groups, topk_groups):
+    l = np.asarray(logits, np.float64)
+    return mo.expert_group_mask(l[:, ::-1], n_expert_groups, topk_groups)[:, ::-1]
+
+
+def _no_group_limit(logits, n_expert_groups, topk_groups):
+    return np.ones(np.asarray(logits).shape, bool)
+
+
+def _dev_loss_sum_f(p, idx, n_groups, n_experts, n_expert_groups):
+    return mo.dev_loss(p, idx, n_groups, n_experts, n_expert_groups) * (n_experts // n_expert_groups)
+
+
+def _dev_loss_mean_p(p, idx, n_groups, n_experts, n_expert_groups):
+    return mo.dev_loss(p, idx, n_groups, n_experts, n_expert_groups) / (n_experts // n_expert_groups)
+
+
 def _rows_group_major(idx, pos, count):
     G, E = count.shape
     N, k = idx.shape
@@ -728,6 +830,11 @@ MUTANTS = {
     "zloss_not_squared": dict(z_loss=_zloss_not_squared),
     "zloss_of_max": dict(z_loss=_zloss_of_max),
     "zloss_sum_not_mean": dict(z_loss=_zloss_sum_not_mean),
+    "group_score_sum": dict(expert_group_mask=_group_score_sum),
+    "group_ties_high": dict(expert_group_mask=_group_ties_high),
+    "no_group_limit": dict(expert_group_mask=_no_group_limit),
+    "dev_loss_sum_f": dict(dev_loss=_dev_loss_sum_f),
+    "dev_loss_mean_p": dict(dev_loss=_dev_loss_mean_p),
 }
 
 
