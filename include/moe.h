@@ -36,7 +36,9 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3   /* 2: gated (SwiGLU) experts; 3: p-norm gates, router z-loss */
+/* 2: gated (SwiGLU) experts; 3: p-norm gates, router z-loss; 4: group-limited routing,
+ * device-level balance loss */
+#define MOE_ABI_VERSION 4
 
 enum moe_status {
   MOE_OK = 0,
@@ -79,6 +81,12 @@ enum moe_dtype { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 };
  *   dtype          enum moe_dtype.
  *   norm_p         P of MOE_NORM_P: finite and > 0 (MOE_EINVAL otherwise); ignored for the
  *                  other gate_norm values.
+ *   expert_groups  D, 1 <= D <= 32, E % D == 0: the experts form D contiguous groups of
+ *                  E/D ([Lec16] "DeepSeek V3 MoE (670B)": expert groups / limited groups).
+ *   topk_groups    1 <= topk_groups <= D: each token keeps the topk_groups groups whose best
+ *                  logit is largest (ties to the lower group index) and takes its top-k
+ *                  among their experts; needs k <= topk_groups * E/D.  D = 1 (with
+ *                  topk_groups = 1) is plain top-k.  The groups also define dev_loss.
  * Shape constraints (MOE_EUNSUPPORTED otherwise):
  *   bf16: M % 128 == 0 and H % 128 == 0.   fp32: M % 64 == 0 and H % 64 == 0.
  */
@@ -97,12 +105,15 @@ typedef struct moe_cfg {
   int32_t residual;
   int32_t dtype;
   float norm_p;
+  int32_t expert_groups;
+  int32_t topk_groups;
 } moe_cfg;
 
 /*
  * Dispatch metadata: caller-allocated device arrays the layer fills ([MegaBlocks] section 2
  * returns scores, expert weights and top experts; [Lec16] "MoE Kernel 优化" keeps a dense
- * token-to-expert table).  Every pointer but z_loss is required (16-byte aligned).
+ * token-to-expert table).  Every pointer but z_loss and dev_loss is required, and every
+ * non-NULL one must be 16-byte aligned.
  *   logits    [N, E] fp32   router logits x Wg^T (+ bg)   (moe_forward only; moe_route
  *                           reads its logits from its own argument and ignores this one)
  *   topk_idx  [N, k] int32  selected experts, descending logit, BEFORE capacity / random
@@ -118,6 +129,11 @@ typedef struct moe_cfg {
  *   z_loss    [1]    fp32   router z-loss, the mean over all N tokens of
  *                           logsumexp(logits_n)^2 ([MegaBlocks] section 2), or NULL: not
  *                           computed.  fp32 logsumexp per token, fp64 fixed-order mean.
+ *   dev_loss  [1]    fp32   device-level balance loss over the cfg.expert_groups groups
+ *                           ([Lec16] "DeepSeek MoE 的负载均衡"): per token group,
+ *                           sum_j f_j P_j with f_j the mean over expert group j of
+ *                           f_e = E c_e / (k S) and P_j the sum of m_e over it, averaged
+ *                           over token groups (fp64); or NULL: not computed.
  */
 typedef struct moe_meta {
   float* logits;
@@ -129,6 +145,7 @@ typedef struct moe_meta {
   int32_t* offset;
   int32_t* stats;
   float* z_loss;
+  float* dev_loss;
 } moe_meta;
 
 /* Number of stage boundaries recorded by moe_forward_timed. */

@@ -28,7 +28,9 @@ class MoeCfg(ctypes.Structure):
 
 
 META_FIELDS = ("logits", "topk_idx", "topk_w", "pos", "row", "count", "offset", "stats",
-               "z_loss")
+               "z_loss", "dev_loss")
+# moe_cfg fields a workload dict may leave out, and the values that turn them off
+CFG_DEFAULTS = {"norm_p": 1.0, "expert_groups": 1, "topk_groups": 1}
 
 
 class MoeMetaC(ctypes.Structure):
@@ -89,8 +91,10 @@ def make_cfg(cfg):
     """dict (configs.py style) or MoeCfg -> MoeCfg."""
     if isinstance(cfg, MoeCfg):
         return cfg
-    return MoeCfg(**{f: float(cfg.get(f, 1.0)) if f in _FLOAT_FIELDS else int(cfg[f])
-                     for f in CFG_FIELDS})
+    def val(f):
+        v = cfg[f] if f in cfg else CFG_DEFAULTS[f]
+        return float(v) if f in _FLOAT_FIELDS else int(v)
+    return MoeCfg(**{f: val(f) for f in CFG_FIELDS})
 
 
 def moe_workspace_size(cfg):
@@ -136,7 +140,8 @@ def alloc_meta(cfg, device="cuda"):
                 pos=torch.empty((N, k), **i32), row=torch.empty((N, k), **i32),
                 count=torch.empty((G, E), **i32), offset=torch.empty((E + 1,), **i32),
                 stats=torch.empty((4,), **i32),
-                z_loss=torch.empty((4,), dtype=torch.float32, device=device))
+                z_loss=torch.empty((4,), dtype=torch.float32, device=device),
+                dev_loss=torch.empty((4,), dtype=torch.float32, device=device))
 
 
 def alloc_workspace(cfg, device="cuda"):

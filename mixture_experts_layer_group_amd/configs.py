@@ -17,12 +17,13 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 
 def _cfg(name, *, n_tokens, n_groups, d_model, d_ff, n_experts, top_k, capacity,
          act, gate_norm, dtype, n_shared=0, random_routing=0, residual=1,
-         norm_p=1.0, zipf_s=0.0, seed=0, desc=""):
+         norm_p=1.0, expert_groups=1, topk_groups=1, zipf_s=0.0, seed=0, desc=""):
     return dict(name=name, n_tokens=n_tokens, n_groups=n_groups, d_model=d_model,
                 d_ff=d_ff, n_experts=n_experts, n_shared=n_shared, top_k=top_k,
                 capacity=capacity, act=act, gate_norm=gate_norm,
                 random_routing=random_routing, residual=residual, dtype=dtype,
-                norm_p=norm_p, zipf_s=zipf_s, seed=seed, desc=desc)
+                norm_p=norm_p, expert_groups=expert_groups, topk_groups=topk_groups,
+                zipf_s=zipf_s, seed=seed, desc=desc)
 
 
 # The five reference workloads.
@@ -63,6 +64,16 @@ WORKLOADS = {
         gate_norm=NORM_SUM, dtype=DTYPE_BF16, zipf_s=1.2,
         desc="shared+routed SwiGLU bf16: 32768 tokens, M=2048, 2 shared + 64 routed experts "
              "(Swish(x W1) * x W2) W3 with H=1408, top-6, C=4608, Zipf(1.2) offsets"),
+    # Fine-grained experts with group-limited routing, after [Lec16] "DeepSeek V3 MoE
+    # (670B)": 256 routed experts in 8 groups of which each token may use 4, 8 active, one
+    # shared expert, SwiGLU experts; hidden sizes scaled to M=2048, H=512.
+    "fine_grained_grouped_bf16": _cfg(
+        "fine_grained_grouped_bf16", n_tokens=16384, n_groups=1, d_model=2048, d_ff=512,
+        n_experts=256, n_shared=1, top_k=8, capacity=640, act=ACT_SWIGLU,
+        gate_norm=NORM_SUM, expert_groups=8, topk_groups=4, dtype=DTYPE_BF16,
+        desc="fine-grained grouped SwiGLU bf16: 16384 tokens, M=2048, 256 routed experts "
+             "(H=512) in 8 groups, 4 groups and 8 experts per token, 1 shared expert, "
+             "C=1.25*8N/256=640"),
 }
 
 # The workload the benchmark times by default.
@@ -103,6 +114,10 @@ SMALL = {
         "small_pnorm_top4", n_tokens=896, n_groups=2, d_model=256, d_ff=256,
         n_experts=16, top_k=4, capacity=140, act=ACT_GELU, gate_norm=NORM_P, norm_p=2.0,
         dtype=DTYPE_BF16, zipf_s=0.5, seed=18),
+    "small_grouped_top4": _cfg(
+        "small_grouped_top4", n_tokens=1024, n_groups=2, d_model=256, d_ff=256,
+        n_experts=32, top_k=4, capacity=96, act=ACT_SWIGLU, gate_norm=NORM_SUM,
+        expert_groups=8, topk_groups=3, dtype=DTYPE_BF16, zipf_s=0.3, seed=20),
     "small_pnorm_half_fp32": _cfg(
         "small_pnorm_half_fp32", n_tokens=384, n_groups=3, d_model=64, d_ff=128,
         n_experts=7, top_k=3, capacity=40, act=ACT_RELU, gate_norm=NORM_P, norm_p=0.5,
@@ -113,7 +128,7 @@ ALL = {**WORKLOADS, **SMALL}
 
 CFG_FIELDS = ("n_tokens", "n_groups", "d_model", "d_ff", "n_experts", "n_shared",
               "top_k", "capacity", "act", "gate_norm", "random_routing", "residual",
-              "dtype", "norm_p")
+              "dtype", "norm_p", "expert_groups", "topk_groups")
 
 
 def with_overrides(cfg, **kw):

@@ -48,7 +48,12 @@ int check_cfg(const moe_cfg* c) {
   if (c->random_routing && c->top_k != 2) return MOE_EINVAL;
   if (c->residual != 0 && c->residual != 1) return MOE_EINVAL;
   if (c->dtype != MOE_DTYPE_F32 && c->dtype != MOE_DTYPE_BF16) return MOE_EINVAL;
-  if (c->n_experts > moe::kMaxExperts || c->top_k > moe::kMaxTopK) return MOE_EUNSUPPORTED;
+  if (c->expert_groups < 1 || c->n_experts % c->expert_groups != 0) return MOE_EINVAL;
+  if (c->topk_groups < 1 || c->topk_groups > c->expert_groups) return MOE_EINVAL;
+  if (c->top_k > c->topk_groups * (c->n_experts / c->expert_groups)) return MOE_EINVAL;
+  if (c->n_experts > moe::kMaxExperts || c->top_k > moe::kMaxTopK ||
+      c->expert_groups > moe::kMaxExpertGroups)
+    return MOE_EUNSUPPORTED;
   if (c->dtype == MOE_DTYPE_BF16) {
     if (c->d_model % 128 || c->d_ff % 128) return MOE_EUNSUPPORTED;
   } else {
@@ -108,14 +113,16 @@ int check_meta(const moe_meta* m, bool need_logits) {
   for (const void* p : ps)
     if (!p || !aligned16(p)) return MOE_EINVAL;
   if (need_logits && (!m->logits || !aligned16(m->logits))) return MOE_EINVAL;
-  if (m->z_loss && !aligned16(m->z_loss)) return MOE_EINVAL;  // optional output
+  if (m->z_loss && !aligned16(m->z_loss)) return MOE_EINVAL;  // optional outputs
+  if (m->dev_loss && !aligned16(m->dev_loss)) return MOE_EINVAL;
   return MOE_OK;
 }
 
-// N == 0: only count, offset, stats (and z_loss if requested) are written.
+// N == 0: only count, offset, stats (and z_loss / dev_loss if requested) are written.
 int check_meta_empty(const moe_meta* m) {
   if (!m || !m->count || !m->offset || !m->stats) return MOE_EINVAL;
   if (m->z_loss && !aligned16(m->z_loss)) return MOE_EINVAL;
+  if (m->dev_loss && !aligned16(m->dev_loss)) return MOE_EINVAL;
   return MOE_OK;
 }
 
@@ -148,6 +155,7 @@ int run_routing(const Run& r, const void* x, const void* Wg, const float* bg, co
   ra.ahist = reinterpret_cast<int32_t*>(ws + L.ahist);
   ra.zpart = reinterpret_cast<double*>(ws + L.zpart);
   ra.norm_p = c->norm_p;
+  ra.n_eg = c->expert_groups; ra.topk_eg = c->topk_groups;
   ra.N = c->n_tokens; ra.G = c->n_groups; ra.S = static_cast<int>(L.S); ra.M = c->d_model;
   ra.E = c->n_experts; ra.k = c->top_k; ra.norm = c->gate_norm; ra.rr = c->random_routing;
   ra.nbg = static_cast<int>(L.nbg); ra.dtype = c->dtype;
@@ -197,6 +205,8 @@ moe::CombineArgs combine_args(const Run& r, const void* x, void* y, float* aux,
   ca.aux = aux;
   ca.zpart = reinterpret_cast<const double*>(r.ws + r.L.zpart);
   ca.z_loss = m->z_loss;
+  ca.dev_loss = m->dev_loss;
+  ca.n_eg = c->expert_groups;
   ca.nblocks = static_cast<int>(c->n_groups * r.L.nbg);
   ca.N = c->n_tokens; ca.M = c->d_model; ca.k = c->top_k; ca.residual = c->residual;
   ca.dtype = c->dtype; ca.G = c->n_groups; ca.E = c->n_experts; ca.S = static_cast<int>(r.L.S);
@@ -204,7 +214,8 @@ moe::CombineArgs combine_args(const Run& r, const void* x, void* y, float* aux,
 }
 
 int empty_call(const moe_cfg* c, const moe_meta* m, float* aux, hipStream_t s, void* const* ev) {
-  moe::EmptyArgs ea{m->count, m->offset, m->stats, aux, m->z_loss, c->n_groups, c->n_experts};
+  moe::EmptyArgs ea{m->count, m->offset, m->stats, aux, m->z_loss, m->dev_loss,
+                    c->n_groups, c->n_experts};
   for (int i = 0; i < MOE_N_EVENTS - 1; ++i) record(ev, i, s);
   const int rc = status_of(moe::launch_empty(ea, s));
   record(ev, MOE_N_EVENTS - 1, s);

@@ -11,7 +11,9 @@
 // aux = (1/G) sum_g E/(k S) sum_e m_{g,e} c_{g,e},  m_{g,e} = P_{g,e} / S, from the per-
 // (group, expert) sums of probabilities P and selections c, and the router z-loss of
 // [MegaBlocks] section 2, (1/N) sum_n logsumexp(logits_n)^2, from the router blocks' partial
-// sums; both in fp64 with fixed-order reductions (deterministic).
+// sums, and the device-level balance loss of [Lec16] "DeepSeek MoE 的负载均衡" (the
+// expert-level terms grouped by the D expert groups: mean f times summed P per group); all
+// in fp64 with fixed-order reductions (deterministic).
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -21,17 +23,32 @@ namespace {
 constexpr int kTok = 16;  // tokens per block
 
 __device__ void aux_final(const CombineArgs& a) {
-  __shared__ double red[8];
+  __shared__ double red[12];
   const int t = threadIdx.x;
-  double s = 0.0, z = 0.0;
+  double s = 0.0, z = 0.0, dv = 0.0;
   const int n = a.G * a.E;
   for (int i = t; i < n; i += 256) s += a.Pg[i] * static_cast<double>(a.Cg[i]);
   for (int i = t; i < a.nblocks; i += 256) z += a.zpart[i];
+  // device-level loss: per (token group, expert group) the selections and probability sums
+  // of the group's experts
+  const int gs = a.E / a.n_eg;
+  for (int i = t; i < a.G * a.n_eg; i += 256) {
+    const int64_t base = static_cast<int64_t>(i) * gs;  // (g, d) -> experts [d gs, +gs) of g
+    double P = 0.0;
+    int64_t C = 0;
+    for (int x = 0; x < gs; ++x) {
+      P += a.Pg[base + x];
+      C += a.Cg[base + x];
+    }
+    dv += static_cast<double>(C) * P;
+  }
   s = wave_sum(s);
   z = wave_sum(z);
+  dv = wave_sum(dv);
   if ((t & 63) == 0) {
     red[t >> 6] = s;
     red[4 + (t >> 6)] = z;
+    red[8 + (t >> 6)] = dv;
   }
   __syncthreads();
   if (t == 0) {
@@ -42,6 +59,11 @@ __device__ void aux_final(const CombineArgs& a) {
     if (a.z_loss) {
       const double zt = ((red[4] + red[5]) + red[6]) + red[7];
       *a.z_loss = static_cast<float>(zt / static_cast<double>(a.N));
+    }
+    if (a.dev_loss) {  // (1/G) sum_g sum_j (D / (k S)) C_gj (P_gj / S)
+      const double dt = ((red[8] + red[9]) + red[10]) + red[11];
+      *a.dev_loss = static_cast<float>(static_cast<double>(a.n_eg) * dt /
+                                       (static_cast<double>(a.G) * a.k * S * S));
     }
   }
 }

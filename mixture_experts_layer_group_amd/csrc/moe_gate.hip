@@ -111,6 +111,7 @@ __global__ void empty_kernel(EmptyArgs a) {
   if (t == 0) {
     *a.aux = 0.f;
     if (a.z_loss) *a.z_loss = 0.f;
+    if (a.dev_loss) *a.dev_loss = 0.f;
   }
 }
 

@@ -10,6 +10,7 @@ namespace moe {
 constexpr int kRouteTokens = 64;  // tokens per router / dispatch block (one wave of lanes)
 constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 8;
+constexpr int kMaxExpertGroups = 32;  // group-limited routing: one bit per group in a lane
 
 // Router GEMM + softmax + top-k + gates + random routing + per-block histograms.
 // Blocks never straddle a group: block b covers tokens [g*S + bi*64, min(+64, (g+1)*S)),
@@ -29,6 +30,7 @@ struct RouterArgs {
   int32_t* ahist;         // [G][k][E][nbg] active slots per rank
   double* zpart;          // [G * nbg] sum over the block's tokens of logsumexp(logits)^2
   float norm_p;           // P of the p-norm gate normalisation (norm == 2)
+  int n_eg, topk_eg;      // expert groups and groups kept per token (n_eg == 1: no limit)
   int N, G, S, M, E, k, norm, rr, nbg, dtype;
 };
 
@@ -115,12 +117,15 @@ struct CombineArgs {
   float* aux;             // scalar
   const double* zpart;    // [nblocks] router-block partial sums of logsumexp^2
   float* z_loss;          // scalar or nullptr (not requested)
+  float* dev_loss;        // scalar or nullptr (not requested)
   int nblocks;
+  int n_eg;               // expert groups of the device-level loss
   int N, M, k, residual, dtype, G, E, S;
 };
 
 struct EmptyArgs {         // N == 0: zero the small outputs
-  int32_t* count; int32_t* offset; int32_t* stats; float* aux; float* z_loss; int G, E;
+  int32_t* count; int32_t* offset; int32_t* stats; float* aux; float* z_loss; float* dev_loss;
+  int G, E;
 };
 
 int gemm_block_m(int dtype);                           // BM of the expert GEMM tiles

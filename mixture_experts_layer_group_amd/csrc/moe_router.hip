@@ -303,9 +303,52 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
 #pragma unroll
   for (int off = 1; off < L; off <<= 1) se += __shfl_xor(se, off, 64);
 
+  // Group-limited routing ([Lec16] "DeepSeek V3 MoE (670B)"): the E experts form n_eg
+  // contiguous groups; a group scores its best logit, and the topk_eg best groups (ties to
+  // the lower index) stay open.  Lane q scores groups q and q + L.
+  uint32_t taken = 0;  // bit i <-> expert q + L i already selected (E <= 256 -> i < 16)
+  if (a.n_eg > 1) {
+    const int D = a.n_eg, gs = E / D;
+    float gv[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int d = q + h * L;
+      float v = -INFINITY;
+      if (d < D)
+        for (int i = 0; i < gs; ++i) {
+          const float x = row[d * gs + i];
+          v = x != x ? v : fmaxf(v, x);  // NaN never scores
+        }
+      gv[h] = v;
+    }
+    uint32_t open = 0;
+    for (int r = 0; r < a.topk_eg; ++r) {
+      float bv = -INFINITY;
+      int bd = 0x7fffffff;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int d = q + h * L;
+        if (d < D && !((open >> d) & 1u) && (gv[h] > bv || (gv[h] == bv && d < bd))) {
+          bv = gv[h];
+          bd = d;
+        }
+      }
+#pragma unroll
+      for (int off = 1; off < L; off <<= 1) {
+        const float ov = __shfl_xor(bv, off, 64);
+        const int od = __shfl_xor(bd, off, 64);
+        if (ov > bv || (ov == bv && od < bd)) { bv = ov; bd = od; }
+      }
+      open |= 1u << bd;
+    }
+    // experts of closed groups count as taken, so the top-k below never picks them
+    int i = 0;
+    for (int e = q; e < E; e += L, ++i)
+      if (!((open >> (e / gs)) & 1u)) taken |= 1u << i;
+  }
+
   int sel_e[kMaxTopK];
   float sel_l[kMaxTopK];
-  uint32_t taken = 0;  // bit i <-> expert q + L i already selected (E <= 256 -> i < 16)
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) {
     sel_e[j] = 0;

@@ -49,6 +49,7 @@ def run_gpu(cfg, dev, workspace=None):
     out["y"] = y.float().cpu().numpy()
     out["aux"] = float(aux.cpu().numpy()[0])
     out["z_loss"] = float(out["z_loss"][0])
+    out["dev_loss"] = float(out["dev_loss"][0])
     return out
 
 
@@ -78,12 +79,14 @@ def check_routing(cfg, g, ref):
         assert rel <= AUX_TOL, f"aux {g['aux']} vs {ref['aux']} (rel {rel})"
     else:
         assert g["aux"] == 0.0
-    if "z_loss" in g:
-        if ref["z_loss"] != 0:
-            rel = abs(g["z_loss"] - ref["z_loss"]) / abs(ref["z_loss"])
-            assert rel <= AUX_TOL, f"z_loss {g['z_loss']} vs {ref['z_loss']} (rel {rel})"
+    for f in ("z_loss", "dev_loss"):
+        if f not in g:
+            continue
+        if ref[f] != 0:
+            rel = abs(g[f] - ref[f]) / abs(ref[f])
+            assert rel <= AUX_TOL, f"{f} {g[f]} vs {ref[f]} (rel {rel})"
         else:
-            assert g["z_loss"] == 0.0
+            assert g[f] == 0.0
 
 
 def rel_err(a, ref):
@@ -134,7 +137,8 @@ def full_check(cfg, n_sample=None, seed=None, inp=None):
     if cfg["residual"] and cfg["n_shared"] == 0 and dropped.size:
         assert (g["y"][dropped] == inp.x[dropped]).all(), "dropped tokens must pass x through"
     rep = dict(name=name, logits_err=lerr, y_err=yerr, aux=g["aux"], aux_ref=ref["aux"],
-               z_loss=g["z_loss"], z_loss_ref=ref["z_loss"],
+               z_loss=g["z_loss"], z_loss_ref=ref["z_loss"], dev_loss=g["dev_loss"],
+               dev_loss_ref=ref["dev_loss"],
                stats=g["stats"].tolist(), sampled=len(toks), rr_margin=margin)
     say(f"[gpu] {name}: ok {rep}")
     return rep, g, ref, inp, dev

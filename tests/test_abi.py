@@ -69,6 +69,12 @@ BAD = [
     (dict(gate_norm=2, norm_p=-1.0), binding.MOE_EINVAL),
     (dict(gate_norm=2, norm_p=float("nan")), binding.MOE_EINVAL),
     (dict(gate_norm=2, norm_p=float("inf")), binding.MOE_EINVAL),
+    (dict(expert_groups=0), binding.MOE_EINVAL),
+    (dict(expert_groups=3), binding.MOE_EINVAL),                    # E = 8 % 3 != 0
+    (dict(expert_groups=4, topk_groups=5), binding.MOE_EINVAL),
+    (dict(expert_groups=4, topk_groups=0), binding.MOE_EINVAL),
+    (dict(expert_groups=8, topk_groups=1), binding.MOE_EINVAL),     # k = 2 > 1 * 8/8
+    (dict(n_experts=128, expert_groups=64, topk_groups=2), binding.MOE_EUNSUPPORTED),
     (dict(random_routing=1, top_k=1), binding.MOE_EINVAL),
     (dict(residual=2), binding.MOE_EINVAL),
     (dict(dtype=5), binding.MOE_EINVAL),
@@ -130,6 +136,7 @@ INVALID_CALLS = [
     ("misaligned bg", dict(bg=FakeTensor(0x28000002)), binding.MOE_EINVAL),
     ("misaligned meta.row", dict(meta=_fake_meta(bad="row")), binding.MOE_EINVAL),
     ("misaligned meta.z_loss", dict(meta=_fake_meta(bad="z_loss")), binding.MOE_EINVAL),
+    ("misaligned meta.dev_loss", dict(meta=_fake_meta(bad="dev_loss")), binding.MOE_EINVAL),
     ("null meta.logits", dict(meta=binding.Meta(**{f: FakeTensor(0x10000000 + 0x1000 * i)
                                                    for i, f in enumerate(binding.Meta.FIELDS)
                                                    if f != "logits"})), binding.MOE_EINVAL),

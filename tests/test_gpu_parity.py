@@ -34,7 +34,7 @@ def test_small_layer_parity(name):
 
 SAMPLES = {"tiny_fp32": None, "gshard_bf16": 2048, "switch_bf16": 2048,
            "large_expert_bf16": 512, "shared_routed_bf16": 1024,
-           "shared_routed_swiglu_bf16": 1024}
+           "shared_routed_swiglu_bf16": 1024, "fine_grained_grouped_bf16": 1024}
 
 
 @pytest.mark.parametrize("name", list(configs.WORKLOADS))
@@ -48,7 +48,8 @@ def test_route_from_oracle_logits():
     """Reverse direction: moe_route fed the oracle's own logits (rounded to fp32)."""
     h = harness()
     from oracle import moe_oracle as mo
-    for name in ("small_top2_rr", "small_shared_top3", "small_pnorm_top4", "gshard_bf16"):
+    for name in ("small_top2_rr", "small_shared_top3", "small_pnorm_top4", "small_grouped_top4",
+                 "gshard_bf16"):
         cfg = configs.ALL[name]
         h.say(f"[gpu] moe_route {name}")
         inp = synth.make_inputs(cfg)
@@ -63,6 +64,7 @@ def test_route_from_oracle_logits():
         g = meta.to_numpy()
         g["aux"] = float(aux[0].cpu())
         g["z_loss"] = float(g["z_loss"][0])
+        g["dev_loss"] = float(g["dev_loss"][0])
         h.check_routing(cfg, g, ref)
 
 
@@ -81,7 +83,8 @@ def test_deterministic_and_padding_never_read():
     for o in outs[1:]:
         for f in ("y", "logits", "topk_idx", "topk_w", "pos", "row", "count", "offset", "stats"):
             assert np.array_equal(o[f], outs[0][f], equal_nan=False), f
-        assert o["aux"] == outs[0]["aux"] and o["z_loss"] == outs[0]["z_loss"]
+        for f in ("aux", "z_loss", "dev_loss"):
+            assert o[f] == outs[0][f], f
     assert np.isfinite(outs[0]["y"]).all()
 
 
@@ -106,6 +109,13 @@ EDGE = {
     "one_token": _cfg(n_tokens=1, capacity=1),
     "pnorm_p8_top8": _cfg(n_experts=32, top_k=8, capacity=64, gate_norm=2, norm_p=8.0,
                           n_groups=2),
+    "grouped_fp32": _cfg(dtype=0, n_tokens=330, n_experts=12, top_k=3, capacity=60,
+                         d_model=64, d_ff=128, expert_groups=4, topk_groups=2, n_groups=3),
+    "grouped_32_groups_top8": _cfg(n_tokens=640, n_experts=256, top_k=8, capacity=24,
+                                   d_model=256, d_ff=256, expert_groups=32, topk_groups=4,
+                                   zipf_s=0.5),
+    "grouped_one_group": _cfg(n_experts=16, top_k=4, capacity=100, expert_groups=4,
+                              topk_groups=1, act=2),
 }
 
 
@@ -134,6 +144,7 @@ def test_empty_batch():
     meta.offset.fill_(7)
     meta.stats.fill_(7)
     meta.z_loss.fill_(7)
+    meta.dev_loss.fill_(7)
     ws = binding.alloc_workspace(cfg)
     aux = torch.full((4,), 5.0, device="cuda")
     empty = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
@@ -141,7 +152,7 @@ def test_empty_batch():
     torch.cuda.synchronize()
     assert int(meta.count.abs().sum()) == 0 and int(meta.offset.abs().sum()) == 0
     assert int(meta.stats.abs().sum()) == 0 and float(aux[0]) == 0.0
-    assert float(meta.z_loss[0]) == 0.0
+    assert float(meta.z_loss[0]) == 0.0 and float(meta.dev_loss[0]) == 0.0
 
 
 @pytest.mark.parametrize("act", [1, 2], ids=["gelu", "swiglu"])
