@@ -30,17 +30,19 @@ __device__ void aux_final(const CombineArgs& a) {
   for (int i = t; i < n; i += 256) s += a.Pg[i] * static_cast<double>(a.Cg[i]);
   for (int i = t; i < a.nblocks; i += 256) z += a.zpart[i];
   // device-level loss: per (token group, expert group) the selections and probability sums
-  // of the group's experts
-  const int gs = a.E / a.n_eg;
-  for (int i = t; i < a.G * a.n_eg; i += 256) {
-    const int64_t base = static_cast<int64_t>(i) * gs;  // (g, d) -> experts [d gs, +gs) of g
+  // of the group's experts, one wave per pair, its lanes over the experts
+  const int gs = a.E / a.n_eg, lane = t & 63;
+  for (int pr = t >> 6; pr < a.G * a.n_eg; pr += 4) {
+    const int64_t base = static_cast<int64_t>(pr) * gs;  // (g, d) -> experts [d gs, +gs) of g
     double P = 0.0;
-    int64_t C = 0;
-    for (int x = 0; x < gs; ++x) {
+    int C = 0;
+    for (int x = lane; x < gs; x += 64) {
       P += a.Pg[base + x];
       C += a.Cg[base + x];
     }
-    dv += static_cast<double>(C) * P;
+    P = wave_sum(P);
+    C = wave_sum(C);
+    if (lane == 0) dv += static_cast<double>(C) * P;
   }
   s = wave_sum(s);
   z = wave_sum(z);

@@ -29,14 +29,31 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
 }
 
-// Exact GELU, 0.5 z (1 + erf(z / sqrt 2)), with the device library's erff.
-__device__ __forceinline__ float gelu_erf(float z) {
-  return 0.5f * z * (1.0f + erff(z * 0.70710678118654752440f));
+// erf(x) by Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26:
+// erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2), t = 1 / (1 + p x),
+// x >= 0, odd extension; |error| <= 1.5e-7.  One reciprocal and one exponential (hardware
+// v_rcp_f32 / v_exp_f32) instead of a general-purpose erf in the GEMM epilogues.
+__device__ __forceinline__ float erf_as7126(float x) {
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
+  float p = fmaf(1.061405429f, t, -1.453152027f);
+  p = fmaf(p, t, 1.421413741f);
+  p = fmaf(p, t, -0.284496736f);
+  p = fmaf(p, t, 0.254829592f);
+  const float y = fmaf(-p * t, __expf(-ax * ax), 1.0f);
+  return copysignf(y, x);
 }
 
-// Swish with beta = 1: z * sigmoid(z) = z / (1 + exp(-z)), with the device library's expf
-// (exp(-z) = inf for very negative z gives -0).
-__device__ __forceinline__ float swish(float z) { return z / (1.0f + expf(-z)); }
+// GELU in its erf form, 0.5 z (1 + erf(z / sqrt 2)).
+__device__ __forceinline__ float gelu_erf(float z) {
+  return 0.5f * z * (1.0f + erf_as7126(z * 0.70710678118654752440f));
+}
+
+// Swish with beta = 1: z * sigmoid(z) = z / (1 + exp(-z)) (exp(-z) = inf for very negative z
+// gives -0).
+__device__ __forceinline__ float swish(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 __device__ __forceinline__ float apply_act(float z, int act) {
   if (act == 0) return fmaxf(z, 0.0f);

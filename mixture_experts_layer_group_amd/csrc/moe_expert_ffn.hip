@@ -30,6 +30,15 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
+// K depth of one LDS stage of the bf16 GEMM and the number of stages.  64 x 2 (one 128-byte
+// line per operand row per chunk) measured fastest; 32 x 4 and 32 x 5 keep more chunks in
+// flight but split every line over two requests and were 7-8% slower.
+#ifndef MOE_GEMM_BK
+#define MOE_GEMM_BK 64
+#define MOE_GEMM_STAGES 2
+#endif
+constexpr int kGemmBK = MOE_GEMM_BK;
+constexpr int kGemmStages = MOE_GEMM_STAGES;
 
 struct Job {
   const char* A;   // first row of the tile (bytes)
@@ -130,12 +139,19 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
                                            0x00020000);
 }
 
-// XOR pattern of the 16-byte columns of LDS row r (128-byte rows).  Among any 8 aligned
-// consecutive rows it takes 8 distinct values, and among any 16 aligned consecutive rows the
-// rows of equal parity take 8 distinct values, so a ds_read_b128 of one column from 16
-// consecutive rows touches every bank once whether the LDS serves 8 lanes per cycle from
-// 32 banks or 16 lanes from 64 banks.
-__device__ __forceinline__ int lds_swz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+// XOR pattern of the 16-byte columns of LDS row r, for rows of ROW bytes.  The LDS serves
+// a ds_read_b128 16 lanes at a time from 64 banks; the fragment reads take one column from
+// 16 consecutive rows, which must then cover every bank once.
+//  * 128-byte rows (8 columns): rows r and r + 2 share banks; ((r >> 1) & 7) ^ ((r & 1) << 2)
+//    gives the 8 row pairs 8 distinct columns, the two rows of a pair differing in bit 2;
+//  * 64-byte rows (4 columns): rows r and r + 4 share banks; (r >> 2) & 3 gives the 4 rows
+//    of each bank class 4 distinct columns.
+template <int ROW>
+__device__ __forceinline__ int lds_swz(int r) {
+  static_assert(ROW == 128 || ROW == 64, "LDS row size");
+  if (ROW == 128) return ((r >> 1) & 7) ^ ((r & 1) << 2);
+  return (r >> 2) & 3;
+}
 
 template <int ACT>
 __device__ __forceinline__ float act_fn(float z) {
@@ -163,23 +179,25 @@ __device__ __forceinline__ void dma16(rsrc_t r, unsigned char* lds, uint32_t vof
 //  * 2 x WN waves; wave (wm, wn) owns rows [wm BM/2, +BM/2) and columns [wn BN/WN, +BN/WN) as
 //    v_mfma_f32_32x32x16_bf16 tiles (the weight fragment is the first operand, so a lane holds
 //    one token row and runs of 4 features);
-//  * K advances in chunks of 64 through two LDS stages of 128-byte rows.  Operands go from
-//    global memory straight into LDS (buffer_load ... lds, 16 bytes per lane), chunk k+1
-//    landing while chunk k is multiplied; full 128-byte lines per row keep the L2 requests
-//    whole.  Lane i of a load instruction writes LDS unit i, so the XOR column swizzle is
-//    applied on the global side: LDS unit (row r, column p) receives global column
-//    p ^ lds_swz(r);
+//  * K advances in chunks of BK through NST LDS stages of BK*2-byte rows.  Operands go from
+//    global memory straight into LDS (buffer_load ... lds, 16 bytes per lane), NST - 1 chunks
+//    in flight ahead of the one being multiplied (the loads take longer than one chunk of
+//    MFMA work under full load).  Lane i of a load instruction writes LDS unit i, so the XOR
+//    column swizzle is applied on the global side: LDS unit (row r, column p) receives
+//    global column p ^ lds_swz(r);
 //  * a barrier without a global-memory fence separates the stages, so the loads in flight are
-//    never drained by it;
+//    never drained by it; each wave waits (vmcnt) only for its own part of the chunk it is
+//    about to read;
 //  * the epilogue applies the activation, packs bf16 and stages the tile in LDS (16-byte
 //    columns XOR (row % columns)), then writes whole rows, 16 bytes per lane;
 //  * gated (ACT == kActSwiglu): LDS B rows [64 s, 64 s + 32) hold the gate rows of output
 //    columns [32 s, 32 s + 32) and rows [64 s + 32, 64 s + 64) their up rows, so wave wn's two
 //    32-column MFMA blocks are the gate and up halves of the same 32 outputs, held by the
 //    same lanes in the same registers; the tile writes BN / 2 columns.
-template <int BM, int BN, int WN, int ACT>
+template <int BM, int BN, int WN, int ACT, int BK, int NST>
 __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
-  constexpr int BK = 64, ROW = 128, NST = 2;
+  constexpr int ROW = BK * 2, CPR = ROW / 16;  // bytes and 16-byte columns per LDS row
+  static_assert(NST >= 2 && NST <= 5 && BK * (NST - 1) <= 128, "K % 128 == 0 covers the prologue");
   constexpr int NT = 128 * WN, NW = 2 * WN;
   constexpr int STAGE = (BM + BN) * ROW;
   constexpr int WTM = BM / 2, WTN = BN / WN;
@@ -191,7 +209,7 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
 
   constexpr bool GLU = ACT == kActSwiglu;
   constexpr int OUTN = GLU ? BN / 2 : BN;    // output columns of the tile
-  static_assert(!GLU || WN * 64 == BN, "gated tiles: every wave holds one gate/up block pair");
+  static_assert(!GLU || (BN / WN) % 64 == 0, "gated tiles: every wave holds gate/up block pairs");
   Job j;
   if (!decode_tile<BM, OUTN, 2>(g, j)) return;
   const int t = threadIdx.x, lane = t & 63;
@@ -206,16 +224,16 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
                                           static_cast<int64_t>(j.ncols) * j.ldb);
 
   // Load slot q of this wave fills LDS units [(w + NW q) 64, +64) of its operand: unit u is
-  // row u / 8, physical column u % 8.
+  // row u / CPR, physical column u % CPR.
   uint32_t aoff[AQ], boff[BQ];
 #pragma unroll
   for (int q = 0; q < AQ; ++q) {
-    const int u = (w + NW * q) * 64 + lane, r = u >> 3, c = (u & 7) ^ lds_swz(r);
+    const int u = (w + NW * q) * 64 + lane, r = u / CPR, c = (u % CPR) ^ lds_swz<ROW>(r);
     aoff[q] = r * lda + c * 16;
   }
 #pragma unroll
   for (int q = 0; q < BQ; ++q) {
-    const int u = (w + NW * q) * 64 + lane, r = u >> 3, c = (u & 7) ^ lds_swz(r);
+    const int u = (w + NW * q) * 64 + lane, r = u / CPR, c = (u % CPR) ^ lds_swz<ROW>(r);
     if (GLU)   // LDS row r: output column 32 (r / 64) + r % 32, gate or up half by bit 5
       boff[q] = ((r >> 6) * 32 + (r & 31)) * ldb + ((r >> 5) & 1) * static_cast<uint32_t>(j.upb) +
                 c * 16;
@@ -251,7 +269,7 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
 
   const int arow = wm * WTM + (lane & 31);
   const int brow = wn * WTN + (lane & 31);
-  const int sw = lds_swz(lane & 31);
+  const int sw = lds_swz<ROW>(lane & 31);  // the fragment rows are congruent to lane & 31 mod 16
   auto compute = [&](int st) {
     const unsigned char* As = smem + st * STAGE;
     const unsigned char* Bs = As + BM * ROW;
@@ -274,17 +292,35 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
     }
   };
 
-  const int KT = j.K / BK;
-  issue(0, 0);
-  for (int kt = 0; kt + 1 < KT; ++kt) {
-    MOE_WAIT_VMCNT(0);   // this wave's part of chunk kt is in LDS
-    lds_barrier();       // ... and every wave's; stage (kt+1)&1 is no longer being read
-    issue(kt + 1, (kt + 1) & 1);
-    compute(kt & 1);
+  // Chunk kt lives in stage kt % NST.  Before multiplying chunk kt a wave lets the chunks
+  // issued after it stay in flight (Q vector-memory operations each), then the barrier
+  // makes every wave's part visible and frees the stage that chunk kt + NST - 1 refills.
+  constexpr int Q = AQ + BQ;
+  auto wait_chunk = [&](int ahead) {
+    if (NST > 4 && ahead >= 3) MOE_WAIT_VMCNT(3 * Q);
+    else if (NST > 3 && ahead >= 2) MOE_WAIT_VMCNT(2 * Q);
+    else if (NST > 2 && ahead >= 1) MOE_WAIT_VMCNT(Q);
+    else MOE_WAIT_VMCNT(0);
+  };
+  const int KT = j.K / BK;  // >= NST - 1
+#pragma unroll
+  for (int p = 0; p < NST - 1; ++p) issue(p, p);
+  int st = 0;
+  for (int kt = 0; kt + NST - 1 < KT; ++kt) {
+    wait_chunk(NST - 2);
+    lds_barrier();
+    const int sf = st == 0 ? NST - 1 : st - 1;  // (kt + NST - 1) % NST
+    issue(kt + NST - 1, sf);
+    compute(st);
+    st = st == NST - 1 ? 0 : st + 1;
   }
-  MOE_WAIT_VMCNT(0);
-  lds_barrier();
-  compute((KT - 1) & 1);
+#pragma unroll
+  for (int i = 0; i < NST - 1; ++i) {  // the last NST - 1 chunks: nothing left to issue
+    wait_chunk(NST - 2 - i);
+    lds_barrier();
+    compute(st);
+    st = st == NST - 1 ? 0 : st + 1;
+  }
 
   // Epilogue through LDS: D[feature][token] -> tile[token][feature] bf16 (rows of OUTN*2
   // bytes, NCH 16-byte columns XOR (row % NCH)), then whole rows to global memory.
@@ -400,8 +436,9 @@ hipError_t launch_expert_gemm(const GemmArgs& a, hipStream_t s) {
   const int grid = grid_of(a, gemm_block_n(a.dtype, act));
   if (grid == 0) return hipSuccess;
   if (a.dtype == 1) {
-#define MOE_GEMM_LAUNCH(ACTV) \
-  hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 4, ACTV>), dim3(grid), dim3(512), 0, s, a)
+#define MOE_GEMM_LAUNCH(ACTV)                                                              \
+  hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 4, ACTV, kGemmBK, kGemmStages>), dim3(grid), \
+                     dim3(512), 0, s, a)
     if (act == kActRelu) MOE_GEMM_LAUNCH(kActRelu);
     else if (act == kActGelu) MOE_GEMM_LAUNCH(kActGelu);
     else if (act == kActSwiglu) MOE_GEMM_LAUNCH(kActSwiglu);
