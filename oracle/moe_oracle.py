@@ -287,15 +287,16 @@ def dev_loss(p, idx, n_groups, n_experts, n_expert_groups):
     return total / G
 
 
-def route(cfg, logits32, u=None):
+def route(cfg, logits32, u=None, exact=False):
     """Routing, positions, dispatch rows and aux from given fp32 logits (no FFN).
 
     Mirrors the C ABI's ``moe_route``: the same steps the layer runs after the router
-    GEMM.  ``logits32`` is treated as exact fp32 values.
+    GEMM.  ``logits32`` is treated as exact fp32 values; with ``exact=True`` float64 logits
+    are used as given (no rounding), for finite-difference checks of the backward pass.
     """
     N, E, k = cfg["n_tokens"], cfg["n_experts"], cfg["top_k"]
     G, C = cfg["n_groups"], cfg["capacity"]
-    l32 = np.asarray(logits32, dtype=np.float32).reshape(N, E)
+    l32 = np.asarray(logits32, dtype=np.float64 if exact else np.float32).reshape(N, E)
     if N == 0:
         z = np.zeros((0, k), dtype=np.int32)
         return dict(topk_idx=z, active=z.astype(bool), pos=z, row=z,

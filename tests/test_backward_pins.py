@@ -1,0 +1,204 @@
+"""Pins of the backward-pass oracle (oracle/moe_backward.py): central finite differences of
+the forward oracle's loss, L = <dy, y> + a_aux aux + a_z z_loss + a_dev dev_loss, with
+float64 routing, on small layers that exercise every flag; and planted mistakes.
+
+Routing decisions are piecewise constant; each perturbed evaluation checks that the routing
+(selection, random-routing activity, capacity positions) did not change, so the finite
+difference sees only the smooth part.
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+from oracle import moe_backward as mb
+from oracle import moe_oracle as mo
+
+
+def cfg_of(**kw):
+    base = dict(n_tokens=8, n_groups=1, d_model=5, d_ff=4, n_experts=4, n_shared=0,
+                top_k=2, capacity=8, act=0, gate_norm=1, random_routing=0, residual=1,
+                dtype=0, norm_p=1.0, expert_groups=1, topk_groups=1)
+    base.update(kw)
+    return base
+
+
+CASES = {
+    "relu_sum_groups_drops": cfg_of(n_groups=2, capacity=2, act=0),
+    "gelu_none_shared_top1": cfg_of(top_k=1, gate_norm=0, act=1, n_shared=1, capacity=3),
+    "swiglu_pnorm2_expert_groups": cfg_of(act=2, gate_norm=2, norm_p=2.0, expert_groups=2,
+                                          topk_groups=1, capacity=5),
+    "gelu_random_routing_bare": cfg_of(act=1, random_routing=1, residual=0, capacity=4),
+    "swiglu_pnorm_half_shared": cfg_of(act=2, gate_norm=2, norm_p=0.5, n_shared=2,
+                                       n_tokens=6, n_groups=2, capacity=3),
+}
+COEFS = dict(coef_aux=0.7, coef_z=0.3, coef_dev=0.45)
+
+
+def make(cfg, seed):
+    rng = np.random.default_rng(seed)
+    N, M, H, E, Es = (cfg[f] for f in ("n_tokens", "d_model", "d_ff", "n_experts", "n_shared"))
+    H1 = 2 * H if cfg["act"] == 2 else H
+    return dict(x=rng.standard_normal((N, M)), Wg=rng.standard_normal((E, M)),
+                bg=0.5 * rng.standard_normal(E), W1=0.7 * rng.standard_normal((E + Es, H1, M)),
+                W2=0.7 * rng.standard_normal((E + Es, M, H)), u=rng.random(N).astype(np.float32),
+                dy=rng.standard_normal((N, M)))
+
+
+def same_routing(a, b):
+    return all(np.array_equal(a[f], b[f]) for f in ("topk_idx", "active", "pos"))
+
+
+def finite_differences(cfg, t, coefs, eps=1e-6):
+    """Central differences of L for every entry of x, Wg, bg, W1, W2."""
+    def L(tt):
+        return mb.loss(cfg, tt["x"], tt["Wg"], tt["bg"], tt["W1"], tt["W2"], tt["u"], tt["dy"],
+                       **coefs)
+    _, r0 = L(t)
+    grads, skipped = {}, 0
+    for name in ("x", "Wg", "bg", "W1", "W2"):
+        g = np.zeros_like(t[name])
+        for i in np.ndindex(t[name].shape):
+            vals = []
+            for sgn in (1.0, -1.0):
+                tt = dict(t)
+                arr = t[name].copy()
+                arr[i] += sgn * eps
+                tt[name] = arr
+                v, r = L(tt)
+                if not same_routing(r, r0):
+                    vals = None
+                    break
+                vals.append(v)
+            if vals is None:
+                skipped += 1
+                g[i] = np.nan
+            else:
+                g[i] = (vals[0] - vals[1]) / (2 * eps)
+        grads[name] = g
+    return grads, skipped
+
+
+def check_against_fd(back, cfg, t, coefs):
+    fd, skipped = finite_differences(cfg, t, coefs)
+    total = sum(v.size for v in fd.values())
+    assert skipped <= 0.02 * total, f"{skipped} of {total} entries changed the routing"
+    for name, key in (("x", "dx"), ("Wg", "dWg"), ("bg", "dbg"), ("W1", "dW1"), ("W2", "dW2")):
+        a, f = back[key], fd[name]
+        ok = ~np.isnan(f)
+        scale = max(1.0, np.abs(f[ok]).max())
+        err = np.abs(a[ok] - f[ok]).max() / scale
+        assert err < 2e-6, f"{name}: analytic vs finite difference rel err {err}"
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_backward_matches_finite_differences(name):
+    cfg = CASES[name]
+    t = make(cfg, seed=zlib.crc32(name.encode()) % 1000)
+    back = mb.layer_backward(cfg, t["x"], t["Wg"], t["bg"], t["W1"], t["W2"], t["u"], t["dy"],
+                             exact=True, **COEFS)
+    r = back["routing"]
+    assert r["stats"][1] > 0 or name not in ("relu_sum_groups_drops",), "the case should drop"
+    check_against_fd(back, cfg, t, COEFS)
+
+
+def test_backward_is_linear_in_dy_and_coefficients():
+    """The gradient is linear in (dy, a_aux, a_z, a_dev): g(2 dy, 2a) = 2 g(dy, a) and the
+    sum of the dy-only and coefficient-only gradients is the full one."""
+    cfg = CASES["swiglu_pnorm2_expert_groups"]
+    t = make(cfg, 5)
+    args = (cfg, t["x"], t["Wg"], t["bg"], t["W1"], t["W2"], t["u"])
+    full = mb.layer_backward(*args, t["dy"], exact=True, **COEFS)
+    only_dy = mb.layer_backward(*args, t["dy"], exact=True)
+    only_c = mb.layer_backward(*args, np.zeros_like(t["dy"]), exact=True, **COEFS)
+    double = mb.layer_backward(*args, 2 * t["dy"], exact=True,
+                               **{k: 2 * v for k, v in COEFS.items()})
+    for key in ("dx", "dWg", "dbg", "dW1", "dW2"):
+        np.testing.assert_allclose(full[key], only_dy[key] + only_c[key], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(double[key], 2 * full[key], rtol=1e-12, atol=1e-12)
+    # with dy = 0 only the router sees gradient; experts get none
+    assert np.abs(only_c["dW1"]).max() == 0 and np.abs(only_c["dW2"]).max() == 0
+
+
+def test_dropped_and_unrouted_experts_get_no_gradient():
+    """A token whose slots are all dropped contributes dy only through the residual (and the
+    router's balance terms); an expert that received no row gets dW = 0."""
+    cfg = cfg_of(capacity=1, n_experts=4, top_k=1, gate_norm=0)
+    t = make(cfg, 9)
+    t["Wg"][:] = 0.0
+    t["Wg"][0, 0] = 5.0                      # every token prefers expert 0 (x[:, 0] > 0)
+    t["x"][:, 0] = np.abs(t["x"][:, 0]) + 1.0
+    t["bg"][:] = 0.0
+    back = mb.layer_backward(cfg, t["x"], t["Wg"], t["bg"], t["W1"], t["W2"], t["u"], t["dy"],
+                             exact=True)
+    r = back["routing"]
+    assert r["count"].tolist() == [[1, 0, 0, 0]]
+    assert np.abs(back["dW1"][1:]).max() == 0 and np.abs(back["dW2"][1:]).max() == 0
+    assert np.abs(back["dw"][1:]).max() == 0
+    check_against_fd(back, cfg, t, {})
+
+
+# ----------------------------------------------------------------------------- planted mistakes
+
+_ORIG = {n: getattr(mb, n) for n in ("gate_weight_grad", "z_loss_grad", "balance_grad")}
+
+def _softmax_no_centering(p, dp):
+    return p * dp
+
+
+def _gate_grad_no_second_term(p, idx, gate_norm, norm_p, dw):
+    """Keeps only dw_i / D of the normalisation's derivative."""
+    if gate_norm == 0:
+        return _ORIG["gate_weight_grad"](p, idx, 0, norm_p, dw)
+    ps = np.take_along_axis(p, idx.astype(np.int64), axis=1)
+    P = 1.0 if gate_norm == 1 else norm_p
+    D = (ps ** P).sum(axis=1, keepdims=True) ** (1.0 / P)
+    return _ORIG["gate_weight_grad"](p, idx, 0, norm_p, dw / D)
+
+
+def _gelu_grad_no_density(z, act):
+    z = np.asarray(z, np.float64)
+    if act == 0:
+        return (z > 0).astype(np.float64)
+    from scipy.special import ndtr
+    return ndtr(z)
+
+
+def _swish_grad_is_sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-np.asarray(z, np.float64)))
+
+
+def _z_grad_no_factor_two(l, p, coef_z):
+    return _ORIG["z_loss_grad"](l, p, coef_z) / 2.0
+
+
+def _balance_aux_per_token(cfg, idx, coef_aux, coef_dev):
+    return _ORIG["balance_grad"](cfg, idx, coef_aux, coef_dev) * (cfg["n_tokens"] // cfg["n_groups"])
+
+
+BACK_MUTANTS = {
+    "softmax_no_centering": ("softmax_grad", _softmax_no_centering),
+    "gate_norm_no_second_term": ("gate_weight_grad", _gate_grad_no_second_term),
+    "gelu_grad_no_density": ("act_grad", _gelu_grad_no_density),
+    "swish_grad_is_sigmoid": ("swish_grad", _swish_grad_is_sigmoid),
+    "z_grad_no_factor_two": ("z_loss_grad", _z_grad_no_factor_two),
+    "balance_grad_scaled_by_S": ("balance_grad", _balance_aux_per_token),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BACK_MUTANTS))
+def test_planted_backward_mistakes_are_caught(name, monkeypatch):
+    attr, fn = BACK_MUTANTS[name]
+    monkeypatch.setattr(mb, attr, fn)
+    caught = False
+    for cname in sorted(CASES):
+        cfg = CASES[cname]
+        t = make(cfg, seed=zlib.crc32(cname.encode()) % 1000)
+        back = mb.layer_backward(cfg, t["x"], t["Wg"], t["bg"], t["W1"], t["W2"], t["u"],
+                                 t["dy"], exact=True, **COEFS)
+        try:
+            check_against_fd(back, cfg, t, COEFS)
+        except AssertionError:
+            caught = True
+            break
+    assert caught, f"mutant {name} passed every finite-difference check"
