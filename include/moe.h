@@ -37,8 +37,8 @@ extern "C" {
 #endif
 
 /* 2: gated (SwiGLU) experts; 3: p-norm gates, router z-loss; 4: group-limited routing,
- * device-level balance loss */
-#define MOE_ABI_VERSION 4
+ * device-level balance loss; 5: backward pass */
+#define MOE_ABI_VERSION 5
 
 enum moe_status {
   MOE_OK = 0,
@@ -201,6 +201,45 @@ int moe_forward_timed(const moe_cfg* cfg, const void* x, const void* Wg, const f
                       const void* W1, const void* W2, const float* u, void* y,
                       float* aux_loss, const moe_meta* meta, void* workspace,
                       size_t workspace_bytes, void* stream, void* const* events);
+
+/*
+ * Device workspace (bytes) that moe_backward needs for this cfg (larger than the forward's).
+ * Host only.  Errors: MOE_EINVAL, MOE_EUNSUPPORTED.
+ */
+int moe_backward_workspace_size(const moe_cfg* cfg, size_t* bytes);
+
+/*
+ * Backward pass of the layer: gradients of
+ *   L = sum_n <dy_n, y_n> + coef_aux * aux_loss + coef_z * z_loss + coef_dev * dev_loss
+ * with respect to x, Wg, bg, W1 and W2 (y, aux_loss, z_loss and dev_loss as in moe_forward).
+ * Routing decisions (top-k, group limits, random routing, capacity drops) are constants of
+ * the pass ([MegaBlocks] "3. 负载均衡损失": the balance loss reaches the router only through
+ * the scores); the rest is the chain rule through combine, the expert FFNs ([GShard] "MoE
+ * Transformer"; [Lec16] "DeepSeek V3 MoE (670B)" for the gated form), the gate
+ * normalisation and the softmax.  The routing and the expert activations are recomputed
+ * from the inputs (the results match a moe_forward of the same inputs bit for bit).
+ *   x, Wg, bg, W1, W2, u   as in moe_forward
+ *   dy        [N, M] T      upstream gradient of y
+ *   coef_*    host floats (finite) weighting the three auxiliary losses
+ *   dx        [N, M] T      out
+ *   dWg       [E, M] fp32   out
+ *   dbg       [E] fp32 or NULL: gradient of the router offsets
+ *   dW1, dW2  fp32, the shapes of W1 and W2: out (experts that received no row get zeros)
+ *   meta      as in moe_forward: receives the recomputed routing (logits, topk_idx, topk_w,
+ *             pos, row, count, offset, stats); z_loss / dev_loss are not written
+ *   workspace device scratch of at least moe_backward_workspace_size(cfg) bytes
+ * Precision: the bf16 layer keeps the recomputed pre-activations, activations and every
+ * intermediate gradient in bf16, accumulates in fp32, and writes the weight gradients in
+ * fp32 (each the sum over its rows in one fixed order: bitwise deterministic).
+ * N == 0: the weight gradients are zeroed; meta count/offset/stats are zeroed.
+ * Check order: cfg, workspace (MOE_EINVAL), workspace_bytes (MOE_EWORKSPACE), weight-gradient
+ * pointers and coefficients, then meta and tensor pointers (MOE_EINVAL).
+ */
+int moe_backward(const moe_cfg* cfg, const void* x, const void* Wg, const float* bg,
+                 const void* W1, const void* W2, const float* u, const void* dy, float coef_aux,
+                 float coef_z, float coef_dev, void* dx, float* dWg, float* dbg, float* dW1,
+                 float* dW2, const moe_meta* meta, void* workspace, size_t workspace_bytes,
+                 void* stream);
 
 /*
  * Routing only, from caller-given logits [N, E] fp32: softmax, top-k, gate weights, random

@@ -67,6 +67,12 @@ def load_library(path=LIB_PATH):
     lib.moe_forward.argtypes = fwd
     lib.moe_forward_timed.restype = i32
     lib.moe_forward_timed.argtypes = fwd + [ctypes.POINTER(vp)]
+    lib.moe_backward_workspace_size.restype = i32
+    lib.moe_backward_workspace_size.argtypes = [cfgp, ctypes.POINTER(sz)]
+    f32 = ctypes.c_float
+    lib.moe_backward.restype = i32
+    lib.moe_backward.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, f32, f32, f32, vp, vp, vp, vp,
+                                 vp, metap, vp, sz, vp]
     lib.moe_route.restype = i32
     lib.moe_route.argtypes = [cfgp, vp, vp, metap, vp, vp, sz, vp]
     _lib = lib
@@ -142,6 +148,47 @@ def alloc_meta(cfg, device="cuda"):
                 stats=torch.empty((4,), **i32),
                 z_loss=torch.empty((4,), dtype=torch.float32, device=device),
                 dev_loss=torch.empty((4,), dtype=torch.float32, device=device))
+
+
+def moe_backward_workspace_size(cfg):
+    n = ctypes.c_size_t(0)
+    rc = load_library().moe_backward_workspace_size(ctypes.byref(make_cfg(cfg)), ctypes.byref(n))
+    if rc:
+        raise MoeError(rc, "moe_backward_workspace_size")
+    return n.value
+
+
+def moe_backward(cfg, x, Wg, bg, W1, W2, u, dy, coef_aux, coef_z, coef_dev, dx, dWg, dbg, dW1,
+                 dW2, meta, workspace, stream=None):
+    """C ABI moe_backward on torch tensors (see include/moe.h)."""
+    c = make_cfg(cfg)
+    m = meta.as_struct()
+    rc = load_library().moe_backward(
+        ctypes.byref(c), _ptr(x), _ptr(Wg), _ptr(bg), _ptr(W1), _ptr(W2), _ptr(u), _ptr(dy),
+        float(coef_aux), float(coef_z), float(coef_dev), _ptr(dx), _ptr(dWg), _ptr(dbg),
+        _ptr(dW1), _ptr(dW2), ctypes.byref(m), _ptr(workspace), workspace.numel(),
+        _stream(stream))
+    if rc:
+        raise MoeError(rc, "moe_backward")
+
+
+def backward(cfg, x, Wg, W1, W2, dy, bg=None, u=None, coef_aux=0.0, coef_z=0.0, coef_dev=0.0,
+             workspace=None, meta=None, stream=None):
+    """Allocate the gradients (torch.empty) and run moe_backward.
+    Returns dict(dx, dWg, dbg, dW1, dW2) and the meta."""
+    import torch
+    dev = x.device
+    meta = alloc_meta(cfg, dev) if meta is None else meta
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = dict(dx=torch.empty_like(x), dWg=torch.empty(tuple(Wg.shape), **f32),
+               dbg=torch.empty((cfg["n_experts"],), **f32),
+               dW1=torch.empty(tuple(W1.shape), **f32), dW2=torch.empty(tuple(W2.shape), **f32))
+    if workspace is None:
+        workspace = torch.empty(max(1, moe_backward_workspace_size(cfg)), dtype=torch.uint8,
+                                device=dev)
+    moe_backward(cfg, x, Wg, bg, W1, W2, u, dy, coef_aux, coef_z, coef_dev, out["dx"],
+                 out["dWg"], out["dbg"], out["dW1"], out["dW2"], meta, workspace, stream)
+    return out, meta
 
 
 def alloc_workspace(cfg, device="cuda"):

@@ -10,6 +10,7 @@
 
 #include <algorithm>
 #include <cfloat>
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 
@@ -306,6 +307,328 @@ int forward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* b
   return rc;
 }
 
+// ---------------------------------------------------------------------------- backward
+
+// Workspace of moe_backward: the forward layout (routing buffers, dispatch rows, h, shared h,
+// and the shared-output buffer reused for the shared experts' dx), then the backward's own
+// regions.
+struct BwdLayout {
+  Layout F;
+  size_t z1, o, dout, dh, dz1, dbuf, z1sh, dhsh, dz1sh, w1t, w2t, doT, hT, dz1T, bufT, dyT,
+      xT, hshT, dz1shT, dl, dw, part, src0, cnt, dst0, segblk, width, e2, e1, total;
+  int64_t H1, RT, Npad, nchunks;
+};
+
+int make_bwd_layout(const moe_cfg* c, BwdLayout* B) {
+  int rc = make_layout(c, &B->F);
+  if (rc) return rc;
+  const Layout& L = B->F;
+  const int64_t N = c->n_tokens, M = c->d_model, H = c->d_ff, E = c->n_experts;
+  const int64_t Es = c->n_shared, k = c->top_k;
+  const int64_t H1 = c->act == MOE_ACT_SWIGLU ? 2 * H : H;
+  B->H1 = H1;
+  if (Es > 256) return MOE_EUNSUPPORTED;          // one setup thread per shared expert
+  B->RT = L.Rmax + 128 * E;                       // per-expert K padded to 128
+  B->Npad = (N + 127) / 128 * 128;
+  B->nchunks = (N + 255) / 256;
+  const int64_t lim = (int64_t{1} << 31) - 1;
+  if (L.rows_alloc * H1 > lim || (E + Es) * H1 * M > lim || H1 * B->RT > lim ||
+      std::max(M, Es * H1) * std::max(B->RT, B->Npad) > lim || N * Es * H1 > lim ||
+      B->nchunks * E * M > lim)
+    return MOE_EUNSUPPORTED;
+  size_t off = L.total;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  const size_t esz = static_cast<size_t>(L.esz), ra = static_cast<size_t>(L.rows_alloc);
+  B->z1 = take(ra * H1 * esz);
+  B->o = take(ra * M * esz);
+  B->dout = take(ra * M * esz);
+  B->dh = take(ra * H * esz);
+  B->dz1 = take(ra * H1 * esz);
+  B->dbuf = take(ra * M * esz);
+  B->z1sh = take(static_cast<size_t>(N * Es * H1) * esz);
+  B->dhsh = take(static_cast<size_t>(N * Es * H) * esz);
+  B->dz1sh = take(static_cast<size_t>(N * Es * H1) * esz);
+  B->w1t = take(static_cast<size_t>((E + Es) * H1 * M) * esz);
+  B->w2t = take(static_cast<size_t>((E + Es) * M * H) * esz);
+  B->doT = take(static_cast<size_t>(M * B->RT) * esz);
+  B->hT = take(static_cast<size_t>(H * B->RT) * esz);
+  B->dz1T = take(static_cast<size_t>(H1 * B->RT) * esz);
+  B->bufT = take(static_cast<size_t>(M * B->RT) * esz);
+  B->dyT = take(static_cast<size_t>(Es ? M * B->Npad : 0) * esz);
+  B->xT = take(static_cast<size_t>(Es ? M * B->Npad : 0) * esz);
+  B->hshT = take(static_cast<size_t>(Es * H * B->Npad) * esz);
+  B->dz1shT = take(static_cast<size_t>(Es * H1 * B->Npad) * esz);
+  B->dl = take(static_cast<size_t>(N * E) * 4);
+  B->dw = take(static_cast<size_t>(N * k) * 4);
+  B->part = take(static_cast<size_t>(B->nchunks * E * M) * 4);
+  B->src0 = take(static_cast<size_t>(E) * 4);
+  B->cnt = take(static_cast<size_t>(E) * 4);
+  B->dst0 = take(static_cast<size_t>(E) * 4);
+  B->segblk = take(static_cast<size_t>(B->RT / 64 + 1) * 4);
+  B->width = take(16);
+  B->e2 = take(static_cast<size_t>(E + Es) * sizeof(moe::BatchEntry));
+  B->e1 = take(static_cast<size_t>(E + Es) * sizeof(moe::BatchEntry));
+  B->total = off;
+  return MOE_OK;
+}
+
+moe::GemmProblem routed_problem(const void* A, int64_t lda, const void* Bm, int64_t ldb,
+                                int64_t bstride, void* C, int64_t ldc, int N, int K,
+                                int a_rows, const Layout& L, const moe::TileDesc* tiles,
+                                const int32_t* ntiles) {
+  moe::GemmProblem p{};
+  p.A = A; p.lda = lda; p.B = Bm; p.ldb = ldb; p.b_stride = bstride; p.kseg = K;
+  p.C = C; p.ldc = ldc; p.N = N; p.K = K; p.a_rows = a_rows; p.act = moe::kActNone;
+  p.tiles = tiles; p.num_tiles = ntiles; p.max_tiles = static_cast<int>(L.max_tiles);
+  return p;
+}
+
+moe::GemmProblem dense_problem(const void* A, int64_t lda, const void* Bm, int64_t ldb,
+                               void* C, int64_t ldc, int N, int K, int rows, int BM) {
+  moe::GemmProblem p{};
+  p.A = A; p.lda = lda; p.B = Bm; p.ldb = ldb; p.kseg = K;
+  p.C = C; p.ldc = ldc; p.N = N; p.K = K; p.a_rows = rows; p.act = moe::kActNone;
+  p.max_tiles = (rows + BM - 1) / BM; p.dense_rows = rows;
+  return p;
+}
+
+moe::GemmProblem batched_problem(const void* A, int64_t lda, const void* Bm, int64_t ldb,
+                                 float* C, int64_t ldc, int N, int rows, int entries, int BM,
+                                 const moe::BatchEntry* batch) {
+  moe::GemmProblem p{};
+  p.A = A; p.lda = lda; p.B = Bm; p.ldb = ldb; p.kseg = int64_t{1} << 30;  // no K segments
+  p.C = C; p.ldc = ldc; p.N = N; p.K = 0; p.a_rows = rows; p.act = moe::kActNone;
+  p.max_tiles = entries * ((rows + BM - 1) / BM); p.dense_rows = rows;
+  p.batch = batch; p.out_f32 = 1;
+  return p;
+}
+
+int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* bg,
+                  const void* W1, const void* W2, const float* u, const void* dy,
+                  float coef_aux, float coef_z, float coef_dev, void* dx, float* dWg,
+                  float* dbg, float* dW1, float* dW2, const moe_meta* m, void* workspace,
+                  size_t wbytes, void* stream) {
+  BwdLayout B;
+  int rc = make_bwd_layout(c, &B);
+  if (rc) return rc;
+  if (!workspace || !aligned16(workspace)) return MOE_EINVAL;
+  if (wbytes < B.total) return MOE_EWORKSPACE;
+  const float* req_f[] = {dWg, dW1, dW2};
+  for (const float* p : req_f)
+    if (!p || !aligned16(p)) return MOE_EINVAL;
+  if (dbg && !aligned16(dbg)) return MOE_EINVAL;
+  if (!std::isfinite(coef_aux) || !std::isfinite(coef_z) || !std::isfinite(coef_dev))
+    return MOE_EINVAL;
+  const int64_t N = c->n_tokens, M = c->d_model, H = c->d_ff, E = c->n_experts;
+  const int64_t Es = c->n_shared, k = c->top_k, H1 = B.H1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (N == 0) {  // no tokens: every gradient is zero
+    rc = check_meta_empty(m);
+    if (rc) return rc;
+    rc = status_of(moe::launch_zero(dWg, E * M, s));
+    if (!rc) rc = status_of(moe::launch_zero(dW1, (E + Es) * H1 * M, s));
+    if (!rc) rc = status_of(moe::launch_zero(dW2, (E + Es) * M * H, s));
+    if (!rc && dbg) rc = status_of(moe::launch_zero(dbg, E, s));
+    if (rc) return rc;
+    moe::EmptyArgs ea{m->count, m->offset, m->stats, nullptr, m->z_loss, m->dev_loss,
+                      c->n_groups, c->n_experts};
+    return status_of(moe::launch_empty(ea, s));
+  }
+  rc = check_meta(m, true);
+  if (rc) return rc;
+  if (c->random_routing && (!u || !aligned16(u))) return MOE_EINVAL;
+  if (bg && !aligned16(bg)) return MOE_EINVAL;
+  const void* req[] = {x, Wg, W1, W2, dy, dx};
+  for (const void* p : req)
+    if (!p || !aligned16(p)) return MOE_EINVAL;
+
+  Run r;
+  r.c = c;
+  r.L = B.F;
+  r.ws = static_cast<char*>(workspace);
+  r.s = s;
+  const Layout& L = B.F;
+  char* ws = r.ws;
+  const int BM = L.BM, dt = c->dtype;
+  const size_t esz = static_cast<size_t>(L.esz);
+  // 1. routing again (deterministic: the forward's routing), rows dispatched into buf
+  rc = run_routing(r, x, Wg, bg, u, nullptr, m, BM, nullptr);
+  if (rc) return rc;
+  const moe::TileDesc* tiles = reinterpret_cast<const moe::TileDesc*>(ws + L.tiles);
+  const int32_t* ntiles = reinterpret_cast<const int32_t*>(ws + L.ntiles);
+  const int32_t* Rdev = m->offset + E;  // kept rows
+  const int a_rows = static_cast<int>(L.rows_alloc);
+  const char* W1c = static_cast<const char*>(W1);
+  const char* W2c = static_cast<const char*>(W2);
+  auto gemm = [&](const moe::GemmProblem& p0, const moe::GemmProblem* p1) {
+    moe::GemmArgs g{};
+    g.dtype = dt; g.p0 = p0; g.nprob = 1;
+    if (p1) { g.p1 = *p1; g.nprob = 2; }
+    return status_of(moe::launch_expert_gemm(g, s));
+  };
+  // 2. pre-activations z1 = buf W1_e^T (routed) and x W1_sh^T (shared), then h = act(z1)
+  {
+    auto p0 = routed_problem(ws + L.buf, M, W1, M, H1 * M, ws + B.z1, H1, static_cast<int>(H1),
+                             static_cast<int>(M), a_rows, L, tiles, ntiles);
+    auto p1 = dense_problem(x, M, W1c + E * H1 * M * esz, M, ws + B.z1sh, Es * H1,
+                            static_cast<int>(Es * H1), static_cast<int>(M),
+                            static_cast<int>(N), BM);
+    rc = gemm(p0, Es ? &p1 : nullptr);
+    if (rc) return rc;
+    moe::BwdEltArgs ea{};
+    ea.z = ws + B.z1; ea.h = ws + L.h; ea.rows_ptr = Rdev; ea.nexp = 1;
+    ea.H = static_cast<int>(H); ea.act = c->act; ea.dtype = dt;
+    rc = status_of(moe::launch_act_fwd(ea, L.Rmax * H, s));
+    if (rc) return rc;
+    if (Es) {
+      ea.z = ws + B.z1sh; ea.h = ws + L.hsh; ea.rows_ptr = nullptr;
+      ea.rows = static_cast<int>(N); ea.nexp = static_cast<int>(Es);
+      rc = status_of(moe::launch_act_fwd(ea, N * Es * H, s));
+      if (rc) return rc;
+    }
+  }
+  // 3. expert outputs o = h W2_e^T (routed; the combine weights' gradient needs them)
+  rc = gemm(routed_problem(ws + L.h, H, W2, H, M * H, ws + B.o, M, static_cast<int>(M),
+                           static_cast<int>(H), a_rows, L, tiles, ntiles), nullptr);
+  if (rc) return rc;
+  // 4. combine backward: dw, do
+  {
+    moe::CombineBwdArgs cb{dy, ws + B.o, m->row, m->topk_w, reinterpret_cast<float*>(ws + B.dw),
+                           ws + B.dout, static_cast<int>(N), static_cast<int>(M),
+                           static_cast<int>(k), dt};
+    rc = status_of(moe::launch_combine_bwd(cb, s));
+    if (rc) return rc;
+  }
+  // 5. transposed weights W2T [E', H, M], W1T [E', M, H1]
+  {
+    moe::MatTransposeArgs t2{W2, ws + B.w2t, static_cast<int>(M), static_cast<int>(H),
+                             static_cast<int>(E + Es), dt};
+    rc = status_of(moe::launch_mat_transpose(t2, s));
+    if (rc) return rc;
+    moe::MatTransposeArgs t1{W1, ws + B.w1t, static_cast<int>(H1), static_cast<int>(M),
+                             static_cast<int>(E + Es), dt};
+    rc = status_of(moe::launch_mat_transpose(t1, s));
+    if (rc) return rc;
+  }
+  // 6. dh = do W2_e (routed), dy W2_sh (shared); dz = dh act'(z1)
+  {
+    auto p0 = routed_problem(ws + B.dout, M, ws + B.w2t, M, H * M, ws + B.dh, H,
+                             static_cast<int>(H), static_cast<int>(M), a_rows, L, tiles, ntiles);
+    auto p1 = dense_problem(dy, M, ws + B.w2t + E * H * M * esz, M, ws + B.dhsh, Es * H,
+                            static_cast<int>(Es * H), static_cast<int>(M),
+                            static_cast<int>(N), BM);
+    rc = gemm(p0, Es ? &p1 : nullptr);
+    if (rc) return rc;
+    moe::BwdEltArgs ea{};
+    ea.z = ws + B.z1; ea.dh = ws + B.dh; ea.dz = ws + B.dz1; ea.rows_ptr = Rdev; ea.nexp = 1;
+    ea.H = static_cast<int>(H); ea.act = c->act; ea.dtype = dt;
+    rc = status_of(moe::launch_act_bwd(ea, L.Rmax * H, s));
+    if (rc) return rc;
+    if (Es) {
+      ea.z = ws + B.z1sh; ea.dh = ws + B.dhsh; ea.dz = ws + B.dz1sh; ea.rows_ptr = nullptr;
+      ea.rows = static_cast<int>(N); ea.nexp = static_cast<int>(Es);
+      rc = status_of(moe::launch_act_bwd(ea, N * Es * H, s));
+      if (rc) return rc;
+    }
+  }
+  // 7. dx rows = dz W1_e (routed), shared: dz_sh [W1_sh...] (K segments of H1)
+  {
+    auto p0 = routed_problem(ws + B.dz1, H1, ws + B.w1t, H1, M * H1, ws + B.dbuf, M,
+                             static_cast<int>(M), static_cast<int>(H1), a_rows, L, tiles, ntiles);
+    auto p1 = dense_problem(ws + B.dz1sh, Es * H1, ws + B.w1t + E * M * H1 * esz, H1,
+                            ws + L.osh, M, static_cast<int>(M), static_cast<int>(Es * H1),
+                            static_cast<int>(N), BM);
+    p1.kseg = H1;
+    p1.seg_stride = M * H1;
+    rc = gemm(p0, Es ? &p1 : nullptr);
+    if (rc) return rc;
+  }
+  // 8. router backward and dx
+  {
+    moe::RouterBwdArgs ra{};
+    ra.logits = m->logits; ra.topk_idx = m->topk_idx;
+    ra.dw = reinterpret_cast<const float*>(ws + B.dw);
+    ra.Cg = reinterpret_cast<const int32_t*>(ws + L.Cg);
+    ra.dl = reinterpret_cast<float*>(ws + B.dl);
+    ra.coef_aux = coef_aux; ra.coef_z = coef_z; ra.coef_dev = coef_dev; ra.norm_p = c->norm_p;
+    ra.N = static_cast<int>(N); ra.E = static_cast<int>(E); ra.k = static_cast<int>(k);
+    ra.G = c->n_groups; ra.S = static_cast<int>(L.S); ra.norm = c->gate_norm;
+    ra.n_eg = c->expert_groups;
+    rc = status_of(moe::launch_router_bwd(ra, s));
+    if (rc) return rc;
+    moe::DxArgs da{dy, ws + B.dbuf, Es ? ws + L.osh : nullptr, ra.dl, Wg, m->row, dx,
+                   static_cast<int>(N), static_cast<int>(M), static_cast<int>(E),
+                   static_cast<int>(k), c->residual, dt};
+    rc = status_of(moe::launch_dx_final(da, s));
+    if (rc) return rc;
+    moe::DwgArgs wa{ra.dl, x, reinterpret_cast<float*>(ws + B.part), dWg, dbg,
+                    static_cast<int>(N), static_cast<int>(E), static_cast<int>(M),
+                    static_cast<int>(B.nchunks), dt};
+    rc = status_of(moe::launch_dwg(wa, s));
+    if (rc) return rc;
+  }
+  // 9. weight gradients: per-expert K = kept rows padded to 128 (transposed compact buffers)
+  {
+    moe::BwdSetupArgs sa{};
+    sa.offset = m->offset;
+    sa.src0 = reinterpret_cast<int32_t*>(ws + B.src0);
+    sa.cnt = reinterpret_cast<int32_t*>(ws + B.cnt);
+    sa.dst0 = reinterpret_cast<int32_t*>(ws + B.dst0);
+    sa.seg_of_blk = reinterpret_cast<int32_t*>(ws + B.segblk);
+    sa.width = reinterpret_cast<int32_t*>(ws + B.width);
+    sa.dw2 = reinterpret_cast<moe::BatchEntry*>(ws + B.e2);
+    sa.dw1 = reinterpret_cast<moe::BatchEntry*>(ws + B.e1);
+    sa.E = static_cast<int>(E); sa.Es = static_cast<int>(Es); sa.M = static_cast<int>(M);
+    sa.H = static_cast<int>(H); sa.H1 = static_cast<int>(H1);
+    sa.Npad = static_cast<int>(B.Npad);
+    rc = status_of(moe::launch_bwd_setup(sa, s));
+    if (rc) return rc;
+    auto seg_t = [&](const void* X, size_t dst, int W) {
+      moe::TransposeArgs t{};
+      t.X = X; t.XT = ws + dst; t.seg_of_blk = sa.seg_of_blk; t.src0 = sa.src0; t.cnt = sa.cnt;
+      t.dst0 = sa.dst0; t.ncols_ptr = sa.width; t.W = W; t.ldT = B.RT; t.dtype = dt;
+      return status_of(moe::launch_seg_transpose(t, static_cast<int>(B.RT), s));
+    };
+    auto dense_t = [&](const void* X, size_t dst, int W) {
+      moe::TransposeArgs t{};
+      t.X = X; t.XT = ws + dst; t.ncols = static_cast<int>(B.Npad); t.rows = static_cast<int>(N);
+      t.W = W; t.ldT = B.Npad; t.dtype = dt;
+      return status_of(moe::launch_seg_transpose(t, static_cast<int>(B.Npad), s));
+    };
+    if ((rc = seg_t(ws + B.dout, B.doT, static_cast<int>(M)))) return rc;
+    if ((rc = seg_t(ws + L.h, B.hT, static_cast<int>(H)))) return rc;
+    if ((rc = seg_t(ws + B.dz1, B.dz1T, static_cast<int>(H1)))) return rc;
+    if ((rc = seg_t(ws + L.buf, B.bufT, static_cast<int>(M)))) return rc;
+    if (Es) {
+      if ((rc = dense_t(dy, B.dyT, static_cast<int>(M)))) return rc;
+      if ((rc = dense_t(x, B.xT, static_cast<int>(M)))) return rc;
+      if ((rc = dense_t(ws + L.hsh, B.hshT, static_cast<int>(Es * H)))) return rc;
+      if ((rc = dense_t(ws + B.dz1sh, B.dz1shT, static_cast<int>(Es * H1)))) return rc;
+    }
+    const moe::BatchEntry* e2 = sa.dw2;
+    const moe::BatchEntry* e1 = sa.dw1;
+    // dW2_e [M, H] = doT_e hT_e^T ; shared: dyT hshT_q^T
+    auto q0 = batched_problem(ws + B.doT, B.RT, ws + B.hT, B.RT, dW2, H, static_cast<int>(H),
+                              static_cast<int>(M), static_cast<int>(E), BM, e2);
+    auto q1 = batched_problem(ws + B.dyT, B.Npad, ws + B.hshT, B.Npad, dW2, H,
+                              static_cast<int>(H), static_cast<int>(M), static_cast<int>(Es), BM,
+                              e2 + E);
+    if ((rc = gemm(q0, Es ? &q1 : nullptr))) return rc;
+    // dW1_e [H1, M] = dz1T_e bufT_e^T ; shared: dz1shT_q xT^T
+    auto w0 = batched_problem(ws + B.dz1T, B.RT, ws + B.bufT, B.RT, dW1, M, static_cast<int>(M),
+                              static_cast<int>(H1), static_cast<int>(E), BM, e1);
+    auto w1 = batched_problem(ws + B.dz1shT, B.Npad, ws + B.xT, B.Npad, dW1, M,
+                              static_cast<int>(M), static_cast<int>(H1), static_cast<int>(Es), BM,
+                              e1 + E);
+    if ((rc = gemm(w0, Es ? &w1 : nullptr))) return rc;
+  }
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -346,6 +669,24 @@ int moe_forward_timed(const moe_cfg* cfg, const void* x, const void* Wg, const f
   if (!events) return MOE_EINVAL;
   return forward_impl(cfg, x, Wg, bg, W1, W2, u, y, aux_loss, meta, workspace, workspace_bytes,
                       stream, events);
+}
+
+int moe_backward_workspace_size(const moe_cfg* cfg, size_t* bytes) {
+  if (!bytes) return MOE_EINVAL;
+  BwdLayout B;
+  const int rc = make_bwd_layout(cfg, &B);
+  if (rc) return rc;
+  *bytes = B.total;
+  return MOE_OK;
+}
+
+int moe_backward(const moe_cfg* cfg, const void* x, const void* Wg, const float* bg,
+                 const void* W1, const void* W2, const float* u, const void* dy, float coef_aux,
+                 float coef_z, float coef_dev, void* dx, float* dWg, float* dbg, float* dW1,
+                 float* dW2, const moe_meta* meta, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  return backward_impl(cfg, x, Wg, bg, W1, W2, u, dy, coef_aux, coef_z, coef_dev, dx, dWg, dbg,
+                       dW1, dW2, meta, workspace, workspace_bytes, stream);
 }
 
 int moe_route(const moe_cfg* cfg, const float* logits, const float* u, const moe_meta* meta,

@@ -1,0 +1,497 @@
+// moe_backward: the kernels of the layer's backward pass besides the expert GEMMs.
+//
+// The loss is L = sum_n <dy_n, y_n> + a_aux aux + a_z z_loss + a_dev dev_loss.  Routing
+// decisions (top-k, group limits, random routing, capacity) are piecewise constant and carry
+// no gradient ([MegaBlocks] "3. 负载均衡损失": the balance loss reaches the router only
+// through the scores, the token counts being constants).  The expert part runs the chain rule
+// backwards through combine, GEMM 2, the activation and GEMM 1 ([GShard] "MoE Transformer":
+// the expert FFN; [Lec16] "DeepSeek V3 MoE (670B)": the gated form); the router part through
+// the gate normalisation, the softmax and the balance and z losses.  Every reduction runs in
+// a fixed order, so the results are bitwise deterministic.
+#include <math.h>
+
+#include <algorithm>
+#include <type_traits>
+
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+template <int DT>
+__device__ __forceinline__ float ld_elem(const void* p, int64_t i) {
+  if (DT == 1) return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+  return static_cast<const float*>(p)[i];
+}
+
+template <int DT>
+__device__ __forceinline__ void st_elem(void* p, int64_t i, float v) {
+  if (DT == 1)
+    static_cast<uint16_t*>(p)[i] = f32_to_bf16(v);
+  else
+    static_cast<float*>(p)[i] = v;
+}
+
+__device__ __forceinline__ int rows_of(const BwdEltArgs& a) {
+  return a.rows_ptr ? *a.rows_ptr : a.rows;
+}
+
+// GELU'(z) = Phi(z) + z phi(z), Phi(z) = (1 + erf(z / sqrt 2)) / 2, phi the normal density.
+__device__ __forceinline__ float gelu_grad(float z) {
+  const float Phi = 0.5f * (1.0f + erf_as7126(z * 0.70710678118654752440f));
+  return Phi + z * 0.39894228040143267794f * __expf(-0.5f * z * z);
+}
+
+// d/dz z sigmoid(z) = sigmoid(z) (1 + z (1 - sigmoid(z))).
+__device__ __forceinline__ float swish_grad(float z) {
+  const float s = __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+  return s * (1.0f + z * (1.0f - s));
+}
+
+// h = act(z) from the pre-activations: per row, nexp blocks of H1 inputs -> H outputs
+// (gated: h = Swish(g) * u with g, u the two halves of the block).
+template <int DT>
+__global__ __launch_bounds__(256) void act_fwd_kernel(BwdEltArgs a) {
+  const int rows = rows_of(a);
+  const int64_t W = static_cast<int64_t>(a.nexp) * a.H;
+  const int64_t total = static_cast<int64_t>(rows) * W;
+  const int H1 = a.act == kActSwiglu ? 2 * a.H : a.H;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < total; i += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t r = i / W;
+    const int c = static_cast<int>(i - r * W);
+    const int q = c / a.H, cc = c - q * a.H;
+    const int64_t zi = r * a.nexp * H1 + static_cast<int64_t>(q) * H1 + cc;
+    const float z = ld_elem<DT>(a.z, zi);
+    float h;
+    if (a.act == kActSwiglu)
+      h = swish(z) * ld_elem<DT>(a.z, zi + a.H);
+    else if (a.act == kActGelu)
+      h = gelu_erf(z);
+    else
+      h = fmaxf(z, 0.0f);
+    st_elem<DT>(a.h, i, h);
+  }
+}
+
+// dz = dh * act'(z); gated: dg = dh * u * Swish'(g), du = dh * Swish(g).
+template <int DT>
+__global__ __launch_bounds__(256) void act_bwd_kernel(BwdEltArgs a) {
+  const int rows = rows_of(a);
+  const int64_t W = static_cast<int64_t>(a.nexp) * a.H;
+  const int64_t total = static_cast<int64_t>(rows) * W;
+  const int H1 = a.act == kActSwiglu ? 2 * a.H : a.H;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < total; i += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t r = i / W;
+    const int c = static_cast<int>(i - r * W);
+    const int q = c / a.H, cc = c - q * a.H;
+    const int64_t zi = r * a.nexp * H1 + static_cast<int64_t>(q) * H1 + cc;
+    const float dh = ld_elem<DT>(a.dh, i);
+    const float z = ld_elem<DT>(a.z, zi);
+    if (a.act == kActSwiglu) {
+      const float u = ld_elem<DT>(a.z, zi + a.H);
+      st_elem<DT>(a.dz, zi, dh * u * swish_grad(z));
+      st_elem<DT>(a.dz, zi + a.H, dh * swish(z));
+    } else if (a.act == kActGelu) {
+      st_elem<DT>(a.dz, zi, dh * gelu_grad(z));
+    } else {
+      st_elem<DT>(a.dz, zi, z > 0.0f ? dh : 0.0f);
+    }
+  }
+}
+
+// One wave per token: dw_nj = <dy_n, o_row> for kept slots (0 otherwise), and
+// do_row = w_nj dy_n into the compact expert-major buffer.
+template <int DT>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(CombineBwdArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= a.N) return;
+  const int64_t rowoff = static_cast<int64_t>(n) * a.M;
+  for (int j = 0; j < a.k; ++j) {
+    const int r = a.row[static_cast<int64_t>(n) * a.k + j];
+    float d = 0.0f;
+    if (r >= 0) {
+      const float w = a.topk_w[static_cast<int64_t>(n) * a.k + j];
+      const int64_t ro = static_cast<int64_t>(r) * a.M;
+      for (int m = lane; m < a.M; m += 64) {
+        const float g = ld_elem<DT>(a.dy, rowoff + m);
+        d = fmaf(g, ld_elem<DT>(a.o, ro + m), d);
+        st_elem<DT>(a.dout, ro + m, w * g);
+      }
+      d = wave_sum(d);
+    }
+    if (lane == 0) a.dw[static_cast<int64_t>(n) * a.k + j] = d;
+  }
+}
+
+// Segmented transpose with zero padding: XT[w][dst0_s + i] = i < cnt_s ? X[src0_s + i][w] : 0
+// for every segment s (experts of the compact buffer, or one dense segment).  Blocks own
+// 64 x 64 tiles of XT; a tile's 64 columns lie inside one segment (segments are padded to
+// multiples of 128 columns), found through seg_of_blk.
+template <int DT>
+__global__ __launch_bounds__(256) void seg_transpose_kernel(TransposeArgs a) {
+  typedef typename std::conditional<DT == 1, uint16_t, float>::type E_t;
+  __shared__ E_t tile[64][65];
+  const int cb = blockIdx.x;          // 64-column block of XT
+  const int wb = blockIdx.y;          // 64-row block of XT (= column block of X)
+  const int ncols = a.ncols_ptr ? *a.ncols_ptr : a.ncols;
+  if (cb * 64 >= ncols) return;
+  const int s = a.seg_of_blk ? a.seg_of_blk[cb] : 0;
+  const int src0 = a.src0 ? a.src0[s] : 0;
+  const int cnt = a.cnt ? a.cnt[s] : a.rows;
+  const int dst0 = a.dst0 ? a.dst0[s] : 0;
+  const E_t* X = static_cast<const E_t*>(a.X);
+  E_t* XT = static_cast<E_t*>(a.XT);
+  const int t = threadIdx.x;
+  for (int idx = t; idx < 64 * 64; idx += 256) {
+    const int r = idx >> 6, c = idx & 63;   // r: source row within the tile, c: column of X
+    const int i = cb * 64 + r - dst0;       // index inside the segment
+    E_t v = E_t(0);
+    if (i < cnt) v = X[static_cast<int64_t>(src0 + i) * a.W + wb * 64 + c];
+    tile[r][c] = v;
+  }
+  __syncthreads();
+  for (int idx = t; idx < 64 * 64; idx += 256) {
+    const int w = idx >> 6, c = idx & 63;
+    XT[static_cast<int64_t>(wb * 64 + w) * a.ldT + cb * 64 + c] = tile[c][w];
+  }
+}
+
+// Batched matrix transpose: dst[b][c][r] = src[b][r][c] for [rows, cols] matrices.
+template <int DT>
+__global__ __launch_bounds__(256) void mat_transpose_kernel(MatTransposeArgs a) {
+  typedef typename std::conditional<DT == 1, uint16_t, float>::type E_t;
+  __shared__ E_t tile[64][65];
+  const int cb = blockIdx.x, rb = blockIdx.y, b = blockIdx.z;
+  const E_t* src = static_cast<const E_t*>(a.src) + static_cast<int64_t>(b) * a.rows * a.cols;
+  E_t* dst = static_cast<E_t*>(a.dst) + static_cast<int64_t>(b) * a.rows * a.cols;
+  const int t = threadIdx.x;
+  for (int idx = t; idx < 64 * 64; idx += 256) {
+    const int r = idx >> 6, c = idx & 63;
+    tile[r][c] = src[static_cast<int64_t>(rb * 64 + r) * a.cols + cb * 64 + c];
+  }
+  __syncthreads();
+  for (int idx = t; idx < 64 * 64; idx += 256) {
+    const int c = idx >> 6, r = idx & 63;
+    dst[static_cast<int64_t>(cb * 64 + c) * a.rows + rb * 64 + r] = tile[r][c];
+  }
+}
+
+// One block: per-expert padded K offsets of the transposed compact buffers (kofs[e] =
+// sum over e' < e of the expert's kept rows rounded up to 128), the segment of every
+// 64-column block, the padded width, and the batched weight-gradient GEMM entries.
+__global__ __launch_bounds__(256) void bwd_setup_kernel(BwdSetupArgs a) {
+  __shared__ int sc[4];
+  const int t = threadIdx.x, E = a.E;
+  int cnt = 0;
+  if (t < E) cnt = a.offset[t + 1] - a.offset[t];
+  const int pad = (cnt + 127) / 128 * 128;
+  // block exclusive scan of pad over 256 threads
+  const int lane = t & 63, w = t >> 6;
+  const int inc = wave_inclusive_scan(pad);
+  if (lane == 63) sc[w] = inc;
+  __syncthreads();
+  int before = 0, total = 0;
+  for (int i = 0; i < 4; ++i) {
+    if (i < w) before += sc[i];
+    total += sc[i];
+  }
+  const int kofs = before + inc - pad;
+  if (t < E) {
+    a.src0[t] = a.offset[t];
+    a.cnt[t] = cnt;
+    a.dst0[t] = kofs;
+    for (int b = kofs / 64; b < (kofs + pad) / 64; ++b) a.seg_of_blk[b] = t;
+    // dW2_e [M, H] = doT_e . hT_e^T ; dW1_e [H1, M] = dz1T_e . bufT_e^T
+    BatchEntry d2, d1;
+    d2.a_off = kofs; d2.b_off = kofs; d2.c_off = static_cast<int64_t>(t) * a.M * a.H;
+    d2.K = pad; d2.pad = 0;
+    d1.a_off = kofs; d1.b_off = kofs; d1.c_off = static_cast<int64_t>(t) * a.H1 * a.M;
+    d1.K = pad; d1.pad = 0;
+    a.dw2[t] = d2;
+    a.dw1[t] = d1;
+  }
+  if (t < a.Es) {  // shared experts: K = padded N, rows q of the transposed shared buffers
+    BatchEntry d2, d1;
+    d2.a_off = 0; d2.b_off = static_cast<int64_t>(t) * a.H * a.Npad;
+    d2.c_off = static_cast<int64_t>(E + t) * a.M * a.H; d2.K = a.Npad; d2.pad = 0;
+    d1.a_off = static_cast<int64_t>(t) * a.H1 * a.Npad; d1.b_off = 0;
+    d1.c_off = static_cast<int64_t>(E + t) * a.H1 * a.M; d1.K = a.Npad; d1.pad = 0;
+    a.dw2[E + t] = d2;
+    a.dw1[E + t] = d1;
+  }
+  if (t == 0) *a.width = total;
+}
+
+// Router backward, one wave per token: dL/dp through the gate normalisation (none, sum or
+// p-norm of the selected probabilities), the balance losses (counts are constants), the
+// softmax, and the z-loss: dl_e = p_e (dp_e - sum_i p_i dp_i) + a_z 2 lse p_e / N.
+__global__ __launch_bounds__(256) void router_bwd_kernel(RouterBwdArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= a.N) return;
+  const int E = a.E, k = a.k;
+  const float* l = a.logits + static_cast<int64_t>(n) * E;
+  float mx = -INFINITY;
+  for (int e = lane; e < E; e += 64) mx = fmaxf(mx, l[e]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  float se = 0.0f;
+  for (int e = lane; e < E; e += 64) se += expf(l[e] - mx);
+  se = wave_sum(se);
+  const float lse = mx + logf(se);
+
+  // gradient of the selected probabilities through the normalisation
+  float dps[kMaxTopK];
+  int sel[kMaxTopK];
+  {
+    float ps[kMaxTopK], dw[kMaxTopK];
+    float s = 0.0f, D = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      sel[j] = -1;
+      ps[j] = dw[j] = dps[j] = 0.0f;
+      if (j < k) {
+        sel[j] = a.topk_idx[static_cast<int64_t>(n) * k + j];
+        ps[j] = expf(l[sel[j]] - mx) / se;
+        dw[j] = a.dw[static_cast<int64_t>(n) * k + j];
+        s += dw[j] * ps[j];
+      }
+    }
+    if (a.norm == 0) {
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j) dps[j] = dw[j];
+    } else {
+      const float P = a.norm == 1 ? 1.0f : a.norm_p;
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j)
+        if (j < k) D += a.norm == 1 ? ps[j] : powf(ps[j], P);
+      if (a.norm == 2) D = powf(D, 1.0f / P);
+      const float c = a.norm == 1 ? s / (D * D) : s * powf(D, -1.0f - P);
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j)
+        if (j < k) dps[j] = dw[j] / D - (a.norm == 1 ? 1.0f : powf(ps[j], P - 1.0f)) * c;
+    }
+  }
+  const int g = n / a.S;
+  const float inv_gs = 1.0f / (static_cast<float>(a.G) * a.S);
+  const int gs = E / a.n_eg;
+  float pe[4], dp[4];
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    pe[i] = dp[i] = 0.0f;
+    if (e < E) {
+      pe[i] = expf(l[e] - mx) / se;
+      float d = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j)
+        if (j < k && sel[j] == e) d += dps[j];
+      const float c_e = static_cast<float>(a.Cg[static_cast<int64_t>(g) * E + e]);
+      d += a.coef_aux * E * c_e * inv_gs / (static_cast<float>(k) * a.S);
+      if (a.coef_dev != 0.0f) {  // f_j = mean over the expert group of E c / (k S)
+        const int j0 = (e / gs) * gs;
+        float cs = 0.0f;
+        for (int x = 0; x < gs; ++x) cs += static_cast<float>(a.Cg[static_cast<int64_t>(g) * E + j0 + x]);
+        d += a.coef_dev * (E * cs / (gs * static_cast<float>(k) * a.S)) * inv_gs;
+      }
+      dp[i] = d;
+      acc = fmaf(pe[i], d, acc);
+    }
+  }
+  const float sp = wave_sum(acc);
+  const float zc = a.coef_z * 2.0f * lse / static_cast<float>(a.N);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    if (e < E) a.dl[static_cast<int64_t>(n) * E + e] = pe[i] * (dp[i] - sp) + zc * pe[i];
+  }
+}
+
+// dWg partial sums: block (8-expert tile, 256-column tile, 256-token chunk) computes
+// part[chunk][e][m] = sum over the chunk's tokens of dl[n][e] x[n][m], tokens in order.
+template <int DT>
+__global__ __launch_bounds__(256) void dwg_partial_kernel(DwgArgs a) {
+  __shared__ float dls[256][8];
+  const int e0 = blockIdx.x * 8, m = blockIdx.y * 256 + threadIdx.x, ch = blockIdx.z;
+  const int n0 = ch * 256, nn = min(256, a.N - n0);
+  for (int i = threadIdx.x; i < 256 * 8; i += 256) {
+    const int r = i >> 3, c = i & 7;
+    dls[r][c] = (r < nn && e0 + c < a.E) ? a.dl[static_cast<int64_t>(n0 + r) * a.E + e0 + c] : 0.0f;
+  }
+  __syncthreads();
+  if (m >= a.M) return;
+  float acc[8] = {};
+  for (int r = 0; r < nn; ++r) {
+    const float xv = ld_elem<DT>(a.x, static_cast<int64_t>(n0 + r) * a.M + m);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = fmaf(dls[r][c], xv, acc[c]);
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+    if (e0 + c < a.E) a.part[(static_cast<int64_t>(ch) * a.E + e0 + c) * a.M + m] = acc[c];
+}
+
+// dWg = sum of the partials over chunks in order; dbg_e = sum_n dl[n][e] (one wave per e).
+__global__ __launch_bounds__(256) void dwg_reduce_kernel(DwgArgs a) {
+  const int64_t i = blockIdx.x * 256ll + threadIdx.x;
+  const int64_t EM = static_cast<int64_t>(a.E) * a.M;
+  if (i < EM) {
+    float s = 0.0f;
+    for (int ch = 0; ch < a.nchunks; ++ch) s += a.part[ch * EM + i];
+    a.dWg[i] = s;
+  }
+  if (a.dbg && blockIdx.x < static_cast<unsigned>((a.E + 3) / 4)) {
+    const int e = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (e < a.E) {
+      float s = 0.0f;
+      for (int n = lane; n < a.N; n += 64) s += a.dl[static_cast<int64_t>(n) * a.E + e];
+      s = wave_sum(s);
+      if (lane == 0) a.dbg[e] = s;
+    }
+  }
+}
+
+// dx_n = [res] dy_n + sum_j dx_rows[row_nj] + dx_shared_n + sum_e dl_ne Wg_e, summed in
+// that order in fp32; 16 tokens per block, dl rows staged in LDS.
+template <int DT>
+__global__ __launch_bounds__(256) void dx_final_kernel(DxArgs a) {
+  __shared__ float dls[16][kMaxExperts];
+  __shared__ int rows_s[16][kMaxTopK];
+  const int n0 = blockIdx.x * 16, nt = min(16, a.N - n0), E = a.E, k = a.k;
+  for (int i = threadIdx.x; i < 16 * E; i += 256) {
+    const int r = i / E, e = i - r * E;
+    dls[r][e] = r < nt ? a.dl[static_cast<int64_t>(n0 + r) * E + e] : 0.0f;
+  }
+  for (int i = threadIdx.x; i < 16 * k; i += 256) {
+    const int r = i / k, j = i - r * k;
+    rows_s[r][j] = r < nt ? a.row[static_cast<int64_t>(n0 + r) * k + j] : -1;
+  }
+  __syncthreads();
+  for (int m = threadIdx.x; m < a.M; m += 256) {
+    float acc[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    for (int e = 0; e < E; ++e) {
+      const float wv = ld_elem<DT>(a.Wg, static_cast<int64_t>(e) * a.M + m);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = fmaf(dls[r][e], wv, acc[r]);
+    }
+    for (int r = 0; r < nt; ++r) {
+      const int64_t n = n0 + r;
+      float v = a.residual ? ld_elem<DT>(a.dy, n * a.M + m) : 0.0f;
+      for (int j = 0; j < k; ++j) {
+        const int row = rows_s[r][j];
+        if (row >= 0) v += ld_elem<DT>(a.dxr, static_cast<int64_t>(row) * a.M + m);
+      }
+      if (a.dxsh) v += ld_elem<DT>(a.dxsh, n * a.M + m);
+      st_elem<DT>(a.dx, n * a.M + m, v + acc[r]);
+    }
+  }
+}
+
+__global__ void zero_kernel(float* p, int64_t n) {
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * 256)
+    p[i] = 0.0f;
+}
+
+int grid_for(int64_t n) {
+  const int64_t b = (n + 255) / 256;
+  return static_cast<int>(b < 1 ? 1 : (b > 65535 ? 65535 : b));
+}
+
+}  // namespace
+
+hipError_t launch_act_fwd(const BwdEltArgs& a, int64_t max_elems, hipStream_t s) {
+  if (max_elems == 0) return hipSuccess;
+  if (a.dtype == 1)
+    hipLaunchKernelGGL(act_fwd_kernel<1>, dim3(grid_for(max_elems)), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(act_fwd_kernel<0>, dim3(grid_for(max_elems)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_act_bwd(const BwdEltArgs& a, int64_t max_elems, hipStream_t s) {
+  if (max_elems == 0) return hipSuccess;
+  if (a.dtype == 1)
+    hipLaunchKernelGGL(act_bwd_kernel<1>, dim3(grid_for(max_elems)), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(act_bwd_kernel<0>, dim3(grid_for(max_elems)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_bwd(const CombineBwdArgs& a, hipStream_t s) {
+  const int grid = (a.N + 3) / 4;
+  if (grid == 0) return hipSuccess;
+  if (a.dtype == 1)
+    hipLaunchKernelGGL(combine_bwd_kernel<1>, dim3(grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(combine_bwd_kernel<0>, dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_seg_transpose(const TransposeArgs& a, int max_cols, hipStream_t s) {
+  const dim3 grid((max_cols + 63) / 64, a.W / 64);
+  if (grid.x == 0 || grid.y == 0) return hipSuccess;
+  if (a.dtype == 1)
+    hipLaunchKernelGGL(seg_transpose_kernel<1>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(seg_transpose_kernel<0>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_mat_transpose(const MatTransposeArgs& a, hipStream_t s) {
+  const dim3 grid(a.cols / 64, a.rows / 64, a.batch);
+  if (grid.x == 0 || grid.y == 0 || grid.z == 0) return hipSuccess;
+  if (a.dtype == 1)
+    hipLaunchKernelGGL(mat_transpose_kernel<1>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(mat_transpose_kernel<0>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_setup(const BwdSetupArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(bwd_setup_kernel, dim3(1), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_bwd(const RouterBwdArgs& a, hipStream_t s) {
+  const int grid = (a.N + 3) / 4;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(router_bwd_kernel, dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dwg(const DwgArgs& a, hipStream_t s) {
+  const dim3 g1((a.E + 7) / 8, (a.M + 255) / 256, a.nchunks);
+  if (a.nchunks > 0) {
+    if (a.dtype == 1)
+      hipLaunchKernelGGL(dwg_partial_kernel<1>, g1, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(dwg_partial_kernel<0>, g1, dim3(256), 0, s, a);
+  }
+  const int64_t em = static_cast<int64_t>(a.E) * a.M;
+  const int64_t blocks = std::max<int64_t>((em + 255) / 256, (a.E + 3) / 4);
+  hipLaunchKernelGGL(dwg_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dx_final(const DxArgs& a, hipStream_t s) {
+  const int grid = (a.N + 15) / 16;
+  if (grid == 0) return hipSuccess;
+  if (a.dtype == 1)
+    hipLaunchKernelGGL(dx_final_kernel<1>, dim3(grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(dx_final_kernel<0>, dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(float* p, int64_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_kernel, dim3(grid_for(n)), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -86,29 +86,37 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& g, Job& j) {
   const int nt = in / gsz;
 
   const GemmProblem& P = second ? g.p1 : g.p0;
-  int e, row0, nrows;
+  int e = 0, row0, nrows, K = P.K;
+  int64_t aoff = 0, boff = 0, coff = 0;  // batched entries: element offsets
   if (P.tiles) {
     const TileDesc d = P.tiles[mt];
     e = d.expert; row0 = d.row0; nrows = d.nrows;
+  } else if (P.batch) {
+    const int mpe = (P.dense_rows + BM - 1) / BM;  // m-tiles per entry
+    const int be = mt / mpe, ml = mt - be * mpe;
+    const BatchEntry d = P.batch[be];
+    row0 = ml * BM; nrows = min(BM, P.dense_rows - row0);
+    aoff = d.a_off; boff = d.b_off; coff = d.c_off; K = d.K;
   } else {
-    e = 0; row0 = mt * BM; nrows = min(BM, P.dense_rows - row0);
+    row0 = mt * BM; nrows = min(BM, P.dense_rows - row0);
   }
+  const int osz = P.out_f32 ? 4 : ESZ;
   j.lda = P.lda * ESZ;
-  j.A = static_cast<const char*>(P.A) + static_cast<int64_t>(row0) * j.lda;
+  j.A = static_cast<const char*>(P.A) + aoff * ESZ + static_cast<int64_t>(row0) * j.lda;
   j.ldb = P.ldb * ESZ;
   const int c0 = nt * BN;
   // first B row of the tile: output column c0, or for gated problems its gate row
   const int64_t brow = P.act == kActSwiglu
       ? static_cast<int64_t>(c0 / P.glu_h) * 2 * P.glu_h + c0 % P.glu_h : c0;
-  j.B = static_cast<const char*>(P.B) + (static_cast<int64_t>(e) * P.b_stride) * ESZ +
+  j.B = static_cast<const char*>(P.B) + (static_cast<int64_t>(e) * P.b_stride + boff) * ESZ +
         brow * j.ldb;
   j.upb = static_cast<int64_t>(P.glu_h) * j.ldb;
   j.kseg = P.kseg;
   j.segb = P.seg_stride * ESZ;
-  j.ldc = P.ldc * ESZ;
-  j.C = static_cast<char*>(P.C) + static_cast<int64_t>(row0) * j.ldc +
-        static_cast<int64_t>(nt) * BN * ESZ;
-  j.K = P.K;
+  j.ldc = P.ldc * osz;
+  j.C = static_cast<char*>(P.C) + coff * osz + static_cast<int64_t>(row0) * j.ldc +
+        static_cast<int64_t>(c0) * osz;
+  j.K = K;
   j.nrows = nrows;
   j.ncols = min(BN, P.N - nt * BN);
   j.rows_left = P.a_rows - row0;
@@ -194,7 +202,7 @@ __device__ __forceinline__ void dma16(rsrc_t r, unsigned char* lds, uint32_t vof
 //    columns [32 s, 32 s + 32) and rows [64 s + 32, 64 s + 64) their up rows, so wave wn's two
 //    32-column MFMA blocks are the gate and up halves of the same 32 outputs, held by the
 //    same lanes in the same registers; the tile writes BN / 2 columns.
-template <int BM, int BN, int WN, int ACT, int BK, int NST>
+template <int BM, int BN, int WN, int ACT, int BK, int NST, bool OUTF32>
 __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int ROW = BK * 2, CPR = ROW / 16;  // bytes and 16-byte columns per LDS row
   static_assert(NST >= 2 && NST <= 5 && BK * (NST - 1) <= 128, "K % 128 == 0 covers the prologue");
@@ -218,7 +226,7 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
 
   const uint32_t lda = static_cast<uint32_t>(j.lda), ldb = static_cast<uint32_t>(j.ldb);
   const rsrc_t ra_rs = make_rsrc(j.A, static_cast<int64_t>(j.nrows) * j.lda);
-  const int nseg = (j.K + static_cast<int>(j.kseg) - 1) / static_cast<int>(j.kseg);
+  const int nseg = max(1, (j.K + static_cast<int>(j.kseg) - 1) / static_cast<int>(j.kseg));
   // Weight rows past the problem's N (a partial last n-tile) read as zeros.
   const rsrc_t rb_rs = make_rsrc(j.B, (nseg - 1) * j.segb + (GLU ? j.upb : 0) +
                                           static_cast<int64_t>(j.ncols) * j.ldb);
@@ -302,7 +310,8 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
     else if (NST > 2 && ahead >= 1) MOE_WAIT_VMCNT(Q);
     else MOE_WAIT_VMCNT(0);
   };
-  const int KT = j.K / BK;  // >= NST - 1
+  const int KT = j.K / BK;  // 0 (a zero block) or >= NST - 1
+  if (KT > 0) {
 #pragma unroll
   for (int p = 0; p < NST - 1; ++p) issue(p, p);
   int st = 0;
@@ -320,6 +329,27 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
     lds_barrier();
     compute(st);
     st = st == NST - 1 ? 0 : st + 1;
+  }
+  }
+
+  if (OUTF32) {  // fp32 output (no activation): each lane stores its runs of 4 features
+#pragma unroll
+    for (int im = 0; im < TM; ++im) {
+      const int tok = wm * WTM + 32 * im + (lane & 31);
+      if (tok >= j.nrows) continue;
+#pragma unroll
+      for (int jn = 0; jn < TN; ++jn)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const int f = wn * WTN + 32 * jn + 8 * qd + 4 * (lane >> 5);
+          if (f >= j.ncols) continue;
+          f32x4 v;
+#pragma unroll
+          for (int x = 0; x < 4; ++x) v[x] = acc[jn][im][4 * qd + x];
+          *reinterpret_cast<f32x4*>(j.C + static_cast<int64_t>(tok) * j.ldc + f * 4) = v;
+        }
+    }
+    return;
   }
 
   // Epilogue through LDS: D[feature][token] -> tile[token][feature] bf16 (rows of OUTN*2
@@ -436,10 +466,13 @@ hipError_t launch_expert_gemm(const GemmArgs& a, hipStream_t s) {
   const int grid = grid_of(a, gemm_block_n(a.dtype, act));
   if (grid == 0) return hipSuccess;
   if (a.dtype == 1) {
-#define MOE_GEMM_LAUNCH(ACTV)                                                              \
-  hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 4, ACTV, kGemmBK, kGemmStages>), dim3(grid), \
-                     dim3(512), 0, s, a)
-    if (act == kActRelu) MOE_GEMM_LAUNCH(kActRelu);
+#define MOE_GEMM_LAUNCH(ACTV)                                                          \
+  hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 4, ACTV, kGemmBK, kGemmStages, false>),  \
+                     dim3(grid), dim3(512), 0, s, a)
+    if (a.p0.out_f32)
+      hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 4, kActNone, kGemmBK, kGemmStages, true>),
+                         dim3(grid), dim3(512), 0, s, a);
+    else if (act == kActRelu) MOE_GEMM_LAUNCH(kActRelu);
     else if (act == kActGelu) MOE_GEMM_LAUNCH(kActGelu);
     else if (act == kActSwiglu) MOE_GEMM_LAUNCH(kActSwiglu);
     else MOE_GEMM_LAUNCH(kActNone);

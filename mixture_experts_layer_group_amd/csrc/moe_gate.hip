@@ -109,7 +109,7 @@ __global__ void empty_kernel(EmptyArgs a) {
   for (int i = t; i <= a.E; i += blockDim.x) a.offset[i] = 0;
   if (t < 4) a.stats[t] = 0;
   if (t == 0) {
-    *a.aux = 0.f;
+    if (a.aux) *a.aux = 0.f;
     if (a.z_loss) *a.z_loss = 0.f;
     if (a.dev_loss) *a.dev_loss = 0.f;
   }

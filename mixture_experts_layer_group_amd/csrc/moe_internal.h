@@ -75,6 +75,13 @@ struct PermuteArgs {
   int slices;             // column slices per router block (set by the launcher)
 };
 
+// One entry of a batched GEMM problem: element offsets of its A, B and C blocks and its K
+// depth (a multiple of 128; 0 writes a zero block).
+struct BatchEntry {
+  int64_t a_off, b_off, c_off;
+  int32_t K, pad;
+};
+
 // Activation codes of a GEMM problem (the first three are moe_cfg's act values).
 constexpr int kActRelu = 0, kActGelu = 1, kActSwiglu = 2, kActNone = -1;
 
@@ -94,8 +101,11 @@ struct GemmProblem {
   const TileDesc* tiles;  // routed: device tile list (nullptr: dense problem)
   const int32_t* num_tiles;
   int max_tiles;          // routed: grid bound on the tile count; dense: ceil(rows / BM)
-  int dense_rows;         // dense problem: number of rows
+  int dense_rows;         // dense problem: number of rows; batched: rows of every entry
   int glu_h;              // gated problems: hidden width H of one expert (else unused)
+  const BatchEntry* batch;  // batched problem (tiles == nullptr): device entries; max_tiles =
+                            // entries * ceil(dense_rows / BM)
+  int out_f32;            // C is fp32 (act must be none); else C has the input dtype
 };
 
 struct GemmArgs {
@@ -123,10 +133,77 @@ struct CombineArgs {
   int N, M, k, residual, dtype, G, E, S;
 };
 
-struct EmptyArgs {         // N == 0: zero the small outputs
+struct EmptyArgs {         // N == 0: zero the small outputs (aux, z_loss, dev_loss nullable)
   int32_t* count; int32_t* offset; int32_t* stats; float* aux; float* z_loss; float* dev_loss;
   int G, E;
 };
+
+// ---- backward pass (moe_backward.hip)
+
+struct BwdEltArgs {        // elementwise activation forward / backward over rows
+  const void* z;           // [rows, nexp * H1] pre-activations (H1 = 2H for gated experts)
+  void* h;                 // [rows, nexp * H] activations (forward)
+  const void* dh;          // [rows, nexp * H] (backward)
+  void* dz;                // [rows, nexp * H1] (backward)
+  const int32_t* rows_ptr; // device row count (nullptr: rows)
+  int rows, nexp, H, act, dtype;
+};
+
+struct CombineBwdArgs {    // dw_nj = <dy_n, o_row>, do_row = w_nj dy_n
+  const void* dy; const void* o; const int32_t* row; const float* topk_w;
+  float* dw; void* dout;
+  int N, M, k, dtype;
+};
+
+struct TransposeArgs {     // XT[w][dst0_s + i] = i < cnt_s ? X[src0_s + i][w] : 0
+  const void* X; void* XT;
+  const int32_t* seg_of_blk;  // segment of each 64-column block of XT (nullptr: one segment)
+  const int32_t* src0; const int32_t* cnt; const int32_t* dst0;  // per segment (nullptr: dense)
+  const int32_t* ncols_ptr;   // device width of XT in use (nullptr: ncols)
+  int ncols, rows, W;         // rows: dense segment length; W: columns of X (multiple of 64)
+  int64_t ldT;
+  int dtype;
+};
+
+struct MatTransposeArgs {  // dst[b][c][r] = src[b][r][c], [rows, cols] multiples of 64
+  const void* src; void* dst; int rows, cols, batch, dtype;
+};
+
+struct BwdSetupArgs {      // padded per-expert K offsets and batched weight-gradient entries
+  const int32_t* offset;   // [E+1] expert offsets of the compact buffer
+  int32_t* src0; int32_t* cnt; int32_t* dst0; int32_t* seg_of_blk; int32_t* width;
+  BatchEntry* dw2; BatchEntry* dw1;  // [E+Es]
+  int E, Es, M, H, H1, Npad;
+};
+
+struct RouterBwdArgs {
+  const float* logits; const int32_t* topk_idx; const float* dw; const int32_t* Cg;
+  float* dl;
+  float coef_aux, coef_z, coef_dev, norm_p;
+  int N, E, k, G, S, norm, n_eg;
+};
+
+struct DwgArgs {           // dWg = dl^T x (fp32, two passes), dbg = column sums of dl
+  const float* dl; const void* x; float* part; float* dWg; float* dbg;
+  int N, E, M, nchunks, dtype;
+};
+
+struct DxArgs {            // dx = [res] dy + sum_j dx_rows[row] + dx_shared + dl Wg
+  const void* dy; const void* dxr; const void* dxsh; const float* dl; const void* Wg;
+  const int32_t* row; void* dx;
+  int N, M, E, k, residual, dtype;
+};
+
+hipError_t launch_act_fwd(const BwdEltArgs& a, int64_t max_elems, hipStream_t s);
+hipError_t launch_act_bwd(const BwdEltArgs& a, int64_t max_elems, hipStream_t s);
+hipError_t launch_combine_bwd(const CombineBwdArgs& a, hipStream_t s);
+hipError_t launch_seg_transpose(const TransposeArgs& a, int max_cols, hipStream_t s);
+hipError_t launch_mat_transpose(const MatTransposeArgs& a, hipStream_t s);
+hipError_t launch_bwd_setup(const BwdSetupArgs& a, hipStream_t s);
+hipError_t launch_router_bwd(const RouterBwdArgs& a, hipStream_t s);
+hipError_t launch_dwg(const DwgArgs& a, hipStream_t s);
+hipError_t launch_dx_final(const DxArgs& a, hipStream_t s);
+hipError_t launch_zero(float* p, int64_t n, hipStream_t s);
 
 int gemm_block_m(int dtype);                           // BM of the expert GEMM tiles
 int gemm_block_n(int dtype, int act);                  // output columns per tile

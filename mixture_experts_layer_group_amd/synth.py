@@ -86,3 +86,16 @@ class Inputs:
 
 def make_inputs(cfg, seed=None):
     return Inputs(cfg, seed)
+
+
+def upstream_grad(cfg, seed=None):
+    """Seeded upstream gradient dy [N, M] ~ N(0, 1) for the backward pass, drawn from its own
+    stream (SeedSequence entropy [seed, 1]) so the forward inputs are unchanged.  Returns
+    (fp32 values, bf16 bits or None), rounded like the other inputs for bf16 layers."""
+    seed = cfg.get("seed", 0) if seed is None else seed
+    rng = np.random.default_rng([seed, 1])
+    dy = _normal(rng, (cfg["n_tokens"], cfg["d_model"]), 1.0)
+    if cfg["dtype"] == 1:
+        bits = round_to_bf16_bits(dy)
+        return bf16_bits_to_f32(bits), bits
+    return dy, None

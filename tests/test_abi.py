@@ -27,7 +27,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     declared = binding.header_functions()
     assert {"moe_forward", "moe_route", "moe_workspace_size", "moe_strerror",
-            "moe_abi_version", "moe_forward_timed"} <= set(declared)
+            "moe_abi_version", "moe_forward_timed", "moe_backward",
+            "moe_backward_workspace_size"} <= set(declared)
     out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (moe_\w+)", out))
@@ -172,3 +173,43 @@ def test_null_cfg_rejected(lib):
     n = ctypes.c_size_t(0)
     assert lib.moe_workspace_size(None, ctypes.byref(n)) == binding.MOE_EINVAL
     assert lib.moe_forward(None, *([None] * 9), None, 0, None) == binding.MOE_EINVAL
+
+
+def _bwd_call(cfg, **over):
+    a = dict(x=FakeTensor(0x20000000), Wg=FakeTensor(0x21000000), bg=None,
+             W1=FakeTensor(0x22000000), W2=FakeTensor(0x23000000), u=FakeTensor(0x24000000),
+             dy=FakeTensor(0x25000000), coefs=(0.1, 0.01, 0.0), dx=FakeTensor(0x29000000),
+             dWg=FakeTensor(0x2a000000), dbg=None, dW1=FakeTensor(0x2b000000),
+             dW2=FakeTensor(0x2c000000), meta=_fake_meta(),
+             ws=FakeTensor(0x27000000, binding.moe_backward_workspace_size(cfg)))
+    a.update(over)
+    binding.moe_backward(cfg, a["x"], a["Wg"], a["bg"], a["W1"], a["W2"], a["u"], a["dy"],
+                         *a["coefs"], a["dx"], a["dWg"], a["dbg"], a["dW1"], a["dW2"], a["meta"],
+                         a["ws"], stream=_NoStream())
+
+
+INVALID_BWD = [
+    ("null dy", dict(dy=FakeTensor(0)), binding.MOE_EINVAL),
+    ("null dx", dict(dx=FakeTensor(0)), binding.MOE_EINVAL),
+    ("misaligned dW1", dict(dW1=FakeTensor(0x2b000004)), binding.MOE_EINVAL),
+    ("null dWg", dict(dWg=FakeTensor(0)), binding.MOE_EINVAL),
+    ("misaligned dbg", dict(dbg=FakeTensor(0x2d000008)), binding.MOE_EINVAL),
+    ("nan coefficient", dict(coefs=(float("nan"), 0.0, 0.0)), binding.MOE_EINVAL),
+    ("inf coefficient", dict(coefs=(0.0, float("inf"), 0.0)), binding.MOE_EINVAL),
+    ("forward-sized workspace", dict(ws=FakeTensor(0x27000000, 4096)), binding.MOE_EWORKSPACE),
+    ("null u with random routing", dict(u=None), binding.MOE_EINVAL),
+    ("misaligned meta.pos", dict(meta=_fake_meta(bad="pos")), binding.MOE_EINVAL),
+]
+
+
+@pytest.mark.parametrize("what,over,code", INVALID_BWD, ids=[w for w, _, _ in INVALID_BWD])
+def test_invalid_backward_rejected_on_host(lib, what, over, code):
+    cfg = configs.SMALL["small_top2_rr"]
+    with pytest.raises(binding.MoeError) as ei:
+        _bwd_call(cfg, **over)
+    assert ei.value.code == code, what
+
+
+def test_backward_workspace_covers_forward(lib):
+    for cfg in list(configs.SMALL.values()) + list(configs.WORKLOADS.values()):
+        assert binding.moe_backward_workspace_size(cfg) > binding.moe_workspace_size(cfg)
