@@ -122,6 +122,39 @@ def cpu_baseline(cfg, inp, budget_tokens, min_seconds=10.0, max_passes=20):
                        f"{blas_threads}")}
 
 
+def backward_timing(cfg, inp, x, Wg, W1, W2, bg, u, R, steps):
+    """Time moe_backward (routing and expert activations recomputed, all gradients) on the
+    same inputs with a seeded dy; both aux-loss coefficients nonzero.  Algorithmic expert flops
+    of the backward proper: dgrad + wgrad = 2x the forward FFN's (the recompute adds 1x)."""
+    import torch
+    dy32, dybits = synth.upstream_grad(cfg)
+    dy = (torch.from_numpy(dybits.view(np.int16)).cuda().view(torch.bfloat16)
+          if dybits is not None else torch.from_numpy(dy32).cuda())
+    ws = torch.empty(binding.moe_backward_workspace_size(cfg), dtype=torch.uint8, device="cuda")
+    meta = binding.alloc_meta(cfg)
+    coefs = dict(coef_aux=0.01, coef_z=0.001, coef_dev=0.0)
+    out, _ = binding.backward(cfg, x, Wg, W1, W2, dy, bg=bg, u=u, workspace=ws, meta=meta,
+                              **coefs)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        binding.moe_backward(cfg, x, Wg, bg, W1, W2, u, dy, coefs["coef_aux"], coefs["coef_z"],
+                             coefs["coef_dev"], out["dx"], out["dWg"], out["dbg"], out["dW1"],
+                             out["dW2"], meta, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    N, M, H, Es = cfg["n_tokens"], cfg["d_model"], cfg["d_ff"], cfg["n_shared"]
+    gl = 2 if cfg["act"] == configs.ACT_SWIGLU else 1
+    fwd_ffn = (gl + 1) * 2.0 * M * H * (R + N * Es)
+    return {"ms": round(ms, 4), "tokens_per_s": round(N / (ms * 1e-3), 1), "steps": steps,
+            "ffn_flops_backward": 2 * fwd_ffn, "ffn_flops_recompute": fwd_ffn,
+            "tflops_backward_alg": round(2 * fwd_ffn / (ms * 1e-3) / 1e12, 2),
+            "tflops_incl_recompute": round(3 * fwd_ffn / (ms * 1e-3) / 1e12, 2),
+            "workspace_bytes": ws.numel()}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -131,6 +164,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=16384)
     ap.add_argument("--copies", type=int, default=4, help="rotating copies of x and y")
+    ap.add_argument("--backward-steps", type=int, default=10,
+                    help="timed moe_backward calls reported beside the forward (0: skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run 3 device-to-device copies of 1 GiB (the known-size kernel "
                          "that scales the HBM byte counters) and exit")
@@ -298,6 +333,8 @@ def main():
         "aux_loss": float(aux[0].cpu()),
     }
     ev.destroy([e for evs in events for e in evs] + warm)
+    if args.backward_steps > 0:
+        out["backward"] = backward_timing(cfg, inp, x0, Wg, W1, W2, bg, u, R, args.backward_steps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample)
     print(json.dumps(out), flush=True)

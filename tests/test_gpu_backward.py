@@ -43,6 +43,32 @@ def run_backward(cfg, coefs=COEFS, inp=None, seed=None):
     return g, inp, dy32
 
 
+# ReLU' is a decision on the sign of the pre-activation, which the GPU computes with fp32
+# accumulation and the oracle in fp64: for |z| within the accumulation error of 0 either
+# side's decision is valid.  Such a decision moves a whole row dW1[e][h][:] (one term of its
+# sum over rows), so the hidden units with an oracle pre-activation |z| < RELU_DELTA (about
+# 1000x the GPU's accumulation error) are left out of the dW1 comparison and counted.
+RELU_DELTA = 1e-4
+
+
+def relu_ambiguous_rows(cfg, inp, r):
+    E, Es, H = cfg["n_experts"], cfg["n_shared"], cfg["d_ff"]
+    mask = np.zeros((E + Es, np.shape(inp.W1)[1]), bool)
+    if cfg["act"] != 0:
+        return mask
+    x = np.asarray(inp.x, np.float64)
+    kept = r["pos"] >= 0
+    for e in range(E):
+        rows = np.nonzero((kept & (r["topk_idx"] == e)).any(axis=1))[0]
+        if rows.size:
+            z = x[rows] @ np.asarray(inp.W1[e], np.float64).T
+            mask[e] = (np.abs(z) < RELU_DELTA).any(axis=0)
+    for q in range(Es):
+        z = x @ np.asarray(inp.W1[E + q], np.float64).T
+        mask[E + q] = (np.abs(z) < RELU_DELTA).any(axis=0)
+    return mask
+
+
 def check(cfg, coefs=COEFS, seed=None):
     from oracle import moe_backward as mb
     from oracle import moe_oracle as mo
@@ -61,9 +87,15 @@ def check(cfg, coefs=COEFS, seed=None):
                               np.asarray(r[f]).astype(np.int64)), f
     tol = G_TOL[cfg["dtype"]]
     errs = {}
-    for key in ("dx", "dWg", "dbg", "dW1", "dW2"):
+    for key in ("dx", "dWg", "dbg", "dW2"):
         errs[key] = h.rel_err(g[key], ref[key])
-    h.say(f"[gpu-bwd] {name}: {errs}")
+    amb = relu_ambiguous_rows(cfg, inp, r)
+    den = np.abs(ref["dW1"]).max()
+    d1 = np.abs(g["dW1"].astype(np.float64) - ref["dW1"])[~amb]
+    errs["dW1"] = float(d1.max() / (den if den > 0 else 1.0)) if d1.size else 0.0
+    h.say(f"[gpu-bwd] {name}: {errs} (dW1 rows with an ambiguous ReLU decision: "
+          f"{int(amb.sum())} of {amb.size})")
+    assert amb.sum() <= 0.1 * amb.size
     for key, e in errs.items():
         assert e <= tol, f"{key} rel err {e}"
     return g, ref
@@ -142,3 +174,10 @@ def test_backward_empty_batch():
     torch.cuda.synchronize()
     for t in (dWg, dW1, dW2, dbg):
         assert float(t.abs().max()) == 0.0
+
+
+@pytest.mark.parametrize("name", ["gshard_bf16", "switch_bf16"])
+def test_workload_backward(name):
+    """Full-size layers, every gradient element compared (the oracle runs the whole layer in
+    fp64 on the host: about 1 TFLOP for these two)."""
+    check(configs.WORKLOADS[name])
