@@ -315,7 +315,7 @@ int forward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* b
 struct BwdLayout {
   Layout F;
   size_t z1, o, dout, dh, dz1, dbuf, z1sh, dhsh, dz1sh, w1t, w2t, doT, hT, dz1T, bufT, dyT,
-      xT, hshT, dz1shT, dl, dw, part, src0, cnt, dst0, segblk, width, e2, e1, total;
+      xT, hshT, dz1shT, dl, dw, part, partb, src0, cnt, dst0, segblk, width, e2, e1, total;
   int64_t H1, RT, Npad, nchunks;
 };
 
@@ -365,6 +365,7 @@ int make_bwd_layout(const moe_cfg* c, BwdLayout* B) {
   B->dl = take(static_cast<size_t>(N * E) * 4);
   B->dw = take(static_cast<size_t>(N * k) * 4);
   B->part = take(static_cast<size_t>(B->nchunks * E * M) * 4);
+  B->partb = take(static_cast<size_t>(B->nchunks * E) * 4);
   B->src0 = take(static_cast<size_t>(E) * 4);
   B->cnt = take(static_cast<size_t>(E) * 4);
   B->dst0 = take(static_cast<size_t>(E) * 4);
@@ -565,7 +566,8 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
                    static_cast<int>(k), c->residual, dt};
     rc = status_of(moe::launch_dx_final(da, s));
     if (rc) return rc;
-    moe::DwgArgs wa{ra.dl, x, reinterpret_cast<float*>(ws + B.part), dWg, dbg,
+    moe::DwgArgs wa{ra.dl, x, reinterpret_cast<float*>(ws + B.part),
+                    reinterpret_cast<float*>(ws + B.partb), dWg, dbg,
                     static_cast<int>(N), static_cast<int>(E), static_cast<int>(M),
                     static_cast<int>(B.nchunks), dt};
     rc = status_of(moe::launch_dwg(wa, s));

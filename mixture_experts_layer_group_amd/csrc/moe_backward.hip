@@ -49,54 +49,99 @@ __device__ __forceinline__ float swish_grad(float z) {
   return s * (1.0f + z * (1.0f - s));
 }
 
+// 16-byte vectors of the layer dtype: 8 bf16 or 4 fp32 values.
+template <int DT>
+struct Vec {
+  static constexpr int N = DT == 1 ? 8 : 4;
+  float v[N];
+  __device__ __forceinline__ void load(const void* p, int64_t i) {  // i: element index
+    const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p) + i * (DT == 1 ? 2 : 4));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (DT == 1) {
+        v[2 * q] = __uint_as_float(w[q] << 16);
+        v[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+      } else {
+        v[q] = __uint_as_float(w[q]);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(void* p, int64_t i) const {
+    u32x4 w;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      w[q] = DT == 1 ? pack_bf16x2(v[2 * q], v[2 * q + 1]) : __float_as_uint(v[q]);
+    *reinterpret_cast<u32x4*>(static_cast<char*>(p) + i * (DT == 1 ? 2 : 4)) = w;
+  }
+};
+
 // h = act(z) from the pre-activations: per row, nexp blocks of H1 inputs -> H outputs
-// (gated: h = Swish(g) * u with g, u the two halves of the block).
+// (gated: h = Swish(g) * u with g, u the two halves of the block); 16 bytes per thread.
 template <int DT>
 __global__ __launch_bounds__(256) void act_fwd_kernel(BwdEltArgs a) {
+  constexpr int V = Vec<DT>::N;
   const int rows = rows_of(a);
   const int64_t W = static_cast<int64_t>(a.nexp) * a.H;
-  const int64_t total = static_cast<int64_t>(rows) * W;
+  const int64_t total = static_cast<int64_t>(rows) * W / V;
   const int H1 = a.act == kActSwiglu ? 2 * a.H : a.H;
-  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < total; i += static_cast<int64_t>(gridDim.x) * 256) {
+  for (int64_t iv = blockIdx.x * 256ll + threadIdx.x; iv < total; iv += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t i = iv * V;
     const int64_t r = i / W;
     const int c = static_cast<int>(i - r * W);
     const int q = c / a.H, cc = c - q * a.H;
     const int64_t zi = r * a.nexp * H1 + static_cast<int64_t>(q) * H1 + cc;
-    const float z = ld_elem<DT>(a.z, zi);
-    float h;
-    if (a.act == kActSwiglu)
-      h = swish(z) * ld_elem<DT>(a.z, zi + a.H);
-    else if (a.act == kActGelu)
-      h = gelu_erf(z);
-    else
-      h = fmaxf(z, 0.0f);
-    st_elem<DT>(a.h, i, h);
+    Vec<DT> z, h;
+    z.load(a.z, zi);
+    if (a.act == kActSwiglu) {
+      Vec<DT> u;
+      u.load(a.z, zi + a.H);
+#pragma unroll
+      for (int x = 0; x < V; ++x) h.v[x] = swish(z.v[x]) * u.v[x];
+    } else if (a.act == kActGelu) {
+#pragma unroll
+      for (int x = 0; x < V; ++x) h.v[x] = gelu_erf(z.v[x]);
+    } else {
+#pragma unroll
+      for (int x = 0; x < V; ++x) h.v[x] = fmaxf(z.v[x], 0.0f);
+    }
+    h.store(a.h, i);
   }
 }
 
-// dz = dh * act'(z); gated: dg = dh * u * Swish'(g), du = dh * Swish(g).
+// dz = dh * act'(z); gated: dg = dh * u * Swish'(g), du = dh * Swish(g); 16 bytes per thread.
 template <int DT>
 __global__ __launch_bounds__(256) void act_bwd_kernel(BwdEltArgs a) {
+  constexpr int V = Vec<DT>::N;
   const int rows = rows_of(a);
   const int64_t W = static_cast<int64_t>(a.nexp) * a.H;
-  const int64_t total = static_cast<int64_t>(rows) * W;
+  const int64_t total = static_cast<int64_t>(rows) * W / V;
   const int H1 = a.act == kActSwiglu ? 2 * a.H : a.H;
-  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < total; i += static_cast<int64_t>(gridDim.x) * 256) {
+  for (int64_t iv = blockIdx.x * 256ll + threadIdx.x; iv < total; iv += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t i = iv * V;
     const int64_t r = i / W;
     const int c = static_cast<int>(i - r * W);
     const int q = c / a.H, cc = c - q * a.H;
     const int64_t zi = r * a.nexp * H1 + static_cast<int64_t>(q) * H1 + cc;
-    const float dh = ld_elem<DT>(a.dh, i);
-    const float z = ld_elem<DT>(a.z, zi);
+    Vec<DT> dh, z, out;
+    dh.load(a.dh, i);
+    z.load(a.z, zi);
     if (a.act == kActSwiglu) {
-      const float u = ld_elem<DT>(a.z, zi + a.H);
-      st_elem<DT>(a.dz, zi, dh * u * swish_grad(z));
-      st_elem<DT>(a.dz, zi + a.H, dh * swish(z));
+      Vec<DT> u, du;
+      u.load(a.z, zi + a.H);
+#pragma unroll
+      for (int x = 0; x < V; ++x) {
+        out.v[x] = dh.v[x] * u.v[x] * swish_grad(z.v[x]);
+        du.v[x] = dh.v[x] * swish(z.v[x]);
+      }
+      du.store(a.dz, zi + a.H);
     } else if (a.act == kActGelu) {
-      st_elem<DT>(a.dz, zi, dh * gelu_grad(z));
+#pragma unroll
+      for (int x = 0; x < V; ++x) out.v[x] = dh.v[x] * gelu_grad(z.v[x]);
     } else {
-      st_elem<DT>(a.dz, zi, z > 0.0f ? dh : 0.0f);
+#pragma unroll
+      for (int x = 0; x < V; ++x) out.v[x] = z.v[x] > 0.0f ? dh.v[x] : 0.0f;
     }
+    out.store(a.dz, zi);
   }
 }
 
@@ -332,9 +377,14 @@ __global__ __launch_bounds__(256) void dwg_partial_kernel(DwgArgs a) {
 #pragma unroll
   for (int c = 0; c < 8; ++c)
     if (e0 + c < a.E) a.part[(static_cast<int64_t>(ch) * a.E + e0 + c) * a.M + m] = acc[c];
+  if (blockIdx.y == 0 && threadIdx.x < 8 && e0 + threadIdx.x < a.E) {  // dbg chunk partials
+    float sb = 0.0f;
+    for (int r = 0; r < nn; ++r) sb += dls[r][threadIdx.x];
+    a.partb[static_cast<int64_t>(ch) * a.E + e0 + threadIdx.x] = sb;
+  }
 }
 
-// dWg = sum of the partials over chunks in order; dbg_e = sum_n dl[n][e] (one wave per e).
+// dWg = sum of the partials over chunks in order; dbg likewise from the chunk column sums.
 __global__ __launch_bounds__(256) void dwg_reduce_kernel(DwgArgs a) {
   const int64_t i = blockIdx.x * 256ll + threadIdx.x;
   const int64_t EM = static_cast<int64_t>(a.E) * a.M;
@@ -343,14 +393,10 @@ __global__ __launch_bounds__(256) void dwg_reduce_kernel(DwgArgs a) {
     for (int ch = 0; ch < a.nchunks; ++ch) s += a.part[ch * EM + i];
     a.dWg[i] = s;
   }
-  if (a.dbg && blockIdx.x < static_cast<unsigned>((a.E + 3) / 4)) {
-    const int e = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-    if (e < a.E) {
-      float s = 0.0f;
-      for (int n = lane; n < a.N; n += 64) s += a.dl[static_cast<int64_t>(n) * a.E + e];
-      s = wave_sum(s);
-      if (lane == 0) a.dbg[e] = s;
-    }
+  if (a.dbg && i < a.E) {
+    float s = 0.0f;
+    for (int ch = 0; ch < a.nchunks; ++ch) s += a.partb[static_cast<int64_t>(ch) * a.E + i];
+    a.dbg[i] = s;
   }
 }
 
@@ -473,7 +519,7 @@ hipError_t launch_dwg(const DwgArgs& a, hipStream_t s) {
       hipLaunchKernelGGL(dwg_partial_kernel<0>, g1, dim3(256), 0, s, a);
   }
   const int64_t em = static_cast<int64_t>(a.E) * a.M;
-  const int64_t blocks = std::max<int64_t>((em + 255) / 256, (a.E + 3) / 4);
+  const int64_t blocks = std::max<int64_t>((em + 255) / 256, 1);
   hipLaunchKernelGGL(dwg_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -184,7 +184,7 @@ struct RouterBwdArgs {
 };
 
 struct DwgArgs {           // dWg = dl^T x (fp32, two passes), dbg = column sums of dl
-  const float* dl; const void* x; float* part; float* dWg; float* dbg;
+  const float* dl; const void* x; float* part; float* partb; float* dWg; float* dbg;
   int N, E, M, nchunks, dtype;
 };
 
