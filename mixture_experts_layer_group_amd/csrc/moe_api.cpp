@@ -315,8 +315,8 @@ int forward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* b
 struct BwdLayout {
   Layout F;
   size_t z1, o, dout, dh, dz1, dbuf, z1sh, dhsh, dz1sh, w1t, w2t, doT, hT, dz1T, bufT, dyT,
-      xT, hshT, dz1shT, dl, dw, part, partb, src0, cnt, dst0, segblk, width, e2, e1, total;
-  int64_t H1, RT, Npad, nchunks;
+      xT, hshT, dz1shT, dl, dw, part, partb, dlp, wgt, dxrt, src0, cnt, dst0, segblk, width, e2, e1, total;
+  int64_t H1, RT, Npad, nchunks, Ep;
 };
 
 int make_bwd_layout(const moe_cfg* c, BwdLayout* B) {
@@ -366,6 +366,10 @@ int make_bwd_layout(const moe_cfg* c, BwdLayout* B) {
   B->dw = take(static_cast<size_t>(N * k) * 4);
   B->part = take(static_cast<size_t>(B->nchunks * E * M) * 4);
   B->partb = take(static_cast<size_t>(B->nchunks * E) * 4);
+  B->Ep = (E + 63) / 64 * 64;
+  B->dlp = take(static_cast<size_t>(N * B->Ep) * esz);
+  B->wgt = take(static_cast<size_t>(M * B->Ep) * esz);
+  B->dxrt = take(static_cast<size_t>(N * M) * esz);
   B->src0 = take(static_cast<size_t>(E) * 4);
   B->cnt = take(static_cast<size_t>(E) * 4);
   B->dst0 = take(static_cast<size_t>(E) * 4);
@@ -561,9 +565,18 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
     ra.n_eg = c->expert_groups;
     rc = status_of(moe::launch_router_bwd(ra, s));
     if (rc) return rc;
-    moe::DxArgs da{dy, ws + B.dbuf, Es ? ws + L.osh : nullptr, ra.dl, Wg, m->row, dx,
-                   static_cast<int>(N), static_cast<int>(M), static_cast<int>(E),
-                   static_cast<int>(k), c->residual, dt};
+    // router term of dx: dxrt = dl Wg as a dense GEMM over the padded expert axis
+    moe::RouterPrepArgs pa{ra.dl, Wg, ws + B.dlp, ws + B.wgt, static_cast<int>(N),
+                           static_cast<int>(E), static_cast<int>(B.Ep), static_cast<int>(M), dt};
+    rc = status_of(moe::launch_router_dgrad_prep(pa, s));
+    if (rc) return rc;
+    rc = gemm(dense_problem(ws + B.dlp, B.Ep, ws + B.wgt, B.Ep, ws + B.dxrt, M,
+                            static_cast<int>(M), static_cast<int>(B.Ep), static_cast<int>(N), BM),
+              nullptr);
+    if (rc) return rc;
+    moe::DxArgs da{dy, ws + B.dbuf, Es ? ws + L.osh : nullptr, ws + B.dxrt, m->row, dx,
+                   static_cast<int>(N), static_cast<int>(M), static_cast<int>(k), c->residual,
+                   dt};
     rc = status_of(moe::launch_dx_final(da, s));
     if (rc) return rc;
     moe::DwgArgs wa{ra.dl, x, reinterpret_cast<float*>(ws + B.part),

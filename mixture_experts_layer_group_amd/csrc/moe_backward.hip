@@ -400,40 +400,58 @@ __global__ __launch_bounds__(256) void dwg_reduce_kernel(DwgArgs a) {
   }
 }
 
-// dx_n = [res] dy_n + sum_j dx_rows[row_nj] + dx_shared_n + sum_e dl_ne Wg_e, summed in
-// that order in fp32; 16 tokens per block, dl rows staged in LDS.
+// dx_n = [res] dy_n + sum_j dx_rows[row_nj] + dx_shared_n + (dl Wg)_n, summed in that order
+// in fp32; the router term comes from a GEMM (dxrt).  One wave per token, 16 bytes per lane.
 template <int DT>
 __global__ __launch_bounds__(256) void dx_final_kernel(DxArgs a) {
-  __shared__ float dls[16][kMaxExperts];
-  __shared__ int rows_s[16][kMaxTopK];
-  const int n0 = blockIdx.x * 16, nt = min(16, a.N - n0), E = a.E, k = a.k;
-  for (int i = threadIdx.x; i < 16 * E; i += 256) {
-    const int r = i / E, e = i - r * E;
-    dls[r][e] = r < nt ? a.dl[static_cast<int64_t>(n0 + r) * E + e] : 0.0f;
-  }
-  for (int i = threadIdx.x; i < 16 * k; i += 256) {
-    const int r = i / k, j = i - r * k;
-    rows_s[r][j] = r < nt ? a.row[static_cast<int64_t>(n0 + r) * k + j] : -1;
-  }
-  __syncthreads();
-  for (int m = threadIdx.x; m < a.M; m += 256) {
-    float acc[16];
+  constexpr int V = Vec<DT>::N;
+  const int lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= a.N) return;
+  int rows[kMaxTopK];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-    for (int e = 0; e < E; ++e) {
-      const float wv = ld_elem<DT>(a.Wg, static_cast<int64_t>(e) * a.M + m);
+  for (int j = 0; j < kMaxTopK; ++j)
+    rows[j] = j < a.k ? a.row[static_cast<int64_t>(n) * a.k + j] : -1;
+  const int64_t base = static_cast<int64_t>(n) * a.M;
+  for (int m = lane * V; m < a.M; m += 64 * V) {
+    Vec<DT> acc, t;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = fmaf(dls[r][e], wv, acc[r]);
+    for (int x = 0; x < V; ++x) acc.v[x] = 0.0f;
+    if (a.residual) acc.load(a.dy, base + m);
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (rows[j] < 0) continue;
+      t.load(a.dxr, static_cast<int64_t>(rows[j]) * a.M + m);
+#pragma unroll
+      for (int x = 0; x < V; ++x) acc.v[x] += t.v[x];
     }
-    for (int r = 0; r < nt; ++r) {
-      const int64_t n = n0 + r;
-      float v = a.residual ? ld_elem<DT>(a.dy, n * a.M + m) : 0.0f;
-      for (int j = 0; j < k; ++j) {
-        const int row = rows_s[r][j];
-        if (row >= 0) v += ld_elem<DT>(a.dxr, static_cast<int64_t>(row) * a.M + m);
-      }
-      if (a.dxsh) v += ld_elem<DT>(a.dxsh, n * a.M + m);
-      st_elem<DT>(a.dx, n * a.M + m, v + acc[r]);
+    if (a.dxsh) {
+      t.load(a.dxsh, base + m);
+#pragma unroll
+      for (int x = 0; x < V; ++x) acc.v[x] += t.v[x];
+    }
+    t.load(a.dxrt, base + m);
+#pragma unroll
+    for (int x = 0; x < V; ++x) acc.v[x] += t.v[x];
+    acc.store(a.dx, base + m);
+  }
+}
+
+// The router's dgrad operands for the GEMM dxrt = dlp . WgT^T: dlp [N, Ep] = dl in the layer
+// dtype, WgT [M, Ep] = Wg^T, both zero beyond E (Ep = E rounded up to 64).
+template <int DT>
+__global__ __launch_bounds__(256) void router_dgrad_prep_kernel(RouterPrepArgs a) {
+  const int64_t nd = static_cast<int64_t>(a.N) * a.Ep, nw = static_cast<int64_t>(a.M) * a.Ep;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < nd + nw;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    if (i < nd) {
+      const int64_t r = i / a.Ep;
+      const int e = static_cast<int>(i - r * a.Ep);
+      st_elem<DT>(a.dlp, i, e < a.E ? a.dl[r * a.E + e] : 0.0f);
+    } else {
+      const int64_t j = i - nd, m = j / a.Ep;
+      const int e = static_cast<int>(j - m * a.Ep);
+      st_elem<DT>(a.wgt, j, e < a.E ? ld_elem<DT>(a.Wg, static_cast<int64_t>(e) * a.M + m) : 0.0f);
     }
   }
 }
@@ -524,8 +542,17 @@ hipError_t launch_dwg(const DwgArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t launch_router_dgrad_prep(const RouterPrepArgs& a, hipStream_t s) {
+  const int64_t n = (static_cast<int64_t>(a.N) + a.M) * a.Ep;
+  if (a.dtype == 1)
+    hipLaunchKernelGGL(router_dgrad_prep_kernel<1>, dim3(grid_for(n)), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(router_dgrad_prep_kernel<0>, dim3(grid_for(n)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_dx_final(const DxArgs& a, hipStream_t s) {
-  const int grid = (a.N + 15) / 16;
+  const int grid = (a.N + 3) / 4;
   if (grid == 0) return hipSuccess;
   if (a.dtype == 1)
     hipLaunchKernelGGL(dx_final_kernel<1>, dim3(grid), dim3(256), 0, s, a);

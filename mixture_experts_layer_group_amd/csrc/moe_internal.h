@@ -188,10 +188,15 @@ struct DwgArgs {           // dWg = dl^T x (fp32, two passes), dbg = column sums
   int N, E, M, nchunks, dtype;
 };
 
-struct DxArgs {            // dx = [res] dy + sum_j dx_rows[row] + dx_shared + dl Wg
-  const void* dy; const void* dxr; const void* dxsh; const float* dl; const void* Wg;
+struct DxArgs {            // dx = [res] dy + sum_j dx_rows[row] + dx_shared + router term
+  const void* dy; const void* dxr; const void* dxsh; const void* dxrt;
   const int32_t* row; void* dx;
-  int N, M, E, k, residual, dtype;
+  int N, M, k, residual, dtype;
+};
+
+struct RouterPrepArgs {    // dlp [N, Ep] = dl, wgt [M, Ep] = Wg^T (layer dtype, zero-padded)
+  const float* dl; const void* Wg; void* dlp; void* wgt;
+  int N, E, Ep, M, dtype;
 };
 
 hipError_t launch_act_fwd(const BwdEltArgs& a, int64_t max_elems, hipStream_t s);
@@ -202,6 +207,7 @@ hipError_t launch_mat_transpose(const MatTransposeArgs& a, hipStream_t s);
 hipError_t launch_bwd_setup(const BwdSetupArgs& a, hipStream_t s);
 hipError_t launch_router_bwd(const RouterBwdArgs& a, hipStream_t s);
 hipError_t launch_dwg(const DwgArgs& a, hipStream_t s);
+hipError_t launch_router_dgrad_prep(const RouterPrepArgs& a, hipStream_t s);
 hipError_t launch_dx_final(const DxArgs& a, hipStream_t s);
 hipError_t launch_zero(float* p, int64_t n, hipStream_t s);
 
