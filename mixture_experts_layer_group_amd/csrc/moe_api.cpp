@@ -315,7 +315,7 @@ int forward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* b
 struct BwdLayout {
   Layout F;
   size_t z1, o, dout, dh, dz1, dbuf, z1sh, dhsh, dz1sh, w1t, w2t, doT, hT, dz1T, bufT, dyT,
-      xT, hshT, dz1shT, dl, dw, part, partb, dlp, wgt, dxrt, src0, cnt, dst0, segblk, width, e2, e1, total;
+      xT, hshT, dz1shT, dl, dw, partb, dlp, wgt, dxrt, dlT, src0, cnt, dst0, segblk, width, e2, e1, total;
   int64_t H1, RT, Npad, nchunks, Ep;
 };
 
@@ -331,10 +331,11 @@ int make_bwd_layout(const moe_cfg* c, BwdLayout* B) {
   B->RT = L.Rmax + 128 * E;                       // per-expert K padded to 128
   B->Npad = (N + 127) / 128 * 128;
   B->nchunks = (N + 255) / 256;
+  B->Ep = (E + 63) / 64 * 64;
   const int64_t lim = (int64_t{1} << 31) - 1;
   if (L.rows_alloc * H1 > lim || (E + Es) * H1 * M > lim || H1 * B->RT > lim ||
       std::max(M, Es * H1) * std::max(B->RT, B->Npad) > lim || N * Es * H1 > lim ||
-      B->nchunks * E * M > lim)
+      B->Ep * B->Npad > lim)
     return MOE_EUNSUPPORTED;
   size_t off = L.total;
   auto take = [&](size_t bytes) {
@@ -359,17 +360,16 @@ int make_bwd_layout(const moe_cfg* c, BwdLayout* B) {
   B->dz1T = take(static_cast<size_t>(H1 * B->RT) * esz);
   B->bufT = take(static_cast<size_t>(M * B->RT) * esz);
   B->dyT = take(static_cast<size_t>(Es ? M * B->Npad : 0) * esz);
-  B->xT = take(static_cast<size_t>(Es ? M * B->Npad : 0) * esz);
+  B->xT = take(static_cast<size_t>(M * B->Npad) * esz);
   B->hshT = take(static_cast<size_t>(Es * H * B->Npad) * esz);
   B->dz1shT = take(static_cast<size_t>(Es * H1 * B->Npad) * esz);
   B->dl = take(static_cast<size_t>(N * E) * 4);
   B->dw = take(static_cast<size_t>(N * k) * 4);
-  B->part = take(static_cast<size_t>(B->nchunks * E * M) * 4);
   B->partb = take(static_cast<size_t>(B->nchunks * E) * 4);
-  B->Ep = (E + 63) / 64 * 64;
   B->dlp = take(static_cast<size_t>(N * B->Ep) * esz);
   B->wgt = take(static_cast<size_t>(M * B->Ep) * esz);
   B->dxrt = take(static_cast<size_t>(N * M) * esz);
+  B->dlT = take(static_cast<size_t>(B->Ep * B->Npad) * esz);
   B->src0 = take(static_cast<size_t>(E) * 4);
   B->cnt = take(static_cast<size_t>(E) * 4);
   B->dst0 = take(static_cast<size_t>(E) * 4);
@@ -579,11 +579,9 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
                    dt};
     rc = status_of(moe::launch_dx_final(da, s));
     if (rc) return rc;
-    moe::DwgArgs wa{ra.dl, x, reinterpret_cast<float*>(ws + B.part),
-                    reinterpret_cast<float*>(ws + B.partb), dWg, dbg,
-                    static_cast<int>(N), static_cast<int>(E), static_cast<int>(M),
-                    static_cast<int>(B.nchunks), dt};
-    rc = status_of(moe::launch_dwg(wa, s));
+    moe::DwgArgs wa{ra.dl, reinterpret_cast<float*>(ws + B.partb), dbg, static_cast<int>(N),
+                    static_cast<int>(E), static_cast<int>(B.nchunks)};
+    rc = status_of(moe::launch_dbg(wa, s));
     if (rc) return rc;
   }
   // 9. weight gradients: per-expert K = kept rows padded to 128 (transposed compact buffers)
@@ -618,9 +616,18 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
     if ((rc = seg_t(ws + L.h, B.hT, static_cast<int>(H)))) return rc;
     if ((rc = seg_t(ws + B.dz1, B.dz1T, static_cast<int>(H1)))) return rc;
     if ((rc = seg_t(ws + L.buf, B.bufT, static_cast<int>(M)))) return rc;
+    // dWg [E, M] = dl^T x over the padded token axis (fp32 out)
+    if ((rc = dense_t(x, B.xT, static_cast<int>(M)))) return rc;
+    if ((rc = dense_t(ws + B.dlp, B.dlT, static_cast<int>(B.Ep)))) return rc;
+    {
+      moe::GemmProblem p = dense_problem(ws + B.dlT, B.Npad, ws + B.xT, B.Npad, dWg, M,
+                                         static_cast<int>(M), static_cast<int>(B.Npad),
+                                         static_cast<int>(E), BM);
+      p.out_f32 = 1;
+      if ((rc = gemm(p, nullptr))) return rc;
+    }
     if (Es) {
       if ((rc = dense_t(dy, B.dyT, static_cast<int>(M)))) return rc;
-      if ((rc = dense_t(x, B.xT, static_cast<int>(M)))) return rc;
       if ((rc = dense_t(ws + L.hsh, B.hshT, static_cast<int>(Es * H)))) return rc;
       if ((rc = dense_t(ws + B.dz1sh, B.dz1shT, static_cast<int>(Es * H1)))) return rc;
     }

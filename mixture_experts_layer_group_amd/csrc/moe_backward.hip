@@ -146,9 +146,10 @@ __global__ __launch_bounds__(256) void act_bwd_kernel(BwdEltArgs a) {
 }
 
 // One wave per token: dw_nj = <dy_n, o_row> for kept slots (0 otherwise), and
-// do_row = w_nj dy_n into the compact expert-major buffer.
+// do_row = w_nj dy_n into the compact expert-major buffer; 16 bytes per lane.
 template <int DT>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(CombineBwdArgs a) {
+  constexpr int V = Vec<DT>::N;
   const int lane = threadIdx.x & 63;
   const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (n >= a.N) return;
@@ -159,10 +160,16 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(CombineBwdArgs a) {
     if (r >= 0) {
       const float w = a.topk_w[static_cast<int64_t>(n) * a.k + j];
       const int64_t ro = static_cast<int64_t>(r) * a.M;
-      for (int m = lane; m < a.M; m += 64) {
-        const float g = ld_elem<DT>(a.dy, rowoff + m);
-        d = fmaf(g, ld_elem<DT>(a.o, ro + m), d);
-        st_elem<DT>(a.dout, ro + m, w * g);
+      for (int m = lane * V; m < a.M; m += 64 * V) {
+        Vec<DT> g, o, dout;
+        g.load(a.dy, rowoff + m);
+        o.load(a.o, ro + m);
+#pragma unroll
+        for (int x = 0; x < V; ++x) {
+          d = fmaf(g.v[x], o.v[x], d);
+          dout.v[x] = w * g.v[x];
+        }
+        dout.store(a.dout, ro + m);
       }
       d = wave_sum(d);
     }
@@ -177,7 +184,8 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(CombineBwdArgs a) {
 template <int DT>
 __global__ __launch_bounds__(256) void seg_transpose_kernel(TransposeArgs a) {
   typedef typename std::conditional<DT == 1, uint16_t, float>::type E_t;
-  __shared__ E_t tile[64][65];
+  constexpr int V = 16 / sizeof(E_t);   // elements per 16-byte load
+  __shared__ E_t tile[64][64 + 2];
   const int cb = blockIdx.x;          // 64-column block of XT
   const int wb = blockIdx.y;          // 64-row block of XT (= column block of X)
   const int ncols = a.ncols_ptr ? *a.ncols_ptr : a.ncols;
@@ -189,17 +197,25 @@ __global__ __launch_bounds__(256) void seg_transpose_kernel(TransposeArgs a) {
   const E_t* X = static_cast<const E_t*>(a.X);
   E_t* XT = static_cast<E_t*>(a.XT);
   const int t = threadIdx.x;
-  for (int idx = t; idx < 64 * 64; idx += 256) {
-    const int r = idx >> 6, c = idx & 63;   // r: source row within the tile, c: column of X
+  // load: 64 source rows x 64 columns, V columns per thread and step
+  for (int idx = t; idx < 64 * 64 / V; idx += 256) {
+    const int r = idx / (64 / V), c = (idx % (64 / V)) * V;
     const int i = cb * 64 + r - dst0;       // index inside the segment
-    E_t v = E_t(0);
-    if (i < cnt) v = X[static_cast<int64_t>(src0 + i) * a.W + wb * 64 + c];
-    tile[r][c] = v;
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (i < cnt) v = *reinterpret_cast<const u32x4*>(X + static_cast<int64_t>(src0 + i) * a.W + wb * 64 + c);
+    const E_t* e = reinterpret_cast<const E_t*>(&v);
+#pragma unroll
+    for (int x = 0; x < V; ++x) tile[r][c + x] = e[x];
   }
   __syncthreads();
-  for (int idx = t; idx < 64 * 64; idx += 256) {
-    const int w = idx >> 6, c = idx & 63;
-    XT[static_cast<int64_t>(wb * 64 + w) * a.ldT + cb * 64 + c] = tile[c][w];
+  // store: 64 rows of XT (columns w of X) x 64 columns, V columns per thread and step
+  for (int idx = t; idx < 64 * 64 / V; idx += 256) {
+    const int w = idx / (64 / V), c = (idx % (64 / V)) * V;
+    u32x4 v;
+    E_t* e = reinterpret_cast<E_t*>(&v);
+#pragma unroll
+    for (int x = 0; x < V; ++x) e[x] = tile[c + x][w];
+    *reinterpret_cast<u32x4*>(XT + static_cast<int64_t>(wb * 64 + w) * a.ldT + cb * 64 + c) = v;
   }
 }
 
@@ -355,49 +371,23 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(RouterBwdArgs a) {
   }
 }
 
-// dWg partial sums: block (8-expert tile, 256-column tile, 256-token chunk) computes
-// part[chunk][e][m] = sum over the chunk's tokens of dl[n][e] x[n][m], tokens in order.
-template <int DT>
-__global__ __launch_bounds__(256) void dwg_partial_kernel(DwgArgs a) {
-  __shared__ float dls[256][8];
-  const int e0 = blockIdx.x * 8, m = blockIdx.y * 256 + threadIdx.x, ch = blockIdx.z;
-  const int n0 = ch * 256, nn = min(256, a.N - n0);
-  for (int i = threadIdx.x; i < 256 * 8; i += 256) {
-    const int r = i >> 3, c = i & 7;
-    dls[r][c] = (r < nn && e0 + c < a.E) ? a.dl[static_cast<int64_t>(n0 + r) * a.E + e0 + c] : 0.0f;
-  }
-  __syncthreads();
-  if (m >= a.M) return;
-  float acc[8] = {};
-  for (int r = 0; r < nn; ++r) {
-    const float xv = ld_elem<DT>(a.x, static_cast<int64_t>(n0 + r) * a.M + m);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[c] = fmaf(dls[r][c], xv, acc[c]);
-  }
-#pragma unroll
-  for (int c = 0; c < 8; ++c)
-    if (e0 + c < a.E) a.part[(static_cast<int64_t>(ch) * a.E + e0 + c) * a.M + m] = acc[c];
-  if (blockIdx.y == 0 && threadIdx.x < 8 && e0 + threadIdx.x < a.E) {  // dbg chunk partials
+// dbg partial sums: block ch sums dl over its 256 tokens (in order) for every expert.
+__global__ __launch_bounds__(256) void dbg_partial_kernel(DwgArgs a) {
+  const int ch = blockIdx.x, n0 = ch * 256, nn = min(256, a.N - n0);
+  for (int e = threadIdx.x; e < a.E; e += 256) {
     float sb = 0.0f;
-    for (int r = 0; r < nn; ++r) sb += dls[r][threadIdx.x];
-    a.partb[static_cast<int64_t>(ch) * a.E + e0 + threadIdx.x] = sb;
+    for (int r = 0; r < nn; ++r) sb += a.dl[static_cast<int64_t>(n0 + r) * a.E + e];
+    a.partb[static_cast<int64_t>(ch) * a.E + e] = sb;
   }
 }
 
-// dWg = sum of the partials over chunks in order; dbg likewise from the chunk column sums.
-__global__ __launch_bounds__(256) void dwg_reduce_kernel(DwgArgs a) {
-  const int64_t i = blockIdx.x * 256ll + threadIdx.x;
-  const int64_t EM = static_cast<int64_t>(a.E) * a.M;
-  if (i < EM) {
-    float s = 0.0f;
-    for (int ch = 0; ch < a.nchunks; ++ch) s += a.part[ch * EM + i];
-    a.dWg[i] = s;
-  }
-  if (a.dbg && i < a.E) {
-    float s = 0.0f;
-    for (int ch = 0; ch < a.nchunks; ++ch) s += a.partb[static_cast<int64_t>(ch) * a.E + i];
-    a.dbg[i] = s;
-  }
+// dbg = sum of the chunk partials in order.
+__global__ __launch_bounds__(256) void dbg_reduce_kernel(DwgArgs a) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= a.E) return;
+  float s = 0.0f;
+  for (int ch = 0; ch < a.nchunks; ++ch) s += a.partb[static_cast<int64_t>(ch) * a.E + e];
+  a.dbg[e] = s;
 }
 
 // dx_n = [res] dy_n + sum_j dx_rows[row_nj] + dx_shared_n + (dl Wg)_n, summed in that order
@@ -528,17 +518,10 @@ hipError_t launch_router_bwd(const RouterBwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_dwg(const DwgArgs& a, hipStream_t s) {
-  const dim3 g1((a.E + 7) / 8, (a.M + 255) / 256, a.nchunks);
-  if (a.nchunks > 0) {
-    if (a.dtype == 1)
-      hipLaunchKernelGGL(dwg_partial_kernel<1>, g1, dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL(dwg_partial_kernel<0>, g1, dim3(256), 0, s, a);
-  }
-  const int64_t em = static_cast<int64_t>(a.E) * a.M;
-  const int64_t blocks = std::max<int64_t>((em + 255) / 256, 1);
-  hipLaunchKernelGGL(dwg_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
+hipError_t launch_dbg(const DwgArgs& a, hipStream_t s) {
+  if (a.nchunks == 0 || !a.dbg) return hipSuccess;
+  hipLaunchKernelGGL(dbg_partial_kernel, dim3(a.nchunks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(dbg_reduce_kernel, dim3((a.E + 255) / 256), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -183,9 +183,9 @@ struct RouterBwdArgs {
   int N, E, k, G, S, norm, n_eg;
 };
 
-struct DwgArgs {           // dWg = dl^T x (fp32, two passes), dbg = column sums of dl
-  const float* dl; const void* x; float* part; float* partb; float* dWg; float* dbg;
-  int N, E, M, nchunks, dtype;
+struct DwgArgs {           // dbg = column sums of dl (two passes, fixed order)
+  const float* dl; float* partb; float* dbg;
+  int N, E, nchunks;
 };
 
 struct DxArgs {            // dx = [res] dy + sum_j dx_rows[row] + dx_shared + router term
@@ -206,7 +206,7 @@ hipError_t launch_seg_transpose(const TransposeArgs& a, int max_cols, hipStream_
 hipError_t launch_mat_transpose(const MatTransposeArgs& a, hipStream_t s);
 hipError_t launch_bwd_setup(const BwdSetupArgs& a, hipStream_t s);
 hipError_t launch_router_bwd(const RouterBwdArgs& a, hipStream_t s);
-hipError_t launch_dwg(const DwgArgs& a, hipStream_t s);
+hipError_t launch_dbg(const DwgArgs& a, hipStream_t s);
 hipError_t launch_router_dgrad_prep(const RouterPrepArgs& a, hipStream_t s);
 hipError_t launch_dx_final(const DxArgs& a, hipStream_t s);
 hipError_t launch_zero(float* p, int64_t n, hipStream_t s);
