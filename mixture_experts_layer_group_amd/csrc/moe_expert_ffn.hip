@@ -39,6 +39,11 @@ constexpr int kThreads = 256;
 #endif
 constexpr int kGemmBK = MOE_GEMM_BK;
 constexpr int kGemmStages = MOE_GEMM_STAGES;
+// m-tiles that sweep the n-tiles together inside one XCD's range of tiles
+#ifndef MOE_GEMM_GROUP_M
+#define MOE_GEMM_GROUP_M 8
+#endif
+constexpr int kGemmGroupM = MOE_GEMM_GROUP_M;
 
 struct Job {
   const char* A;   // first row of the tile (bytes)
@@ -76,7 +81,7 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& g, Job& j) {
   const int lp = second ? pid - tot0 : pid;
   const int mts = second ? mt1 : mt0;
   const int nts = second ? nt1 : nt0;
-  constexpr int GM = 8;
+  constexpr int GM = kGemmGroupM;
   const int per_group = GM * nts;
   const int grp = lp / per_group;
   const int first = grp * GM;
