@@ -5,6 +5,8 @@ every gating flag) are compared in full.  The five reference workloads are compa
 their full sizes: routing, positions, rows and aux on every token (bit-exact / 1e-5), the
 output y on a seeded token sample plus every dropped token and one row per expert.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -177,3 +179,14 @@ def test_single_expert_is_a_dense_ffn(act):
         hid = torch.nn.functional.silu(pre[:, :H]) * pre[:, H:]
     ref = (x + torch.matmul(hid, w2.t().contiguous())).cpu().numpy()
     assert h.rel_err(g["y"], ref) <= 2e-2
+
+
+@pytest.mark.skipif(os.environ.get("MOE_FULL_PARITY") != "1",
+                    reason="full-size FFN parity: set MOE_FULL_PARITY=1 (minutes of fp64 "
+                           "oracle work on the host per layer)")
+@pytest.mark.parametrize("name", list(configs.WORKLOADS))
+def test_workload_parity_full(name):
+    """Every token of the full-size layer against the fp64 oracle (the oracle evaluates one
+    expert at a time, so host memory stays bounded)."""
+    rep = harness().full_check(configs.WORKLOADS[name], n_sample=None)[0]
+    print(f"[full-parity] {name}: {rep}", flush=True)
