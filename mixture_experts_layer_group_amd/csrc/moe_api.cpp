@@ -23,7 +23,8 @@ using moe::kRouteTokens;
 
 struct Layout {
   // byte offsets inside the workspace
-  size_t buf, h, hsh, osh, active, psum, sel, ahist, abase, ntot, Pg, Cg, tiles, ntiles, zpart;
+  size_t buf, h, hsh, osh, active, psum, sel, ahist, abase, ntot, Pg, Cg, tiles, ntiles, zpart,
+      tokrow;
   size_t total;
   // sizes
   int64_t S, nbg, Rmax, rows_alloc, max_tiles;
@@ -102,6 +103,7 @@ int make_layout(const moe_cfg* c, Layout* L) {
   L->tiles = take(static_cast<size_t>(L->max_tiles) * sizeof(moe::TileDesc));
   L->ntiles = take(16);
   L->zpart = take(static_cast<size_t>(G) * L->nbg * 8);
+  L->tokrow = take(static_cast<size_t>(L->rows_alloc) * 4);
   L->total = off;
   return MOE_OK;
 }
@@ -141,8 +143,11 @@ void record(void* const* ev, int i, hipStream_t s) {
 }
 
 // Router (or routing from given logits) + scan + offsets + positions/scatter.
+// copy_rows: also copy the kept token rows into the compact buffer (the backward reads them);
+// the forward's GEMM 1 gathers them from x through tok_of_row instead.
 int run_routing(const Run& r, const void* x, const void* Wg, const float* bg, const float* u,
-                const float* logits_in, const moe_meta* m, int bm, void* const* ev) {
+                const float* logits_in, const moe_meta* m, int bm, void* const* ev,
+                bool copy_rows) {
   const moe_cfg* c = r.c;
   const Layout& L = r.L;
   char* ws = r.ws;
@@ -180,7 +185,9 @@ int run_routing(const Run& r, const void* x, const void* Wg, const float* bg, co
   record(ev, 2, r.s);
 
   moe::PermuteArgs pa{};
-  pa.x = x; pa.topk_idx = m->topk_idx; pa.active = ra.active; pa.abase = sa.abase;
+  pa.x = copy_rows ? x : nullptr;
+  pa.tok_of_row = reinterpret_cast<int32_t*>(ws + L.tokrow);
+  pa.topk_idx = m->topk_idx; pa.active = ra.active; pa.abase = sa.abase;
   pa.count = m->count; pa.ntot = sa.ntot; pa.offset = m->offset;
   pa.tiles = reinterpret_cast<moe::TileDesc*>(ws + L.tiles);
   pa.num_tiles = reinterpret_cast<int32_t*>(ws + L.ntiles);
@@ -251,7 +258,7 @@ int forward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* b
 
   const int64_t M = c->d_model, H = c->d_ff, E = c->n_experts, Es = c->n_shared;
   const int BM = r.L.BM;
-  rc = run_routing(r, x, Wg, bg, u, nullptr, m, BM, ev);
+  rc = run_routing(r, x, Wg, bg, u, nullptr, m, BM, ev, false);
   if (rc) return rc;
 
   const Layout& L = r.L;
@@ -260,15 +267,17 @@ int forward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* b
   const int32_t* ntiles = reinterpret_cast<const int32_t*>(ws + L.ntiles);
   const int a_rows = static_cast<int>(L.rows_alloc);
 
-  // GEMM 1: h = act(buf . W1_e^T) for every expert (+ shared: h_sh = act(x . W1_sh^T)).
-  // Gated experts: h = Swish(buf . G_e^T) * (buf . U_e^T) from W1_e = [G_e; U_e] (2H rows).
+  // GEMM 1: h = act(x[tok] . W1_e^T) for every expert, the token rows gathered from x in
+  // compact (expert-major) order (+ shared: h_sh = act(x . W1_sh^T)).
+  // Gated experts: h = Swish(x . G_e^T) * (x . U_e^T) from W1_e = [G_e; U_e] (2H rows).
   const int64_t H1 = c->act == MOE_ACT_SWIGLU ? 2 * H : H;  // W1 rows per expert
   moe::GemmArgs g1{};
   g1.dtype = c->dtype;
-  g1.p0 = moe::GemmProblem{ws + L.buf, M, W1, M, H1 * M, M, 0, ws + L.h, H,
-                           static_cast<int>(H), static_cast<int>(M), a_rows, c->act,
+  g1.p0 = moe::GemmProblem{x, M, W1, M, H1 * M, M, 0, ws + L.h, H,
+                           static_cast<int>(H), static_cast<int>(M), c->n_tokens, c->act,
                            tiles, ntiles, static_cast<int>(L.max_tiles), 0,
                            static_cast<int>(H)};
+  g1.p0.a_gather = reinterpret_cast<const int32_t*>(ws + L.tokrow);
   g1.nprob = 1;
   if (Es) {
     const char* w1sh = static_cast<const char*>(W1) + E * H1 * M * L.esz;
@@ -461,7 +470,7 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
   const int BM = L.BM, dt = c->dtype;
   const size_t esz = static_cast<size_t>(L.esz);
   // 1. routing again (deterministic: the forward's routing), rows dispatched into buf
-  rc = run_routing(r, x, Wg, bg, u, nullptr, m, BM, nullptr);
+  rc = run_routing(r, x, Wg, bg, u, nullptr, m, BM, nullptr, true);
   if (rc) return rc;
   const moe::TileDesc* tiles = reinterpret_cast<const moe::TileDesc*>(ws + L.tiles);
   const int32_t* ntiles = reinterpret_cast<const int32_t*>(ws + L.ntiles);
@@ -731,7 +740,7 @@ int moe_route(const moe_cfg* cfg, const float* logits, const float* u, const moe
   if (!logits || !aligned16(logits)) return MOE_EINVAL;
   r.ws = static_cast<char*>(workspace);
   r.s = static_cast<hipStream_t>(stream);
-  rc = run_routing(r, nullptr, nullptr, nullptr, u, logits, meta, r.L.BM, nullptr);
+  rc = run_routing(r, nullptr, nullptr, nullptr, u, logits, meta, r.L.BM, nullptr, false);
   if (rc) return rc;
   moe::CombineArgs ca = combine_args(r, nullptr, nullptr, aux_loss, meta);
   return status_of(moe::launch_aux_only(ca, r.s));

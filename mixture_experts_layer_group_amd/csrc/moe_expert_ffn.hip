@@ -60,6 +60,8 @@ struct Job {
   int rows_left;   // rows readable from the tile's first row (clamp)
   int act;
   int64_t upb;     // gated problems: bytes from a gate row of B to its up row
+  const int32_t* gather;  // A row of tile row r is gather[r] (A then points at row 0), or nullptr
+  int64_t a_bytes;        // gathered A: readable bytes from A
 };
 
 // BN = output columns per tile (a gated tile computes 2 BN columns of A . B^T).
@@ -107,7 +109,10 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& g, Job& j) {
   }
   const int osz = P.out_f32 ? 4 : ESZ;
   j.lda = P.lda * ESZ;
-  j.A = static_cast<const char*>(P.A) + aoff * ESZ + static_cast<int64_t>(row0) * j.lda;
+  j.gather = P.a_gather ? P.a_gather + row0 : nullptr;
+  j.a_bytes = static_cast<int64_t>(P.a_rows) * j.lda;
+  j.A = static_cast<const char*>(P.A) + aoff * ESZ +
+        (P.a_gather ? 0 : static_cast<int64_t>(row0) * j.lda);
   j.ldb = P.ldb * ESZ;
   const int c0 = nt * BN;
   // first B row of the tile: output column c0, or for gated problems its gate row
@@ -230,7 +235,7 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
   const int wm = w / WN, wn = w % WN;
 
   const uint32_t lda = static_cast<uint32_t>(j.lda), ldb = static_cast<uint32_t>(j.ldb);
-  const rsrc_t ra_rs = make_rsrc(j.A, static_cast<int64_t>(j.nrows) * j.lda);
+  const rsrc_t ra_rs = make_rsrc(j.A, j.gather ? j.a_bytes : static_cast<int64_t>(j.nrows) * j.lda);
   const int nseg = max(1, (j.K + static_cast<int>(j.kseg) - 1) / static_cast<int>(j.kseg));
   // Weight rows past the problem's N (a partial last n-tile) read as zeros.
   const rsrc_t rb_rs = make_rsrc(j.B, (nseg - 1) * j.segb + (GLU ? j.upb : 0) +
@@ -242,7 +247,9 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
   for (int q = 0; q < AQ; ++q) {
     const int u = (w + NW * q) * 64 + lane, r = u / CPR, c = (u % CPR) ^ lds_swz<ROW>(r);
-    aoff[q] = r * lda + c * 16;
+    // gathered rows: tile rows past nrows read row gather[0] (their outputs are not stored)
+    const uint32_t ar = j.gather ? static_cast<uint32_t>(j.gather[r < j.nrows ? r : 0]) : r;
+    aoff[q] = ar * lda + c * 16;
   }
 #pragma unroll
   for (int q = 0; q < BQ; ++q) {
@@ -406,7 +413,8 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs g) {
   if (!decode_tile<BM, GLU ? BN / 2 : BN, 4>(g, j)) return;
   const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
   const int lr = t >> 2, lc = (t & 3) * 4;
-  const int ar = lr < j.rows_left ? lr : j.rows_left - 1;
+  const int ar0 = lr < j.rows_left ? lr : j.rows_left - 1;
+  const int ar = j.gather ? j.gather[lr < j.nrows ? lr : 0] : ar0;
   const char* ap = j.A + static_cast<int64_t>(ar) * j.lda + lc * 4;
   const int64_t boffs = GLU ? (2 * (lr >> 2) + (lr & 1)) * j.ldb + ((lr >> 1) & 1) * j.upb
                             : static_cast<int64_t>(lr) * j.ldb;

@@ -70,7 +70,8 @@ struct PermuteArgs {
   int32_t* row;           // [N, k] (meta)
   float* topk_w;          // [N, k] (meta): zeroed where the slot is not kept
   int32_t* stats;         // [4] (meta); stats[2] += fully dropped tokens of the block
-  void* buf;              // [R, M] T compact expert-major rows
+  int32_t* tok_of_row;    // [R] token of every compact row (nullptr: not written)
+  void* buf;              // [R, M] T compact expert-major rows (written iff x != nullptr)
   int N, G, S, M, E, k, C, nbg, dtype, BM;
   int slices;             // column slices per router block (set by the launcher)
 };
@@ -106,6 +107,8 @@ struct GemmProblem {
   const BatchEntry* batch;  // batched problem (tiles == nullptr): device entries; max_tiles =
                             // entries * ceil(dense_rows / BM)
   int out_f32;            // C is fp32 (act must be none); else C has the input dtype
+  const int32_t* a_gather;  // routed problems: A row of compact row r is a_gather[r] (nullptr:
+                            // row r itself); lets GEMM 1 read the tokens of x directly
 };
 
 struct GemmArgs {

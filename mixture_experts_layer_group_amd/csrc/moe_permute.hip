@@ -137,6 +137,7 @@ __global__ __launch_bounds__(256) void permute_kernel(PermuteArgs a) {
         a.pos[o] = kept ? p : -1;
         a.row[o] = r;
         if (!kept) a.topk_w[o] = 0.f;
+        if (kept && a.tok_of_row) a.tok_of_row[r] = n;
       }
       rows_s[lane][j] = r;
       if (kept) kept_any[lane] = 1;
