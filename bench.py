@@ -284,15 +284,16 @@ def main():
     # Memory-bound kernels: algorithmic bytes / time against the HBM peak.
     kept_tokens = N - int(stats[2])
     bytes_router = N * (M * b + 4 * E + 9 * k + (4 if cfg["random_routing"] else 0))
-    bytes_permute = kept_tokens * M * b + R * M * b + N * k * 13
     bytes_combine = (R + N * int(cfg["residual"]) + N * int(Es > 0) + N) * M * b + N * k * 8
     hbm = {}
-    for name, by in (("router", bytes_router), ("permute", bytes_permute),
-                     ("combine", bytes_combine)):
+    for name, by in (("router", bytes_router), ("combine", bytes_combine)):
         t = stage_avg[name]
         gbps = by / (t * 1e-3) / 1e9
         hbm[name] = {"bytes": int(by), "ms": round(t, 5), "GB/s": round(gbps, 1),
                      "frac": round(gbps / PEAK_HBM_GBPS, 4)}
+    hbm["permute"] = {"ms": round(stage_avg["permute"], 5),
+                      "note": "positions, rows and the row->token index only (GEMM 1 gathers "
+                              "the token rows from x); latency-bound"}
     hbm["gate"] = {"ms": round(stage_avg["gate"], 5), "note": "capacity scan; latency-bound"}
 
     # Achievable copy bandwidth in the same run (1 GiB device-to-device clone).
