@@ -44,6 +44,11 @@ constexpr int kGemmStages = MOE_GEMM_STAGES;
 #define MOE_GEMM_GROUP_M 8
 #endif
 constexpr int kGemmGroupM = MOE_GEMM_GROUP_M;
+// waves along N of the bf16 tile (2 x WN waves; 4: 128 x 64 per wave, 2: 128 x 128)
+#ifndef MOE_GEMM_WN
+#define MOE_GEMM_WN 4
+#endif
+constexpr int kGemmWN = MOE_GEMM_WN;
 
 struct Job {
   const char* A;   // first row of the tile (bytes)
@@ -64,16 +69,32 @@ struct Job {
   int64_t a_bytes;        // gathered A: readable bytes from A
 };
 
+// Load through the constant address space: for tables no kernel of this file writes (tile
+// lists, batch entries, tile counts), so that a uniform address gives a scalar load even
+// after the kernel has stored to global memory.
+template <class T>
+__device__ __forceinline__ T load_const(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)(p);
+}
+__device__ __forceinline__ TileDesc load_const(const TileDesc* p) {
+  const int32_t* q = reinterpret_cast<const int32_t*>(p);
+  return TileDesc{load_const(q), load_const(q + 1), load_const(q + 2), 0};
+}
+__device__ __forceinline__ BatchEntry load_const(const BatchEntry* p) {
+  const int64_t* q = reinterpret_cast<const int64_t*>(p);
+  return BatchEntry{load_const(q), load_const(q + 1), load_const(q + 2),
+                    load_const(reinterpret_cast<const int32_t*>(q + 3)), 0};
+}
+
 // BN = output columns per tile (a gated tile computes 2 BN columns of A . B^T).
 template <int BM, int BN, int ESZ>
-__device__ __forceinline__ bool decode_tile(const GemmArgs& g, Job& j) {
+__device__ __forceinline__ bool decode_tile(const GemmArgs& g, Job& j, int bid) {
   const int nt0 = (g.p0.N + BN - 1) / BN;
-  const int mt0 = g.p0.tiles ? *g.p0.num_tiles : g.p0.max_tiles;
+  const int mt0 = g.p0.tiles ? load_const(g.p0.num_tiles) : g.p0.max_tiles;
   const int tot0 = mt0 * nt0;
   const int nt1 = g.nprob > 1 ? (g.p1.N + BN - 1) / BN : 0;
   const int mt1 = g.nprob > 1 ? g.p1.max_tiles : 0;
   const int total = tot0 + mt1 * nt1;
-  const int bid = blockIdx.x;
   if (bid >= total) return false;
   // Blocks are dispatched round-robin over the 8 XCDs (block b -> XCD b % 8); give every
   // XCD a contiguous range of tiles so neighbouring tiles share its L2.
@@ -96,12 +117,12 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& g, Job& j) {
   int e = 0, row0, nrows, K = P.K;
   int64_t aoff = 0, boff = 0, coff = 0;  // batched entries: element offsets
   if (P.tiles) {
-    const TileDesc d = P.tiles[mt];
+    const TileDesc d = load_const(P.tiles + mt);
     e = d.expert; row0 = d.row0; nrows = d.nrows;
   } else if (P.batch) {
     const int mpe = (P.dense_rows + BM - 1) / BM;  // m-tiles per entry
     const int be = mt / mpe, ml = mt - be * mpe;
-    const BatchEntry d = P.batch[be];
+    const BatchEntry d = load_const(P.batch + be);
     row0 = ml * BM; nrows = min(BM, P.dense_rows - row0);
     aoff = d.a_off; boff = d.b_off; coff = d.c_off; K = d.K;
   } else {
@@ -212,148 +233,245 @@ __device__ __forceinline__ void dma16(rsrc_t r, unsigned char* lds, uint32_t vof
 //    columns [32 s, 32 s + 32) and rows [64 s + 32, 64 s + 64) their up rows, so wave wn's two
 //    32-column MFMA blocks are the gate and up halves of the same 32 outputs, held by the
 //    same lanes in the same registers; the tile writes BN / 2 columns.
+template <int BM_, int BN_, int WN_, int BK_, int NST_>
+struct TileShape {
+  static constexpr int BM = BM_, BN = BN_, WN = WN_, BK = BK_, NST = NST_;
+  static constexpr int ROW = BK * 2, CPR = ROW / 16;  // bytes and 16-byte columns per LDS row
+  static constexpr int NT = 128 * WN, NW = 2 * WN;
+  static constexpr int STAGE = (BM + BN) * ROW;
+  static constexpr int WTM = BM / 2, WTN = BN / WN;
+  static constexpr int TM = WTM / 32, TN = WTN / 32;
+  static constexpr int AQ = BM * ROW / 1024 / NW, BQ = BN * ROW / 1024 / NW;  // loads per wave/chunk
+  static constexpr int Q = AQ + BQ;
+  static_assert(NST >= 2 && NST <= 5 && BK * (NST - 1) <= 128, "K % 128 == 0 covers the prologue");
+  static_assert(AQ * NW * 1024 == BM * ROW && BQ * NW * 1024 == BN * ROW, "tile/wave split");
+};
+
+// Where one tile's operand chunks come from: buffer resources, this lane's byte offsets for
+// its load slots, and the K position of B inside its current segment.
+template <class T>
+struct Feed {
+  rsrc_t ra, rb;
+  uint32_t aoff[T::AQ], boff[T::BQ];
+  int kin;          // elements into the current B segment
+  uint32_t segoff;  // byte offset of that segment
+  int kseg;         // elements per B segment
+  uint32_t segb;    // bytes between B segments
+};
+
+// Load slot q of wave w fills LDS units [(w + NW q) 64, +64) of its operand: unit u is row
+// u / CPR, physical column u % CPR.
+template <class T, bool GLU>
+__device__ __forceinline__ void feed_init(const Job& j, int w, int lane, Feed<T>& f) {
+  const uint32_t lda = static_cast<uint32_t>(j.lda), ldb = static_cast<uint32_t>(j.ldb);
+  f.ra = make_rsrc(j.A, j.gather ? j.a_bytes : static_cast<int64_t>(j.nrows) * j.lda);
+  const int nseg = max(1, (j.K + static_cast<int>(j.kseg) - 1) / static_cast<int>(j.kseg));
+  // Weight rows past the problem's N (a partial last n-tile) read as zeros.
+  f.rb = make_rsrc(j.B, (nseg - 1) * j.segb + (GLU ? j.upb : 0) +
+                            static_cast<int64_t>(j.ncols) * j.ldb);
+#pragma unroll
+  for (int q = 0; q < T::AQ; ++q) {
+    const int u = (w + T::NW * q) * 64 + lane, r = u / T::CPR;
+    const int c = (u % T::CPR) ^ lds_swz<T::ROW>(r);
+    // gathered rows: tile rows past nrows read row gather[0] (their outputs are not stored)
+    const uint32_t ar = j.gather ? static_cast<uint32_t>(j.gather[r < j.nrows ? r : 0]) : r;
+    f.aoff[q] = ar * lda + c * 16;
+  }
+#pragma unroll
+  for (int q = 0; q < T::BQ; ++q) {
+    const int u = (w + T::NW * q) * 64 + lane, r = u / T::CPR;
+    const int c = (u % T::CPR) ^ lds_swz<T::ROW>(r);
+    if (GLU)   // LDS row r: output column 32 (r / 64) + r % 32, gate or up half by bit 5
+      f.boff[q] = ((r >> 6) * 32 + (r & 31)) * ldb +
+                  ((r >> 5) & 1) * static_cast<uint32_t>(j.upb) + c * 16;
+    else
+      f.boff[q] = r * ldb + c * 16;
+  }
+  f.kin = 0;
+  f.segoff = 0;
+  f.kseg = static_cast<int>(j.kseg);
+  f.segb = static_cast<uint32_t>(j.segb);
+}
+
+// Issue this wave's loads of the A half of K chunk kt into LDS at As.
+template <class T>
+__device__ __forceinline__ void feed_issue_a(const Feed<T>& f, unsigned char* As, int w, int kt) {
+  const uint32_t ka = static_cast<uint32_t>(kt) * T::ROW;
+#pragma unroll
+  for (int q = 0; q < T::AQ; ++q) dma16(f.ra, As + (w + T::NW * q) * 1024, f.aoff[q], ka);
+}
+
+// Issue this wave's loads of the B half of the next K chunk into LDS at Bs (B chunks are
+// issued in K order).
+template <class T>
+__device__ __forceinline__ void feed_issue_b(Feed<T>& f, unsigned char* Bs, int w) {
+  const uint32_t kb = f.segoff + static_cast<uint32_t>(f.kin) * 2;
+#pragma unroll
+  for (int q = 0; q < T::BQ; ++q) dma16(f.rb, Bs + (w + T::NW * q) * 1024, f.boff[q], kb);
+  f.kin += T::BK;
+  const bool wrap = f.kin == f.kseg;
+  f.kin = wrap ? 0 : f.kin;
+  f.segoff += wrap ? f.segb : 0u;
+}
+
+// Issue K chunk kt (A then B) into one whole-chunk stage.
+template <class T>
+__device__ __forceinline__ void feed_issue(Feed<T>& f, unsigned char* stage, int w, int kt) {
+  feed_issue_a(f, stage, w, kt);
+  feed_issue_b(f, stage + T::BM * T::ROW, w);
+}
+
+// Multiply one K chunk (A rows at As, B rows at Bs in LDS) into the wave's accumulators.
+// arow / brow: the wave's first A and B fragment rows for this lane; sw: the column swizzle
+// of those rows.
+template <class T>
+__device__ __forceinline__ void mma_chunk(const unsigned char* As, const unsigned char* Bs,
+                                          int arow, int brow, int lane, int sw,
+                                          f32x16 (&acc)[T::TN][T::TM]) {
+#pragma unroll
+  for (int s = 0; s < T::BK / 16; ++s) {
+    const int phys = (((2 * s) + (lane >> 5)) ^ sw) * 16;
+    bf16x8 af[T::TM], bfr[T::TN];
+#pragma unroll
+    for (int im = 0; im < T::TM; ++im)
+      af[im] = *reinterpret_cast<const bf16x8*>(As + (arow + 32 * im) * T::ROW + phys);
+#pragma unroll
+    for (int jn = 0; jn < T::TN; ++jn)
+      bfr[jn] = *reinterpret_cast<const bf16x8*>(Bs + (brow + 32 * jn) * T::ROW + phys);
+#pragma unroll
+    for (int jn = 0; jn < T::TN; ++jn)
+#pragma unroll
+      for (int im = 0; im < T::TM; ++im)
+        acc[jn][im] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[jn], af[im], acc[jn][im],
+                                                              0, 0, 0);
+  }
+}
+
+// bf16 epilogue through LDS: D[feature][token] -> tile[token][feature] (rows of OUTN*2 bytes,
+// NCH 16-byte columns XOR (row % NCH)), then whole rows to global memory, 16 bytes per lane.
+// The staging area holds STG bytes; a tile that does not fit goes through it in passes of
+// whole wave-row blocks.  The caller has made the area free (a barrier after its last read);
+// on return every wave's last reads of it are issued but not waited for.
+template <class T, int ACT, int STG>
+__device__ __forceinline__ void store_tile(const Job& j, f32x16 (&acc)[T::TN][T::TM],
+                                           unsigned char* stg, int t, int lane, int wm,
+                                           int wn) {
+  constexpr bool GLU = ACT == kActSwiglu;
+  constexpr int OUTN = GLU ? T::BN / 2 : T::BN;
+  constexpr int RB = OUTN * 2, NCH = RB / 16;
+  constexpr int TNO = GLU ? T::TN / 2 : T::TN, WTNO = OUTN / T::WN;
+  constexpr int RP = STG / RB < T::BM ? STG / RB : T::BM;  // rows per pass
+  static_assert((NCH & (NCH - 1)) == 0, "power-of-two column count");
+  static_assert(RP % T::WTM == 0 && T::BM % RP == 0, "passes of whole wave-row blocks");
+  auto out = [&](int jo, int im, int x) {
+    if (GLU) return swish(acc[2 * jo][im][x]) * acc[2 * jo + 1][im][x];
+    return act_fn<ACT>(acc[jo][im][x]);
+  };
+  const int ncch = j.ncols / 8;   // valid 16-byte columns
+#pragma unroll
+  for (int p = 0; p < T::BM / RP; ++p) {
+    if (p > 0) lds_barrier();   // the previous pass has been read out
+    if (wm * T::WTM / RP == p) {
+#pragma unroll
+      for (int im = 0; im < T::TM; ++im) {
+        const int tok = wm * T::WTM + 32 * im + (lane & 31) - p * RP;
+#pragma unroll
+        for (int jo = 0; jo < TNO; ++jo) {
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            const int f = wn * WTNO + 32 * jo + 8 * qd + 4 * (lane >> 5);
+            u32x2 pk;
+            pk[0] = pack_bf16x2(out(jo, im, 4 * qd + 0), out(jo, im, 4 * qd + 1));
+            pk[1] = pack_bf16x2(out(jo, im, 4 * qd + 2), out(jo, im, 4 * qd + 3));
+            const int ch = f >> 3, within = (f & 7) * 2;
+            *reinterpret_cast<u32x2*>(stg + tok * RB + ((ch ^ (tok & (NCH - 1))) << 4) + within) =
+                pk;
+          }
+        }
+      }
+    }
+    lds_barrier();
+    const int rows = min(RP, j.nrows - p * RP);
+    char* C = j.C + static_cast<int64_t>(p * RP) * j.ldc;
+    for (int i = t; i < rows * NCH; i += T::NT) {
+      const int r = i / NCH, c = i - r * NCH;
+      if (c >= ncch) continue;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * RB + ((c ^ (r & (NCH - 1))) << 4));
+      *reinterpret_cast<u32x4*>(C + static_cast<int64_t>(r) * j.ldc + c * 16) = v;
+    }
+  }
+}
+
+// One tile per block.
 template <int BM, int BN, int WN, int ACT, int BK, int NST, bool OUTF32>
 __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
-  constexpr int ROW = BK * 2, CPR = ROW / 16;  // bytes and 16-byte columns per LDS row
-  static_assert(NST >= 2 && NST <= 5 && BK * (NST - 1) <= 128, "K % 128 == 0 covers the prologue");
-  constexpr int NT = 128 * WN, NW = 2 * WN;
-  constexpr int STAGE = (BM + BN) * ROW;
-  constexpr int WTM = BM / 2, WTN = BN / WN;
-  constexpr int TM = WTM / 32, TN = WTN / 32;
-  constexpr int AQ = BM * ROW / 1024 / NW, BQ = BN * ROW / 1024 / NW;  // loads per wave/chunk
-  constexpr int SMEM = NST * STAGE > BM * BN * 2 ? NST * STAGE : BM * BN * 2;
-  static_assert(AQ * NW * 1024 == BM * ROW && BQ * NW * 1024 == BN * ROW, "tile/wave split");
+  using T = TileShape<BM, BN, WN, BK, NST>;
+  constexpr int SLOT = BM * T::ROW;   // one operand's rows of one chunk
+  constexpr int SMEM = NST * T::STAGE > BM * BN * 2 ? NST * T::STAGE : BM * BN * 2;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
 
   constexpr bool GLU = ACT == kActSwiglu;
   constexpr int OUTN = GLU ? BN / 2 : BN;    // output columns of the tile
   static_assert(!GLU || (BN / WN) % 64 == 0, "gated tiles: every wave holds gate/up block pairs");
   Job j;
-  if (!decode_tile<BM, OUTN, 2>(g, j)) return;
+  if (!decode_tile<BM, OUTN, 2>(g, j, blockIdx.x)) return;
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = w / WN, wn = w % WN;
+  Feed<T> fd;
+  feed_init<T, GLU>(j, w, lane, fd);
 
-  const uint32_t lda = static_cast<uint32_t>(j.lda), ldb = static_cast<uint32_t>(j.ldb);
-  const rsrc_t ra_rs = make_rsrc(j.A, j.gather ? j.a_bytes : static_cast<int64_t>(j.nrows) * j.lda);
-  const int nseg = max(1, (j.K + static_cast<int>(j.kseg) - 1) / static_cast<int>(j.kseg));
-  // Weight rows past the problem's N (a partial last n-tile) read as zeros.
-  const rsrc_t rb_rs = make_rsrc(j.B, (nseg - 1) * j.segb + (GLU ? j.upb : 0) +
-                                          static_cast<int64_t>(j.ncols) * j.ldb);
+  f32x16 acc[T::TN][T::TM];
+#pragma unroll
+  for (int jn = 0; jn < T::TN; ++jn)
+#pragma unroll
+    for (int im = 0; im < T::TM; ++im) acc[jn][im] = f32x16{};
 
-  // Load slot q of this wave fills LDS units [(w + NW q) 64, +64) of its operand: unit u is
-  // row u / CPR, physical column u % CPR.
-  uint32_t aoff[AQ], boff[BQ];
-#pragma unroll
-  for (int q = 0; q < AQ; ++q) {
-    const int u = (w + NW * q) * 64 + lane, r = u / CPR, c = (u % CPR) ^ lds_swz<ROW>(r);
-    // gathered rows: tile rows past nrows read row gather[0] (their outputs are not stored)
-    const uint32_t ar = j.gather ? static_cast<uint32_t>(j.gather[r < j.nrows ? r : 0]) : r;
-    aoff[q] = ar * lda + c * 16;
-  }
-#pragma unroll
-  for (int q = 0; q < BQ; ++q) {
-    const int u = (w + NW * q) * 64 + lane, r = u / CPR, c = (u % CPR) ^ lds_swz<ROW>(r);
-    if (GLU)   // LDS row r: output column 32 (r / 64) + r % 32, gate or up half by bit 5
-      boff[q] = ((r >> 6) * 32 + (r & 31)) * ldb + ((r >> 5) & 1) * static_cast<uint32_t>(j.upb) +
-                c * 16;
-    else
-      boff[q] = r * ldb + c * 16;
-  }
-
-  // K position of B inside its segment (elements) and the segment's byte offset.
-  int kin = 0;
-  uint32_t segoff = 0;
-  const int kseg = static_cast<int>(j.kseg);
-  const uint32_t segb = static_cast<uint32_t>(j.segb);
-  auto issue = [&](int kt, int st) {
-    unsigned char* As = smem + st * STAGE;
-    unsigned char* Bs = As + BM * ROW;
-    const uint32_t ka = static_cast<uint32_t>(kt) * ROW;
-    const uint32_t kb = segoff + static_cast<uint32_t>(kin) * 2;
-#pragma unroll
-    for (int q = 0; q < AQ; ++q) dma16(ra_rs, As + (w + NW * q) * 1024, aoff[q], ka);
-#pragma unroll
-    for (int q = 0; q < BQ; ++q) dma16(rb_rs, Bs + (w + NW * q) * 1024, boff[q], kb);
-    kin += BK;
-    const bool wrap = kin == kseg;
-    kin = wrap ? 0 : kin;
-    segoff += wrap ? segb : 0u;
-  };
-
-  f32x16 acc[TN][TM];
-#pragma unroll
-  for (int jn = 0; jn < TN; ++jn)
-#pragma unroll
-    for (int im = 0; im < TM; ++im) acc[jn][im] = f32x16{};
-
-  const int arow = wm * WTM + (lane & 31);
-  const int brow = wn * WTN + (lane & 31);
-  const int sw = lds_swz<ROW>(lane & 31);  // the fragment rows are congruent to lane & 31 mod 16
-  auto compute = [&](int st) {
-    const unsigned char* As = smem + st * STAGE;
-    const unsigned char* Bs = As + BM * ROW;
-#pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      const int phys = (((2 * s) + (lane >> 5)) ^ sw) * 16;
-      bf16x8 af[TM], bfr[TN];
-#pragma unroll
-      for (int im = 0; im < TM; ++im)
-        af[im] = *reinterpret_cast<const bf16x8*>(As + (arow + 32 * im) * ROW + phys);
-#pragma unroll
-      for (int jn = 0; jn < TN; ++jn)
-        bfr[jn] = *reinterpret_cast<const bf16x8*>(Bs + (brow + 32 * jn) * ROW + phys);
-#pragma unroll
-      for (int jn = 0; jn < TN; ++jn)
-#pragma unroll
-        for (int im = 0; im < TM; ++im)
-          acc[jn][im] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[jn], af[im], acc[jn][im],
-                                                                0, 0, 0);
-    }
-  };
+  const int arow = wm * T::WTM + (lane & 31);
+  const int brow = wn * T::WTN + (lane & 31);
+  const int sw = lds_swz<T::ROW>(lane & 31);  // fragment rows are congruent to lane & 31 mod 16
 
   // Chunk kt lives in stage kt % NST.  Before multiplying chunk kt a wave lets the chunks
   // issued after it stay in flight (Q vector-memory operations each), then the barrier
   // makes every wave's part visible and frees the stage that chunk kt + NST - 1 refills.
-  constexpr int Q = AQ + BQ;
   auto wait_chunk = [&](int ahead) {
-    if (NST > 4 && ahead >= 3) MOE_WAIT_VMCNT(3 * Q);
-    else if (NST > 3 && ahead >= 2) MOE_WAIT_VMCNT(2 * Q);
-    else if (NST > 2 && ahead >= 1) MOE_WAIT_VMCNT(Q);
+    if (NST > 4 && ahead >= 3) MOE_WAIT_VMCNT(3 * T::Q);
+    else if (NST > 3 && ahead >= 2) MOE_WAIT_VMCNT(2 * T::Q);
+    else if (NST > 2 && ahead >= 1) MOE_WAIT_VMCNT(T::Q);
     else MOE_WAIT_VMCNT(0);
   };
   const int KT = j.K / BK;  // 0 (a zero block) or >= NST - 1
   if (KT > 0) {
 #pragma unroll
-  for (int p = 0; p < NST - 1; ++p) issue(p, p);
-  int st = 0;
-  for (int kt = 0; kt + NST - 1 < KT; ++kt) {
-    wait_chunk(NST - 2);
-    lds_barrier();
-    const int sf = st == 0 ? NST - 1 : st - 1;  // (kt + NST - 1) % NST
-    issue(kt + NST - 1, sf);
-    compute(st);
-    st = st == NST - 1 ? 0 : st + 1;
-  }
+    for (int p = 0; p < NST - 1; ++p) feed_issue(fd, smem + p * T::STAGE, w, p);
+    int st = 0;
+    for (int kt = 0; kt + NST - 1 < KT; ++kt) {
+      wait_chunk(NST - 2);
+      lds_barrier();
+      const int sf = st == 0 ? NST - 1 : st - 1;  // (kt + NST - 1) % NST
+      feed_issue(fd, smem + sf * T::STAGE, w, kt + NST - 1);
+      mma_chunk<T>(smem + st * T::STAGE, smem + st * T::STAGE + SLOT, arow, brow, lane, sw, acc);
+      st = st == NST - 1 ? 0 : st + 1;
+    }
 #pragma unroll
-  for (int i = 0; i < NST - 1; ++i) {  // the last NST - 1 chunks: nothing left to issue
-    wait_chunk(NST - 2 - i);
-    lds_barrier();
-    compute(st);
-    st = st == NST - 1 ? 0 : st + 1;
-  }
+    for (int i = 0; i < NST - 1; ++i) {  // the last NST - 1 chunks: nothing left to issue
+      wait_chunk(NST - 2 - i);
+      lds_barrier();
+      mma_chunk<T>(smem + st * T::STAGE, smem + st * T::STAGE + SLOT, arow, brow, lane, sw, acc);
+      st = st == NST - 1 ? 0 : st + 1;
+    }
   }
 
   if (OUTF32) {  // fp32 output (no activation): each lane stores its runs of 4 features
 #pragma unroll
-    for (int im = 0; im < TM; ++im) {
-      const int tok = wm * WTM + 32 * im + (lane & 31);
+    for (int im = 0; im < T::TM; ++im) {
+      const int tok = wm * T::WTM + 32 * im + (lane & 31);
       if (tok >= j.nrows) continue;
 #pragma unroll
-      for (int jn = 0; jn < TN; ++jn)
+      for (int jn = 0; jn < T::TN; ++jn)
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
-          const int f = wn * WTN + 32 * jn + 8 * qd + 4 * (lane >> 5);
+          const int f = wn * T::WTN + 32 * jn + 8 * qd + 4 * (lane >> 5);
           if (f >= j.ncols) continue;
           f32x4 v;
 #pragma unroll
@@ -363,41 +481,8 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
     }
     return;
   }
-
-  // Epilogue through LDS: D[feature][token] -> tile[token][feature] bf16 (rows of OUTN*2
-  // bytes, NCH 16-byte columns XOR (row % NCH)), then whole rows to global memory.
-  constexpr int RB = OUTN * 2, NCH = RB / 16;
-  constexpr int TNO = GLU ? TN / 2 : TN, WTNO = OUTN / WN;
-  static_assert((NCH & (NCH - 1)) == 0, "power-of-two column count");
-  auto out = [&](int jo, int im, int x) {
-    if (GLU) return swish(acc[2 * jo][im][x]) * acc[2 * jo + 1][im][x];
-    return act_fn<ACT>(acc[jo][im][x]);
-  };
   lds_barrier();
-#pragma unroll
-  for (int im = 0; im < TM; ++im) {
-    const int tok = wm * WTM + 32 * im + (lane & 31);
-#pragma unroll
-    for (int jo = 0; jo < TNO; ++jo) {
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const int f = wn * WTNO + 32 * jo + 8 * qd + 4 * (lane >> 5);
-        u32x2 pk;
-        pk[0] = pack_bf16x2(out(jo, im, 4 * qd + 0), out(jo, im, 4 * qd + 1));
-        pk[1] = pack_bf16x2(out(jo, im, 4 * qd + 2), out(jo, im, 4 * qd + 3));
-        const int ch = f >> 3, within = (f & 7) * 2;
-        *reinterpret_cast<u32x2*>(smem + tok * RB + ((ch ^ (tok & (NCH - 1))) << 4) + within) = pk;
-      }
-    }
-  }
-  lds_barrier();
-  const int ncch = j.ncols / 8;   // valid 16-byte columns
-  for (int i = t; i < j.nrows * NCH; i += NT) {
-    const int r = i / NCH, c = i - r * NCH;
-    if (c >= ncch) continue;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * RB + ((c ^ (r & (NCH - 1))) << 4));
-    *reinterpret_cast<u32x4*>(j.C + static_cast<int64_t>(r) * j.ldc + c * 16) = v;
-  }
+  store_tile<T, ACT, SMEM>(j, acc, smem, t, lane, wm, wn);
 }
 
 // Thread (ty, tx) accumulates rows 4 ty + i and LDS B columns 4 tx + jj.  Gated problems:
@@ -410,7 +495,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) float As[BK][LDSW];
   __shared__ __attribute__((aligned(16))) float Bs[BK][LDSW];
   Job j;
-  if (!decode_tile<BM, GLU ? BN / 2 : BN, 4>(g, j)) return;
+  if (!decode_tile<BM, GLU ? BN / 2 : BN, 4>(g, j, blockIdx.x)) return;
   const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
   const int lr = t >> 2, lc = (t & 3) * 4;
   const int ar0 = lr < j.rows_left ? lr : j.rows_left - 1;
@@ -479,12 +564,12 @@ hipError_t launch_expert_gemm(const GemmArgs& a, hipStream_t s) {
   const int grid = grid_of(a, gemm_block_n(a.dtype, act));
   if (grid == 0) return hipSuccess;
   if (a.dtype == 1) {
-#define MOE_GEMM_LAUNCH(ACTV)                                                          \
-  hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 4, ACTV, kGemmBK, kGemmStages, false>),  \
-                     dim3(grid), dim3(512), 0, s, a)
+#define MOE_GEMM_LAUNCH(ACTV)                                                                \
+  hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, kGemmWN, ACTV, kGemmBK, kGemmStages, false>), \
+                     dim3(grid), dim3(128 * kGemmWN), 0, s, a)
     if (a.p0.out_f32)
-      hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 4, kActNone, kGemmBK, kGemmStages, true>),
-                         dim3(grid), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, kGemmWN, kActNone, kGemmBK, kGemmStages, true>),
+                         dim3(grid), dim3(128 * kGemmWN), 0, s, a);
     else if (act == kActRelu) MOE_GEMM_LAUNCH(kActRelu);
     else if (act == kActGelu) MOE_GEMM_LAUNCH(kActGelu);
     else if (act == kActSwiglu) MOE_GEMM_LAUNCH(kActSwiglu);
