@@ -352,13 +352,14 @@ __device__ __forceinline__ void mma_chunk(const unsigned char* As, const unsigne
 // The staging area holds STG bytes; a tile that does not fit goes through it in passes of
 // whole wave-row blocks.  The caller has made the area free (a barrier after its last read);
 // on return every wave's last reads of it are issued but not waited for.
-template <class T, int ACT, int STG>
+template <class T, int ACT, int STG, bool F32 = false>
 __device__ __forceinline__ void store_tile(const Job& j, f32x16 (&acc)[T::TN][T::TM],
                                            unsigned char* stg, int t, int lane, int wm,
                                            int wn) {
   constexpr bool GLU = ACT == kActSwiglu;
+  static_assert(!F32 || ACT == kActNone, "fp32 output carries no activation");
   constexpr int OUTN = GLU ? T::BN / 2 : T::BN;
-  constexpr int RB = OUTN * 2, NCH = RB / 16;
+  constexpr int RB = OUTN * (F32 ? 4 : 2), NCH = RB / 16;
   constexpr int TNO = GLU ? T::TN / 2 : T::TN, WTNO = OUTN / T::WN;
   constexpr int RP = STG / RB < T::BM ? STG / RB : T::BM;  // rows per pass
   static_assert((NCH & (NCH - 1)) == 0, "power-of-two column count");
@@ -367,7 +368,7 @@ __device__ __forceinline__ void store_tile(const Job& j, f32x16 (&acc)[T::TN][T:
     if (GLU) return swish(acc[2 * jo][im][x]) * acc[2 * jo + 1][im][x];
     return act_fn<ACT>(acc[jo][im][x]);
   };
-  const int ncch = j.ncols / 8;   // valid 16-byte columns
+  const int ncch = j.ncols / (F32 ? 4 : 8);   // valid 16-byte columns
 #pragma unroll
   for (int p = 0; p < T::BM / RP; ++p) {
     if (p > 0) lds_barrier();   // the previous pass has been read out
@@ -380,12 +381,20 @@ __device__ __forceinline__ void store_tile(const Job& j, f32x16 (&acc)[T::TN][T:
 #pragma unroll
           for (int qd = 0; qd < 4; ++qd) {
             const int f = wn * WTNO + 32 * jo + 8 * qd + 4 * (lane >> 5);
-            u32x2 pk;
-            pk[0] = pack_bf16x2(out(jo, im, 4 * qd + 0), out(jo, im, 4 * qd + 1));
-            pk[1] = pack_bf16x2(out(jo, im, 4 * qd + 2), out(jo, im, 4 * qd + 3));
-            const int ch = f >> 3, within = (f & 7) * 2;
-            *reinterpret_cast<u32x2*>(stg + tok * RB + ((ch ^ (tok & (NCH - 1))) << 4) + within) =
-                pk;
+            if (F32) {   // 4 fp32 features: one whole 16-byte column
+              f32x4 v;
+#pragma unroll
+              for (int x = 0; x < 4; ++x) v[x] = acc[jo][im][4 * qd + x];
+              const int ch = f >> 2;
+              *reinterpret_cast<f32x4*>(stg + tok * RB + ((ch ^ (tok & (NCH - 1))) << 4)) = v;
+            } else {
+              u32x2 pk;
+              pk[0] = pack_bf16x2(out(jo, im, 4 * qd + 0), out(jo, im, 4 * qd + 1));
+              pk[1] = pack_bf16x2(out(jo, im, 4 * qd + 2), out(jo, im, 4 * qd + 3));
+              const int ch = f >> 3, within = (f & 7) * 2;
+              *reinterpret_cast<u32x2*>(stg + tok * RB + ((ch ^ (tok & (NCH - 1))) << 4) +
+                                        within) = pk;
+            }
           }
         }
       }
@@ -462,27 +471,9 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
     }
   }
 
-  if (OUTF32) {  // fp32 output (no activation): each lane stores its runs of 4 features
-#pragma unroll
-    for (int im = 0; im < T::TM; ++im) {
-      const int tok = wm * T::WTM + 32 * im + (lane & 31);
-      if (tok >= j.nrows) continue;
-#pragma unroll
-      for (int jn = 0; jn < T::TN; ++jn)
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-          const int f = wn * T::WTN + 32 * jn + 8 * qd + 4 * (lane >> 5);
-          if (f >= j.ncols) continue;
-          f32x4 v;
-#pragma unroll
-          for (int x = 0; x < 4; ++x) v[x] = acc[jn][im][4 * qd + x];
-          *reinterpret_cast<f32x4*>(j.C + static_cast<int64_t>(tok) * j.ldc + f * 4) = v;
-        }
-    }
-    return;
-  }
   lds_barrier();
-  store_tile<T, ACT, SMEM>(j, acc, smem, t, lane, wm, wn);
+  // fp32 output (the weight-gradient GEMMs): rows of 1 KB, staged in passes of 128 rows
+  store_tile<T, ACT, SMEM, OUTF32>(j, acc, smem, t, lane, wm, wn);
 }
 
 // Thread (ty, tx) accumulates rows 4 ty + i and LDS B columns 4 tx + jj.  Gated problems:
