@@ -324,8 +324,9 @@ int forward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* b
 struct BwdLayout {
   Layout F;
   size_t z1, o, dout, dh, dz1, dbuf, z1sh, dhsh, dz1sh, w1t, w2t, doT, hT, dz1T, bufT, dyT,
-      xT, hshT, dz1shT, dl, dw, partb, dlp, wgt, dxrt, dlT, src0, cnt, dst0, segblk, width, e2, e1, total;
-  int64_t H1, RT, Npad, nchunks, Ep;
+      xT, hshT, dz1shT, dl, dw, partb, dlp, wgt, dxrt, dlT, src0, cnt, dst0, segblk, width, e2, e1,
+      eg, dwgp, total;
+  int64_t H1, RT, Npad, nchunks, Ep, nsplit, ksplit;
 };
 
 int make_bwd_layout(const moe_cfg* c, BwdLayout* B) {
@@ -341,6 +342,14 @@ int make_bwd_layout(const moe_cfg* c, BwdLayout* B) {
   B->Npad = (N + 127) / 128 * 128;
   B->nchunks = (N + 255) / 256;
   B->Ep = (E + 63) / 64 * 64;
+  // dWg [E, M] contracts over all N tokens but has few output tiles: split the token axis
+  // into ranges of a multiple of 128 tokens so that about 256 tiles run, partials in fp32
+  {
+    const int64_t tiles = ((E + 255) / 256) * ((M + 255) / 256);
+    int64_t S = std::max<int64_t>(1, std::min<int64_t>((256 + tiles - 1) / tiles, B->Npad / 128));
+    B->ksplit = std::max<int64_t>(128, (B->Npad / S + 127) / 128 * 128);
+    B->nsplit = (B->Npad + B->ksplit - 1) / B->ksplit;   // 0 for an empty batch
+  }
   const int64_t lim = (int64_t{1} << 31) - 1;
   if (L.rows_alloc * H1 > lim || (E + Es) * H1 * M > lim || H1 * B->RT > lim ||
       std::max(M, Es * H1) * std::max(B->RT, B->Npad) > lim || N * Es * H1 > lim ||
@@ -386,6 +395,8 @@ int make_bwd_layout(const moe_cfg* c, BwdLayout* B) {
   B->width = take(16);
   B->e2 = take(static_cast<size_t>(E + Es) * sizeof(moe::BatchEntry));
   B->e1 = take(static_cast<size_t>(E + Es) * sizeof(moe::BatchEntry));
+  B->eg = take(static_cast<size_t>(B->nsplit) * sizeof(moe::BatchEntry));
+  B->dwgp = take(static_cast<size_t>(B->nsplit * E * M) * 4);
   B->total = off;
   return MOE_OK;
 }
@@ -607,6 +618,9 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
     sa.E = static_cast<int>(E); sa.Es = static_cast<int>(Es); sa.M = static_cast<int>(M);
     sa.H = static_cast<int>(H); sa.H1 = static_cast<int>(H1);
     sa.Npad = static_cast<int>(B.Npad);
+    sa.dwg = reinterpret_cast<moe::BatchEntry*>(ws + B.eg);
+    sa.nsplit = static_cast<int>(B.nsplit);
+    sa.ksplit = static_cast<int>(B.ksplit);
     rc = status_of(moe::launch_bwd_setup(sa, s));
     if (rc) return rc;
     auto seg_t = [&](const void* X, size_t dst, int W) {
@@ -625,15 +639,18 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
     if ((rc = seg_t(ws + L.h, B.hT, static_cast<int>(H)))) return rc;
     if ((rc = seg_t(ws + B.dz1, B.dz1T, static_cast<int>(H1)))) return rc;
     if ((rc = seg_t(ws + L.buf, B.bufT, static_cast<int>(M)))) return rc;
-    // dWg [E, M] = dl^T x over the padded token axis (fp32 out)
+    // dWg [E, M] = dl^T x over the padded token axis (fp32 out): one batched GEMM over
+    // token ranges into fp32 partials, then their sum in range order
     if ((rc = dense_t(x, B.xT, static_cast<int>(M)))) return rc;
     if ((rc = dense_t(ws + B.dlp, B.dlT, static_cast<int>(B.Ep)))) return rc;
     {
-      moe::GemmProblem p = dense_problem(ws + B.dlT, B.Npad, ws + B.xT, B.Npad, dWg, M,
-                                         static_cast<int>(M), static_cast<int>(B.Npad),
-                                         static_cast<int>(E), BM);
-      p.out_f32 = 1;
+      float* part = reinterpret_cast<float*>(ws + B.dwgp);
+      auto p = batched_problem(ws + B.dlT, B.Npad, ws + B.xT, B.Npad, part, M,
+                               static_cast<int>(M), static_cast<int>(E),
+                               static_cast<int>(B.nsplit), BM, sa.dwg);
       if ((rc = gemm(p, nullptr))) return rc;
+      if ((rc = status_of(moe::launch_split_reduce(part, dWg, E * M, static_cast<int>(B.nsplit), s))))
+        return rc;
     }
     if (Es) {
       if ((rc = dense_t(dy, B.dyT, static_cast<int>(M)))) return rc;

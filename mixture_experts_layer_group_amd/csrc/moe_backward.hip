@@ -282,6 +282,13 @@ __global__ __launch_bounds__(256) void bwd_setup_kernel(BwdSetupArgs a) {
     a.dw2[E + t] = d2;
     a.dw1[E + t] = d1;
   }
+  for (int q = t; q < a.nsplit; q += 256) {  // dWg [E, M] = dlT . xT^T over token range q
+    BatchEntry g;
+    g.a_off = static_cast<int64_t>(q) * a.ksplit; g.b_off = g.a_off;
+    g.c_off = static_cast<int64_t>(q) * E * a.M;
+    g.K = min(a.ksplit, a.Npad - q * a.ksplit); g.pad = 0;
+    a.dwg[q] = g;
+  }
   if (t == 0) *a.width = total;
 }
 
@@ -373,12 +380,45 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(RouterBwdArgs a) {
 
 // dbg partial sums: block ch sums dl over its 256 tokens (in order) for every expert.
 __global__ __launch_bounds__(256) void dbg_partial_kernel(DwgArgs a) {
-  const int ch = blockIdx.x, n0 = ch * 256, nn = min(256, a.N - n0);
-  for (int e = threadIdx.x; e < a.E; e += 256) {
-    float sb = 0.0f;
-    for (int r = 0; r < nn; ++r) sb += a.dl[static_cast<int64_t>(n0 + r) * a.E + e];
-    a.partb[static_cast<int64_t>(ch) * a.E + e] = sb;
+  // block (chunk of 256 tokens, 64 experts); wave w sums tokens [64 w, 64 w + 64) of the chunk
+  // for expert e = 64 eb + lane, then the 4 wave sums are added in wave order
+  __shared__ float part[4][64];
+  const int ch = blockIdx.x, eb = blockIdx.y, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int e = eb * 64 + lane;
+  const int n0 = ch * 256 + w * 64, nn = max(0, min(64, a.N - n0));
+  float sb = 0.0f;
+  if (e < a.E) {
+    const float* p = a.dl + static_cast<int64_t>(n0) * a.E + e;
+    int r = 0;
+    for (; r + 8 <= nn; r += 8) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = p[static_cast<int64_t>(r + i) * a.E];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sb += v[i];
+    }
+    for (; r < nn; ++r) sb += p[static_cast<int64_t>(r) * a.E];
   }
+  part[w][lane] = sb;
+  __syncthreads();
+  if (w == 0 && e < a.E)
+    a.partb[static_cast<int64_t>(ch) * a.E + e] = ((part[0][lane] + part[1][lane]) + part[2][lane]) +
+                                                   part[3][lane];
+}
+
+// out = sum of S fp32 partial arrays in order, 4 elements per thread.
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part,
+                                                           float* __restrict__ out, int64_t n,
+                                                           int S) {
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(part + i);
+  for (int q = 1; q < S; ++q) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(part + static_cast<int64_t>(q) * n + i);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) acc[x] += v[x];
+  }
+  *reinterpret_cast<f32x4*>(out + i) = acc;
 }
 
 // dbg = sum of the chunk partials in order.
@@ -520,8 +560,16 @@ hipError_t launch_router_bwd(const RouterBwdArgs& a, hipStream_t s) {
 
 hipError_t launch_dbg(const DwgArgs& a, hipStream_t s) {
   if (a.nchunks == 0 || !a.dbg) return hipSuccess;
-  hipLaunchKernelGGL(dbg_partial_kernel, dim3(a.nchunks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(dbg_partial_kernel, dim3(a.nchunks, (a.E + 63) / 64), dim3(256), 0, s, a);
   hipLaunchKernelGGL(dbg_reduce_kernel, dim3((a.E + 255) / 256), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_reduce(const float* part, float* out, int64_t n, int S, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const int64_t grid = (n / 4 + 255) / 256;
+  hipLaunchKernelGGL(split_reduce_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s,
+                     part, out, n, S);
   return hipGetLastError();
 }
 

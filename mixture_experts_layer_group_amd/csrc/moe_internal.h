@@ -176,7 +176,8 @@ struct BwdSetupArgs {      // padded per-expert K offsets and batched weight-gra
   const int32_t* offset;   // [E+1] expert offsets of the compact buffer
   int32_t* src0; int32_t* cnt; int32_t* dst0; int32_t* seg_of_blk; int32_t* width;
   BatchEntry* dw2; BatchEntry* dw1;  // [E+Es]
-  int E, Es, M, H, H1, Npad;
+  BatchEntry* dwg;                   // [nsplit] token ranges of the router weight gradient
+  int E, Es, M, H, H1, Npad, nsplit, ksplit;
 };
 
 struct RouterBwdArgs {
@@ -210,6 +211,8 @@ hipError_t launch_mat_transpose(const MatTransposeArgs& a, hipStream_t s);
 hipError_t launch_bwd_setup(const BwdSetupArgs& a, hipStream_t s);
 hipError_t launch_router_bwd(const RouterBwdArgs& a, hipStream_t s);
 hipError_t launch_dbg(const DwgArgs& a, hipStream_t s);
+// out[i] = sum over s < S of part[s][i], in order of s (n a multiple of 4)
+hipError_t launch_split_reduce(const float* part, float* out, int64_t n, int S, hipStream_t s);
 hipError_t launch_router_dgrad_prep(const RouterPrepArgs& a, hipStream_t s);
 hipError_t launch_dx_final(const DxArgs& a, hipStream_t s);
 hipError_t launch_zero(float* p, int64_t n, hipStream_t s);

@@ -213,3 +213,12 @@ def test_invalid_backward_rejected_on_host(lib, what, over, code):
 def test_backward_workspace_covers_forward(lib):
     for cfg in list(configs.SMALL.values()) + list(configs.WORKLOADS.values()):
         assert binding.moe_backward_workspace_size(cfg) > binding.moe_workspace_size(cfg)
+
+
+def test_backward_workspace_sizes_small_batches(lib):
+    # the token-range split of the router weight gradient must handle every batch size,
+    # the empty batch included (no token range at all)
+    base = configs.SMALL["small_top2_rr"]
+    for n in (0, 1, 127, 128, 129, 4096):
+        cfg = configs.with_overrides(base, n_tokens=n, n_groups=1)
+        assert binding.moe_backward_workspace_size(cfg) > 0, n
