@@ -85,6 +85,70 @@ __device__ __forceinline__ int rswz(int r) {
   return ROWB == 256 ? (r & 15) : (((r >> 1) & 7) ^ ((r & 1) << 2));
 }
 
+// Cross-lane steps inside one 16-lane DPP row (the lanes of one token): swap neighbours
+// (quad_perm 1,0,3,2), swap pairs (quad_perm 2,3,0,1), mirror within 8 lanes, mirror within
+// 16 lanes.  Each step pairs every lane with one other lane of its aligned group of 2, 4, 8,
+// 16, so after log2(N) steps of a commutative combine every lane of an aligned group of N
+// holds the group's total, the same bits in every lane.  DPP moves are VALU operations; the
+// LDS-routed ds_bpermute of a generic shuffle costs an LDS round trip per step.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, v)));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = static_cast<uint32_t>(dpp_i<CTRL>(static_cast<int>(u & 0xffffffffu)));
+  const uint32_t hi = static_cast<uint32_t>(dpp_i<CTRL>(static_cast<int>(u >> 32)));
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Reductions over aligned groups of N <= 16 lanes.
+template <int N>
+__device__ __forceinline__ float group_max(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  if (N > 2) v = fmaxf(v, dpp_f<kDppXor2>(v));
+  if (N > 4) v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  if (N > 8) v = fmaxf(v, dpp_f<kDppMirror>(v));
+  return v;
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp_f<kDppXor1>(v);
+  if (N > 2) v += dpp_f<kDppXor2>(v);
+  if (N > 4) v += dpp_f<kDppHalfMirror>(v);
+  if (N > 8) v += dpp_f<kDppMirror>(v);
+  return v;
+}
+template <int N>
+__device__ __forceinline__ double group_sum(double v) {
+  v += dpp_d<kDppXor1>(v);
+  if (N > 2) v += dpp_d<kDppXor2>(v);
+  if (N > 4) v += dpp_d<kDppHalfMirror>(v);
+  if (N > 8) v += dpp_d<kDppMirror>(v);
+  return v;
+}
+// Best (value, index) over the group: larger value, ties to the lower index.
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& bv, int& bi) {
+  const float ov = dpp_f<CTRL>(bv);
+  const int oi = dpp_i<CTRL>(bi);
+  if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+}
+template <int N>
+__device__ __forceinline__ void group_argmax(float& bv, int& bi) {
+  argmax_step<kDppXor1>(bv, bi);
+  if (N > 2) argmax_step<kDppXor2>(bv, bi);
+  if (N > 4) argmax_step<kDppHalfMirror>(bv, bi);
+  if (N > 8) argmax_step<kDppMirror>(bv, bi);
+}
+
 // x[64 tokens, M] . Wg[E, M]^T -> lg[64][ls] (bf16, v_mfma_f32_32x32x16_bf16, fp32 sums).
 // K is streamed in row chunks of ROWB bytes through RouterPipe::kStages LDS stages, each
 // filled by buffer_load ... lds (lane i of a wave instruction -> 16 bytes at LDS unit i), so
@@ -294,14 +358,22 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
   const int n = tok0 + tl;
   float* row = lg + tl * ls;
 
+  static_assert(L == 16, "one token per 16-lane DPP row");
+  // The lane's logits (experts q + L i) stay in registers for the max, the sum and top-k.
+  constexpr int NV = EPAD / L;
+  float rv[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) rv[i] = q + L * i < E ? row[q + L * i] : -INFINITY;
   float mx = -INFINITY;
-  for (int e = q; e < E; e += L) mx = fmaxf(mx, row[e]);
 #pragma unroll
-  for (int off = 1; off < L; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  for (int i = 0; i < NV; ++i)
+    if (q + L * i < E) mx = fmaxf(mx, rv[i]);
+  mx = group_max<L>(mx);
   float se = 0.f;
-  for (int e = q; e < E; e += L) se += expf(row[e] - mx);
 #pragma unroll
-  for (int off = 1; off < L; off <<= 1) se += __shfl_xor(se, off, 64);
+  for (int i = 0; i < NV; ++i)
+    if (q + L * i < E) se += expf(rv[i] - mx);
+  se = group_sum<L>(se);
 
   // Group-limited routing ([Lec16] "DeepSeek V3 MoE (670B)"): the E experts form n_eg
   // contiguous groups; a group scores its best logit, and the topk_eg best groups (ties to
@@ -333,12 +405,7 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
           bd = d;
         }
       }
-#pragma unroll
-      for (int off = 1; off < L; off <<= 1) {
-        const float ov = __shfl_xor(bv, off, 64);
-        const int od = __shfl_xor(bd, off, 64);
-        if (ov > bv || (ov == bv && od < bd)) { bv = ov; bd = od; }
-      }
+      group_argmax<L>(bv, bd);
       open |= 1u << bd;
     }
     // experts of closed groups count as taken, so the top-k below never picks them
@@ -356,20 +423,16 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
     if (j < k) {
       float bv = -INFINITY;
       int bix = 0x7fffffff;
-      int i = 0;
-      for (int e = q; e < E; e += L, ++i) {
-        if (!((taken >> i) & 1u)) {
-          float v = row[e];
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int e = q + L * i;
+        if (e < E && !((taken >> i) & 1u)) {
+          float v = rv[i];
           if (v != v) v = -INFINITY;  // a NaN never wins, so bix is always a real expert
           if (v > bv || (v == bv && e < bix)) { bv = v; bix = e; }
         }
       }
-#pragma unroll
-      for (int off = 1; off < L; off <<= 1) {
-        const float ov = __shfl_xor(bv, off, 64);
-        const int oi = __shfl_xor(bix, off, 64);
-        if (ov > bv || (ov == bv && oi < bix)) { bv = ov; bix = oi; }
-      }
+      group_argmax<L>(bv, bix);
       sel_e[j] = bix;
       sel_l[j] = bv;
       if (bix % L == q) taken |= 1u << (bix / L);
@@ -433,7 +496,9 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
   }
   // Softmax probabilities for the block's column sums; each lane rewrites only its own
   // entries of its own row, which no other lane reads before the barrier.
-  for (int e = q; e < E; e += L) row[e] = valid ? expf(row[e] - mx) / se : 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    if (q + L * i < E) row[q + L * i] = valid ? expf(rv[i] - mx) / se : 0.f;
   __syncthreads();
 
   // Column sums of the probabilities: SPC consecutive lanes per expert, each summing every
@@ -444,8 +509,12 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
     double s = 0.0;
     if (e < E)
       for (int r = part; r < nt; r += SPC) s += static_cast<double>(lg[r * ls + e]);
+    if (SPC <= 16) {
+      s = group_sum<(SPC <= 16 ? SPC : 16)>(s);
+    } else {
 #pragma unroll
-    for (int off = 1; off < SPC; off <<= 1) s += __shfl_xor(s, off, 64);
+      for (int off = 1; off < SPC; off <<= 1) s += __shfl_xor(s, off, 64);
+    }
     if (e < E && part == 0) {
       const size_t o = (static_cast<size_t>(g) * E + e) * a.nbg + bi;
       a.psum[o] = s;
