@@ -320,13 +320,13 @@ int forward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* b
 
 // Workspace of moe_backward: the forward layout (routing buffers, dispatch rows, h, shared h,
 // and the shared-output buffer reused for the shared experts' dx), then the backward's own
-// regions.
+// regions.  Every GEMM reads its operands in place (weights and activations as K-major
+// operands where the contraction runs along their rows), so no transposed copies are kept.
 struct BwdLayout {
   Layout F;
-  size_t z1, o, dout, dh, dz1, dbuf, z1sh, dhsh, dz1sh, w1t, w2t, doT, hT, dz1T, bufT, dyT,
-      xT, hshT, dz1shT, dl, dw, partb, dlp, wgt, dxrt, dlT, src0, cnt, dst0, segblk, width, e2, e1,
+  size_t z1, o, dout, dh, dz1, dbuf, z1sh, dhsh, dz1sh, dl, dw, partb, dlp, wgt, dxrt, e2, e1, eh,
       eg, dwgp, total;
-  int64_t H1, RT, Npad, nchunks, Ep, nsplit, ksplit;
+  int64_t H1, nchunks, Ep, nsplit, ksplit;
 };
 
 int make_bwd_layout(const moe_cfg* c, BwdLayout* B) {
@@ -338,22 +338,22 @@ int make_bwd_layout(const moe_cfg* c, BwdLayout* B) {
   const int64_t H1 = c->act == MOE_ACT_SWIGLU ? 2 * H : H;
   B->H1 = H1;
   if (Es > 256) return MOE_EUNSUPPORTED;          // one setup thread per shared expert
-  B->RT = L.Rmax + 128 * E;                       // per-expert K padded to 128
-  B->Npad = (N + 127) / 128 * 128;
   B->nchunks = (N + 255) / 256;
   B->Ep = (E + 63) / 64 * 64;
   // dWg [E, M] contracts over all N tokens but has few output tiles: split the token axis
   // into ranges of a multiple of 128 tokens so that about 256 tiles run, partials in fp32
   {
     const int64_t tiles = ((E + 255) / 256) * ((M + 255) / 256);
-    int64_t S = std::max<int64_t>(1, std::min<int64_t>((256 + tiles - 1) / tiles, B->Npad / 128));
-    B->ksplit = std::max<int64_t>(128, (B->Npad / S + 127) / 128 * 128);
-    B->nsplit = (B->Npad + B->ksplit - 1) / B->ksplit;   // 0 for an empty batch
+    const int64_t Npad = (N + 127) / 128 * 128;
+    const int64_t S = std::max<int64_t>(1, std::min<int64_t>((256 + tiles - 1) / tiles, Npad / 128));
+    B->ksplit = std::max<int64_t>(128, (Npad / S + 127) / 128 * 128);
+    B->nsplit = (N + B->ksplit - 1) / B->ksplit;   // 0 for an empty batch
   }
+  // every operand a GEMM reads through a buffer resource stays under 2 GiB
   const int64_t lim = (int64_t{1} << 31) - 1;
-  if (L.rows_alloc * H1 > lim || (E + Es) * H1 * M > lim || H1 * B->RT > lim ||
-      std::max(M, Es * H1) * std::max(B->RT, B->Npad) > lim || N * Es * H1 > lim ||
-      B->Ep * B->Npad > lim)
+  const int64_t esz = L.esz, ra = L.rows_alloc;
+  if (ra * H1 * esz > lim || ra * M * esz > lim || (E + Es) * H1 * M * esz > lim ||
+      N * Es * H1 * esz > lim || N * std::max(M, B->Ep) * esz > lim || N * Es * H * esz > lim)
     return MOE_EUNSUPPORTED;
   size_t off = L.total;
   auto take = [&](size_t bytes) {
@@ -361,40 +361,25 @@ int make_bwd_layout(const moe_cfg* c, BwdLayout* B) {
     off = align_up(off + bytes, 256);
     return o;
   };
-  const size_t esz = static_cast<size_t>(L.esz), ra = static_cast<size_t>(L.rows_alloc);
-  B->z1 = take(ra * H1 * esz);
-  B->o = take(ra * M * esz);
-  B->dout = take(ra * M * esz);
-  B->dh = take(ra * H * esz);
-  B->dz1 = take(ra * H1 * esz);
-  B->dbuf = take(ra * M * esz);
-  B->z1sh = take(static_cast<size_t>(N * Es * H1) * esz);
-  B->dhsh = take(static_cast<size_t>(N * Es * H) * esz);
-  B->dz1sh = take(static_cast<size_t>(N * Es * H1) * esz);
-  B->w1t = take(static_cast<size_t>((E + Es) * H1 * M) * esz);
-  B->w2t = take(static_cast<size_t>((E + Es) * M * H) * esz);
-  B->doT = take(static_cast<size_t>(M * B->RT) * esz);
-  B->hT = take(static_cast<size_t>(H * B->RT) * esz);
-  B->dz1T = take(static_cast<size_t>(H1 * B->RT) * esz);
-  B->bufT = take(static_cast<size_t>(M * B->RT) * esz);
-  B->dyT = take(static_cast<size_t>(Es ? M * B->Npad : 0) * esz);
-  B->xT = take(static_cast<size_t>(M * B->Npad) * esz);
-  B->hshT = take(static_cast<size_t>(Es * H * B->Npad) * esz);
-  B->dz1shT = take(static_cast<size_t>(Es * H1 * B->Npad) * esz);
+  const size_t es = static_cast<size_t>(esz), rs = static_cast<size_t>(ra);
+  B->z1 = take(rs * H1 * es);
+  B->o = take(rs * M * es);
+  B->dout = take(rs * M * es);
+  B->dh = take(rs * H * es);
+  B->dz1 = take(rs * H1 * es);
+  B->dbuf = take(rs * M * es);
+  B->z1sh = take(static_cast<size_t>(N * Es * H1) * es);
+  B->dhsh = take(static_cast<size_t>(N * Es * H) * es);
+  B->dz1sh = take(static_cast<size_t>(N * Es * H1) * es);
   B->dl = take(static_cast<size_t>(N * E) * 4);
   B->dw = take(static_cast<size_t>(N * k) * 4);
   B->partb = take(static_cast<size_t>(B->nchunks * E) * 4);
-  B->dlp = take(static_cast<size_t>(N * B->Ep) * esz);
-  B->wgt = take(static_cast<size_t>(M * B->Ep) * esz);
-  B->dxrt = take(static_cast<size_t>(N * M) * esz);
-  B->dlT = take(static_cast<size_t>(B->Ep * B->Npad) * esz);
-  B->src0 = take(static_cast<size_t>(E) * 4);
-  B->cnt = take(static_cast<size_t>(E) * 4);
-  B->dst0 = take(static_cast<size_t>(E) * 4);
-  B->segblk = take(static_cast<size_t>(B->RT / 64 + 1) * 4);
-  B->width = take(16);
+  B->dlp = take(static_cast<size_t>(N * B->Ep) * es);
+  B->wgt = take(static_cast<size_t>(M * B->Ep) * es);
+  B->dxrt = take(static_cast<size_t>(N * M) * es);
   B->e2 = take(static_cast<size_t>(E + Es) * sizeof(moe::BatchEntry));
   B->e1 = take(static_cast<size_t>(E + Es) * sizeof(moe::BatchEntry));
+  B->eh = take(static_cast<size_t>(Es) * sizeof(moe::BatchEntry));
   B->eg = take(static_cast<size_t>(B->nsplit) * sizeof(moe::BatchEntry));
   B->dwgp = take(static_cast<size_t>(B->nsplit * E * M) * 4);
   B->total = off;
@@ -421,14 +406,16 @@ moe::GemmProblem dense_problem(const void* A, int64_t lda, const void* Bm, int64
   return p;
 }
 
+// Batched problem: entry i multiplies rows [0, rows) of A + a_off_i by B + b_off_i over its own
+// K into C + c_off_i (entries built on the device).
 moe::GemmProblem batched_problem(const void* A, int64_t lda, const void* Bm, int64_t ldb,
-                                 float* C, int64_t ldc, int N, int rows, int entries, int BM,
-                                 const moe::BatchEntry* batch) {
+                                 void* C, int64_t ldc, int N, int rows, int entries, int BM,
+                                 const moe::BatchEntry* batch, bool out_f32) {
   moe::GemmProblem p{};
   p.A = A; p.lda = lda; p.B = Bm; p.ldb = ldb; p.kseg = int64_t{1} << 30;  // no K segments
   p.C = C; p.ldc = ldc; p.N = N; p.K = 0; p.a_rows = rows; p.act = moe::kActNone;
   p.max_tiles = entries * ((rows + BM - 1) / BM); p.dense_rows = rows;
-  p.batch = batch; p.out_f32 = 1;
+  p.batch = batch; p.out_f32 = out_f32 ? 1 : 0;
   return p;
 }
 
@@ -495,6 +482,20 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
     if (p1) { g.p1 = *p1; g.nprob = 2; }
     return status_of(moe::launch_expert_gemm(g, s));
   };
+  // batched GEMM entries of the steps below, from the expert offsets
+  moe::BwdSetupArgs sa{};
+  sa.offset = m->offset;
+  sa.dw2 = reinterpret_cast<moe::BatchEntry*>(ws + B.e2);
+  sa.dw1 = reinterpret_cast<moe::BatchEntry*>(ws + B.e1);
+  sa.dhsh = reinterpret_cast<moe::BatchEntry*>(ws + B.eh);
+  sa.dwg = reinterpret_cast<moe::BatchEntry*>(ws + B.eg);
+  sa.E = static_cast<int>(E); sa.Es = static_cast<int>(Es); sa.M = static_cast<int>(M);
+  sa.H = static_cast<int>(H); sa.H1 = static_cast<int>(H1); sa.N = static_cast<int>(N);
+  sa.Ep = static_cast<int>(B.Ep);
+  sa.nsplit = static_cast<int>(B.nsplit);
+  sa.ksplit = static_cast<int>(B.ksplit);
+  rc = status_of(moe::launch_bwd_setup(sa, s));
+  if (rc) return rc;
   // 2. pre-activations z1 = buf W1_e^T (routed) and x W1_sh^T (shared), then h = act(z1)
   {
     auto p0 = routed_problem(ws + L.buf, M, W1, M, H1 * M, ws + B.z1, H1, static_cast<int>(H1),
@@ -528,24 +529,15 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
     rc = status_of(moe::launch_combine_bwd(cb, s));
     if (rc) return rc;
   }
-  // 5. transposed weights W2T [E', H, M], W1T [E', M, H1]
+  // 5. dh = do W2_e (routed), dy W2_{E+q} (shared, output columns q H); dz = dh act'(z1).
+  //    W2_e [M, H] is read in place as a K-major operand (k = m).
   {
-    moe::MatTransposeArgs t2{W2, ws + B.w2t, static_cast<int>(M), static_cast<int>(H),
-                             static_cast<int>(E + Es), dt};
-    rc = status_of(moe::launch_mat_transpose(t2, s));
-    if (rc) return rc;
-    moe::MatTransposeArgs t1{W1, ws + B.w1t, static_cast<int>(H1), static_cast<int>(M),
-                             static_cast<int>(E + Es), dt};
-    rc = status_of(moe::launch_mat_transpose(t1, s));
-    if (rc) return rc;
-  }
-  // 6. dh = do W2_e (routed), dy W2_sh (shared); dz = dh act'(z1)
-  {
-    auto p0 = routed_problem(ws + B.dout, M, ws + B.w2t, M, H * M, ws + B.dh, H,
-                             static_cast<int>(H), static_cast<int>(M), a_rows, L, tiles, ntiles);
-    auto p1 = dense_problem(dy, M, ws + B.w2t + E * H * M * esz, M, ws + B.dhsh, Es * H,
-                            static_cast<int>(Es * H), static_cast<int>(M),
-                            static_cast<int>(N), BM);
+    auto p0 = routed_problem(ws + B.dout, M, W2, H, M * H, ws + B.dh, H, static_cast<int>(H),
+                             static_cast<int>(M), a_rows, L, tiles, ntiles);
+    p0.b_kmajor = 1;
+    auto p1 = batched_problem(dy, M, W2, H, ws + B.dhsh, Es * H, static_cast<int>(H),
+                              static_cast<int>(N), static_cast<int>(Es), BM, sa.dhsh, false);
+    p1.b_kmajor = 1;
     rc = gemm(p0, Es ? &p1 : nullptr);
     if (rc) return rc;
     moe::BwdEltArgs ea{};
@@ -560,19 +552,20 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
       if (rc) return rc;
     }
   }
-  // 7. dx rows = dz W1_e (routed), shared: dz_sh [W1_sh...] (K segments of H1)
+  // 6. dx rows = dz W1_e (routed); shared: dz_sh W1_sh over k = (q, h'), whose K-major rows
+  //    are the consecutive rows of W1_{E..E+Es-1}
   {
-    auto p0 = routed_problem(ws + B.dz1, H1, ws + B.w1t, H1, M * H1, ws + B.dbuf, M,
+    auto p0 = routed_problem(ws + B.dz1, H1, W1, M, H1 * M, ws + B.dbuf, M,
                              static_cast<int>(M), static_cast<int>(H1), a_rows, L, tiles, ntiles);
-    auto p1 = dense_problem(ws + B.dz1sh, Es * H1, ws + B.w1t + E * M * H1 * esz, H1,
-                            ws + L.osh, M, static_cast<int>(M), static_cast<int>(Es * H1),
+    p0.b_kmajor = 1;
+    auto p1 = dense_problem(ws + B.dz1sh, Es * H1, W1c + E * H1 * M * esz, M, ws + L.osh, M,
+                            static_cast<int>(M), static_cast<int>(Es * H1),
                             static_cast<int>(N), BM);
-    p1.kseg = H1;
-    p1.seg_stride = M * H1;
+    p1.b_kmajor = 1;
     rc = gemm(p0, Es ? &p1 : nullptr);
     if (rc) return rc;
   }
-  // 8. router backward and dx
+  // 7. router backward and dx
   {
     moe::RouterBwdArgs ra{};
     ra.logits = m->logits; ra.topk_idx = m->topk_idx;
@@ -604,74 +597,30 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
     rc = status_of(moe::launch_dbg(wa, s));
     if (rc) return rc;
   }
-  // 9. weight gradients: per-expert K = kept rows padded to 128 (transposed compact buffers)
+  // 8. weight gradients, fp32: batched GEMMs over the experts with K = the expert's kept rows
+  //    (shared experts: all tokens), every operand read in place as a K-major operand
   {
-    moe::BwdSetupArgs sa{};
-    sa.offset = m->offset;
-    sa.src0 = reinterpret_cast<int32_t*>(ws + B.src0);
-    sa.cnt = reinterpret_cast<int32_t*>(ws + B.cnt);
-    sa.dst0 = reinterpret_cast<int32_t*>(ws + B.dst0);
-    sa.seg_of_blk = reinterpret_cast<int32_t*>(ws + B.segblk);
-    sa.width = reinterpret_cast<int32_t*>(ws + B.width);
-    sa.dw2 = reinterpret_cast<moe::BatchEntry*>(ws + B.e2);
-    sa.dw1 = reinterpret_cast<moe::BatchEntry*>(ws + B.e1);
-    sa.E = static_cast<int>(E); sa.Es = static_cast<int>(Es); sa.M = static_cast<int>(M);
-    sa.H = static_cast<int>(H); sa.H1 = static_cast<int>(H1);
-    sa.Npad = static_cast<int>(B.Npad);
-    sa.dwg = reinterpret_cast<moe::BatchEntry*>(ws + B.eg);
-    sa.nsplit = static_cast<int>(B.nsplit);
-    sa.ksplit = static_cast<int>(B.ksplit);
-    rc = status_of(moe::launch_bwd_setup(sa, s));
-    if (rc) return rc;
-    auto seg_t = [&](const void* X, size_t dst, int W) {
-      moe::TransposeArgs t{};
-      t.X = X; t.XT = ws + dst; t.seg_of_blk = sa.seg_of_blk; t.src0 = sa.src0; t.cnt = sa.cnt;
-      t.dst0 = sa.dst0; t.ncols_ptr = sa.width; t.W = W; t.ldT = B.RT; t.dtype = dt;
-      return status_of(moe::launch_seg_transpose(t, static_cast<int>(B.RT), s));
-    };
-    auto dense_t = [&](const void* X, size_t dst, int W) {
-      moe::TransposeArgs t{};
-      t.X = X; t.XT = ws + dst; t.ncols = static_cast<int>(B.Npad); t.rows = static_cast<int>(N);
-      t.W = W; t.ldT = B.Npad; t.dtype = dt;
-      return status_of(moe::launch_seg_transpose(t, static_cast<int>(B.Npad), s));
-    };
-    if ((rc = seg_t(ws + B.dout, B.doT, static_cast<int>(M)))) return rc;
-    if ((rc = seg_t(ws + L.h, B.hT, static_cast<int>(H)))) return rc;
-    if ((rc = seg_t(ws + B.dz1, B.dz1T, static_cast<int>(H1)))) return rc;
-    if ((rc = seg_t(ws + L.buf, B.bufT, static_cast<int>(M)))) return rc;
-    // dWg [E, M] = dl^T x over the padded token axis (fp32 out): one batched GEMM over
-    // token ranges into fp32 partials, then their sum in range order
-    if ((rc = dense_t(x, B.xT, static_cast<int>(M)))) return rc;
-    if ((rc = dense_t(ws + B.dlp, B.dlT, static_cast<int>(B.Ep)))) return rc;
-    {
-      float* part = reinterpret_cast<float*>(ws + B.dwgp);
-      auto p = batched_problem(ws + B.dlT, B.Npad, ws + B.xT, B.Npad, part, M,
-                               static_cast<int>(M), static_cast<int>(E),
-                               static_cast<int>(B.nsplit), BM, sa.dwg);
-      if ((rc = gemm(p, nullptr))) return rc;
-      if ((rc = status_of(moe::launch_split_reduce(part, dWg, E * M, static_cast<int>(B.nsplit), s))))
-        return rc;
-    }
-    if (Es) {
-      if ((rc = dense_t(dy, B.dyT, static_cast<int>(M)))) return rc;
-      if ((rc = dense_t(ws + L.hsh, B.hshT, static_cast<int>(Es * H)))) return rc;
-      if ((rc = dense_t(ws + B.dz1sh, B.dz1shT, static_cast<int>(Es * H1)))) return rc;
-    }
-    const moe::BatchEntry* e2 = sa.dw2;
-    const moe::BatchEntry* e1 = sa.dw1;
-    // dW2_e [M, H] = doT_e hT_e^T ; shared: dyT hshT_q^T
-    auto q0 = batched_problem(ws + B.doT, B.RT, ws + B.hT, B.RT, dW2, H, static_cast<int>(H),
-                              static_cast<int>(M), static_cast<int>(E), BM, e2);
-    auto q1 = batched_problem(ws + B.dyT, B.Npad, ws + B.hshT, B.Npad, dW2, H,
-                              static_cast<int>(H), static_cast<int>(M), static_cast<int>(Es), BM,
-                              e2 + E);
+    // dWg [E, M] = dl^T x: token ranges into fp32 partials, then their sum in range order
+    float* part = reinterpret_cast<float*>(ws + B.dwgp);
+    auto p = batched_problem(ws + B.dlp, B.Ep, x, M, part, M, static_cast<int>(M),
+                             static_cast<int>(E), static_cast<int>(B.nsplit), BM, sa.dwg, true);
+    p.a_kmajor = 1; p.b_kmajor = 1;
+    if ((rc = gemm(p, nullptr))) return rc;
+    if ((rc = status_of(moe::launch_split_reduce(part, dWg, E * M, static_cast<int>(B.nsplit), s))))
+      return rc;
+    // dW2_e [M, H] = dout_e^T h_e ; shared: dy^T hsh_q
+    auto q0 = batched_problem(ws + B.dout, M, ws + L.h, H, dW2, H, static_cast<int>(H),
+                              static_cast<int>(M), static_cast<int>(E), BM, sa.dw2, true);
+    auto q1 = batched_problem(dy, M, ws + L.hsh, Es * H, dW2, H, static_cast<int>(H),
+                              static_cast<int>(M), static_cast<int>(Es), BM, sa.dw2 + E, true);
+    q0.a_kmajor = q0.b_kmajor = q1.a_kmajor = q1.b_kmajor = 1;
     if ((rc = gemm(q0, Es ? &q1 : nullptr))) return rc;
-    // dW1_e [H1, M] = dz1T_e bufT_e^T ; shared: dz1shT_q xT^T
-    auto w0 = batched_problem(ws + B.dz1T, B.RT, ws + B.bufT, B.RT, dW1, M, static_cast<int>(M),
-                              static_cast<int>(H1), static_cast<int>(E), BM, e1);
-    auto w1 = batched_problem(ws + B.dz1shT, B.Npad, ws + B.xT, B.Npad, dW1, M,
-                              static_cast<int>(M), static_cast<int>(H1), static_cast<int>(Es), BM,
-                              e1 + E);
+    // dW1_e [H1, M] = dz1_e^T buf_e ; shared: dz1sh_q^T x
+    auto w0 = batched_problem(ws + B.dz1, H1, ws + L.buf, M, dW1, M, static_cast<int>(M),
+                              static_cast<int>(H1), static_cast<int>(E), BM, sa.dw1, true);
+    auto w1 = batched_problem(ws + B.dz1sh, Es * H1, x, M, dW1, M, static_cast<int>(M),
+                              static_cast<int>(H1), static_cast<int>(Es), BM, sa.dw1 + E, true);
+    w0.a_kmajor = w0.b_kmajor = w1.a_kmajor = w1.b_kmajor = 1;
     if ((rc = gemm(w0, Es ? &w1 : nullptr))) return rc;
   }
   return MOE_OK;

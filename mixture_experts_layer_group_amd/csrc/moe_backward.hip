@@ -177,119 +177,41 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(CombineBwdArgs a) {
   }
 }
 
-// Segmented transpose with zero padding: XT[w][dst0_s + i] = i < cnt_s ? X[src0_s + i][w] : 0
-// for every segment s (experts of the compact buffer, or one dense segment).  Blocks own
-// 64 x 64 tiles of XT; a tile's 64 columns lie inside one segment (segments are padded to
-// multiples of 128 columns), found through seg_of_blk.
-template <int DT>
-__global__ __launch_bounds__(256) void seg_transpose_kernel(TransposeArgs a) {
-  typedef typename std::conditional<DT == 1, uint16_t, float>::type E_t;
-  constexpr int V = 16 / sizeof(E_t);   // elements per 16-byte load
-  __shared__ E_t tile[64][64 + 2];
-  const int cb = blockIdx.x;          // 64-column block of XT
-  const int wb = blockIdx.y;          // 64-row block of XT (= column block of X)
-  const int ncols = a.ncols_ptr ? *a.ncols_ptr : a.ncols;
-  if (cb * 64 >= ncols) return;
-  const int s = a.seg_of_blk ? a.seg_of_blk[cb] : 0;
-  const int src0 = a.src0 ? a.src0[s] : 0;
-  const int cnt = a.cnt ? a.cnt[s] : a.rows;
-  const int dst0 = a.dst0 ? a.dst0[s] : 0;
-  const E_t* X = static_cast<const E_t*>(a.X);
-  E_t* XT = static_cast<E_t*>(a.XT);
-  const int t = threadIdx.x;
-  // load: 64 source rows x 64 columns, V columns per thread and step
-  for (int idx = t; idx < 64 * 64 / V; idx += 256) {
-    const int r = idx / (64 / V), c = (idx % (64 / V)) * V;
-    const int i = cb * 64 + r - dst0;       // index inside the segment
-    u32x4 v = u32x4{0u, 0u, 0u, 0u};
-    if (i < cnt) v = *reinterpret_cast<const u32x4*>(X + static_cast<int64_t>(src0 + i) * a.W + wb * 64 + c);
-    const E_t* e = reinterpret_cast<const E_t*>(&v);
-#pragma unroll
-    for (int x = 0; x < V; ++x) tile[r][c + x] = e[x];
-  }
-  __syncthreads();
-  // store: 64 rows of XT (columns w of X) x 64 columns, V columns per thread and step
-  for (int idx = t; idx < 64 * 64 / V; idx += 256) {
-    const int w = idx / (64 / V), c = (idx % (64 / V)) * V;
-    u32x4 v;
-    E_t* e = reinterpret_cast<E_t*>(&v);
-#pragma unroll
-    for (int x = 0; x < V; ++x) e[x] = tile[c + x][w];
-    *reinterpret_cast<u32x4*>(XT + static_cast<int64_t>(wb * 64 + w) * a.ldT + cb * 64 + c) = v;
-  }
-}
-
-// Batched matrix transpose: dst[b][c][r] = src[b][r][c] for [rows, cols] matrices.
-template <int DT>
-__global__ __launch_bounds__(256) void mat_transpose_kernel(MatTransposeArgs a) {
-  typedef typename std::conditional<DT == 1, uint16_t, float>::type E_t;
-  __shared__ E_t tile[64][65];
-  const int cb = blockIdx.x, rb = blockIdx.y, b = blockIdx.z;
-  const E_t* src = static_cast<const E_t*>(a.src) + static_cast<int64_t>(b) * a.rows * a.cols;
-  E_t* dst = static_cast<E_t*>(a.dst) + static_cast<int64_t>(b) * a.rows * a.cols;
-  const int t = threadIdx.x;
-  for (int idx = t; idx < 64 * 64; idx += 256) {
-    const int r = idx >> 6, c = idx & 63;
-    tile[r][c] = src[static_cast<int64_t>(rb * 64 + r) * a.cols + cb * 64 + c];
-  }
-  __syncthreads();
-  for (int idx = t; idx < 64 * 64; idx += 256) {
-    const int c = idx >> 6, r = idx & 63;
-    dst[static_cast<int64_t>(cb * 64 + c) * a.rows + rb * 64 + r] = tile[r][c];
-  }
-}
-
-// One block: per-expert padded K offsets of the transposed compact buffers (kofs[e] =
-// sum over e' < e of the expert's kept rows rounded up to 128), the segment of every
-// 64-column block, the padded width, and the batched weight-gradient GEMM entries.
+// One block: the batched GEMM entries of the weight gradients, which read the compact
+// buffers, x and dl in place as K-major operands (K = rows of the expert, or tokens).
+//   dW2_e [M, H]  = dout_e^T h_e        dW1_e [H1, M] = dz1_e^T buf_e
+//   shared q:       dy^T hsh_q                          dz1sh_q^T x
+//   dWg token range s [E, M] = dl_s^T x_s (fp32 partials)
+// and of the shared experts' dh_q = dy W2_{E+q} (K-major weights, output columns q H).
 __global__ __launch_bounds__(256) void bwd_setup_kernel(BwdSetupArgs a) {
-  __shared__ int sc[4];
   const int t = threadIdx.x, E = a.E;
-  int cnt = 0;
-  if (t < E) cnt = a.offset[t + 1] - a.offset[t];
-  const int pad = (cnt + 127) / 128 * 128;
-  // block exclusive scan of pad over 256 threads
-  const int lane = t & 63, w = t >> 6;
-  const int inc = wave_inclusive_scan(pad);
-  if (lane == 63) sc[w] = inc;
-  __syncthreads();
-  int before = 0, total = 0;
-  for (int i = 0; i < 4; ++i) {
-    if (i < w) before += sc[i];
-    total += sc[i];
-  }
-  const int kofs = before + inc - pad;
-  if (t < E) {
-    a.src0[t] = a.offset[t];
-    a.cnt[t] = cnt;
-    a.dst0[t] = kofs;
-    for (int b = kofs / 64; b < (kofs + pad) / 64; ++b) a.seg_of_blk[b] = t;
-    // dW2_e [M, H] = doT_e . hT_e^T ; dW1_e [H1, M] = dz1T_e . bufT_e^T
+  const int64_t M = a.M, H = a.H, H1 = a.H1;
+  for (int e = t; e < E; e += 256) {
+    const int64_t o = a.offset[e];
+    const int cnt = a.offset[e + 1] - a.offset[e];
     BatchEntry d2, d1;
-    d2.a_off = kofs; d2.b_off = kofs; d2.c_off = static_cast<int64_t>(t) * a.M * a.H;
-    d2.K = pad; d2.pad = 0;
-    d1.a_off = kofs; d1.b_off = kofs; d1.c_off = static_cast<int64_t>(t) * a.H1 * a.M;
-    d1.K = pad; d1.pad = 0;
-    a.dw2[t] = d2;
-    a.dw1[t] = d1;
+    d2.a_off = o * M; d2.b_off = o * H; d2.c_off = e * M * H; d2.K = cnt; d2.pad = 0;
+    d1.a_off = o * H1; d1.b_off = o * M; d1.c_off = e * H1 * M; d1.K = cnt; d1.pad = 0;
+    a.dw2[e] = d2;
+    a.dw1[e] = d1;
   }
-  if (t < a.Es) {  // shared experts: K = padded N, rows q of the transposed shared buffers
-    BatchEntry d2, d1;
-    d2.a_off = 0; d2.b_off = static_cast<int64_t>(t) * a.H * a.Npad;
-    d2.c_off = static_cast<int64_t>(E + t) * a.M * a.H; d2.K = a.Npad; d2.pad = 0;
-    d1.a_off = static_cast<int64_t>(t) * a.H1 * a.Npad; d1.b_off = 0;
-    d1.c_off = static_cast<int64_t>(E + t) * a.H1 * a.M; d1.K = a.Npad; d1.pad = 0;
-    a.dw2[E + t] = d2;
-    a.dw1[E + t] = d1;
+  for (int q = t; q < a.Es; q += 256) {  // shared experts: every token
+    BatchEntry d2, d1, dh;
+    d2.a_off = 0; d2.b_off = q * H; d2.c_off = (E + q) * M * H; d2.K = a.N; d2.pad = 0;
+    d1.a_off = q * H1; d1.b_off = 0; d1.c_off = (E + q) * H1 * M; d1.K = a.N; d1.pad = 0;
+    dh.a_off = 0; dh.b_off = (E + q) * M * H; dh.c_off = q * H; dh.K = static_cast<int>(M);
+    dh.pad = 0;
+    a.dw2[E + q] = d2;
+    a.dw1[E + q] = d1;
+    a.dhsh[q] = dh;
   }
-  for (int q = t; q < a.nsplit; q += 256) {  // dWg [E, M] = dlT . xT^T over token range q
+  for (int q = t; q < a.nsplit; q += 256) {  // dWg [E, M] over token range q
     BatchEntry g;
-    g.a_off = static_cast<int64_t>(q) * a.ksplit; g.b_off = g.a_off;
-    g.c_off = static_cast<int64_t>(q) * E * a.M;
-    g.K = min(a.ksplit, a.Npad - q * a.ksplit); g.pad = 0;
+    const int64_t n0 = static_cast<int64_t>(q) * a.ksplit;
+    g.a_off = n0 * a.Ep; g.b_off = n0 * M; g.c_off = static_cast<int64_t>(q) * E * M;
+    g.K = static_cast<int>(min<int64_t>(a.ksplit, a.N - n0)); g.pad = 0;
     a.dwg[q] = g;
   }
-  if (t == 0) *a.width = total;
 }
 
 // Router backward, one wave per token: dL/dp through the gate normalisation (none, sum or
@@ -523,26 +445,6 @@ hipError_t launch_combine_bwd(const CombineBwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(combine_bwd_kernel<1>, dim3(grid), dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(combine_bwd_kernel<0>, dim3(grid), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_seg_transpose(const TransposeArgs& a, int max_cols, hipStream_t s) {
-  const dim3 grid((max_cols + 63) / 64, a.W / 64);
-  if (grid.x == 0 || grid.y == 0) return hipSuccess;
-  if (a.dtype == 1)
-    hipLaunchKernelGGL(seg_transpose_kernel<1>, grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(seg_transpose_kernel<0>, grid, dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_mat_transpose(const MatTransposeArgs& a, hipStream_t s) {
-  const dim3 grid(a.cols / 64, a.rows / 64, a.batch);
-  if (grid.x == 0 || grid.y == 0 || grid.z == 0) return hipSuccess;
-  if (a.dtype == 1)
-    hipLaunchKernelGGL(mat_transpose_kernel<1>, grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(mat_transpose_kernel<0>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -67,6 +67,9 @@ struct Job {
   int64_t upb;     // gated problems: bytes from a gate row of B to its up row
   const int32_t* gather;  // A row of tile row r is gather[r] (A then points at row 0), or nullptr
   int64_t a_bytes;        // gathered A: readable bytes from A
+  // K-major operands ([K][rows], lda / ldb = pitch between k): A / B point at the tile's first
+  // row of k = 0
+  int akm, bkm;
 };
 
 // Load through the constant address space: for tables no kernel of this file writes (tile
@@ -132,15 +135,18 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& g, Job& j, int bid) 
   j.lda = P.lda * ESZ;
   j.gather = P.a_gather ? P.a_gather + row0 : nullptr;
   j.a_bytes = static_cast<int64_t>(P.a_rows) * j.lda;
+  j.akm = P.a_kmajor;
+  j.bkm = P.b_kmajor;
   j.A = static_cast<const char*>(P.A) + aoff * ESZ +
-        (P.a_gather ? 0 : static_cast<int64_t>(row0) * j.lda);
+        (P.a_kmajor ? static_cast<int64_t>(row0) * ESZ
+                    : P.a_gather ? 0 : static_cast<int64_t>(row0) * j.lda);
   j.ldb = P.ldb * ESZ;
   const int c0 = nt * BN;
   // first B row of the tile: output column c0, or for gated problems its gate row
   const int64_t brow = P.act == kActSwiglu
       ? static_cast<int64_t>(c0 / P.glu_h) * 2 * P.glu_h + c0 % P.glu_h : c0;
   j.B = static_cast<const char*>(P.B) + (static_cast<int64_t>(e) * P.b_stride + boff) * ESZ +
-        brow * j.ldb;
+        (P.b_kmajor ? static_cast<int64_t>(c0) * ESZ : brow * j.ldb);
   j.upb = static_cast<int64_t>(P.glu_h) * j.ldb;
   j.kseg = P.kseg;
   j.segb = P.seg_stride * ESZ;
@@ -257,54 +263,99 @@ struct Feed {
   uint32_t segoff;  // byte offset of that segment
   int kseg;         // elements per B segment
   uint32_t segb;    // bytes between B segments
+  uint32_t kstepa, kstepb;  // K-major operands: bytes per K chunk
 };
 
-// Load slot q of wave w fills LDS units [(w + NW q) 64, +64) of its operand: unit u is row
-// u / CPR, physical column u % CPR.
-template <class T, bool GLU>
+// K-major operand tiles in LDS: BK rows (one per k) of TILE * 2 bytes whose 16-byte units
+// are XOR-permuted by kmaj_swz(k), so that the four consecutive k one transposed read covers
+// fall on distinct banks.  The DMA applies the permutation on the global side.
+__device__ __forceinline__ int kmaj_swz(int k) { return (k & 3) << 2; }
+
+// Load slot q of wave w fills LDS units [(w + NW q) 64, +64) of its operand: for a row-major
+// operand unit u is row u / CPR, physical column u % CPR; for a K-major one, k-row u / UPR.
+template <class T, bool GLU, bool AKM, bool BKM>
 __device__ __forceinline__ void feed_init(const Job& j, int w, int lane, Feed<T>& f) {
   const uint32_t lda = static_cast<uint32_t>(j.lda), ldb = static_cast<uint32_t>(j.ldb);
-  f.ra = make_rsrc(j.A, j.gather ? j.a_bytes : static_cast<int64_t>(j.nrows) * j.lda);
-  const int nseg = max(1, (j.K + static_cast<int>(j.kseg) - 1) / static_cast<int>(j.kseg));
-  // Weight rows past the problem's N (a partial last n-tile) read as zeros.
-  f.rb = make_rsrc(j.B, (nseg - 1) * j.segb + (GLU ? j.upb : 0) +
-                            static_cast<int64_t>(j.ncols) * j.ldb);
+  static_assert(!(GLU && BKM), "a gated B is row-major");
+  // K-major operands: rows of k >= K read as zeros.  The range ends at the last k-row's valid
+  // columns rounded up to 16 bytes: a 16-byte load that crosses the end of a buffer range
+  // reads as zeros as a whole.  (Pitches are multiples of 16 bytes, so the rounded bytes stay
+  // inside that row.)
+  if (AKM) {
+    f.ra = make_rsrc(j.A, j.K > 0 ? static_cast<int64_t>(j.K - 1) * j.lda + ((j.nrows * 2 + 15) & ~15)
+                                  : 0);
+    constexpr int UPR = T::BM * 2 / 16;
 #pragma unroll
-  for (int q = 0; q < T::AQ; ++q) {
-    const int u = (w + T::NW * q) * 64 + lane, r = u / T::CPR;
-    const int c = (u % T::CPR) ^ lds_swz<T::ROW>(r);
-    // gathered rows: tile rows past nrows read row gather[0] (their outputs are not stored)
-    const uint32_t ar = j.gather ? static_cast<uint32_t>(j.gather[r < j.nrows ? r : 0]) : r;
-    f.aoff[q] = ar * lda + c * 16;
+    for (int q = 0; q < T::AQ; ++q) {
+      const int u = (w + T::NW * q) * 64 + lane, kr = u / UPR, c = (u % UPR) ^ kmaj_swz(kr);
+      f.aoff[q] = kr * lda + c * 16;
+    }
+  } else {
+    f.ra = make_rsrc(j.A, j.gather ? j.a_bytes : static_cast<int64_t>(j.nrows) * j.lda);
+#pragma unroll
+    for (int q = 0; q < T::AQ; ++q) {
+      const int u = (w + T::NW * q) * 64 + lane, r = u / T::CPR;
+      const int c = (u % T::CPR) ^ lds_swz<T::ROW>(r);
+      // gathered rows: tile rows past nrows read row gather[0] (their outputs are not stored)
+      const uint32_t ar = j.gather ? static_cast<uint32_t>(j.gather[r < j.nrows ? r : 0]) : r;
+      f.aoff[q] = ar * lda + c * 16;
+    }
   }
+  if (BKM) {
+    f.rb = make_rsrc(j.B, j.K > 0 ? static_cast<int64_t>(j.K - 1) * j.ldb + ((j.ncols * 2 + 15) & ~15)
+                                  : 0);
+    constexpr int UPR = T::BN * 2 / 16;
 #pragma unroll
-  for (int q = 0; q < T::BQ; ++q) {
-    const int u = (w + T::NW * q) * 64 + lane, r = u / T::CPR;
-    const int c = (u % T::CPR) ^ lds_swz<T::ROW>(r);
-    if (GLU)   // LDS row r: output column 32 (r / 64) + r % 32, gate or up half by bit 5
-      f.boff[q] = ((r >> 6) * 32 + (r & 31)) * ldb +
-                  ((r >> 5) & 1) * static_cast<uint32_t>(j.upb) + c * 16;
-    else
-      f.boff[q] = r * ldb + c * 16;
+    for (int q = 0; q < T::BQ; ++q) {
+      const int u = (w + T::NW * q) * 64 + lane, kr = u / UPR, c = (u % UPR) ^ kmaj_swz(kr);
+      f.boff[q] = kr * ldb + c * 16;
+    }
+  } else {
+    const int nseg = max(1, (j.K + static_cast<int>(j.kseg) - 1) / static_cast<int>(j.kseg));
+    // Weight rows past the problem's N (a partial last n-tile) read as zeros.
+    f.rb = make_rsrc(j.B, (nseg - 1) * j.segb + (GLU ? j.upb : 0) +
+                              static_cast<int64_t>(j.ncols) * j.ldb);
+#pragma unroll
+    for (int q = 0; q < T::BQ; ++q) {
+      const int u = (w + T::NW * q) * 64 + lane, r = u / T::CPR;
+      const int c = (u % T::CPR) ^ lds_swz<T::ROW>(r);
+      if (GLU)   // LDS row r: output column 32 (r / 64) + r % 32, gate or up half by bit 5
+        f.boff[q] = ((r >> 6) * 32 + (r & 31)) * ldb +
+                    ((r >> 5) & 1) * static_cast<uint32_t>(j.upb) + c * 16;
+      else
+        f.boff[q] = r * ldb + c * 16;
+    }
   }
   f.kin = 0;
   f.segoff = 0;
   f.kseg = static_cast<int>(j.kseg);
   f.segb = static_cast<uint32_t>(j.segb);
+  f.kstepa = static_cast<uint32_t>(T::BK) * lda;
+  f.kstepb = static_cast<uint32_t>(T::BK) * ldb;
 }
 
-// Issue this wave's loads of the A half of K chunk kt into LDS at As.
-template <class T>
+// Issue this wave's loads of the A half of K chunk kt into LDS at As.  K-major operands move
+// by whole k rows, through the per-lane offset so that the buffer bounds see the k rows.
+template <class T, bool AKM>
 __device__ __forceinline__ void feed_issue_a(const Feed<T>& f, unsigned char* As, int w, int kt) {
-  const uint32_t ka = static_cast<uint32_t>(kt) * T::ROW;
+  const uint32_t ka = static_cast<uint32_t>(kt) * (AKM ? f.kstepa : T::ROW);
 #pragma unroll
-  for (int q = 0; q < T::AQ; ++q) dma16(f.ra, As + (w + T::NW * q) * 1024, f.aoff[q], ka);
+  for (int q = 0; q < T::AQ; ++q) {
+    if (AKM) dma16(f.ra, As + (w + T::NW * q) * 1024, f.aoff[q] + ka, 0);
+    else dma16(f.ra, As + (w + T::NW * q) * 1024, f.aoff[q], ka);
+  }
 }
 
-// Issue this wave's loads of the B half of the next K chunk into LDS at Bs (B chunks are
-// issued in K order).
-template <class T>
-__device__ __forceinline__ void feed_issue_b(Feed<T>& f, unsigned char* Bs, int w) {
+// Issue this wave's loads of the B half of K chunk kt into LDS at Bs (B chunks are issued in
+// K order: a row-major B follows its K segments).
+template <class T, bool BKM>
+__device__ __forceinline__ void feed_issue_b(Feed<T>& f, unsigned char* Bs, int w, int kt) {
+  if (BKM) {
+    const uint32_t kb = static_cast<uint32_t>(kt) * f.kstepb;
+#pragma unroll
+    for (int q = 0; q < T::BQ; ++q) dma16(f.rb, Bs + (w + T::NW * q) * 1024, f.boff[q] + kb, 0);
+    return;
+  }
   const uint32_t kb = f.segoff + static_cast<uint32_t>(f.kin) * 2;
 #pragma unroll
   for (int q = 0; q < T::BQ; ++q) dma16(f.rb, Bs + (w + T::NW * q) * 1024, f.boff[q], kb);
@@ -315,16 +366,42 @@ __device__ __forceinline__ void feed_issue_b(Feed<T>& f, unsigned char* Bs, int 
 }
 
 // Issue K chunk kt (A then B) into one whole-chunk stage.
-template <class T>
+template <class T, bool AKM, bool BKM>
 __device__ __forceinline__ void feed_issue(Feed<T>& f, unsigned char* stage, int w, int kt) {
-  feed_issue_a(f, stage, w, kt);
-  feed_issue_b(f, stage + T::BM * T::ROW, w);
+  feed_issue_a<T, AKM>(f, stage, w, kt);
+  feed_issue_b<T, BKM>(f, stage + T::BM * T::ROW, w, kt);
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
+
+// MFMA operand fragment from a K-major tile with rows of RK bytes: row ibase + lane % 32,
+// k = 16 s + 8 (lane / 32) + 0..7, by two ds_read_b64_tr_b16.  Within each 16-lane group
+// that instruction hands lane i element i % 4 of the 8-byte loads of lanes 4 r + i / 4,
+// r = 0..3: lane i addresses k-row k0 + i / 4 at columns c0 + 4 (i % 4) .. + 3 and receives
+// column c0 + i of the k-rows k0 .. k0 + 3.
+template <int RK>
+__device__ __forceinline__ bf16x8 frag_kmajor(const unsigned char* S, int s, int ibase, int lane) {
+  const int i = lane & 15, g = lane >> 4;
+  const int col = ibase + 16 * (g & 1) + 4 * (i & 3);
+  u32x4 out;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int k = 16 * s + 8 * (g >> 1) + 4 * h + (i >> 2);
+    const unsigned char* p = S + k * RK + (((col >> 3) ^ kmaj_swz(k)) << 4) + (col & 7) * 2;
+    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16_ptr)(const_cast<unsigned char*>(p)));
+    const u32x2 x2 = __builtin_bit_cast(u32x2, v);
+    out[2 * h] = x2[0];
+    out[2 * h + 1] = x2[1];
+  }
+  return __builtin_bit_cast(bf16x8, out);
 }
 
 // Multiply one K chunk (A rows at As, B rows at Bs in LDS) into the wave's accumulators.
 // arow / brow: the wave's first A and B fragment rows for this lane; sw: the column swizzle
-// of those rows.
-template <class T>
+// of those rows (row-major operands).
+template <class T, bool AKM, bool BKM>
 __device__ __forceinline__ void mma_chunk(const unsigned char* As, const unsigned char* Bs,
                                           int arow, int brow, int lane, int sw,
                                           f32x16 (&acc)[T::TN][T::TM]) {
@@ -334,10 +411,12 @@ __device__ __forceinline__ void mma_chunk(const unsigned char* As, const unsigne
     bf16x8 af[T::TM], bfr[T::TN];
 #pragma unroll
     for (int im = 0; im < T::TM; ++im)
-      af[im] = *reinterpret_cast<const bf16x8*>(As + (arow + 32 * im) * T::ROW + phys);
+      af[im] = AKM ? frag_kmajor<T::BM * 2>(As, s, arow - (lane & 31) + 32 * im, lane)
+                   : *reinterpret_cast<const bf16x8*>(As + (arow + 32 * im) * T::ROW + phys);
 #pragma unroll
     for (int jn = 0; jn < T::TN; ++jn)
-      bfr[jn] = *reinterpret_cast<const bf16x8*>(Bs + (brow + 32 * jn) * T::ROW + phys);
+      bfr[jn] = BKM ? frag_kmajor<T::BN * 2>(Bs, s, brow - (lane & 31) + 32 * jn, lane)
+                    : *reinterpret_cast<const bf16x8*>(Bs + (brow + 32 * jn) * T::ROW + phys);
 #pragma unroll
     for (int jn = 0; jn < T::TN; ++jn)
 #pragma unroll
@@ -412,9 +491,11 @@ __device__ __forceinline__ void store_tile(const Job& j, f32x16 (&acc)[T::TN][T:
 }
 
 // One tile per block.
-template <int BM, int BN, int WN, int ACT, int BK, int NST, bool OUTF32>
+// KM: bit 0 = A is K-major, bit 1 = B is K-major.
+template <int BM, int BN, int WN, int ACT, int BK, int NST, bool OUTF32, int KM>
 __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
   using T = TileShape<BM, BN, WN, BK, NST>;
+  constexpr bool AKM = KM & 1, BKM = (KM >> 1) & 1;
   constexpr int SLOT = BM * T::ROW;   // one operand's rows of one chunk
   constexpr int SMEM = NST * T::STAGE > BM * BN * 2 ? NST * T::STAGE : BM * BN * 2;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
@@ -428,7 +509,7 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = w / WN, wn = w % WN;
   Feed<T> fd;
-  feed_init<T, GLU>(j, w, lane, fd);
+  feed_init<T, GLU, AKM, BKM>(j, w, lane, fd);
 
   f32x16 acc[T::TN][T::TM];
 #pragma unroll
@@ -449,24 +530,27 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
     else if (NST > 2 && ahead >= 1) MOE_WAIT_VMCNT(T::Q);
     else MOE_WAIT_VMCNT(0);
   };
-  const int KT = j.K / BK;  // 0 (a zero block) or >= NST - 1
+  // 0 (a zero block) or >= NST - 1; a K-major operand's last chunk may be partial
+  const int KT = (AKM || BKM) ? (j.K + BK - 1) / BK : j.K / BK;
   if (KT > 0) {
 #pragma unroll
-    for (int p = 0; p < NST - 1; ++p) feed_issue(fd, smem + p * T::STAGE, w, p);
+    for (int p = 0; p < NST - 1; ++p) feed_issue<T, AKM, BKM>(fd, smem + p * T::STAGE, w, p);
     int st = 0;
     for (int kt = 0; kt + NST - 1 < KT; ++kt) {
       wait_chunk(NST - 2);
       lds_barrier();
       const int sf = st == 0 ? NST - 1 : st - 1;  // (kt + NST - 1) % NST
-      feed_issue(fd, smem + sf * T::STAGE, w, kt + NST - 1);
-      mma_chunk<T>(smem + st * T::STAGE, smem + st * T::STAGE + SLOT, arow, brow, lane, sw, acc);
+      feed_issue<T, AKM, BKM>(fd, smem + sf * T::STAGE, w, kt + NST - 1);
+      mma_chunk<T, AKM, BKM>(smem + st * T::STAGE, smem + st * T::STAGE + SLOT, arow, brow, lane,
+                             sw, acc);
       st = st == NST - 1 ? 0 : st + 1;
     }
 #pragma unroll
     for (int i = 0; i < NST - 1; ++i) {  // the last NST - 1 chunks: nothing left to issue
       wait_chunk(NST - 2 - i);
       lds_barrier();
-      mma_chunk<T>(smem + st * T::STAGE, smem + st * T::STAGE + SLOT, arow, brow, lane, sw, acc);
+      mma_chunk<T, AKM, BKM>(smem + st * T::STAGE, smem + st * T::STAGE + SLOT, arow, brow, lane,
+                             sw, acc);
       st = st == NST - 1 ? 0 : st + 1;
     }
   }
@@ -480,9 +564,11 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
 // LDS B column n holds output 2 (n / 4) + n % 2, its gate row for n % 4 < 2 and its up row
 // otherwise, so a thread writes Swish(acc[i][jj]) * acc[i][jj + 2] for outputs 2 tx + jj,
 // jj < 2 (32 output columns per tile).
-template <bool GLU>
+template <bool GLU, int KM>
 __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs g) {
   constexpr int BM = 64, BN = 64, BK = 16, LDSW = 68;
+  constexpr bool AKM = KM & 1, BKM = (KM >> 1) & 1;
+  static_assert(!(GLU && BKM), "a gated B is row-major");
   __shared__ __attribute__((aligned(16))) float As[BK][LDSW];
   __shared__ __attribute__((aligned(16))) float Bs[BK][LDSW];
   Job j;
@@ -495,14 +581,32 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs g) {
   const int64_t boffs = GLU ? (2 * (lr >> 2) + (lr & 1)) * j.ldb + ((lr >> 1) & 1) * j.upb
                             : static_cast<int64_t>(lr) * j.ldb;
   const char* bp = j.B + boffs + lc * 4;
+  // K-major operands: thread t loads k-row kt BK + t / 16, columns 4 (t % 16) .. + 3; k-rows
+  // past K and columns past the tile's valid rows / columns load zeros
+  const int kr = t >> 4, kc = (t & 15) * 4;
   float acc[4][4] = {};
-  for (int kt = 0; kt < j.K / BK; ++kt) {
-    const f32x4 av = *reinterpret_cast<const f32x4*>(ap + static_cast<int64_t>(kt) * BK * 4);
-    const f32x4 bv = *reinterpret_cast<const f32x4*>(bp + bseg_offset(j, kt * BK, 4));
+  const int KT = (AKM || BKM) ? (j.K + BK - 1) / BK : j.K / BK;
+  for (int kt = 0; kt < KT; ++kt) {
+    const int kg = kt * BK + kr;
+    if (AKM) {
+      f32x4 av = {0.f, 0.f, 0.f, 0.f};
+      if (kg < j.K && kc < j.nrows)
+        av = *reinterpret_cast<const f32x4*>(j.A + static_cast<int64_t>(kg) * j.lda + kc * 4);
+      *reinterpret_cast<f32x4*>(&As[kr][kc]) = av;
+    } else {
+      const f32x4 av = *reinterpret_cast<const f32x4*>(ap + static_cast<int64_t>(kt) * BK * 4);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      As[lc + q][lr] = av[q];
-      Bs[lc + q][lr] = bv[q];
+      for (int q = 0; q < 4; ++q) As[lc + q][lr] = av[q];
+    }
+    if (BKM) {
+      f32x4 bv = {0.f, 0.f, 0.f, 0.f};
+      if (kg < j.K && kc < j.ncols)
+        bv = *reinterpret_cast<const f32x4*>(j.B + static_cast<int64_t>(kg) * j.ldb + kc * 4);
+      *reinterpret_cast<f32x4*>(&Bs[kr][kc]) = bv;
+    } else {
+      const f32x4 bv = *reinterpret_cast<const f32x4*>(bp + bseg_offset(j, kt * BK, 4));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) Bs[lc + q][lr] = bv[q];
     }
     __syncthreads();
 #pragma unroll
@@ -551,25 +655,46 @@ int gemm_block_n(int dtype, int act) {
 }
 
 hipError_t launch_expert_gemm(const GemmArgs& a, hipStream_t s) {
-  const int act = a.p0.act;  // both problems of one launch share the activation
+  const int act = a.p0.act;  // both problems of one launch share the activation and layouts
+  const int km = (a.p0.a_kmajor ? 1 : 0) | (a.p0.b_kmajor ? 2 : 0);
+  if (a.nprob > 1 && ((a.p1.a_kmajor ? 1 : 0) | (a.p1.b_kmajor ? 2 : 0)) != km)
+    return hipErrorInvalidValue;
+  // supported layouts: row-major (any activation); K-major B (no activation); K-major A and
+  // B (fp32 output)
+  if ((km == 2 && act != kActNone) || km == 1 || (km == 3 && !a.p0.out_f32) ||
+      (km != 0 && a.p0.a_gather))
+    return hipErrorInvalidValue;
   const int grid = grid_of(a, gemm_block_n(a.dtype, act));
   if (grid == 0) return hipSuccess;
+  const dim3 blk(128 * kGemmWN);
   if (a.dtype == 1) {
-#define MOE_GEMM_LAUNCH(ACTV)                                                                \
-  hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, kGemmWN, ACTV, kGemmBK, kGemmStages, false>), \
-                     dim3(grid), dim3(128 * kGemmWN), 0, s, a)
-    if (a.p0.out_f32)
-      hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, kGemmWN, kActNone, kGemmBK, kGemmStages, true>),
-                         dim3(grid), dim3(128 * kGemmWN), 0, s, a);
-    else if (act == kActRelu) MOE_GEMM_LAUNCH(kActRelu);
-    else if (act == kActGelu) MOE_GEMM_LAUNCH(kActGelu);
-    else if (act == kActSwiglu) MOE_GEMM_LAUNCH(kActSwiglu);
-    else MOE_GEMM_LAUNCH(kActNone);
+#define MOE_GEMM_LAUNCH(ACTV, OUTF, KMV)                                                    \
+  hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, kGemmWN, ACTV, kGemmBK, kGemmStages, OUTF, \
+                                       KMV>),                                             \
+                     dim3(grid), blk, 0, s, a)
+    if (a.p0.out_f32) {
+      if (km == 3) MOE_GEMM_LAUNCH(kActNone, true, 3);
+      else MOE_GEMM_LAUNCH(kActNone, true, 0);
+    } else if (km == 2) {
+      MOE_GEMM_LAUNCH(kActNone, false, 2);
+    } else if (act == kActRelu) {
+      MOE_GEMM_LAUNCH(kActRelu, false, 0);
+    } else if (act == kActGelu) {
+      MOE_GEMM_LAUNCH(kActGelu, false, 0);
+    } else if (act == kActSwiglu) {
+      MOE_GEMM_LAUNCH(kActSwiglu, false, 0);
+    } else {
+      MOE_GEMM_LAUNCH(kActNone, false, 0);
+    }
 #undef MOE_GEMM_LAUNCH
   } else if (act == kActSwiglu) {
-    hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((gemm_f32_kernel<true, 0>), dim3(grid), dim3(kThreads), 0, s, a);
+  } else if (km == 3) {
+    hipLaunchKernelGGL((gemm_f32_kernel<false, 3>), dim3(grid), dim3(kThreads), 0, s, a);
+  } else if (km == 2) {
+    hipLaunchKernelGGL((gemm_f32_kernel<false, 2>), dim3(grid), dim3(kThreads), 0, s, a);
   } else {
-    hipLaunchKernelGGL(gemm_f32_kernel<false>, dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((gemm_f32_kernel<false, 0>), dim3(grid), dim3(kThreads), 0, s, a);
   }
   return hipGetLastError();
 }

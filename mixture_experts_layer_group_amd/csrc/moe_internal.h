@@ -109,6 +109,10 @@ struct GemmProblem {
   int out_f32;            // C is fp32 (act must be none); else C has the input dtype
   const int32_t* a_gather;  // routed problems: A row of compact row r is a_gather[r] (nullptr:
                             // row r itself); lets GEMM 1 read the tokens of x directly
+  // K-major operands: stored [K][rows] with rows contiguous and lda / ldb the pitch between
+  // consecutive k (elements).  Rows of k >= K read as zeros, so K need not be a multiple of
+  // the GEMM's K chunk.  Not combined with a_gather, K segments or a gated B.
+  int a_kmajor, b_kmajor;
 };
 
 struct GemmArgs {
@@ -158,26 +162,12 @@ struct CombineBwdArgs {    // dw_nj = <dy_n, o_row>, do_row = w_nj dy_n
   int N, M, k, dtype;
 };
 
-struct TransposeArgs {     // XT[w][dst0_s + i] = i < cnt_s ? X[src0_s + i][w] : 0
-  const void* X; void* XT;
-  const int32_t* seg_of_blk;  // segment of each 64-column block of XT (nullptr: one segment)
-  const int32_t* src0; const int32_t* cnt; const int32_t* dst0;  // per segment (nullptr: dense)
-  const int32_t* ncols_ptr;   // device width of XT in use (nullptr: ncols)
-  int ncols, rows, W;         // rows: dense segment length; W: columns of X (multiple of 64)
-  int64_t ldT;
-  int dtype;
-};
-
-struct MatTransposeArgs {  // dst[b][c][r] = src[b][r][c], [rows, cols] multiples of 64
-  const void* src; void* dst; int rows, cols, batch, dtype;
-};
-
-struct BwdSetupArgs {      // padded per-expert K offsets and batched weight-gradient entries
+struct BwdSetupArgs {      // batched GEMM entries of the backward (built on the device)
   const int32_t* offset;   // [E+1] expert offsets of the compact buffer
-  int32_t* src0; int32_t* cnt; int32_t* dst0; int32_t* seg_of_blk; int32_t* width;
-  BatchEntry* dw2; BatchEntry* dw1;  // [E+Es]
+  BatchEntry* dw2; BatchEntry* dw1;  // [E+Es] weight gradients
+  BatchEntry* dhsh;                  // [Es] shared experts' dh
   BatchEntry* dwg;                   // [nsplit] token ranges of the router weight gradient
-  int E, Es, M, H, H1, Npad, nsplit, ksplit;
+  int E, Es, M, H, H1, N, Ep, nsplit, ksplit;
 };
 
 struct RouterBwdArgs {
@@ -206,8 +196,6 @@ struct RouterPrepArgs {    // dlp [N, Ep] = dl, wgt [M, Ep] = Wg^T (layer dtype,
 hipError_t launch_act_fwd(const BwdEltArgs& a, int64_t max_elems, hipStream_t s);
 hipError_t launch_act_bwd(const BwdEltArgs& a, int64_t max_elems, hipStream_t s);
 hipError_t launch_combine_bwd(const CombineBwdArgs& a, hipStream_t s);
-hipError_t launch_seg_transpose(const TransposeArgs& a, int max_cols, hipStream_t s);
-hipError_t launch_mat_transpose(const MatTransposeArgs& a, hipStream_t s);
 hipError_t launch_bwd_setup(const BwdSetupArgs& a, hipStream_t s);
 hipError_t launch_router_bwd(const RouterBwdArgs& a, hipStream_t s);
 hipError_t launch_dbg(const DwgArgs& a, hipStream_t s);
