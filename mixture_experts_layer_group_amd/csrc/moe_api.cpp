@@ -324,8 +324,8 @@ int forward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* b
 // operands where the contraction runs along their rows), so no transposed copies are kept.
 struct BwdLayout {
   Layout F;
-  size_t z1, o, dout, dh, dz1, dbuf, z1sh, dhsh, dz1sh, dl, dw, partb, dlp, wgt, dxrt, e2, e1, eh,
-      eg, dwgp, total;
+  size_t z1, o, dout, dz1, dbuf, z1sh, dz1sh, dl, dw, partb, dlp, wgt, dxrt, e2, e1, eh, eg, dwgp,
+      total;
   int64_t H1, nchunks, Ep, nsplit, ksplit;
 };
 
@@ -362,14 +362,13 @@ int make_bwd_layout(const moe_cfg* c, BwdLayout* B) {
     return o;
   };
   const size_t es = static_cast<size_t>(esz), rs = static_cast<size_t>(ra);
-  B->z1 = take(rs * H1 * es);
+  const bool relu = c->act == MOE_ACT_RELU;   // ReLU keeps h instead of z1
+  B->z1 = take(relu ? 0 : rs * H1 * es);
   B->o = take(rs * M * es);
   B->dout = take(rs * M * es);
-  B->dh = take(rs * H * es);
   B->dz1 = take(rs * H1 * es);
   B->dbuf = take(rs * M * es);
-  B->z1sh = take(static_cast<size_t>(N * Es * H1) * es);
-  B->dhsh = take(static_cast<size_t>(N * Es * H) * es);
+  B->z1sh = take(relu ? 0 : static_cast<size_t>(N * Es * H1) * es);
   B->dz1sh = take(static_cast<size_t>(N * Es * H1) * es);
   B->dl = take(static_cast<size_t>(N * E) * 4);
   B->dw = take(static_cast<size_t>(N * k) * 4);
@@ -496,8 +495,20 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
   sa.ksplit = static_cast<int>(B.ksplit);
   rc = status_of(moe::launch_bwd_setup(sa, s));
   if (rc) return rc;
-  // 2. pre-activations z1 = buf W1_e^T (routed) and x W1_sh^T (shared), then h = act(z1)
-  {
+  // 2. pre-activations z1 = buf W1_e^T (routed) and x W1_sh^T (shared), then h = act(z1).
+  //    ReLU needs no z1: ReLU'(z1) is 1 exactly where h > 0, so GEMM 1 writes h as in the
+  //    forward.
+  const bool relu = c->act == MOE_ACT_RELU;
+  if (relu) {
+    auto p0 = routed_problem(ws + L.buf, M, W1, M, H1 * M, ws + L.h, H, static_cast<int>(H),
+                             static_cast<int>(M), a_rows, L, tiles, ntiles);
+    auto p1 = dense_problem(x, M, W1c + E * H1 * M * esz, M, ws + L.hsh, Es * H,
+                            static_cast<int>(Es * H), static_cast<int>(M),
+                            static_cast<int>(N), BM);
+    p0.act = p1.act = moe::kActRelu;
+    rc = gemm(p0, Es ? &p1 : nullptr);
+    if (rc) return rc;
+  } else {
     auto p0 = routed_problem(ws + L.buf, M, W1, M, H1 * M, ws + B.z1, H1, static_cast<int>(H1),
                              static_cast<int>(M), a_rows, L, tiles, ntiles);
     auto p1 = dense_problem(x, M, W1c + E * H1 * M * esz, M, ws + B.z1sh, Es * H1,
@@ -529,28 +540,22 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
     rc = status_of(moe::launch_combine_bwd(cb, s));
     if (rc) return rc;
   }
-  // 5. dh = do W2_e (routed), dy W2_{E+q} (shared, output columns q H); dz = dh act'(z1).
-  //    W2_e [M, H] is read in place as a K-major operand (k = m).
+  // 5. dz = (do W2_e) act'(z1) (routed) and (dy W2_{E+q}) act'(z1sh) (shared, output columns
+  //    q H1): the GEMM applies the activation gradient in its epilogue and writes dz (for
+  //    SwiGLU dg and du), so dh is never stored.  W2_e [M, H] is read in place as a K-major
+  //    operand (k = m); z is z1, or h for ReLU (same layout: H1 = H).
   {
-    auto p0 = routed_problem(ws + B.dout, M, W2, H, M * H, ws + B.dh, H, static_cast<int>(H),
+    auto p0 = routed_problem(ws + B.dout, M, W2, H, M * H, ws + B.dz1, H1, static_cast<int>(H),
                              static_cast<int>(M), a_rows, L, tiles, ntiles);
-    p0.b_kmajor = 1;
-    auto p1 = batched_problem(dy, M, W2, H, ws + B.dhsh, Es * H, static_cast<int>(H),
+    auto p1 = batched_problem(dy, M, W2, H, ws + B.dz1sh, Es * H1, static_cast<int>(H),
                               static_cast<int>(N), static_cast<int>(Es), BM, sa.dhsh, false);
-    p1.b_kmajor = 1;
+    p0.b_kmajor = p1.b_kmajor = 1;
+    p0.dact = p1.dact = 1 + c->act;
+    p0.glu_h = p1.glu_h = static_cast<int>(H);
+    p0.z = relu ? ws + L.h : ws + B.z1;
+    p1.z = relu ? ws + L.hsh : ws + B.z1sh;
     rc = gemm(p0, Es ? &p1 : nullptr);
     if (rc) return rc;
-    moe::BwdEltArgs ea{};
-    ea.z = ws + B.z1; ea.dh = ws + B.dh; ea.dz = ws + B.dz1; ea.rows_ptr = Rdev; ea.nexp = 1;
-    ea.H = static_cast<int>(H); ea.act = c->act; ea.dtype = dt;
-    rc = status_of(moe::launch_act_bwd(ea, L.Rmax * H, s));
-    if (rc) return rc;
-    if (Es) {
-      ea.z = ws + B.z1sh; ea.dh = ws + B.dhsh; ea.dz = ws + B.dz1sh; ea.rows_ptr = nullptr;
-      ea.rows = static_cast<int>(N); ea.nexp = static_cast<int>(Es);
-      rc = status_of(moe::launch_act_bwd(ea, N * Es * H, s));
-      if (rc) return rc;
-    }
   }
   // 6. dx rows = dz W1_e (routed); shared: dz_sh W1_sh over k = (q, h'), whose K-major rows
   //    are the consecutive rows of W1_{E..E+Es-1}

@@ -37,18 +37,6 @@ __device__ __forceinline__ int rows_of(const BwdEltArgs& a) {
   return a.rows_ptr ? *a.rows_ptr : a.rows;
 }
 
-// GELU'(z) = Phi(z) + z phi(z), Phi(z) = (1 + erf(z / sqrt 2)) / 2, phi the normal density.
-__device__ __forceinline__ float gelu_grad(float z) {
-  const float Phi = 0.5f * (1.0f + erf_as7126(z * 0.70710678118654752440f));
-  return Phi + z * 0.39894228040143267794f * __expf(-0.5f * z * z);
-}
-
-// d/dz z sigmoid(z) = sigmoid(z) (1 + z (1 - sigmoid(z))).
-__device__ __forceinline__ float swish_grad(float z) {
-  const float s = __builtin_amdgcn_rcpf(1.0f + __expf(-z));
-  return s * (1.0f + z * (1.0f - s));
-}
-
 // 16-byte vectors of the layer dtype: 8 bf16 or 4 fp32 values.
 template <int DT>
 struct Vec {
@@ -108,43 +96,6 @@ __global__ __launch_bounds__(256) void act_fwd_kernel(BwdEltArgs a) {
   }
 }
 
-// dz = dh * act'(z); gated: dg = dh * u * Swish'(g), du = dh * Swish(g); 16 bytes per thread.
-template <int DT>
-__global__ __launch_bounds__(256) void act_bwd_kernel(BwdEltArgs a) {
-  constexpr int V = Vec<DT>::N;
-  const int rows = rows_of(a);
-  const int64_t W = static_cast<int64_t>(a.nexp) * a.H;
-  const int64_t total = static_cast<int64_t>(rows) * W / V;
-  const int H1 = a.act == kActSwiglu ? 2 * a.H : a.H;
-  for (int64_t iv = blockIdx.x * 256ll + threadIdx.x; iv < total; iv += static_cast<int64_t>(gridDim.x) * 256) {
-    const int64_t i = iv * V;
-    const int64_t r = i / W;
-    const int c = static_cast<int>(i - r * W);
-    const int q = c / a.H, cc = c - q * a.H;
-    const int64_t zi = r * a.nexp * H1 + static_cast<int64_t>(q) * H1 + cc;
-    Vec<DT> dh, z, out;
-    dh.load(a.dh, i);
-    z.load(a.z, zi);
-    if (a.act == kActSwiglu) {
-      Vec<DT> u, du;
-      u.load(a.z, zi + a.H);
-#pragma unroll
-      for (int x = 0; x < V; ++x) {
-        out.v[x] = dh.v[x] * u.v[x] * swish_grad(z.v[x]);
-        du.v[x] = dh.v[x] * swish(z.v[x]);
-      }
-      du.store(a.dz, zi + a.H);
-    } else if (a.act == kActGelu) {
-#pragma unroll
-      for (int x = 0; x < V; ++x) out.v[x] = dh.v[x] * gelu_grad(z.v[x]);
-    } else {
-#pragma unroll
-      for (int x = 0; x < V; ++x) out.v[x] = z.v[x] > 0.0f ? dh.v[x] : 0.0f;
-    }
-    out.store(a.dz, zi);
-  }
-}
-
 // One wave per token: dw_nj = <dy_n, o_row> for kept slots (0 otherwise), and
 // do_row = w_nj dy_n into the compact expert-major buffer; 16 bytes per lane.
 template <int DT>
@@ -182,7 +133,8 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(CombineBwdArgs a) {
 //   dW2_e [M, H]  = dout_e^T h_e        dW1_e [H1, M] = dz1_e^T buf_e
 //   shared q:       dy^T hsh_q                          dz1sh_q^T x
 //   dWg token range s [E, M] = dl_s^T x_s (fp32 partials)
-// and of the shared experts' dh_q = dy W2_{E+q} (K-major weights, output columns q H).
+// and of the shared experts' dz_q = (dy W2_{E+q}) act'(z_q) (K-major weights, output columns
+// q H1 of dz1sh).
 __global__ __launch_bounds__(256) void bwd_setup_kernel(BwdSetupArgs a) {
   const int t = threadIdx.x, E = a.E;
   const int64_t M = a.M, H = a.H, H1 = a.H1;
@@ -199,7 +151,7 @@ __global__ __launch_bounds__(256) void bwd_setup_kernel(BwdSetupArgs a) {
     BatchEntry d2, d1, dh;
     d2.a_off = 0; d2.b_off = q * H; d2.c_off = (E + q) * M * H; d2.K = a.N; d2.pad = 0;
     d1.a_off = q * H1; d1.b_off = 0; d1.c_off = (E + q) * H1 * M; d1.K = a.N; d1.pad = 0;
-    dh.a_off = 0; dh.b_off = (E + q) * M * H; dh.c_off = q * H; dh.K = static_cast<int>(M);
+    dh.a_off = 0; dh.b_off = (E + q) * M * H; dh.c_off = q * H1; dh.K = static_cast<int>(M);
     dh.pad = 0;
     a.dw2[E + q] = d2;
     a.dw1[E + q] = d1;
@@ -426,15 +378,6 @@ hipError_t launch_act_fwd(const BwdEltArgs& a, int64_t max_elems, hipStream_t s)
     hipLaunchKernelGGL(act_fwd_kernel<1>, dim3(grid_for(max_elems)), dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(act_fwd_kernel<0>, dim3(grid_for(max_elems)), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_act_bwd(const BwdEltArgs& a, int64_t max_elems, hipStream_t s) {
-  if (max_elems == 0) return hipSuccess;
-  if (a.dtype == 1)
-    hipLaunchKernelGGL(act_bwd_kernel<1>, dim3(grid_for(max_elems)), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(act_bwd_kernel<0>, dim3(grid_for(max_elems)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -55,6 +55,18 @@ __device__ __forceinline__ float swish(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
+// GELU'(z) = Phi(z) + z phi(z), Phi(z) = (1 + erf(z / sqrt 2)) / 2, phi the normal density.
+__device__ __forceinline__ float gelu_grad(float z) {
+  const float Phi = 0.5f * (1.0f + erf_as7126(z * 0.70710678118654752440f));
+  return Phi + z * 0.39894228040143267794f * __expf(-0.5f * z * z);
+}
+
+// d/dz z sigmoid(z) = sigmoid(z) (1 + z (1 - sigmoid(z))).
+__device__ __forceinline__ float swish_grad(float z) {
+  const float s = __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+  return s * (1.0f + z * (1.0f - s));
+}
+
 __device__ __forceinline__ float apply_act(float z, int act) {
   if (act == 0) return fmaxf(z, 0.0f);
   if (act == 1) return gelu_erf(z);

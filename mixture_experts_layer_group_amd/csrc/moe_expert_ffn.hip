@@ -70,6 +70,8 @@ struct Job {
   // K-major operands ([K][rows], lda / ldb = pitch between k): A / B point at the tile's first
   // row of k = 0
   int akm, bkm;
+  const char* Z;   // fused activation gradient: z at the tile's first element (C's layout)
+  int64_t zup;     // gated: bytes from a g column to its u column (in z and in C)
 };
 
 // Load through the constant address space: for tables no kernel of this file writes (tile
@@ -153,6 +155,8 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& g, Job& j, int bid) 
   j.ldc = P.ldc * osz;
   j.C = static_cast<char*>(P.C) + coff * osz + static_cast<int64_t>(row0) * j.ldc +
         static_cast<int64_t>(c0) * osz;
+  j.Z = P.z ? static_cast<const char*>(P.z) + (j.C - static_cast<char*>(P.C)) : nullptr;
+  j.zup = static_cast<int64_t>(P.glu_h) * osz;
   j.K = K;
   j.nrows = nrows;
   j.ncols = min(BN, P.N - nt * BN);
@@ -426,12 +430,49 @@ __device__ __forceinline__ void mma_chunk(const unsigned char* As, const unsigne
   }
 }
 
+// Activation gradient on 8 bf16 values: out = d * act'(z) (gated: dg = d u Swish'(g) at cp and
+// du = d Swish(g) zup bytes later, z = g at zp and u zup bytes later).
+__device__ __forceinline__ void unpack_bf16x8(u32x4 v, float (&f)[8]) {
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    f[2 * x] = __builtin_bit_cast(float, v[x] << 16);
+    f[2 * x + 1] = __builtin_bit_cast(float, v[x] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ u32x4 pack_bf16x8(const float (&f)[8]) {
+  u32x4 v;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) v[x] = pack_bf16x2(f[2 * x], f[2 * x + 1]);
+  return v;
+}
+template <int DACT>
+__device__ __forceinline__ void dact_bf16x8(u32x4 d, const char* zp, int64_t zup, char* cp) {
+  float dv[8], zv[8], o[8];
+  unpack_bf16x8(d, dv);
+  unpack_bf16x8(*reinterpret_cast<const u32x4*>(zp), zv);
+  if (DACT == kActSwiglu) {
+    float uv[8], du[8];
+    unpack_bf16x8(*reinterpret_cast<const u32x4*>(zp + zup), uv);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      o[x] = dv[x] * uv[x] * swish_grad(zv[x]);
+      du[x] = dv[x] * swish(zv[x]);
+    }
+    *reinterpret_cast<u32x4*>(cp + zup) = pack_bf16x8(du);
+  } else {
+#pragma unroll
+    for (int x = 0; x < 8; ++x)
+      o[x] = DACT == kActGelu ? dv[x] * gelu_grad(zv[x]) : (zv[x] > 0.0f ? dv[x] : 0.0f);
+  }
+  *reinterpret_cast<u32x4*>(cp) = pack_bf16x8(o);
+}
+
 // bf16 epilogue through LDS: D[feature][token] -> tile[token][feature] (rows of OUTN*2 bytes,
 // NCH 16-byte columns XOR (row % NCH)), then whole rows to global memory, 16 bytes per lane.
 // The staging area holds STG bytes; a tile that does not fit goes through it in passes of
 // whole wave-row blocks.  The caller has made the area free (a barrier after its last read);
 // on return every wave's last reads of it are issued but not waited for.
-template <class T, int ACT, int STG, bool F32 = false>
+template <class T, int ACT, int STG, bool F32 = false, int DACT = -1>
 __device__ __forceinline__ void store_tile(const Job& j, f32x16 (&acc)[T::TN][T::TM],
                                            unsigned char* stg, int t, int lane, int wm,
                                            int wn) {
@@ -480,19 +521,24 @@ __device__ __forceinline__ void store_tile(const Job& j, f32x16 (&acc)[T::TN][T:
     }
     lds_barrier();
     const int rows = min(RP, j.nrows - p * RP);
-    char* C = j.C + static_cast<int64_t>(p * RP) * j.ldc;
+    const int64_t poff = static_cast<int64_t>(p * RP) * j.ldc;
+    char* C = j.C + poff;
     for (int i = t; i < rows * NCH; i += T::NT) {
       const int r = i / NCH, c = i - r * NCH;
       if (c >= ncch) continue;
       const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * RB + ((c ^ (r & (NCH - 1))) << 4));
-      *reinterpret_cast<u32x4*>(C + static_cast<int64_t>(r) * j.ldc + c * 16) = v;
+      const int64_t o = static_cast<int64_t>(r) * j.ldc + c * 16;
+      if (DACT < 0)
+        *reinterpret_cast<u32x4*>(C + o) = v;
+      else   // fused activation gradient: z has C's layout
+        dact_bf16x8<DACT>(v, j.Z + poff + o, j.zup, C + o);
     }
   }
 }
 
 // One tile per block.
-// KM: bit 0 = A is K-major, bit 1 = B is K-major.
-template <int BM, int BN, int WN, int ACT, int BK, int NST, bool OUTF32, int KM>
+// KM: bit 0 = A is K-major, bit 1 = B is K-major.  DACT: fused activation gradient (-1: none).
+template <int BM, int BN, int WN, int ACT, int BK, int NST, bool OUTF32, int KM, int DACT>
 __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
   using T = TileShape<BM, BN, WN, BK, NST>;
   constexpr bool AKM = KM & 1, BKM = (KM >> 1) & 1;
@@ -557,14 +603,14 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
 
   lds_barrier();
   // fp32 output (the weight-gradient GEMMs): rows of 1 KB, staged in passes of 128 rows
-  store_tile<T, ACT, SMEM, OUTF32>(j, acc, smem, t, lane, wm, wn);
+  store_tile<T, ACT, SMEM, OUTF32, DACT>(j, acc, smem, t, lane, wm, wn);
 }
 
 // Thread (ty, tx) accumulates rows 4 ty + i and LDS B columns 4 tx + jj.  Gated problems:
 // LDS B column n holds output 2 (n / 4) + n % 2, its gate row for n % 4 < 2 and its up row
 // otherwise, so a thread writes Swish(acc[i][jj]) * acc[i][jj + 2] for outputs 2 tx + jj,
 // jj < 2 (32 output columns per tile).
-template <bool GLU, int KM>
+template <bool GLU, int KM, int DACT>
 __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs g) {
   constexpr int BM = 64, BN = 64, BK = 16, LDSW = 68;
   constexpr bool AKM = KM & 1, BKM = (KM >> 1) & 1;
@@ -629,6 +675,26 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs g) {
       o[0] = swish(acc[i][0]) * acc[i][2];
       o[1] = swish(acc[i][1]) * acc[i][3];
       *reinterpret_cast<f32x2*>(j.C + static_cast<int64_t>(r) * j.ldc + tx * 8) = o;
+    } else if (DACT >= 0) {   // fused activation gradient: z has C's layout
+      const int64_t o = static_cast<int64_t>(r) * j.ldc + tx * 16;
+      const f32x4 z = *reinterpret_cast<const f32x4*>(j.Z + o);
+      f32x4 d;
+      if (DACT == kActSwiglu) {
+        const f32x4 u = *reinterpret_cast<const f32x4*>(j.Z + o + j.zup);
+        f32x4 du;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          d[jj] = acc[i][jj] * u[jj] * swish_grad(z[jj]);
+          du[jj] = acc[i][jj] * swish(z[jj]);
+        }
+        *reinterpret_cast<f32x4*>(j.C + o + j.zup) = du;
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          d[jj] = DACT == kActGelu ? acc[i][jj] * gelu_grad(z[jj])
+                                   : (z[jj] > 0.0f ? acc[i][jj] : 0.0f);
+      }
+      *reinterpret_cast<f32x4*>(j.C + o) = d;
     } else {
       f32x4 o;
 #pragma unroll
@@ -657,44 +723,55 @@ int gemm_block_n(int dtype, int act) {
 hipError_t launch_expert_gemm(const GemmArgs& a, hipStream_t s) {
   const int act = a.p0.act;  // both problems of one launch share the activation and layouts
   const int km = (a.p0.a_kmajor ? 1 : 0) | (a.p0.b_kmajor ? 2 : 0);
-  if (a.nprob > 1 && ((a.p1.a_kmajor ? 1 : 0) | (a.p1.b_kmajor ? 2 : 0)) != km)
+  const int dact = a.p0.dact;  // 0: none, else 1 + activation code
+  if (a.nprob > 1 && (((a.p1.a_kmajor ? 1 : 0) | (a.p1.b_kmajor ? 2 : 0)) != km ||
+                      a.p1.dact != dact))
     return hipErrorInvalidValue;
-  // supported layouts: row-major (any activation); K-major B (no activation); K-major A and
-  // B (fp32 output)
+  // supported layouts: row-major (any activation); K-major B (no activation, optionally the
+  // fused activation gradient); K-major A and B (fp32 output)
   if ((km == 2 && act != kActNone) || km == 1 || (km == 3 && !a.p0.out_f32) ||
-      (km != 0 && a.p0.a_gather))
+      (km != 0 && a.p0.a_gather) || (dact && (km != 2 || !a.p0.z)) || dact < 0 || dact > 3)
     return hipErrorInvalidValue;
   const int grid = grid_of(a, gemm_block_n(a.dtype, act));
   if (grid == 0) return hipSuccess;
   const dim3 blk(128 * kGemmWN);
   if (a.dtype == 1) {
-#define MOE_GEMM_LAUNCH(ACTV, OUTF, KMV)                                                    \
+#define MOE_GEMM_LAUNCH(ACTV, OUTF, KMV, DACTV)                                             \
   hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, kGemmWN, ACTV, kGemmBK, kGemmStages, OUTF, \
-                                       KMV>),                                             \
+                                       KMV, DACTV>),                                      \
                      dim3(grid), blk, 0, s, a)
     if (a.p0.out_f32) {
-      if (km == 3) MOE_GEMM_LAUNCH(kActNone, true, 3);
-      else MOE_GEMM_LAUNCH(kActNone, true, 0);
+      if (km == 3) MOE_GEMM_LAUNCH(kActNone, true, 3, -1);
+      else MOE_GEMM_LAUNCH(kActNone, true, 0, -1);
     } else if (km == 2) {
-      MOE_GEMM_LAUNCH(kActNone, false, 2);
+      if (dact == 1 + kActRelu) MOE_GEMM_LAUNCH(kActNone, false, 2, kActRelu);
+      else if (dact == 1 + kActGelu) MOE_GEMM_LAUNCH(kActNone, false, 2, kActGelu);
+      else if (dact == 1 + kActSwiglu) MOE_GEMM_LAUNCH(kActNone, false, 2, kActSwiglu);
+      else MOE_GEMM_LAUNCH(kActNone, false, 2, -1);
     } else if (act == kActRelu) {
-      MOE_GEMM_LAUNCH(kActRelu, false, 0);
+      MOE_GEMM_LAUNCH(kActRelu, false, 0, -1);
     } else if (act == kActGelu) {
-      MOE_GEMM_LAUNCH(kActGelu, false, 0);
+      MOE_GEMM_LAUNCH(kActGelu, false, 0, -1);
     } else if (act == kActSwiglu) {
-      MOE_GEMM_LAUNCH(kActSwiglu, false, 0);
+      MOE_GEMM_LAUNCH(kActSwiglu, false, 0, -1);
     } else {
-      MOE_GEMM_LAUNCH(kActNone, false, 0);
+      MOE_GEMM_LAUNCH(kActNone, false, 0, -1);
     }
 #undef MOE_GEMM_LAUNCH
   } else if (act == kActSwiglu) {
-    hipLaunchKernelGGL((gemm_f32_kernel<true, 0>), dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((gemm_f32_kernel<true, 0, -1>), dim3(grid), dim3(kThreads), 0, s, a);
   } else if (km == 3) {
-    hipLaunchKernelGGL((gemm_f32_kernel<false, 3>), dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((gemm_f32_kernel<false, 3, -1>), dim3(grid), dim3(kThreads), 0, s, a);
   } else if (km == 2) {
-    hipLaunchKernelGGL((gemm_f32_kernel<false, 2>), dim3(grid), dim3(kThreads), 0, s, a);
+#define MOE_F32_DACT(DACTV) \
+  hipLaunchKernelGGL((gemm_f32_kernel<false, 2, DACTV>), dim3(grid), dim3(kThreads), 0, s, a)
+    if (dact == 1 + kActRelu) MOE_F32_DACT(kActRelu);
+    else if (dact == 1 + kActGelu) MOE_F32_DACT(kActGelu);
+    else if (dact == 1 + kActSwiglu) MOE_F32_DACT(kActSwiglu);
+    else MOE_F32_DACT(-1);
+#undef MOE_F32_DACT
   } else {
-    hipLaunchKernelGGL((gemm_f32_kernel<false, 0>), dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((gemm_f32_kernel<false, 0, -1>), dim3(grid), dim3(kThreads), 0, s, a);
   }
   return hipGetLastError();
 }

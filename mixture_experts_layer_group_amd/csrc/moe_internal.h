@@ -113,6 +113,12 @@ struct GemmProblem {
   // consecutive k (elements).  Rows of k >= K read as zeros, so K need not be a multiple of
   // the GEMM's K chunk.  Not combined with a_gather, K segments or a gated B.
   int a_kmajor, b_kmajor;
+  // Fused activation gradient (dgrad of GEMM 2): 0 = off, else 1 + the activation code.  The
+  // product d (the gradient at the activation's output) is written as d * act'(z) to C, where
+  // z has C's layout (same offsets and pitch); gated: z holds [g | u] with the u half
+  // glu_h columns after the g half, and C receives dg there and du glu_h columns later.
+  const void* z;
+  int dact;
 };
 
 struct GemmArgs {
@@ -147,11 +153,9 @@ struct EmptyArgs {         // N == 0: zero the small outputs (aux, z_loss, dev_l
 
 // ---- backward pass (moe_backward.hip)
 
-struct BwdEltArgs {        // elementwise activation forward / backward over rows
+struct BwdEltArgs {        // elementwise activation over rows (the backward's recompute)
   const void* z;           // [rows, nexp * H1] pre-activations (H1 = 2H for gated experts)
-  void* h;                 // [rows, nexp * H] activations (forward)
-  const void* dh;          // [rows, nexp * H] (backward)
-  void* dz;                // [rows, nexp * H1] (backward)
+  void* h;                 // [rows, nexp * H] activations
   const int32_t* rows_ptr; // device row count (nullptr: rows)
   int rows, nexp, H, act, dtype;
 };
@@ -194,7 +198,6 @@ struct RouterPrepArgs {    // dlp [N, Ep] = dl, wgt [M, Ep] = Wg^T (layer dtype,
 };
 
 hipError_t launch_act_fwd(const BwdEltArgs& a, int64_t max_elems, hipStream_t s);
-hipError_t launch_act_bwd(const BwdEltArgs& a, int64_t max_elems, hipStream_t s);
 hipError_t launch_combine_bwd(const CombineBwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_setup(const BwdSetupArgs& a, hipStream_t s);
 hipError_t launch_router_bwd(const RouterBwdArgs& a, hipStream_t s);
