@@ -325,8 +325,8 @@ int forward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* b
 struct BwdLayout {
   Layout F;
   size_t z1, o, dout, dz1, dbuf, z1sh, dz1sh, dl, dw, partb, dlp, wgt, dxrt, e2, e1, eh, eg, dwgp,
-      total;
-  int64_t H1, nchunks, Ep, nsplit, ksplit;
+      shp2, shp1, total;
+  int64_t H1, nchunks, Ep, nsplit, ksplit, nshared, kshared;
 };
 
 int make_bwd_layout(const moe_cfg* c, BwdLayout* B) {
@@ -348,6 +348,15 @@ int make_bwd_layout(const moe_cfg* c, BwdLayout* B) {
     const int64_t S = std::max<int64_t>(1, std::min<int64_t>((256 + tiles - 1) / tiles, Npad / 128));
     B->ksplit = std::max<int64_t>(128, (Npad / S + 127) / 128 * 128);
     B->nsplit = (N + B->ksplit - 1) / B->ksplit;   // 0 for an empty batch
+  }
+  // The shared experts' weight gradients contract over all N tokens: split that axis into
+  // ranges about as long as a routed expert's kept rows (N k / E), so that their tiles are not
+  // a tail of the launch; partials in fp32 (at most 32 ranges)
+  {
+    const int64_t avg = (N * k + E - 1) / std::max<int64_t>(E, 1);
+    B->kshared = std::max<int64_t>(512, (avg + 127) / 128 * 128);
+    B->kshared = std::max(B->kshared, (N + 31) / 32);
+    B->nshared = Es ? (N + B->kshared - 1) / B->kshared : 0;
   }
   // every operand a GEMM reads through a buffer resource stays under 2 GiB
   const int64_t lim = (int64_t{1} << 31) - 1;
@@ -376,11 +385,13 @@ int make_bwd_layout(const moe_cfg* c, BwdLayout* B) {
   B->dlp = take(static_cast<size_t>(N * B->Ep) * es);
   B->wgt = take(static_cast<size_t>(M * B->Ep) * es);
   B->dxrt = take(static_cast<size_t>(N * M) * es);
-  B->e2 = take(static_cast<size_t>(E + Es) * sizeof(moe::BatchEntry));
-  B->e1 = take(static_cast<size_t>(E + Es) * sizeof(moe::BatchEntry));
+  B->e2 = take(static_cast<size_t>(E + Es * B->nshared) * sizeof(moe::BatchEntry));
+  B->e1 = take(static_cast<size_t>(E + Es * B->nshared) * sizeof(moe::BatchEntry));
   B->eh = take(static_cast<size_t>(Es) * sizeof(moe::BatchEntry));
   B->eg = take(static_cast<size_t>(B->nsplit) * sizeof(moe::BatchEntry));
   B->dwgp = take(static_cast<size_t>(B->nsplit * E * M) * 4);
+  B->shp2 = take(static_cast<size_t>(Es * B->nshared * M * H) * 4);
+  B->shp1 = take(static_cast<size_t>(Es * B->nshared * H1 * M) * 4);
   B->total = off;
   return MOE_OK;
 }
@@ -493,6 +504,8 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
   sa.Ep = static_cast<int>(B.Ep);
   sa.nsplit = static_cast<int>(B.nsplit);
   sa.ksplit = static_cast<int>(B.ksplit);
+  sa.nshared = static_cast<int>(B.nshared);
+  sa.kshared = static_cast<int>(B.kshared);
   rc = status_of(moe::launch_bwd_setup(sa, s));
   if (rc) return rc;
   // 2. pre-activations z1 = buf W1_e^T (routed) and x W1_sh^T (shared), then h = act(z1).
@@ -613,20 +626,32 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
     if ((rc = gemm(p, nullptr))) return rc;
     if ((rc = status_of(moe::launch_split_reduce(part, dWg, E * M, static_cast<int>(B.nsplit), s))))
       return rc;
-    // dW2_e [M, H] = dout_e^T h_e ; shared: dy^T hsh_q
+    // dW2_e [M, H] = dout_e^T h_e ; shared q: dy^T hsh_q over token ranges into partials
+    const int nsh = static_cast<int>(Es * B.nshared);
+    float* shp2 = reinterpret_cast<float*>(ws + B.shp2);
+    float* shp1 = reinterpret_cast<float*>(ws + B.shp1);
     auto q0 = batched_problem(ws + B.dout, M, ws + L.h, H, dW2, H, static_cast<int>(H),
                               static_cast<int>(M), static_cast<int>(E), BM, sa.dw2, true);
-    auto q1 = batched_problem(dy, M, ws + L.hsh, Es * H, dW2, H, static_cast<int>(H),
-                              static_cast<int>(M), static_cast<int>(Es), BM, sa.dw2 + E, true);
+    auto q1 = batched_problem(dy, M, ws + L.hsh, Es * H, shp2, H, static_cast<int>(H),
+                              static_cast<int>(M), nsh, BM, sa.dw2 + E, true);
     q0.a_kmajor = q0.b_kmajor = q1.a_kmajor = q1.b_kmajor = 1;
     if ((rc = gemm(q0, Es ? &q1 : nullptr))) return rc;
-    // dW1_e [H1, M] = dz1_e^T buf_e ; shared: dz1sh_q^T x
+    // dW1_e [H1, M] = dz1_e^T buf_e ; shared q: dz1sh_q^T x over token ranges into partials
     auto w0 = batched_problem(ws + B.dz1, H1, ws + L.buf, M, dW1, M, static_cast<int>(M),
                               static_cast<int>(H1), static_cast<int>(E), BM, sa.dw1, true);
-    auto w1 = batched_problem(ws + B.dz1sh, Es * H1, x, M, dW1, M, static_cast<int>(M),
-                              static_cast<int>(H1), static_cast<int>(Es), BM, sa.dw1 + E, true);
+    auto w1 = batched_problem(ws + B.dz1sh, Es * H1, x, M, shp1, M, static_cast<int>(M),
+                              static_cast<int>(H1), nsh, BM, sa.dw1 + E, true);
     w0.a_kmajor = w0.b_kmajor = w1.a_kmajor = w1.b_kmajor = 1;
     if ((rc = gemm(w0, Es ? &w1 : nullptr))) return rc;
+    for (int64_t q = 0; q < Es; ++q) {   // the shared experts' partials, summed in range order
+      rc = status_of(moe::launch_split_reduce(shp2 + q * B.nshared * M * H, dW2 + (E + q) * M * H,
+                                              M * H, static_cast<int>(B.nshared), s));
+      if (!rc)
+        rc = status_of(moe::launch_split_reduce(shp1 + q * B.nshared * H1 * M,
+                                                dW1 + (E + q) * H1 * M, H1 * M,
+                                                static_cast<int>(B.nshared), s));
+      if (rc) return rc;
+    }
   }
   return MOE_OK;
 }

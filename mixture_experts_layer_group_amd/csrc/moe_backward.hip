@@ -131,7 +131,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(CombineBwdArgs a) {
 // One block: the batched GEMM entries of the weight gradients, which read the compact
 // buffers, x and dl in place as K-major operands (K = rows of the expert, or tokens).
 //   dW2_e [M, H]  = dout_e^T h_e        dW1_e [H1, M] = dz1_e^T buf_e
-//   shared q:       dy^T hsh_q                          dz1sh_q^T x
+//   shared q, token range s (fp32 partials):  dy_s^T hsh_q,s    dz1sh_q,s^T x_s
 //   dWg token range s [E, M] = dl_s^T x_s (fp32 partials)
 // and of the shared experts' dz_q = (dy W2_{E+q}) act'(z_q) (K-major weights, output columns
 // q H1 of dz1sh).
@@ -147,15 +147,25 @@ __global__ __launch_bounds__(256) void bwd_setup_kernel(BwdSetupArgs a) {
     a.dw2[e] = d2;
     a.dw1[e] = d1;
   }
-  for (int q = t; q < a.Es; q += 256) {  // shared experts: every token
-    BatchEntry d2, d1, dh;
-    d2.a_off = 0; d2.b_off = q * H; d2.c_off = (E + q) * M * H; d2.K = a.N; d2.pad = 0;
-    d1.a_off = q * H1; d1.b_off = 0; d1.c_off = (E + q) * H1 * M; d1.K = a.N; d1.pad = 0;
+  for (int q = t; q < a.Es; q += 256) {  // shared experts' dz over every token
+    BatchEntry dh;
     dh.a_off = 0; dh.b_off = (E + q) * M * H; dh.c_off = q * H1; dh.K = static_cast<int>(M);
     dh.pad = 0;
-    a.dw2[E + q] = d2;
-    a.dw1[E + q] = d1;
     a.dhsh[q] = dh;
+  }
+  // shared experts' weight gradients over token range s (rows s * kshared ..) into fp32
+  // partials [q][s], summed in range order afterwards
+  for (int i = t; i < a.Es * a.nshared; i += 256) {
+    const int q = i / a.nshared, sr = i - q * a.nshared;
+    const int64_t n0 = static_cast<int64_t>(sr) * a.kshared;
+    const int Kr = static_cast<int>(min<int64_t>(a.kshared, a.N - n0));
+    BatchEntry d2, d1;
+    d2.a_off = n0 * M; d2.b_off = n0 * a.Es * H + q * H; d2.c_off = static_cast<int64_t>(i) * M * H;
+    d2.K = Kr; d2.pad = 0;
+    d1.a_off = n0 * a.Es * H1 + q * H1; d1.b_off = n0 * M; d1.c_off = static_cast<int64_t>(i) * H1 * M;
+    d1.K = Kr; d1.pad = 0;
+    a.dw2[E + i] = d2;
+    a.dw1[E + i] = d1;
   }
   for (int q = t; q < a.nsplit; q += 256) {  // dWg [E, M] over token range q
     BatchEntry g;

@@ -168,10 +168,11 @@ struct CombineBwdArgs {    // dw_nj = <dy_n, o_row>, do_row = w_nj dy_n
 
 struct BwdSetupArgs {      // batched GEMM entries of the backward (built on the device)
   const int32_t* offset;   // [E+1] expert offsets of the compact buffer
-  BatchEntry* dw2; BatchEntry* dw1;  // [E+Es] weight gradients
-  BatchEntry* dhsh;                  // [Es] shared experts' dh
+  BatchEntry* dw2; BatchEntry* dw1;  // [E + Es * nshared] weight gradients (routed, then the
+                                     // shared experts' token ranges)
+  BatchEntry* dhsh;                  // [Es] shared experts' dz
   BatchEntry* dwg;                   // [nsplit] token ranges of the router weight gradient
-  int E, Es, M, H, H1, N, Ep, nsplit, ksplit;
+  int E, Es, M, H, H1, N, Ep, nsplit, ksplit, nshared, kshared;
 };
 
 struct RouterBwdArgs {
