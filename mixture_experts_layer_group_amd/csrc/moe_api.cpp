@@ -144,10 +144,12 @@ void record(void* const* ev, int i, hipStream_t s) {
 
 // Router (or routing from given logits) + scan + offsets + positions/scatter.
 // copy_rows: also copy the kept token rows into the compact buffer (the backward reads them);
-// the forward's GEMM 1 gathers them from x through tok_of_row instead.
+// the forward's GEMM 1 gathers them from x through tok_of_row instead.  The backward also
+// passes dy: then dout[row] = w dy[n] for every kept slot and wrow[row] = w.
 int run_routing(const Run& r, const void* x, const void* Wg, const float* bg, const float* u,
                 const float* logits_in, const moe_meta* m, int bm, void* const* ev,
-                bool copy_rows) {
+                bool copy_rows, const void* dy = nullptr, void* dout = nullptr,
+                float* wrow = nullptr) {
   const moe_cfg* c = r.c;
   const Layout& L = r.L;
   char* ws = r.ws;
@@ -193,6 +195,7 @@ int run_routing(const Run& r, const void* x, const void* Wg, const float* bg, co
   pa.num_tiles = reinterpret_cast<int32_t*>(ws + L.ntiles);
   pa.pos = m->pos; pa.row = m->row; pa.topk_w = m->topk_w;
   pa.stats = m->stats; pa.buf = ws + L.buf;
+  pa.dy = copy_rows ? dy : nullptr; pa.dout = dout; pa.w_of_row = wrow;
   pa.N = c->n_tokens; pa.G = c->n_groups; pa.S = static_cast<int>(L.S); pa.M = c->d_model;
   pa.E = c->n_experts; pa.k = c->top_k; pa.C = c->capacity; pa.nbg = static_cast<int>(L.nbg);
   pa.dtype = c->dtype; pa.BM = bm;
@@ -324,9 +327,9 @@ int forward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* b
 // operands where the contraction runs along their rows), so no transposed copies are kept.
 struct BwdLayout {
   Layout F;
-  size_t z1, o, dout, dz1, dbuf, z1sh, dz1sh, dl, dw, partb, dlp, wgt, dxrt, e2, e1, eh, eg, dwgp,
-      shp2, shp1, total;
-  int64_t H1, nchunks, Ep, nsplit, ksplit, nshared, kshared;
+  size_t z1, dout, wrow, dwp, dz1, dbuf, z1sh, dz1sh, dl, dw, partb, dlp, wgt, dxrt, e2, e1, eh,
+      eg, dwgp, shp2, shp1, total;
+  int64_t H1, nchunks, Ep, nsplit, ksplit, nshared, kshared, ntn;
 };
 
 int make_bwd_layout(const moe_cfg* c, BwdLayout* B) {
@@ -373,8 +376,10 @@ int make_bwd_layout(const moe_cfg* c, BwdLayout* B) {
   const size_t es = static_cast<size_t>(esz), rs = static_cast<size_t>(ra);
   const bool relu = c->act == MOE_ACT_RELU;   // ReLU keeps h instead of z1
   B->z1 = take(relu ? 0 : rs * H1 * es);
-  B->o = take(rs * M * es);
   B->dout = take(rs * M * es);
+  B->ntn = (H + moe::gemm_block_n(c->dtype, moe::kActNone) - 1) / moe::gemm_block_n(c->dtype, moe::kActNone);
+  B->wrow = take(rs * 4);
+  B->dwp = take(rs * static_cast<size_t>(B->ntn) * 4);
   B->dz1 = take(rs * H1 * es);
   B->dbuf = take(rs * M * es);
   B->z1sh = take(relu ? 0 : static_cast<size_t>(N * Es * H1) * es);
@@ -478,7 +483,8 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
   const int BM = L.BM, dt = c->dtype;
   const size_t esz = static_cast<size_t>(L.esz);
   // 1. routing again (deterministic: the forward's routing), rows dispatched into buf
-  rc = run_routing(r, x, Wg, bg, u, nullptr, m, BM, nullptr, true);
+  float* wrow = reinterpret_cast<float*>(ws + B.wrow);
+  rc = run_routing(r, x, Wg, bg, u, nullptr, m, BM, nullptr, true, dy, ws + B.dout, wrow);
   if (rc) return rc;
   const moe::TileDesc* tiles = reinterpret_cast<const moe::TileDesc*>(ws + L.tiles);
   const int32_t* ntiles = reinterpret_cast<const int32_t*>(ws + L.ntiles);
@@ -541,25 +547,21 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
       if (rc) return rc;
     }
   }
-  // 3. expert outputs o = h W2_e^T (routed; the combine weights' gradient needs them)
-  rc = gemm(routed_problem(ws + L.h, H, W2, H, M * H, ws + B.o, M, static_cast<int>(M),
-                           static_cast<int>(H), a_rows, L, tiles, ntiles), nullptr);
-  if (rc) return rc;
-  // 4. combine backward: dw, do
-  {
-    moe::CombineBwdArgs cb{dy, ws + B.o, m->row, m->topk_w, reinterpret_cast<float*>(ws + B.dw),
-                           ws + B.dout, static_cast<int>(N), static_cast<int>(M),
-                           static_cast<int>(k), dt};
-    rc = status_of(moe::launch_combine_bwd(cb, s));
-    if (rc) return rc;
-  }
-  // 5. dz = (do W2_e) act'(z1) (routed) and (dy W2_{E+q}) act'(z1sh) (shared, output columns
-  //    q H1): the GEMM applies the activation gradient in its epilogue and writes dz (for
-  //    SwiGLU dg and du), so dh is never stored.  W2_e [M, H] is read in place as a K-major
+  // 3. dz = w (dy W2_e) act'(z1) (routed rows, dy gathered through the row -> token index,
+  //    w the slot's gate weight) and (dy W2_{E+q}) act'(z1sh) (shared, output columns q H1):
+  //    the GEMM applies the gate weight and the activation gradient in its epilogue and
+  //    writes dz (for SwiGLU dg and du), so dh is never stored.  The same epilogue forms the
+  //    combine weights' gradient dw_nj = <dy_n W2_e, h_row> as per-n-tile partials, so the
+  //    expert outputs o need not be recomputed.  W2_e [M, H] is read in place as a K-major
   //    operand (k = m); z is z1, or h for ReLU (same layout: H1 = H).
+  float* dwp = reinterpret_cast<float*>(ws + B.dwp);
   {
-    auto p0 = routed_problem(ws + B.dout, M, W2, H, M * H, ws + B.dz1, H1, static_cast<int>(H),
-                             static_cast<int>(M), a_rows, L, tiles, ntiles);
+    auto p0 = routed_problem(dy, M, W2, H, M * H, ws + B.dz1, H1, static_cast<int>(H),
+                             static_cast<int>(M), static_cast<int>(N), L, tiles, ntiles);
+    p0.a_gather = reinterpret_cast<const int32_t*>(ws + L.tokrow);
+    p0.row_scale = wrow;
+    p0.hdot = ws + L.h; p0.ldh = H;
+    p0.dwp = dwp; p0.dwp_ld = static_cast<int>(B.ntn);
     auto p1 = batched_problem(dy, M, W2, H, ws + B.dz1sh, Es * H1, static_cast<int>(H),
                               static_cast<int>(N), static_cast<int>(Es), BM, sa.dhsh, false);
     p0.b_kmajor = p1.b_kmajor = 1;
@@ -569,8 +571,12 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
     p1.z = relu ? ws + L.hsh : ws + B.z1sh;
     rc = gemm(p0, Es ? &p1 : nullptr);
     if (rc) return rc;
+    // dw_nj = sum of the row's n-tile partials (0 for dropped slots)
+    rc = status_of(moe::launch_dw_reduce(m->row, dwp, reinterpret_cast<float*>(ws + B.dw),
+                                         N * k, static_cast<int>(B.ntn), s));
+    if (rc) return rc;
   }
-  // 6. dx rows = dz W1_e (routed); shared: dz_sh W1_sh over k = (q, h'), whose K-major rows
+  // 4. dx rows = dz W1_e (routed); shared: dz_sh W1_sh over k = (q, h'), whose K-major rows
   //    are the consecutive rows of W1_{E..E+Es-1}
   {
     auto p0 = routed_problem(ws + B.dz1, H1, W1, M, H1 * M, ws + B.dbuf, M,
@@ -583,7 +589,7 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
     rc = gemm(p0, Es ? &p1 : nullptr);
     if (rc) return rc;
   }
-  // 7. router backward and dx
+  // 5. router backward and dx
   {
     moe::RouterBwdArgs ra{};
     ra.logits = m->logits; ra.topk_idx = m->topk_idx;
@@ -615,7 +621,7 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
     rc = status_of(moe::launch_dbg(wa, s));
     if (rc) return rc;
   }
-  // 8. weight gradients, fp32: batched GEMMs over the experts with K = the expert's kept rows
+  // 6. weight gradients, fp32: batched GEMMs over the experts with K = the expert's kept rows
   //    (shared experts: all tokens), every operand read in place as a K-major operand
   {
     // dWg [E, M] = dl^T x: token ranges into fp32 partials, then their sum in range order

@@ -96,38 +96,6 @@ __global__ __launch_bounds__(256) void act_fwd_kernel(BwdEltArgs a) {
   }
 }
 
-// One wave per token: dw_nj = <dy_n, o_row> for kept slots (0 otherwise), and
-// do_row = w_nj dy_n into the compact expert-major buffer; 16 bytes per lane.
-template <int DT>
-__global__ __launch_bounds__(256) void combine_bwd_kernel(CombineBwdArgs a) {
-  constexpr int V = Vec<DT>::N;
-  const int lane = threadIdx.x & 63;
-  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (n >= a.N) return;
-  const int64_t rowoff = static_cast<int64_t>(n) * a.M;
-  for (int j = 0; j < a.k; ++j) {
-    const int r = a.row[static_cast<int64_t>(n) * a.k + j];
-    float d = 0.0f;
-    if (r >= 0) {
-      const float w = a.topk_w[static_cast<int64_t>(n) * a.k + j];
-      const int64_t ro = static_cast<int64_t>(r) * a.M;
-      for (int m = lane * V; m < a.M; m += 64 * V) {
-        Vec<DT> g, o, dout;
-        g.load(a.dy, rowoff + m);
-        o.load(a.o, ro + m);
-#pragma unroll
-        for (int x = 0; x < V; ++x) {
-          d = fmaf(g.v[x], o.v[x], d);
-          dout.v[x] = w * g.v[x];
-        }
-        dout.store(a.dout, ro + m);
-      }
-      d = wave_sum(d);
-    }
-    if (lane == 0) a.dw[static_cast<int64_t>(n) * a.k + j] = d;
-  }
-}
-
 // One block: the batched GEMM entries of the weight gradients, which read the compact
 // buffers, x and dl in place as K-major operands (K = rows of the expert, or tokens).
 //   dW2_e [M, H]  = dout_e^T h_e        dW1_e [H1, M] = dz1_e^T buf_e
@@ -290,6 +258,20 @@ __global__ __launch_bounds__(256) void dbg_partial_kernel(DwgArgs a) {
                                                    part[3][lane];
 }
 
+// Combine weights' gradient from the dgrad GEMM's per-n-tile partial dot products.
+__global__ __launch_bounds__(256) void dw_reduce_kernel(const int32_t* __restrict__ row,
+                                                        const float* __restrict__ dwp,
+                                                        float* __restrict__ dw, int64_t n,
+                                                        int ntn) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int r = row[i];
+  float s = 0.f;
+  if (r >= 0)
+    for (int t = 0; t < ntn; ++t) s += dwp[static_cast<int64_t>(r) * ntn + t];
+  dw[i] = s;
+}
+
 // out = sum of S fp32 partial arrays in order, 4 elements per thread.
 __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part,
                                                            float* __restrict__ out, int64_t n,
@@ -391,16 +373,6 @@ hipError_t launch_act_fwd(const BwdEltArgs& a, int64_t max_elems, hipStream_t s)
   return hipGetLastError();
 }
 
-hipError_t launch_combine_bwd(const CombineBwdArgs& a, hipStream_t s) {
-  const int grid = (a.N + 3) / 4;
-  if (grid == 0) return hipSuccess;
-  if (a.dtype == 1)
-    hipLaunchKernelGGL(combine_bwd_kernel<1>, dim3(grid), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(combine_bwd_kernel<0>, dim3(grid), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
 hipError_t launch_bwd_setup(const BwdSetupArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(bwd_setup_kernel, dim3(1), dim3(256), 0, s, a);
   return hipGetLastError();
@@ -417,6 +389,14 @@ hipError_t launch_dbg(const DwgArgs& a, hipStream_t s) {
   if (a.nchunks == 0 || !a.dbg) return hipSuccess;
   hipLaunchKernelGGL(dbg_partial_kernel, dim3(a.nchunks, (a.E + 63) / 64), dim3(256), 0, s, a);
   hipLaunchKernelGGL(dbg_reduce_kernel, dim3((a.E + 255) / 256), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dw_reduce(const int32_t* row, const float* dwp, float* dw, int64_t n, int ntn,
+                            hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(dw_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
+                     s, row, dwp, dw, n, ntn);
   return hipGetLastError();
 }
 

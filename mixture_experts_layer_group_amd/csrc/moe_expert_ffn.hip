@@ -72,6 +72,11 @@ struct Job {
   int akm, bkm;
   const char* Z;   // fused activation gradient: z at the tile's first element (C's layout)
   int64_t zup;     // gated: bytes from a g column to its u column (in z and in C)
+  const float* rs; // row scales from the tile's first row, or nullptr
+  const char* Hd;  // h at the tile's first row and column (pitch ldhb), or nullptr
+  int64_t ldhb;
+  float* dwp;      // dot partials of the tile's first row and n-tile (row pitch dwp_ld)
+  int dwp_ld;
 };
 
 // Load through the constant address space: for tables no kernel of this file writes (tile
@@ -156,6 +161,13 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& g, Job& j, int bid) 
   j.C = static_cast<char*>(P.C) + coff * osz + static_cast<int64_t>(row0) * j.ldc +
         static_cast<int64_t>(c0) * osz;
   j.Z = P.z ? static_cast<const char*>(P.z) + (j.C - static_cast<char*>(P.C)) : nullptr;
+  j.rs = P.row_scale ? P.row_scale + row0 : nullptr;
+  j.ldhb = P.ldh * osz;
+  j.Hd = P.hdot ? static_cast<const char*>(P.hdot) + static_cast<int64_t>(row0) * j.ldhb +
+                      static_cast<int64_t>(c0) * osz
+                : nullptr;
+  j.dwp = P.dwp ? P.dwp + static_cast<int64_t>(row0) * P.dwp_ld + nt : nullptr;
+  j.dwp_ld = P.dwp_ld;
   j.zup = static_cast<int64_t>(P.glu_h) * osz;
   j.K = K;
   j.nrows = nrows;
@@ -430,8 +442,8 @@ __device__ __forceinline__ void mma_chunk(const unsigned char* As, const unsigne
   }
 }
 
-// Activation gradient on 8 bf16 values: out = d * act'(z) (gated: dg = d u Swish'(g) at cp and
-// du = d Swish(g) zup bytes later, z = g at zp and u zup bytes later).
+// Activation gradient on 8 bf16 values d scaled by s: out = s d act'(z) (gated: dg = s d u
+// Swish'(g) at cp and du = s d Swish(g) zup bytes later, z = g at zp and u zup bytes later).
 __device__ __forceinline__ void unpack_bf16x8(u32x4 v, float (&f)[8]) {
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
@@ -446,9 +458,12 @@ __device__ __forceinline__ u32x4 pack_bf16x8(const float (&f)[8]) {
   return v;
 }
 template <int DACT>
-__device__ __forceinline__ void dact_bf16x8(u32x4 d, const char* zp, int64_t zup, char* cp) {
+__device__ __forceinline__ void dact_bf16x8(u32x4 d, const char* zp, int64_t zup, char* cp,
+                                            float scale) {
   float dv[8], zv[8], o[8];
   unpack_bf16x8(d, dv);
+#pragma unroll
+  for (int x = 0; x < 8; ++x) dv[x] *= scale;
   unpack_bf16x8(*reinterpret_cast<const u32x4*>(zp), zv);
   if (DACT == kActSwiglu) {
     float uv[8], du[8];
@@ -525,13 +540,32 @@ __device__ __forceinline__ void store_tile(const Job& j, f32x16 (&acc)[T::TN][T:
     char* C = j.C + poff;
     for (int i = t; i < rows * NCH; i += T::NT) {
       const int r = i / NCH, c = i - r * NCH;
+      if (DACT >= 0 && j.dwp) {
+        // <product row, h row> over this n-tile: the NCH = 32 lanes of row r (a half-wave,
+        // every one of them in this iteration) reduce their 8-column partial sums
+        static_assert(DACT < 0 || NCH == 32, "dot partials assume 32 columns chunks per row");
+        float part = 0.f;
+        if (c < ncch) {
+          float gv[8], hv[8];
+          unpack_bf16x8(*reinterpret_cast<const u32x4*>(
+                            stg + r * RB + ((c ^ (r & (NCH - 1))) << 4)), gv);
+          unpack_bf16x8(*reinterpret_cast<const u32x4*>(
+                            j.Hd + static_cast<int64_t>(p * RP + r) * j.ldhb + c * 16), hv);
+#pragma unroll
+          for (int x = 0; x < 8; ++x) part = fmaf(gv[x], hv[x], part);
+        }
+        part = group_sum<16>(part);
+        part += __shfl_xor(part, 16, 64);
+        if (c == 0) j.dwp[static_cast<int64_t>(p * RP + r) * j.dwp_ld] = part;
+      }
       if (c >= ncch) continue;
       const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * RB + ((c ^ (r & (NCH - 1))) << 4));
       const int64_t o = static_cast<int64_t>(r) * j.ldc + c * 16;
       if (DACT < 0)
         *reinterpret_cast<u32x4*>(C + o) = v;
       else   // fused activation gradient: z has C's layout
-        dact_bf16x8<DACT>(v, j.Z + poff + o, j.zup, C + o);
+        dact_bf16x8<DACT>(v, j.Z + poff + o, j.zup, C + o,
+                          j.rs ? j.rs[p * RP + r] : 1.0f);
     }
   }
 }
@@ -677,6 +711,18 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs g) {
       *reinterpret_cast<f32x2*>(j.C + static_cast<int64_t>(r) * j.ldc + tx * 8) = o;
     } else if (DACT >= 0) {   // fused activation gradient: z has C's layout
       const int64_t o = static_cast<int64_t>(r) * j.ldc + tx * 16;
+      if (j.dwp) {   // <product row, h row> over this n-tile: the 16 lanes of row r
+        const f32x4 hv = *reinterpret_cast<const f32x4*>(j.Hd + static_cast<int64_t>(r) * j.ldhb +
+                                                         tx * 16);
+        float part = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) part = fmaf(acc[i][jj], hv[jj], part);
+        part = group_sum<16>(part);
+        if (tx == 0) j.dwp[static_cast<int64_t>(r) * j.dwp_ld] = part;
+      }
+      const float sc = j.rs ? j.rs[r] : 1.0f;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) acc[i][jj] *= sc;
       const f32x4 z = *reinterpret_cast<const f32x4*>(j.Z + o);
       f32x4 d;
       if (DACT == kActSwiglu) {
@@ -730,7 +776,8 @@ hipError_t launch_expert_gemm(const GemmArgs& a, hipStream_t s) {
   // supported layouts: row-major (any activation); K-major B (no activation, optionally the
   // fused activation gradient); K-major A and B (fp32 output)
   if ((km == 2 && act != kActNone) || km == 1 || (km == 3 && !a.p0.out_f32) ||
-      (km != 0 && a.p0.a_gather) || (dact && (km != 2 || !a.p0.z)) || dact < 0 || dact > 3)
+      ((km & 1) && a.p0.a_gather) || (dact && (km != 2 || !a.p0.z)) || dact < 0 || dact > 3 ||
+      (a.p0.dwp && (!dact || !a.p0.hdot || !a.p0.tiles)))
     return hipErrorInvalidValue;
   const int grid = grid_of(a, gemm_block_n(a.dtype, act));
   if (grid == 0) return hipSuccess;

@@ -72,6 +72,11 @@ struct PermuteArgs {
   int32_t* stats;         // [4] (meta); stats[2] += fully dropped tokens of the block
   int32_t* tok_of_row;    // [R] token of every compact row (nullptr: not written)
   void* buf;              // [R, M] T compact expert-major rows (written iff x != nullptr)
+  // backward: dout[row] = w dy[n] for every kept slot, and w_of_row[row] = w (both nullable;
+  // dout needs x)
+  const void* dy;
+  void* dout;
+  float* w_of_row;
   int N, G, S, M, E, k, C, nbg, dtype, BM;
   int slices;             // column slices per router block (set by the launcher)
 };
@@ -119,6 +124,15 @@ struct GemmProblem {
   // glu_h columns after the g half, and C receives dg there and du glu_h columns later.
   const void* z;
   int dact;
+  // With the activation gradient, routed tiles only: row r of the product (compact row
+  // row0 + r) is first multiplied by row_scale[row0 + r] (nullable), and the unscaled product
+  // is dotted with hdot (pitch ldh, compact rows, nullable) over each n-tile into
+  // dwp[(row0 + r) * dwp_ld + n-tile].
+  const float* row_scale;
+  const void* hdot;
+  int64_t ldh;
+  float* dwp;
+  int dwp_ld;
 };
 
 struct GemmArgs {
@@ -160,11 +174,6 @@ struct BwdEltArgs {        // elementwise activation over rows (the backward's r
   int rows, nexp, H, act, dtype;
 };
 
-struct CombineBwdArgs {    // dw_nj = <dy_n, o_row>, do_row = w_nj dy_n
-  const void* dy; const void* o; const int32_t* row; const float* topk_w;
-  float* dw; void* dout;
-  int N, M, k, dtype;
-};
 
 struct BwdSetupArgs {      // batched GEMM entries of the backward (built on the device)
   const int32_t* offset;   // [E+1] expert offsets of the compact buffer
@@ -199,11 +208,13 @@ struct RouterPrepArgs {    // dlp [N, Ep] = dl, wgt [M, Ep] = Wg^T (layer dtype,
 };
 
 hipError_t launch_act_fwd(const BwdEltArgs& a, int64_t max_elems, hipStream_t s);
-hipError_t launch_combine_bwd(const CombineBwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_setup(const BwdSetupArgs& a, hipStream_t s);
 hipError_t launch_router_bwd(const RouterBwdArgs& a, hipStream_t s);
 hipError_t launch_dbg(const DwgArgs& a, hipStream_t s);
 // out[i] = sum over s < S of part[s][i], in order of s (n a multiple of 4)
+// dw[i] = sum over t < ntn of dwp[row[i] * ntn + t] in order of t (0 where row[i] < 0)
+hipError_t launch_dw_reduce(const int32_t* row, const float* dwp, float* dw, int64_t n, int ntn,
+                            hipStream_t s);
 hipError_t launch_split_reduce(const float* part, float* out, int64_t n, int S, hipStream_t s);
 hipError_t launch_router_dgrad_prep(const RouterPrepArgs& a, hipStream_t s);
 hipError_t launch_dx_final(const DxArgs& a, hipStream_t s);

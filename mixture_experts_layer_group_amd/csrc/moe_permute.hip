@@ -100,6 +100,7 @@ __device__ void offsets(const PermuteArgs& a, int g, int* gbase_s, int* scratch)
 
 __global__ __launch_bounds__(256) void permute_kernel(PermuteArgs a) {
   __shared__ int rows_s[kRouteTokens][kMaxTopK];
+  __shared__ float w_s[kRouteTokens][kMaxTopK];   // gate weight of each kept slot
   __shared__ int kept_any[kRouteTokens];
   __shared__ int gbase_s[kMaxExperts];
   __shared__ int scratch[4];
@@ -133,13 +134,17 @@ __global__ __launch_bounds__(256) void permute_kernel(PermuteArgs a) {
       if (act) p = a.abase[((static_cast<size_t>(g) * k + j) * a.E + e) * a.nbg + bi] + prefix;
       const bool kept = act && p < a.C;
       const int r = kept ? gbase_s[e] + p : -1;
+      // kept slots' weights are final (the meta slice zeroes the others only)
+      const float wk = kept ? a.topk_w[o] : 0.f;
       if (meta) {
         a.pos[o] = kept ? p : -1;
         a.row[o] = r;
         if (!kept) a.topk_w[o] = 0.f;
         if (kept && a.tok_of_row) a.tok_of_row[r] = n;
+        if (kept && a.w_of_row) a.w_of_row[r] = wk;
       }
       rows_s[lane][j] = r;
+      w_s[lane][j] = wk;
       if (kept) kept_any[lane] = 1;
     }
   }
@@ -161,11 +166,15 @@ __global__ __launch_bounds__(256) void permute_kernel(PermuteArgs a) {
   char* __restrict__ bb = static_cast<char*>(a.buf) + c0 * 16;
   // U chunks per thread per round: all U loads are issued before any store, so U loads are
   // in flight per lane (the stores may not be reordered above loads the compiler cannot
-  // prove disjoint from them).
+  // prove disjoint from them).  With dy, the same chunk of dy is scaled by each kept slot's
+  // weight into dout (fp32 product, rounded like every stored value).
   constexpr int U = 4;
+  const bool wdy = a.dy != nullptr;
+  const char* __restrict__ yb = wdy ? static_cast<const char*>(a.dy) + c0 * 16 : nullptr;
+  char* __restrict__ ob = wdy ? static_cast<char*>(a.dout) + c0 * 16 : nullptr;
   const int total = nt * ch;
   for (int base = t; base < total; base += 256 * U) {
-    u32x4 v[U];
+    u32x4 v[U], yv[U];
     int tlv[U], cv[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -176,8 +185,9 @@ __global__ __launch_bounds__(256) void permute_kernel(PermuteArgs a) {
         if (kept_any[tl]) {
           tlv[u] = tl;
           cv[u] = c;
-          v[u] = *reinterpret_cast<const u32x4*>(xb + static_cast<size_t>(tok0 + tl) * rowbytes +
-                                                 c * 16);
+          const size_t off = static_cast<size_t>(tok0 + tl) * rowbytes + c * 16;
+          v[u] = *reinterpret_cast<const u32x4*>(xb + off);
+          if (wdy) yv[u] = *reinterpret_cast<const u32x4*>(yb + off);
         }
       }
     }
@@ -186,8 +196,23 @@ __global__ __launch_bounds__(256) void permute_kernel(PermuteArgs a) {
       if (tlv[u] < 0) continue;
       for (int j = 0; j < k; ++j) {
         const int r = rows_s[tlv[u]][j];
-        if (r >= 0)
-          *reinterpret_cast<u32x4*>(bb + static_cast<size_t>(r) * rowbytes + cv[u] * 16) = v[u];
+        if (r < 0) continue;
+        const size_t off = static_cast<size_t>(r) * rowbytes + cv[u] * 16;
+        *reinterpret_cast<u32x4*>(bb + off) = v[u];
+        if (wdy) {
+          const float w = w_s[tlv[u]][j];
+          u32x4 sv;
+          if (a.dtype == 1) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+              sv[x] = pack_bf16x2(w * __builtin_bit_cast(float, yv[u][x] << 16),
+                                  w * __builtin_bit_cast(float, yv[u][x] & 0xffff0000u));
+          } else {   // 4 fp32 values, scaled as a vector
+            const f32x4 yf = __builtin_bit_cast(f32x4, yv[u]);
+            sv = __builtin_bit_cast(u32x4, yf * w);
+          }
+          *reinterpret_cast<u32x4*>(ob + off) = sv;
+        }
       }
     }
   }

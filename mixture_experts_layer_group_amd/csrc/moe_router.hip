@@ -85,70 +85,6 @@ __device__ __forceinline__ int rswz(int r) {
   return ROWB == 256 ? (r & 15) : (((r >> 1) & 7) ^ ((r & 1) << 2));
 }
 
-// Cross-lane steps inside one 16-lane DPP row (the lanes of one token): swap neighbours
-// (quad_perm 1,0,3,2), swap pairs (quad_perm 2,3,0,1), mirror within 8 lanes, mirror within
-// 16 lanes.  Each step pairs every lane with one other lane of its aligned group of 2, 4, 8,
-// 16, so after log2(N) steps of a commutative combine every lane of an aligned group of N
-// holds the group's total, the same bits in every lane.  DPP moves are VALU operations; the
-// LDS-routed ds_bpermute of a generic shuffle costs an LDS round trip per step.
-constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
-
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int v) {
-  return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
-}
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, v)));
-}
-template <int CTRL>
-__device__ __forceinline__ double dpp_d(double v) {
-  const uint64_t u = __builtin_bit_cast(uint64_t, v);
-  const uint32_t lo = static_cast<uint32_t>(dpp_i<CTRL>(static_cast<int>(u & 0xffffffffu)));
-  const uint32_t hi = static_cast<uint32_t>(dpp_i<CTRL>(static_cast<int>(u >> 32)));
-  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
-}
-
-// Reductions over aligned groups of N <= 16 lanes.
-template <int N>
-__device__ __forceinline__ float group_max(float v) {
-  v = fmaxf(v, dpp_f<kDppXor1>(v));
-  if (N > 2) v = fmaxf(v, dpp_f<kDppXor2>(v));
-  if (N > 4) v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
-  if (N > 8) v = fmaxf(v, dpp_f<kDppMirror>(v));
-  return v;
-}
-template <int N>
-__device__ __forceinline__ float group_sum(float v) {
-  v += dpp_f<kDppXor1>(v);
-  if (N > 2) v += dpp_f<kDppXor2>(v);
-  if (N > 4) v += dpp_f<kDppHalfMirror>(v);
-  if (N > 8) v += dpp_f<kDppMirror>(v);
-  return v;
-}
-template <int N>
-__device__ __forceinline__ double group_sum(double v) {
-  v += dpp_d<kDppXor1>(v);
-  if (N > 2) v += dpp_d<kDppXor2>(v);
-  if (N > 4) v += dpp_d<kDppHalfMirror>(v);
-  if (N > 8) v += dpp_d<kDppMirror>(v);
-  return v;
-}
-// Best (value, index) over the group: larger value, ties to the lower index.
-template <int CTRL>
-__device__ __forceinline__ void argmax_step(float& bv, int& bi) {
-  const float ov = dpp_f<CTRL>(bv);
-  const int oi = dpp_i<CTRL>(bi);
-  if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-}
-template <int N>
-__device__ __forceinline__ void group_argmax(float& bv, int& bi) {
-  argmax_step<kDppXor1>(bv, bi);
-  if (N > 2) argmax_step<kDppXor2>(bv, bi);
-  if (N > 4) argmax_step<kDppHalfMirror>(bv, bi);
-  if (N > 8) argmax_step<kDppMirror>(bv, bi);
-}
-
 // x[64 tokens, M] . Wg[E, M]^T -> lg[64][ls] (bf16, v_mfma_f32_32x32x16_bf16, fp32 sums).
 // K is streamed in row chunks of ROWB bytes through RouterPipe::kStages LDS stages, each
 // filled by buffer_load ... lds (lane i of a wave instruction -> 16 bytes at LDS unit i), so
