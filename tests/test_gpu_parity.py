@@ -157,13 +157,23 @@ def test_empty_batch():
     assert float(meta.z_loss[0]) == 0.0 and float(meta.dev_loss[0]) == 0.0
 
 
-@pytest.mark.parametrize("act", [1, 2], ids=["gelu", "swiglu"])
-def test_single_expert_is_a_dense_ffn(act):
+# (act, n_tokens, d_model, d_ff).  The larger shapes give each GEMM more 256 x 256 tiles than
+# the chip has compute units, so blocks of the persistent bf16 kernel run several tiles, with
+# a ragged last m-tile and a partial last n-tile; d_model = 256 makes GEMM 1's K loop (4
+# chunks) shorter than the deferred stores of the previous tile.
+DENSE = {"gelu_small": (1, 700, 256, 384), "swiglu_small": (2, 700, 256, 384),
+         "relu_multi_tile": (0, 16461, 1152, 1152), "gelu_short_k": (1, 16461, 256, 1152),
+         "swiglu_multi_tile": (2, 16461, 1152, 1152), "swiglu_short_k": (2, 16461, 256, 1408)}
+
+
+@pytest.mark.parametrize("case", list(DENSE))
+def test_single_expert_is_a_dense_ffn(case):
     """E=1, k=1, C=N, norm=none: y = x + act(x W1^T) W2^T (gated: (silu(x G^T) * x U^T)
-    W2^T), checked against torch.matmul and torch's gelu / silu in fp32 on the GPU (library
-    routines) rather than against the oracle."""
-    cfg = _cfg(n_tokens=700, n_experts=1, top_k=1, capacity=700, gate_norm=0, act=act,
-               d_model=256, d_ff=384)
+    W2^T), checked against torch.matmul and torch's relu / gelu / silu in fp32 on the GPU
+    (library routines) rather than against the oracle."""
+    act, n, dm, dff = DENSE[case]
+    cfg = _cfg(n_tokens=n, n_experts=1, top_k=1, capacity=n, gate_norm=0, act=act,
+               d_model=dm, d_ff=dff)
     inp = synth.make_inputs(cfg)
     h = harness()
     dev = h.to_device(inp, cfg)
@@ -172,7 +182,9 @@ def test_single_expert_is_a_dense_ffn(act):
     w1 = dev["W1"][0].float().contiguous()
     w2 = dev["W2"][0].float().contiguous()
     pre = torch.matmul(x, w1.t().contiguous())
-    if act == 1:
+    if act == 0:
+        hid = torch.relu(pre)
+    elif act == 1:
         hid = torch.nn.functional.gelu(pre)
     else:
         H = cfg["d_ff"]
