@@ -176,7 +176,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs the MoE layer on exactly one GPU; --gpus {args.gpus} "
-              f"(WORLD_SIZE={world}) is not supported by this build", file=sys.stderr)
+              f"(WORLD_SIZE={world}) is not supported: the layer has no multi-GPU path",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
