@@ -442,8 +442,7 @@ __device__ __forceinline__ void mma_chunk(const unsigned char* As, const unsigne
   }
 }
 
-// Activation gradient on 8 bf16 values d scaled by s: out = s d act'(z) (gated: dg = s d u
-// Swish'(g) at cp and du = s d Swish(g) zup bytes later, z = g at zp and u zup bytes later).
+// 8 bf16 values (one 16-byte chunk) to fp32 and back.
 __device__ __forceinline__ void unpack_bf16x8(u32x4 v, float (&f)[8]) {
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
@@ -457,29 +456,31 @@ __device__ __forceinline__ u32x4 pack_bf16x8(const float (&f)[8]) {
   for (int x = 0; x < 4; ++x) v[x] = pack_bf16x2(f[2 * x], f[2 * x + 1]);
   return v;
 }
+// Activation gradient on 8 bf16 values d of the product scaled by s: returns s d act'(z)
+// (gated: dg = s d u Swish'(g), with du = s d Swish(g) in du; z = g, u the up
+// pre-activations, unused otherwise).
 template <int DACT>
-__device__ __forceinline__ void dact_bf16x8(u32x4 d, const char* zp, int64_t zup, char* cp,
-                                            float scale) {
+__device__ __forceinline__ u32x4 dact_vals(u32x4 d, u32x4 z, u32x4 u, float scale, u32x4& du) {
   float dv[8], zv[8], o[8];
   unpack_bf16x8(d, dv);
 #pragma unroll
   for (int x = 0; x < 8; ++x) dv[x] *= scale;
-  unpack_bf16x8(*reinterpret_cast<const u32x4*>(zp), zv);
+  unpack_bf16x8(z, zv);
   if (DACT == kActSwiglu) {
-    float uv[8], du[8];
-    unpack_bf16x8(*reinterpret_cast<const u32x4*>(zp + zup), uv);
+    float uv[8], dd[8];
+    unpack_bf16x8(u, uv);
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
       o[x] = dv[x] * uv[x] * swish_grad(zv[x]);
-      du[x] = dv[x] * swish(zv[x]);
+      dd[x] = dv[x] * swish(zv[x]);
     }
-    *reinterpret_cast<u32x4*>(cp + zup) = pack_bf16x8(du);
+    du = pack_bf16x8(dd);
   } else {
 #pragma unroll
     for (int x = 0; x < 8; ++x)
       o[x] = DACT == kActGelu ? dv[x] * gelu_grad(zv[x]) : (zv[x] > 0.0f ? dv[x] : 0.0f);
   }
-  *reinterpret_cast<u32x4*>(cp) = pack_bf16x8(o);
+  return pack_bf16x8(o);
 }
 
 // bf16 epilogue through LDS: D[feature][token] -> tile[token][feature] (rows of OUTN*2 bytes,
@@ -538,34 +539,69 @@ __device__ __forceinline__ void store_tile(const Job& j, f32x16 (&acc)[T::TN][T:
     const int rows = min(RP, j.nrows - p * RP);
     const int64_t poff = static_cast<int64_t>(p * RP) * j.ldc;
     char* C = j.C + poff;
+    if constexpr (DACT >= 0) {
+      // Fused activation gradient, in batches of U row chunks per thread: every load of a
+      // batch (z, u for gated layers, h for the dot partials, the row scale) is issued before
+      // the first of them is used, so a batch waits for one memory round trip, not U.  A
+      // half-wave covers one staged row (NCH = 32 chunks), so the batch bounds are uniform
+      // over each half-wave and its 32 lanes reduce the row's dot partial together.
+      static_assert(NCH == 32 && !F32, "one staged row per half-wave");
+      constexpr int U = DACT == kActSwiglu ? 4 : 8;   // gated: three loads per chunk
+      const bool hz = j.Hd == j.Z && j.ldhb == j.ldc;   // ReLU: z is h
+      const char* Zp = j.Z + poff;
+      for (int i0 = t; i0 < rows * NCH; i0 += U * T::NT) {
+        u32x4 sv[U], zv[U], uv[U], hv[U];
+        float sc[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int i = i0 + u * T::NT;
+          sv[u] = zv[u] = uv[u] = hv[u] = u32x4{0u, 0u, 0u, 0u};
+          sc[u] = 1.0f;
+          if (i < rows * NCH) {
+            const int r = i / NCH, c = i - r * NCH;
+            sv[u] = *reinterpret_cast<const u32x4*>(stg + r * RB + ((c ^ (r & (NCH - 1))) << 4));
+            if (j.rs) sc[u] = j.rs[p * RP + r];
+            if (c < ncch) {
+              const int64_t o = static_cast<int64_t>(r) * j.ldc + c * 16;
+              zv[u] = *reinterpret_cast<const u32x4*>(Zp + o);
+              if (DACT == kActSwiglu) uv[u] = *reinterpret_cast<const u32x4*>(Zp + o + j.zup);
+              if (j.dwp && !hz)
+                hv[u] = *reinterpret_cast<const u32x4*>(
+                    j.Hd + static_cast<int64_t>(p * RP + r) * j.ldhb + c * 16);
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int i = i0 + u * T::NT;
+          if (i >= rows * NCH) break;
+          const int r = i / NCH, c = i - r * NCH;
+          if (j.dwp) {
+            // <product row, h row> over this n-tile (zero past the valid columns)
+            float gv[8], hf[8], part = 0.f;
+            unpack_bf16x8(sv[u], gv);
+            unpack_bf16x8(hz ? zv[u] : hv[u], hf);
+#pragma unroll
+            for (int x = 0; x < 8; ++x) part = fmaf(gv[x], hf[x], part);
+            part = group_sum<16>(part);
+            part += __shfl_xor(part, 16, 64);
+            if (c == 0) j.dwp[static_cast<int64_t>(p * RP + r) * j.dwp_ld] = part;
+          }
+          if (c >= ncch) continue;
+          const int64_t o = static_cast<int64_t>(r) * j.ldc + c * 16;
+          u32x4 du;
+          const u32x4 dz = dact_vals<DACT>(sv[u], zv[u], uv[u], sc[u], du);
+          *reinterpret_cast<u32x4*>(C + o) = dz;
+          if (DACT == kActSwiglu) *reinterpret_cast<u32x4*>(C + o + j.zup) = du;
+        }
+      }
+      continue;
+    }
     for (int i = t; i < rows * NCH; i += T::NT) {
       const int r = i / NCH, c = i - r * NCH;
-      if (DACT >= 0 && j.dwp) {
-        // <product row, h row> over this n-tile: the NCH = 32 lanes of row r (a half-wave,
-        // every one of them in this iteration) reduce their 8-column partial sums
-        static_assert(DACT < 0 || NCH == 32, "dot partials assume 32 columns chunks per row");
-        float part = 0.f;
-        if (c < ncch) {
-          float gv[8], hv[8];
-          unpack_bf16x8(*reinterpret_cast<const u32x4*>(
-                            stg + r * RB + ((c ^ (r & (NCH - 1))) << 4)), gv);
-          unpack_bf16x8(*reinterpret_cast<const u32x4*>(
-                            j.Hd + static_cast<int64_t>(p * RP + r) * j.ldhb + c * 16), hv);
-#pragma unroll
-          for (int x = 0; x < 8; ++x) part = fmaf(gv[x], hv[x], part);
-        }
-        part = group_sum<16>(part);
-        part += __shfl_xor(part, 16, 64);
-        if (c == 0) j.dwp[static_cast<int64_t>(p * RP + r) * j.dwp_ld] = part;
-      }
       if (c >= ncch) continue;
       const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * RB + ((c ^ (r & (NCH - 1))) << 4));
-      const int64_t o = static_cast<int64_t>(r) * j.ldc + c * 16;
-      if (DACT < 0)
-        *reinterpret_cast<u32x4*>(C + o) = v;
-      else   // fused activation gradient: z has C's layout
-        dact_bf16x8<DACT>(v, j.Z + poff + o, j.zup, C + o,
-                          j.rs ? j.rs[p * RP + r] : 1.0f);
+      *reinterpret_cast<u32x4*>(C + static_cast<int64_t>(r) * j.ldc + c * 16) = v;
     }
   }
 }
