@@ -13,6 +13,8 @@ launch (2 R M H for the routed rows, + 2 N Es H M for shared experts; R = kept r
 gated experts' GEMM 1 does twice that) averaged over its two launches per step, over their
 average launch time, against the bf16 dense MFMA peak.
 The cpu_baseline object times the CPU oracle on a bounded sample of the same workload.
+The graph object replays the same step from HIP graphs (no host launch work between the
+kernels); the backward object times moe_backward (routing and activations recomputed).
 """
 import argparse
 import ctypes
@@ -158,6 +160,36 @@ def backward_timing(cfg, inp, x, Wg, W1, W2, bg, u, R, steps):
             "workspace_bytes": ws.numel()}
 
 
+def graph_timing(cfg, xs, ys, Wg, bg, W1, W2, u, aux, meta, ws, steps):
+    """The same forward step replayed from HIP graphs (one captured moe_forward per rotating
+    x/y copy), which removes the host launch work between the five kernels."""
+    import torch
+    from mixture_experts_layer_group_amd import binding
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        binding.moe_forward(cfg, xs[0], Wg, bg, W1, W2, u, ys[0], aux, meta, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for c in range(len(xs)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            binding.moe_forward(cfg, xs[c], Wg, bg, W1, W2, u, ys[c], aux, meta, ws)
+        graphs.append(g)
+    for i in range(2 * len(graphs)):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    del graphs
+    return {"ms_per_step": round(ms, 5), "tokens_per_s": round(cfg["n_tokens"] / (ms * 1e-3), 1),
+            "steps": steps, "note": "moe_forward captured in HIP graphs and replayed"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,6 +199,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=16384)
     ap.add_argument("--copies", type=int, default=4, help="rotating copies of x and y")
+    ap.add_argument("--graph-steps", type=int, default=50,
+                    help="forward steps replayed from HIP graphs, reported beside the eager "
+                         "timing (0: skip)")
     ap.add_argument("--backward-steps", type=int, default=10,
                     help="timed moe_backward calls reported beside the forward (0: skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -338,6 +373,9 @@ def main():
         "aux_loss": float(aux[0].cpu()),
     }
     ev.destroy([e for evs in events for e in evs] + warm)
+    if args.graph_steps > 0:
+        out["graph"] = graph_timing(cfg, xs, ys, Wg, bg, W1, W2, u, aux, meta, ws,
+                                    args.graph_steps)
     if args.backward_steps > 0:
         out["backward"] = backward_timing(cfg, inp, x0, Wg, W1, W2, bg, u, R, args.backward_steps)
     if not args.no_cpu_baseline:
