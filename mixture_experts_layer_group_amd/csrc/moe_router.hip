@@ -314,7 +314,7 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
   // Group-limited routing ([Lec16] "DeepSeek V3 MoE (670B)"): the E experts form n_eg
   // contiguous groups; a group scores its best logit, and the topk_eg best groups (ties to
   // the lower index) stay open.  Lane q scores groups q and q + L.
-  uint32_t taken = 0;  // bit i <-> expert q + L i already selected (E <= 256 -> i < 16)
+  uint32_t taken = 0;  // bit i <-> expert q + L i excluded (E <= 256 -> i < 16)
   if (a.n_eg > 1) {
     const int D = a.n_eg, gs = E / D;
     float gv[2];
@@ -344,12 +344,24 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
       group_argmax<L>(bv, bd);
       open |= 1u << bd;
     }
-    // experts of closed groups count as taken, so the top-k below never picks them
+    // experts of closed groups are excluded, so the top-k below never picks them
     int i = 0;
     for (int e = q; e < E; e += L, ++i)
       if (!((open >> (e / gs)) & 1u)) taken |= 1u << i;
   }
 
+  // k rounds of argmax over the candidates (bit i <-> expert q + L i, not yet taken and below
+  // E).  The comparisons are selects, not branches: a divergent branch per element would cost
+  // an exec-mask save, test and restore each.  A NaN logit scores -inf, so it never beats a
+  // number, and ties (also among -inf) go to the lower expert index, so bix is always a real
+  // candidate.
+  float rk[NV];
+  uint32_t cand = ~taken;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    rk[i] = rv[i] != rv[i] ? -INFINITY : rv[i];
+    if (q + L * i >= E) cand &= ~(1u << i);
+  }
   int sel_e[kMaxTopK];
   float sel_l[kMaxTopK];
 #pragma unroll
@@ -362,16 +374,14 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         const int e = q + L * i;
-        if (e < E && !((taken >> i) & 1u)) {
-          float v = rv[i];
-          if (v != v) v = -INFINITY;  // a NaN never wins, so bix is always a real expert
-          if (v > bv || (v == bv && e < bix)) { bv = v; bix = e; }
-        }
+        const bool better = ((cand >> i) & 1u) & ((rk[i] > bv) | ((rk[i] == bv) & (e < bix)));
+        bv = better ? rk[i] : bv;
+        bix = better ? e : bix;
       }
       group_argmax<L>(bv, bix);
       sel_e[j] = bix;
       sel_l[j] = bv;
-      if (bix % L == q) taken |= 1u << (bix / L);
+      cand &= bix % L == q ? ~(1u << (bix / L)) : ~0u;
     }
   }
 
