@@ -49,6 +49,11 @@ constexpr int kGemmGroupM = MOE_GEMM_GROUP_M;
 #define MOE_GEMM_WN 4
 #endif
 constexpr int kGemmWN = MOE_GEMM_WN;
+// two-stage K loop with fragments read one step ahead, interleaved with the MFMAs
+#ifndef MOE_GEMM_PIPELINED
+#define MOE_GEMM_PIPELINED 1
+#endif
+constexpr bool kGemmPipelined = MOE_GEMM_PIPELINED;
 
 struct Job {
   const char* A;   // first row of the tile (bytes)
@@ -442,6 +447,45 @@ __device__ __forceinline__ void mma_chunk(const unsigned char* As, const unsigne
   }
 }
 
+// The same multiply split into its two halves, for the pipelined K loop: the fragments of
+// one 16-deep step (row-major: one ds_read_b128 each; K-major: two transposed reads each) ...
+template <class T, bool AKM, bool BKM>
+__device__ __forceinline__ void read_step(const unsigned char* As, const unsigned char* Bs, int s,
+                                          int arow, int brow, int lane, int sw,
+                                          bf16x8 (&af)[T::TM], bf16x8 (&bfr)[T::TN]) {
+  const int phys = (((2 * s) + (lane >> 5)) ^ sw) * 16;
+#pragma unroll
+  for (int im = 0; im < T::TM; ++im)
+    af[im] = AKM ? frag_kmajor<T::BM * 2>(As, s, arow - (lane & 31) + 32 * im, lane)
+                 : *reinterpret_cast<const bf16x8*>(As + (arow + 32 * im) * T::ROW + phys);
+#pragma unroll
+  for (int jn = 0; jn < T::TN; ++jn)
+    bfr[jn] = BKM ? frag_kmajor<T::BN * 2>(Bs, s, brow - (lane & 31) + 32 * jn, lane)
+                  : *reinterpret_cast<const bf16x8*>(Bs + (brow + 32 * jn) * T::ROW + phys);
+}
+// ... and its MFMAs.
+template <class T>
+__device__ __forceinline__ void mfma_step(const bf16x8 (&af)[T::TM], const bf16x8 (&bfr)[T::TN],
+                                          f32x16 (&acc)[T::TN][T::TM]) {
+#pragma unroll
+  for (int jn = 0; jn < T::TN; ++jn)
+#pragma unroll
+    for (int im = 0; im < T::TM; ++im)
+      acc[jn][im] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[jn], af[im], acc[jn][im], 0, 0, 0);
+}
+// Instruction order inside one step of the pipelined loop: the next step's LDS reads spread one
+// after each MFMA (then the remaining MFMAs), so the reads run in the MFMA shadow instead of in
+// a burst the MFMAs wait behind.
+template <int NRD, int NMF>
+__device__ __forceinline__ void interleave_step() {
+#pragma unroll
+  for (int i = 0; i < NRD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one DS read
+    if (i < NMF) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+  }
+  if (NMF > NRD) __builtin_amdgcn_sched_group_barrier(0x008, NMF - NRD, 0);
+}
+
 // 8 bf16 values (one 16-byte chunk) to fp32 and back.
 __device__ __forceinline__ void unpack_bf16x8(u32x4 v, float (&f)[8]) {
 #pragma unroll
@@ -648,7 +692,43 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
   };
   // 0 (a zero block) or >= NST - 1; a K-major operand's last chunk may be partial
   const int KT = (AKM || BKM) ? (j.K + BK - 1) / BK : j.K / BK;
-  if (KT > 0) {
+  if (kGemmPipelined && NST == 2 && KT > 0) {
+    // Two stages, fragments one 16-deep step ahead in two register sets.  Step s of chunk kt
+    // multiplies set s & 1 while the reads of step s + 1 fill the other set; at the last
+    // step the block waits for chunk kt + 1, passes the barrier (every wave has read chunk
+    // kt's stage into registers by then), refills that stage with chunk kt + 2 and reads
+    // chunk kt + 1's first step, so no MFMA waits for a fragment read at a chunk boundary.
+    constexpr int NS = BK / 16;
+    static_assert(NS % 2 == 0, "an even number of steps per chunk keeps the register sets aligned");
+    constexpr int NRD = (T::TM + T::TN) * (AKM || BKM ? 2 : 1);   // wide upper bound
+    constexpr int NMF = T::TM * T::TN;
+    bf16x8 fa[2][T::TM], fb[2][T::TN];
+    feed_issue<T, AKM, BKM>(fd, smem, w, 0);
+    MOE_WAIT_VMCNT(0);
+    lds_barrier();
+    if (KT > 1) feed_issue<T, AKM, BKM>(fd, smem + T::STAGE, w, 1);
+    read_step<T, AKM, BKM>(smem, smem + SLOT, 0, arow, brow, lane, sw, fa[0], fb[0]);
+    for (int kt = 0; kt < KT; ++kt) {
+      const int st = kt & 1;
+      const unsigned char* S = smem + st * T::STAGE;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        if (s + 1 < NS) {
+          read_step<T, AKM, BKM>(S, S + SLOT, s + 1, arow, brow, lane, sw, fa[(s + 1) & 1],
+                                 fb[(s + 1) & 1]);
+        } else if (kt + 1 < KT) {
+          MOE_WAIT_VMCNT(0);
+          lds_barrier();
+          if (kt + 2 < KT) feed_issue<T, AKM, BKM>(fd, smem + st * T::STAGE, w, kt + 2);
+          const unsigned char* Sn = smem + (st ^ 1) * T::STAGE;
+          read_step<T, AKM, BKM>(Sn, Sn + SLOT, 0, arow, brow, lane, sw, fa[0], fb[0]);
+        }
+        mfma_step<T>(fa[s & 1], fb[s & 1], acc);
+        interleave_step<NRD, NMF>();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  } else if (KT > 0) {
 #pragma unroll
     for (int p = 0; p < NST - 1; ++p) feed_issue<T, AKM, BKM>(fd, smem + p * T::STAGE, w, p);
     int st = 0;
