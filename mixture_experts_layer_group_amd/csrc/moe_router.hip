@@ -306,9 +306,12 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
     if (q + L * i < E) mx = fmaxf(mx, rv[i]);
   mx = group_max<L>(mx);
   float se = 0.f;
+  float ev[NV];   // exp(l - max), kept for the probabilities below
 #pragma unroll
-  for (int i = 0; i < NV; ++i)
-    if (q + L * i < E) se += expf(rv[i] - mx);
+  for (int i = 0; i < NV; ++i) {
+    ev[i] = q + L * i < E ? expf(rv[i] - mx) : 0.f;
+    se += ev[i];
+  }
   se = group_sum<L>(se);
 
   // Group-limited routing ([Lec16] "DeepSeek V3 MoE (670B)"): the E experts form n_eg
@@ -442,9 +445,10 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
   }
   // Softmax probabilities for the block's column sums; each lane rewrites only its own
   // entries of its own row, which no other lane reads before the barrier.
+  const float inv_se = 1.0f / se;
 #pragma unroll
   for (int i = 0; i < NV; ++i)
-    if (q + L * i < E) row[q + L * i] = valid ? expf(rv[i] - mx) / se : 0.f;
+    if (q + L * i < E) row[q + L * i] = valid ? ev[i] * inv_se : 0.f;
   __syncthreads();
 
   // Column sums of the probabilities: SPC consecutive lanes per expert, each summing every
