@@ -279,7 +279,19 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
   const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
   if (i >= n) return;
   f32x4 acc = *reinterpret_cast<const f32x4*>(part + i);
-  for (int q = 1; q < S; ++q) {
+  // partials 1 .. S-1 added in order, their loads issued 8 at a time
+  int q = 1;
+  for (; q + 8 <= S; q += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = *reinterpret_cast<const f32x4*>(part + static_cast<int64_t>(q + u) * n + i);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) acc[x] += v[u][x];
+  }
+  for (; q < S; ++q) {
     const f32x4 v = *reinterpret_cast<const f32x4*>(part + static_cast<int64_t>(q) * n + i);
 #pragma unroll
     for (int x = 0; x < 4; ++x) acc[x] += v[x];
@@ -292,7 +304,15 @@ __global__ __launch_bounds__(256) void dbg_reduce_kernel(DwgArgs a) {
   const int e = blockIdx.x * 256 + threadIdx.x;
   if (e >= a.E) return;
   float s = 0.0f;
-  for (int ch = 0; ch < a.nchunks; ++ch) s += a.partb[static_cast<int64_t>(ch) * a.E + e];
+  int ch = 0;
+  for (; ch + 8 <= a.nchunks; ch += 8) {   // in order, loads issued 8 at a time
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = a.partb[static_cast<int64_t>(ch + u) * a.E + e];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; ch < a.nchunks; ++ch) s += a.partb[static_cast<int64_t>(ch) * a.E + e];
   a.dbg[e] = s;
 }
 
