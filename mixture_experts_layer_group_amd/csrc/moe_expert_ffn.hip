@@ -54,6 +54,12 @@ constexpr int kGemmWN = MOE_GEMM_WN;
 #define MOE_GEMM_PIPELINED 1
 #endif
 constexpr bool kGemmPipelined = MOE_GEMM_PIPELINED;
+// pipelined loop: the wm = 1 waves refill the freed stage after the last step's MFMAs rather
+// than before them
+#ifndef MOE_GEMM_STAGGER
+#define MOE_GEMM_STAGGER 1
+#endif
+constexpr bool kGemmStagger = MOE_GEMM_STAGGER;
 
 struct Job {
   const char* A;   // first row of the tile (bytes)
@@ -719,13 +725,20 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
         } else if (kt + 1 < KT) {
           MOE_WAIT_VMCNT(0);
           lds_barrier();
-          if (kt + 2 < KT) feed_issue<T, AKM, BKM>(fd, smem + st * T::STAGE, w, kt + 2);
+          if (kt + 2 < KT && !(kGemmStagger && wm == 1))
+            feed_issue<T, AKM, BKM>(fd, smem + st * T::STAGE, w, kt + 2);
           const unsigned char* Sn = smem + (st ^ 1) * T::STAGE;
           read_step<T, AKM, BKM>(Sn, Sn + SLOT, 0, arow, brow, lane, sw, fa[0], fb[0]);
         }
         mfma_step<T>(fa[s & 1], fb[s & 1], acc);
         interleave_step<NRD, NMF>();
         __builtin_amdgcn_sched_barrier(0);
+        // the two waves of a SIMD (wm = 0 and 1) refill the stage at different moments, so
+        // that one issues MFMAs while the other issues its DMA
+        if (kGemmStagger && s + 1 == NS && wm == 1 && kt + 2 < KT) {
+          feed_issue<T, AKM, BKM>(fd, smem + st * T::STAGE, w, kt + 2);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
   } else if (KT > 0) {
