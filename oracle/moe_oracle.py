@@ -15,7 +15,7 @@ Sources, cited by page title and section:
                (quidproquo.cc).
 
 Where the pages are silent, garbled or disagree, the reading taken is stated at the
-function that depends on it (and listed in the design doc):
+function that depends on it, and summarised here:
   R-norm   top-k selection is made on the logits (softmax is monotone, so this is the
            same set as selecting on the softmax); norm=sum gives w_j = p_j / sum_sel p
            (the "softmax over the selected logits" of [Lec16] and the renormalised top-k
