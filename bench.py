@@ -330,10 +330,25 @@ def main():
         gbps = by / (t * 1e-3) / 1e9
         hbm[name] = {"bytes": int(by), "ms": round(t, 5), "GB/s": round(gbps, 1),
                      "frac": round(gbps / PEAK_HBM_GBPS, 4)}
-    hbm["permute"] = {"ms": round(stage_avg["permute"], 5),
-                      "note": "positions, rows and the row->token index only (GEMM 1 gathers "
-                              "the token rows from x); latency-bound"}
-    hbm["gate"] = {"ms": round(stage_avg["gate"], 5), "note": "capacity scan; latency-bound"}
+    # Metadata kernels (64-token router blocks, nbg per group).  Capacity scan: per (g, e) it
+    # reads the k rank histograms, the probability sums (fp64) and selection counts of every
+    # router block and writes the k per-block bases, count, the rank totals, P and c.
+    # Dispatch (forward): per slot it reads the expert id, the active flag and the gate weight
+    # and writes pos, row and the weight (zero when dropped); per kept row the row->token
+    # index; per router block its rank bases; the count table once.
+    G = cfg["n_groups"]
+    nbg = -(-(N // G) // 64)
+    bytes_gate = G * E * (8 * k * nbg + 12 * nbg + 4 * k + 16)
+    bytes_permute = N * k * 21 + 4 * R + 4 * G * k * E * nbg + 4 * G * E
+    for name, by, note in (
+            ("permute", bytes_permute, "positions, rows and the row->token index only (GEMM 1 "
+                                       "gathers the token rows from x); latency-bound"),
+            ("gate", bytes_gate, "capacity scan over the router blocks' histograms; "
+                                 "latency-bound")):
+        t = stage_avg[name]
+        gbps = by / (t * 1e-3) / 1e9
+        hbm[name] = {"bytes": int(by), "ms": round(t, 5), "GB/s": round(gbps, 1),
+                     "frac": round(gbps / PEAK_HBM_GBPS, 4), "note": note}
 
     # Achievable copy bandwidth in the same run (1 GiB device-to-device clone).
     src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
