@@ -76,10 +76,14 @@ int make_layout(const moe_cfg* c, Layout* L) {
   L->Rmax = std::min<int64_t>(k * N, G * E * std::min<int64_t>(C, L->S));
   L->rows_alloc = L->Rmax + L->BM;
   L->max_tiles = L->Rmax / L->BM + E + 1;
-  // 32-bit index limits used by the kernels
+  // 32-bit limits of the kernels: element indices, and the byte range of a buffer resource
+  // (GEMM 1 gathers its rows from the whole of x through one resource; h, o and the shared
+  // output are addressed from tile bases inside their buffers)
   const int64_t lim = (int64_t{1} << 31) - 1;
-  if (N * k > lim || N * std::max<int64_t>(M, E) > lim || L->rows_alloc * std::max(M, H) > lim ||
-      (E + Es) * M * H > lim || N * Es * H > lim || G * k * E * L->nbg > lim)
+  const int64_t eb = L->esz;
+  if (N * k > lim || N * std::max<int64_t>(M, E) > lim || N * M * eb > lim ||
+      L->rows_alloc * std::max(M, H) * eb > lim || (E + Es) * M * H > lim ||
+      N * Es * H * eb > lim || G * k * E * L->nbg > lim)
     return MOE_EUNSUPPORTED;
   size_t off = 0;
   auto take = [&](size_t bytes) {

@@ -83,7 +83,16 @@ BAD = [
     (dict(d_ff=320), binding.MOE_EUNSUPPORTED),
     (dict(dtype=0, d_model=96), binding.MOE_EUNSUPPORTED),
     (dict(n_shared=-1), binding.MOE_EINVAL),
+    # x of 2 GiB: GEMM 1 gathers rows from all of x through one 32-bit buffer range
+    (dict(n_tokens=1 << 22, n_groups=2), binding.MOE_EUNSUPPORTED),
+    (dict(n_tokens=1 << 21, n_groups=2, dtype=0), binding.MOE_EUNSUPPORTED),
 ]
+
+
+def test_largest_x_under_the_buffer_range_is_accepted(lib):
+    # bf16 x of 2^31 - 1024 bytes, one token short of the 32-bit buffer range
+    cfg = dict(configs.SMALL["small_top2_rr"], n_tokens=(1 << 22) - 2, n_groups=2)
+    assert binding.moe_workspace_size(cfg) > 0
 
 
 @pytest.mark.parametrize("patch,code", BAD, ids=[str(p) for p, _ in BAD])
