@@ -89,6 +89,10 @@ enum moe_dtype { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 };
  *                  topk_groups = 1) is plain top-k.  The groups also define dev_loss.
  * Shape constraints (MOE_EUNSUPPORTED otherwise):
  *   bf16: M % 128 == 0 and H % 128 == 0.   fp32: M % 64 == 0 and H % 64 == 0.
+ *   Sizes: x (N*M elements), the compact row buffers (rows * max(M, H)) and the shared
+ *   experts' activations (N*E_sh*H) each under 2^31 bytes, because the kernels address
+ *   them through 32-bit buffer ranges.  The backward adds the same bound for its
+ *   gradient buffers (see moe_backward_workspace_size).
  */
 typedef struct moe_cfg {
   int32_t n_tokens;
