@@ -103,36 +103,17 @@ __global__ __launch_bounds__(256) void act_fwd_kernel(BwdEltArgs a) {
 //   dWg token range s [E, M] = dl_s^T x_s (fp32 partials)
 // and of the shared experts' dz_q = (dy W2_{E+q}) act'(z_q) (K-major weights, output columns
 // q H1 of dz1sh).
-// Slot of weight-gradient entry i among the T entries of one problem.  The expert GEMM hands
-// each of the 8 XCDs one contiguous range of tiles, and an entry's K is its expert's kept
-// rows, which a skewed router makes very unequal (its favoured experts are neighbours).
-// Dealing the entries round-robin into 8 bins laid out one after another puts every 8th
-// expert, not 8 neighbouring ones, into one XCD's range, while each expert's tiles stay
-// contiguous on one XCD (its operands shared through that L2).  Outputs go by c_off, so the
-// order changes the schedule only.
-__device__ __forceinline__ int xcd_slot(int i, int T) {
-  const int b = i & 7;
-  int base = 0;
-  for (int c = 0; c < b; ++c) base += (T - c + 7) >> 3;   // bin c holds ceil((T - c) / 8)
-  return base + (i >> 3);
-}
-
 __global__ __launch_bounds__(256) void bwd_setup_kernel(BwdSetupArgs a) {
   const int t = threadIdx.x, E = a.E;
   const int64_t M = a.M, H = a.H, H1 = a.H1;
-  // The routed entries [0, E) and the shared experts' range entries [E, E + nsh) are two
-  // problems of one launch, each read with its own operand bases: each is reordered only
-  // among its own slots.
-  const int nsh = a.Es * a.nshared;
   for (int e = t; e < E; e += 256) {
     const int64_t o = a.offset[e];
     const int cnt = a.offset[e + 1] - a.offset[e];
     BatchEntry d2, d1;
     d2.a_off = o * M; d2.b_off = o * H; d2.c_off = e * M * H; d2.K = cnt; d2.pad = 0;
     d1.a_off = o * H1; d1.b_off = o * M; d1.c_off = e * H1 * M; d1.K = cnt; d1.pad = 0;
-    const int slot = xcd_slot(e, E);
-    a.dw2[slot] = d2;
-    a.dw1[slot] = d1;
+    a.dw2[e] = d2;
+    a.dw1[e] = d1;
   }
   for (int q = t; q < a.Es; q += 256) {  // shared experts' dz over every token
     BatchEntry dh;
@@ -151,9 +132,8 @@ __global__ __launch_bounds__(256) void bwd_setup_kernel(BwdSetupArgs a) {
     d2.K = Kr; d2.pad = 0;
     d1.a_off = n0 * a.Es * H1 + q * H1; d1.b_off = n0 * M; d1.c_off = static_cast<int64_t>(i) * H1 * M;
     d1.K = Kr; d1.pad = 0;
-    const int slot = E + xcd_slot(i, nsh);
-    a.dw2[slot] = d2;
-    a.dw1[slot] = d1;
+    a.dw2[E + i] = d2;
+    a.dw1[E + i] = d1;
   }
   for (int q = t; q < a.nsplit; q += 256) {  // dWg [E, M] over token range q
     BatchEntry g;

@@ -120,7 +120,27 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& g, Job& j, int bid) 
   // Blocks are dispatched round-robin over the 8 XCDs (block b -> XCD b % 8); give every
   // XCD a contiguous range of tiles so neighbouring tiles share its L2.
   const int xcd = bid & 7, loc = bid >> 3, q = total >> 3, r = total & 7;
-  const int pid = xcd * q + min(xcd, r) + loc;
+  int pid = xcd * q + min(xcd, r) + loc;
+  // Batched problems (the weight gradients: one entry per expert or token range, each with
+  // its own K, which a skewed router makes very unequal): when every entry of both problems
+  // has the same number of tiles, the entries are dealt round-robin over the 8 ranges, so
+  // each XCD gets every 8th entry rather than 8 neighbouring ones, and an entry's tiles stay
+  // together.  Slot s lies in bin b (bins of ceil((T - b) / 8) slots, laid out in order) and
+  // holds entry 8 (s - start of bin b) + b.  A bijection on [0, total).
+  if (g.p0.batch && (g.nprob == 1 || g.p1.batch)) {
+    const int tpe = ((g.p0.dense_rows + BM - 1) / BM) * nt0;   // tiles per entry
+    const bool same = g.nprob == 1 || ((g.p1.dense_rows + BM - 1) / BM) * nt1 == tpe;
+    const int T = tpe > 0 ? total / tpe : 0;
+    if (same && T > 0 && T * tpe == total) {
+      const int sl = pid / tpe, rr = pid - sl * tpe;
+      int b = 0, base = 0;
+      while (b < 7 && base + ((T - b + 7) >> 3) <= sl) {
+        base += (T - b + 7) >> 3;
+        ++b;
+      }
+      pid = (8 * (sl - base) + b) * tpe + rr;
+    }
+  }
   const bool second = pid >= tot0;
   const int lp = second ? pid - tot0 : pid;
   const int mts = second ? mt1 : mt0;
