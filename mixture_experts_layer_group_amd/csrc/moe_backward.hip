@@ -105,43 +105,23 @@ __global__ __launch_bounds__(256) void act_fwd_kernel(BwdEltArgs a) {
 // q H1 of dz1sh).
 __global__ __launch_bounds__(256) void bwd_setup_kernel(BwdSetupArgs a) {
   const int t = threadIdx.x, E = a.E;
-  const int64_t M = a.M, H = a.H, H1 = a.H1;
   for (int e = t; e < E; e += 256) {
     const int64_t o = a.offset[e];
     const int cnt = a.offset[e + 1] - a.offset[e];
-    BatchEntry d2, d1;
-    d2.a_off = o * M; d2.b_off = o * H; d2.c_off = e * M * H; d2.K = cnt; d2.pad = 0;
-    d1.a_off = o * H1; d1.b_off = o * M; d1.c_off = e * H1 * M; d1.K = cnt; d1.pad = 0;
-    a.dw2[e] = d2;
-    a.dw1[e] = d1;
+    a.dw2[e] = dw2_routed_entry(e, o, cnt, a.M, a.H);
+    a.dw1[e] = dw1_routed_entry(e, o, cnt, a.M, a.H1);
   }
-  for (int q = t; q < a.Es; q += 256) {  // shared experts' dz over every token
-    BatchEntry dh;
-    dh.a_off = 0; dh.b_off = (E + q) * M * H; dh.c_off = q * H1; dh.K = static_cast<int>(M);
-    dh.pad = 0;
-    a.dhsh[q] = dh;
-  }
+  for (int q = t; q < a.Es; q += 256)  // shared experts' dz over every token
+    a.dhsh[q] = dhsh_entry(q, E, a.M, a.H, a.H1);
   // shared experts' weight gradients over token range s (rows s * kshared ..) into fp32
   // partials [q][s], summed in range order afterwards
   for (int i = t; i < a.Es * a.nshared; i += 256) {
     const int q = i / a.nshared, sr = i - q * a.nshared;
-    const int64_t n0 = static_cast<int64_t>(sr) * a.kshared;
-    const int Kr = static_cast<int>(min<int64_t>(a.kshared, a.N - n0));
-    BatchEntry d2, d1;
-    d2.a_off = n0 * M; d2.b_off = n0 * a.Es * H + q * H; d2.c_off = static_cast<int64_t>(i) * M * H;
-    d2.K = Kr; d2.pad = 0;
-    d1.a_off = n0 * a.Es * H1 + q * H1; d1.b_off = n0 * M; d1.c_off = static_cast<int64_t>(i) * H1 * M;
-    d1.K = Kr; d1.pad = 0;
-    a.dw2[E + i] = d2;
-    a.dw1[E + i] = d1;
+    a.dw2[E + i] = dw2_shared_entry(q, sr, a.nshared, a.kshared, a.N, a.Es, a.M, a.H);
+    a.dw1[E + i] = dw1_shared_entry(q, sr, a.nshared, a.kshared, a.N, a.Es, a.M, a.H1);
   }
-  for (int q = t; q < a.nsplit; q += 256) {  // dWg [E, M] over token range q
-    BatchEntry g;
-    const int64_t n0 = static_cast<int64_t>(q) * a.ksplit;
-    g.a_off = n0 * a.Ep; g.b_off = n0 * M; g.c_off = static_cast<int64_t>(q) * E * M;
-    g.K = static_cast<int>(min<int64_t>(a.ksplit, a.N - n0)); g.pad = 0;
-    a.dwg[q] = g;
-  }
+  for (int q = t; q < a.nsplit; q += 256)  // dWg [E, M] over token range q
+    a.dwg[q] = dwg_entry(q, a.ksplit, a.N, a.Ep, a.M, E);
 }
 
 // Router backward, one wave per token: dL/dp through the gate normalisation (none, sum or

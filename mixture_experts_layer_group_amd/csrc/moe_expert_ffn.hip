@@ -107,52 +107,22 @@ __device__ __forceinline__ BatchEntry load_const(const BatchEntry* p) {
                     load_const(reinterpret_cast<const int32_t*>(q + 3)), 0};
 }
 
-// BN = output columns per tile (a gated tile computes 2 BN columns of A . B^T).
+// BN = output columns per tile (a gated tile computes 2 BN columns of A . B^T).  The block ->
+// tile order (XCD ranges, dealt batched entries, m-tile groups) is tile_coord's.
 template <int BM, int BN, int ESZ>
 __device__ __forceinline__ bool decode_tile(const GemmArgs& g, Job& j, int bid) {
   const int nt0 = (g.p0.N + BN - 1) / BN;
   const int mt0 = g.p0.tiles ? load_const(g.p0.num_tiles) : g.p0.max_tiles;
-  const int tot0 = mt0 * nt0;
   const int nt1 = g.nprob > 1 ? (g.p1.N + BN - 1) / BN : 0;
   const int mt1 = g.nprob > 1 ? g.p1.max_tiles : 0;
-  const int total = tot0 + mt1 * nt1;
-  if (bid >= total) return false;
-  // Blocks are dispatched round-robin over the 8 XCDs (block b -> XCD b % 8); give every
-  // XCD a contiguous range of tiles so neighbouring tiles share its L2.
-  const int xcd = bid & 7, loc = bid >> 3, q = total >> 3, r = total & 7;
-  int pid = xcd * q + min(xcd, r) + loc;
-  // Batched problems (the weight gradients: one entry per expert or token range, each with
-  // its own K, which a skewed router makes very unequal): when every entry of both problems
-  // has the same number of tiles, the entries are dealt round-robin over the 8 ranges, so
-  // each XCD gets every 8th entry rather than 8 neighbouring ones, and an entry's tiles stay
-  // together.  Slot s lies in bin b (bins of ceil((T - b) / 8) slots, laid out in order) and
-  // holds entry 8 (s - start of bin b) + b.  A bijection on [0, total).
-  if (g.p0.batch && (g.nprob == 1 || g.p1.batch)) {
-    const int tpe = ((g.p0.dense_rows + BM - 1) / BM) * nt0;   // tiles per entry
-    const bool same = g.nprob == 1 || ((g.p1.dense_rows + BM - 1) / BM) * nt1 == tpe;
-    const int T = tpe > 0 ? total / tpe : 0;
-    if (same && T > 0 && T * tpe == total) {
-      const int sl = pid / tpe, rr = pid - sl * tpe;
-      int b = 0, base = 0;
-      while (b < 7 && base + ((T - b + 7) >> 3) <= sl) {
-        base += (T - b + 7) >> 3;
-        ++b;
-      }
-      pid = (8 * (sl - base) + b) * tpe + rr;
-    }
-  }
-  const bool second = pid >= tot0;
-  const int lp = second ? pid - tot0 : pid;
-  const int mts = second ? mt1 : mt0;
-  const int nts = second ? nt1 : nt0;
-  constexpr int GM = kGemmGroupM;
-  const int per_group = GM * nts;
-  const int grp = lp / per_group;
-  const int first = grp * GM;
-  const int gsz = min(mts - first, GM);
-  const int in = lp - grp * per_group;
-  const int mt = first + in % gsz;
-  const int nt = in / gsz;
+  const bool batched = g.p0.batch && (g.nprob == 1 || g.p1.batch);
+  const TileSpace sp = tile_space(mt0, nt0, mt1, nt1, g.nprob, batched,
+                                  (g.p0.dense_rows + BM - 1) / BM,
+                                  (g.p1.dense_rows + BM - 1) / BM);
+  TileCoord tc;
+  if (!tile_coord(sp, bid, kGemmGroupM, tc)) return false;
+  const bool second = tc.prob == 1;
+  const int mt = tc.mt, nt = tc.nt;
 
   const GemmProblem& P = second ? g.p1 : g.p0;
   int e = 0, row0, nrows, K = P.K;
@@ -161,10 +131,9 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& g, Job& j, int bid) 
     const TileDesc d = load_const(P.tiles + mt);
     e = d.expert; row0 = d.row0; nrows = d.nrows;
   } else if (P.batch) {
-    const int mpe = (P.dense_rows + BM - 1) / BM;  // m-tiles per entry
-    const int be = mt / mpe, ml = mt - be * mpe;
+    int be;
+    batch_tile(mt, P.dense_rows, BM, be, row0, nrows);
     const BatchEntry d = load_const(P.batch + be);
-    row0 = ml * BM; nrows = min(BM, P.dense_rows - row0);
     aoff = d.a_off; boff = d.b_off; coff = d.c_off; K = d.K;
   } else {
     row0 = mt * BM; nrows = min(BM, P.dense_rows - row0);

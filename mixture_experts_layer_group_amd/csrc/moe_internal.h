@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "moe_tile_map.h"
+
 namespace moe {
 
 constexpr int kRouteTokens = 64;  // tokens per router / dispatch block (one wave of lanes)
@@ -49,10 +51,6 @@ struct ScanArgs {
   int G, E, k, C, nbg;
 };
 
-struct TileDesc {         // one BM-row tile of one expert in the compact buffer
-  int32_t expert, row0, nrows, pad;
-};
-
 // Offsets, capacity positions, dispatch rows, dropped-weight zeroing and the row scatter
 // of x.  Every block derives its group's row bases from count; block 0 writes offset,
 // the tile list and stats[0,1,3].
@@ -79,13 +77,6 @@ struct PermuteArgs {
   float* w_of_row;
   int N, G, S, M, E, k, C, nbg, dtype, BM;
   int slices;             // column slices per router block (set by the launcher)
-};
-
-// One entry of a batched GEMM problem: element offsets of its A, B and C blocks and its K
-// depth (a multiple of 128; 0 writes a zero block).
-struct BatchEntry {
-  int64_t a_off, b_off, c_off;
-  int32_t K, pad;
 };
 
 // Activation codes of a GEMM problem (the first three are moe_cfg's act values).

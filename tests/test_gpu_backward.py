@@ -10,6 +10,8 @@ import pytest
 
 from mixture_experts_layer_group_amd import binding, configs, synth
 
+import relu_slack
+
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
@@ -43,32 +45,6 @@ def run_backward(cfg, coefs=COEFS, inp=None, seed=None):
     return g, inp, dy32
 
 
-# ReLU' is a decision on the sign of the pre-activation, which the GPU computes with fp32
-# accumulation and the oracle in fp64: for |z| within the accumulation error of 0 either
-# side's decision is valid.  Such a decision moves a whole row dW1[e][h][:] (one term of its
-# sum over rows), so the hidden units with an oracle pre-activation |z| < RELU_DELTA (about
-# 1000x the GPU's accumulation error) are left out of the dW1 comparison and counted.
-RELU_DELTA = 1e-4
-
-
-def relu_ambiguous_rows(cfg, inp, r):
-    E, Es, H = cfg["n_experts"], cfg["n_shared"], cfg["d_ff"]
-    mask = np.zeros((E + Es, np.shape(inp.W1)[1]), bool)
-    if cfg["act"] != 0:
-        return mask
-    x = np.asarray(inp.x, np.float64)
-    kept = r["pos"] >= 0
-    for e in range(E):
-        rows = np.nonzero((kept & (r["topk_idx"] == e)).any(axis=1))[0]
-        if rows.size:
-            z = x[rows] @ np.asarray(inp.W1[e], np.float64).T
-            mask[e] = (np.abs(z) < RELU_DELTA).any(axis=0)
-    for q in range(Es):
-        z = x @ np.asarray(inp.W1[E + q], np.float64).T
-        mask[E + q] = (np.abs(z) < RELU_DELTA).any(axis=0)
-    return mask
-
-
 def check(cfg, coefs=COEFS, seed=None):
     from oracle import moe_backward as mb
     from oracle import moe_oracle as mo
@@ -89,15 +65,19 @@ def check(cfg, coefs=COEFS, seed=None):
     errs = {}
     for key in ("dx", "dWg", "dbg", "dW2"):
         errs[key] = h.rel_err(g[key], ref[key])
-    amb = relu_ambiguous_rows(cfg, inp, r)
+    slack, n_amb = relu_slack.relu_decision_slack(cfg, inp, r, dy)
     den = np.abs(ref["dW1"]).max()
-    d1 = np.abs(g["dW1"].astype(np.float64) - ref["dW1"])[~amb]
-    errs["dW1"] = float(d1.max() / (den if den > 0 else 1.0)) if d1.size else 0.0
-    h.say(f"[gpu-bwd] {name}: {errs} (dW1 rows with an ambiguous ReLU decision: "
-          f"{int(amb.sum())} of {amb.size})")
-    assert amb.sum() <= 0.1 * amb.size
+    den = den if den > 0 else 1.0
+    d1 = np.abs(g["dW1"].astype(np.float64) - ref["dW1"])
+    # the GPU's dh carries its bf16 roundings too: 2% headroom on the decision terms
+    excess = d1 - 1.02 * slack
+    errs["dW1"] = float(excess.max() / den) if excess.size else 0.0
+    errs["dW1_plain"] = float(d1.max() / den) if d1.size else 0.0
+    h.say(f"[gpu-bwd] {name}: {errs} (ambiguous ReLU decisions: {n_amb} (row, unit) pairs; "
+          f"dW1_plain ignores them)")
     for key, e in errs.items():
-        assert e <= tol, f"{key} rel err {e}"
+        if key != "dW1_plain":
+            assert e <= tol, f"{key} rel err {e}"
     return g, ref
 
 
