@@ -76,8 +76,8 @@ WORKLOADS = {
              "C=1.25*8N/256=640"),
 }
 
-# The workload the benchmark times by default.
-BENCH_WORKLOAD = "gshard_bf16"
+# The headline workload of the benchmark (the largest reference layer).
+BENCH_WORKLOAD = "large_expert_bf16"
 
 # Small layers the CPU oracle finishes in well under a second that still span several
 # GEMM tiles, ragged expert tails, several groups and every gating flag.

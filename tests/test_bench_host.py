@@ -53,10 +53,31 @@ def test_cpu_baseline_object():
 def test_traffic_is_only_reported_for_the_profiled_kernel_source():
     with open(bench.TRAFFIC_FILE) as f:
         t = json.load(f)
-    wl = t["workload"]
-    if t["kernel_hash"] == bench.kernel_hash():
-        assert bench.load_traffic(wl, 1.0) == t["hbm_bytes_per_launch"]
-    else:
-        assert bench.load_traffic(wl, 1.0) is None
-    other = next(w for w in configs.WORKLOADS if w != wl)
-    assert bench.load_traffic(other, 1.0) is None
+    for wl, rec in t["workloads"].items():
+        if t["kernel_hash"] == bench.kernel_hash():
+            assert bench.load_traffic(wl) == rec["hbm_bytes_per_launch"]
+        else:
+            assert bench.load_traffic(wl) is None
+    other = next(w for w in configs.WORKLOADS if w not in t["workloads"])
+    assert bench.load_traffic(other) is None
+
+
+def test_cpu_baseline_names_the_host_cpu():
+    cfg = configs.WORKLOADS["tiny_fp32"]
+    inp = synth.make_inputs(cfg)
+    cb = bench.cpu_baseline(cfg, inp, budget_tokens=32, min_seconds=0.0, max_passes=1)
+    assert bench.cpu_model() in cb["sample"] and "os.cpu_count()" in cb["sample"]
+
+
+def test_roofline_bound_follows_the_layer_shapes():
+    """MFMA for the contractions, HBM for the weight-streaming Switch-style layer; frac is the
+    fraction against that bound's peak."""
+    for name in ("gshard_bf16", "large_expert_bf16", "shared_routed_bf16", "switch_bf16"):
+        cfg = configs.WORKLOADS[name]
+        ro = bench.gemm_roofline(cfg, name, R=cfg["n_tokens"], live=cfg["n_experts"],
+                                 gemm_ms=1.0)
+        want = "hbm" if name == "switch_bf16" else "mfma"
+        assert ro["bound"] == want
+        frac = ro["hbm_frac"] if want == "hbm" else ro["mfma_frac"]
+        assert ro["frac"] == frac and ro["peak"] == (bench.PEAK_HBM_GBPS if want == "hbm"
+                                                     else bench.PEAK_BF16_TFLOPS)
