@@ -20,7 +20,8 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  All work is enqueued
  *     asynchronously on it; outputs are valid once the stream has been synchronised.
  *   - The library allocates no device memory, keeps no pointer after returning and has
- *     no global state: calls with distinct workspaces may run concurrently.
+ *     no global state: calls with distinct workspaces may run concurrently.  The one
+ *     exception is moe_forward_noalloc's static scratch array (one per GPU, see there).
  *   - Return value: MOE_OK (0) or a negative MOE_E* code.  All argument checks run on the
  *     host before anything is enqueued; a call that fails them enqueues nothing and writes
  *     nothing.  MOE_EHIP reports a launch error (hipGetLastError) after enqueueing.
@@ -37,15 +38,17 @@ extern "C" {
 #endif
 
 /* 2: gated (SwiGLU) experts; 3: p-norm gates, router z-loss; 4: group-limited routing,
- * device-level balance loss; 5: backward pass */
-#define MOE_ABI_VERSION 5
+ * device-level balance loss; 5: backward pass; 6: moe_forward_noalloc */
+#define MOE_ABI_VERSION 6
 
 enum moe_status {
   MOE_OK = 0,
   MOE_EINVAL = -1,        /* bad cfg, NULL required pointer, pointer not 16-byte aligned */
   MOE_EWORKSPACE = -2,    /* workspace_bytes < moe_workspace_size(cfg) */
   MOE_EUNSUPPORTED = -3,  /* valid cfg outside the kernels' shape constraints */
-  MOE_EHIP = -4           /* a HIP launch failed */
+  MOE_EHIP = -4,          /* a HIP launch failed */
+  MOE_ESCRATCH = -5       /* moe_forward_noalloc: the layer needs more workspace than
+                             MOE_NOALLOC_SCRATCH_BYTES */
 };
 
 /* GELU: exact erf form.  SWIGLU: the gated expert (Swish(x W1) * (x W2)) W3 of [Lec16]
@@ -205,6 +208,29 @@ int moe_forward_timed(const moe_cfg* cfg, const void* x, const void* Wg, const f
                       const void* W1, const void* W2, const float* u, void* y,
                       float* aux_loss, const moe_meta* meta, void* workspace,
                       size_t workspace_bytes, void* stream, void* const* events);
+
+/* Size of moe_forward_noalloc's static scratch array on each GPU (64 MiB). */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * moe_forward for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  The caller passes the inputs and
+ * outputs of moe_forward (same meaning, layouts, results and check order) but no workspace:
+ * the library uses a static device array of MOE_NOALLOC_SCRATCH_BYTES on each GPU, which it
+ * holds from the first use on that GPU until the process ends.  The call allocates nothing
+ * and runs the same kernels as moe_forward.
+ *   - The current device (hipSetDevice) must be the device of `stream` and of the tensors.
+ *   - MOE_ESCRATCH: moe_workspace_size(cfg) > MOE_NOALLOC_SCRATCH_BYTES (checked on the host
+ *     right after cfg; nothing is enqueued).  MOE_EHIP: the scratch array's address could not
+ *     be obtained on the current device.
+ *   - Every call on one GPU shares that GPU's array, and the array keeps the last call's
+ *     contents (none of it needs to start cleared).  Calls that overlap on one GPU (two host
+ *     threads, or two streams without ordering between them) race on the array and give
+ *     undefined results: serialise them, e.g. on one stream.
+ */
+int moe_forward_noalloc(const moe_cfg* cfg, const void* x, const void* Wg, const float* bg,
+                        const void* W1, const void* W2, const float* u, void* y,
+                        float* aux_loss, const moe_meta* meta, void* stream);
 
 /*
  * Device workspace (bytes) that moe_backward needs for this cfg (larger than the forward's).

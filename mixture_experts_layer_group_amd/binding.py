@@ -14,7 +14,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "moe.h")
 
-MOE_OK, MOE_EINVAL, MOE_EWORKSPACE, MOE_EUNSUPPORTED, MOE_EHIP = 0, -1, -2, -3, -4
+MOE_OK, MOE_EINVAL, MOE_EWORKSPACE, MOE_EUNSUPPORTED, MOE_EHIP, MOE_ESCRATCH = 0, -1, -2, -3, -4, -5
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 MOE_N_EVENTS = 7
 STAGES = ("router", "gate", "permute", "ffn1", "ffn2", "combine")
 
@@ -67,6 +68,8 @@ def load_library(path=LIB_PATH):
     lib.moe_forward.argtypes = fwd
     lib.moe_forward_timed.restype = i32
     lib.moe_forward_timed.argtypes = fwd + [ctypes.POINTER(vp)]
+    lib.moe_forward_noalloc.restype = i32
+    lib.moe_forward_noalloc.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, metap, vp]
     lib.moe_backward_workspace_size.restype = i32
     lib.moe_backward_workspace_size.argtypes = [cfgp, ctypes.POINTER(sz)]
     f32 = ctypes.c_float
@@ -211,6 +214,17 @@ def moe_forward(cfg, x, Wg, bg, W1, W2, u, y, aux_loss, meta, workspace, stream=
         _ptr(aux_loss), ctypes.byref(m), _ptr(workspace), workspace.numel(), _stream(stream))
     if rc:
         raise MoeError(rc, "moe_forward")
+
+
+def moe_forward_noalloc(cfg, x, Wg, bg, W1, W2, u, y, aux_loss, meta, stream=None):
+    """C ABI moe_forward_noalloc (moe_forward on the library's static per-GPU scratch)."""
+    c = make_cfg(cfg)
+    m = meta.as_struct()
+    rc = load_library().moe_forward_noalloc(
+        ctypes.byref(c), _ptr(x), _ptr(Wg), _ptr(bg), _ptr(W1), _ptr(W2), _ptr(u), _ptr(y),
+        _ptr(aux_loss), ctypes.byref(m), _stream(stream))
+    if rc:
+        raise MoeError(rc, "moe_forward_noalloc")
 
 
 def moe_forward_timed(cfg, x, Wg, bg, W1, W2, u, y, aux_loss, meta, workspace, events,

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 SOURCES = ["moe_router.hip", "moe_gate.hip", "moe_permute.hip", "moe_expert_ffn.hip",
-           "moe_combine.hip", "moe_backward.hip", "moe_api.cpp"]
+           "moe_combine.hip", "moe_backward.hip", "moe_noalloc.hip", "moe_api.cpp"]
 ARCH = "gfx950"
 
 

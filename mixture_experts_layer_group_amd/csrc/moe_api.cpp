@@ -237,10 +237,11 @@ int empty_call(const moe_cfg* c, const moe_meta* m, float* aux, hipStream_t s, v
   return rc;
 }
 
+// check_only: run every host check and return without enqueueing anything.
 int forward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* bg,
                  const void* W1, const void* W2, const float* u, void* y, float* aux,
                  const moe_meta* m, void* workspace, size_t wbytes, void* stream,
-                 void* const* ev) {
+                 void* const* ev, bool check_only = false) {
   Run r;
   r.c = c;
   int rc = make_layout(c, &r.L);
@@ -250,7 +251,7 @@ int forward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* b
   if (c->n_tokens == 0) {
     // Nothing to route: only the small outputs are written; token pointers may be NULL.
     rc = check_meta_empty(m);
-    if (rc) return rc;
+    if (rc || check_only) return rc;
     return empty_call(c, m, aux, static_cast<hipStream_t>(stream), ev);
   }
   rc = check_meta(m, true);
@@ -260,6 +261,7 @@ int forward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* b
   const void* req[] = {x, Wg, W1, W2, y};
   for (const void* p : req)
     if (!p || !aligned16(p)) return MOE_EINVAL;
+  if (check_only) return MOE_OK;
   r.ws = static_cast<char*>(workspace);
   r.s = static_cast<hipStream_t>(stream);
 
@@ -668,6 +670,16 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
 
 }  // namespace
 
+namespace moe {
+int forward_workspace(const moe_cfg* cfg, const void* x, const void* Wg, const float* bg,
+                      const void* W1, const void* W2, const float* u, void* y, float* aux,
+                      const moe_meta* m, void* workspace, size_t wbytes, void* stream,
+                      bool check_only) {
+  return forward_impl(cfg, x, Wg, bg, W1, W2, u, y, aux, m, workspace, wbytes, stream, nullptr,
+                      check_only);
+}
+}  // namespace moe
+
 extern "C" {
 
 int moe_abi_version(void) { return MOE_ABI_VERSION; }
@@ -679,6 +691,9 @@ const char* moe_strerror(int code) {
     case MOE_EWORKSPACE: return "workspace too small";
     case MOE_EUNSUPPORTED: return "shape outside the kernels' constraints";
     case MOE_EHIP: return "HIP launch error";
+    case MOE_ESCRATCH:
+      return "layer needs more workspace than moe_forward_noalloc's static scratch "
+             "(MOE_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown error";
   }
 }

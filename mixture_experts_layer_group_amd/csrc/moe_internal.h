@@ -7,6 +7,9 @@
 
 #include "moe_tile_map.h"
 
+struct moe_cfg;
+struct moe_meta;
+
 namespace moe {
 
 constexpr int kRouteTokens = 64;  // tokens per router / dispatch block (one wave of lanes)
@@ -221,5 +224,12 @@ hipError_t launch_expert_gemm(const GemmArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_aux_only(const CombineArgs& a, hipStream_t s);
 hipError_t launch_empty(const EmptyArgs& a, hipStream_t s);
+
+// moe_forward with a given workspace (moe_api.cpp), shared by the entry points;
+// check_only: run the host checks only (nothing is enqueued).
+int forward_workspace(const moe_cfg* cfg, const void* x, const void* Wg, const float* bg,
+                      const void* W1, const void* W2, const float* u, void* y, float* aux,
+                      const moe_meta* m, void* workspace, size_t wbytes, void* stream,
+                      bool check_only);
 
 }  // namespace moe

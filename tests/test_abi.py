@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib):
 def test_version_and_strerror(lib):
     hdr = open(binding.HEADER).read()
     assert int(re.search(r"#define MOE_ABI_VERSION (\d+)", hdr).group(1)) == binding.moe_abi_version()
-    for code in (0, -1, -2, -3, -4, 99):
+    for code in (0, -1, -2, -3, -4, -5, 99):
         assert isinstance(binding.moe_strerror(code), str) and binding.moe_strerror(code)
     assert binding.moe_strerror(-2) != binding.moe_strerror(-1)
 
@@ -231,3 +231,52 @@ def test_backward_workspace_sizes_small_batches(lib):
     for n in (0, 1, 127, 128, 129, 4096):
         cfg = configs.with_overrides(base, n_tokens=n, n_groups=1)
         assert binding.moe_backward_workspace_size(cfg) > 0, n
+
+
+# ---- moe_forward_noalloc: host-side checks (the scratch array is never touched here)
+
+def test_noalloc_scratch_size_matches_header(lib):
+    hdr = open(binding.HEADER).read()
+    m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == binding.MOE_NOALLOC_SCRATCH_BYTES
+
+
+def _noalloc_call(cfg, **over):
+    a = dict(x=FakeTensor(0x20000000), Wg=FakeTensor(0x21000000), bg=None,
+             W1=FakeTensor(0x22000000), W2=FakeTensor(0x23000000), u=FakeTensor(0x24000000),
+             y=FakeTensor(0x25000000), aux=FakeTensor(0x26000000), meta=_fake_meta())
+    a.update(over)
+    binding.moe_forward_noalloc(cfg, a["x"], a["Wg"], a["bg"], a["W1"], a["W2"], a["u"],
+                                a["y"], a["aux"], a["meta"], stream=_NoStream())
+
+
+NOALLOC_BAD = [
+    ("bad cfg", dict(n_groups=0), {}, binding.MOE_EINVAL),
+    ("unsupported cfg", dict(d_model=200), {}, binding.MOE_EUNSUPPORTED),
+    # the GShard-style layer needs 0.3 GB of workspace
+    ("larger than the scratch", dict(configs.WORKLOADS["gshard_bf16"]), {}, binding.MOE_ESCRATCH),
+    ("null x", {}, dict(x=FakeTensor(0)), binding.MOE_EINVAL),
+    ("misaligned aux", {}, dict(aux=FakeTensor(0x26000004)), binding.MOE_EINVAL),
+    ("null u with random routing", {}, dict(u=None), binding.MOE_EINVAL),
+    ("misaligned meta.pos", {}, dict(meta=_fake_meta(bad="pos")), binding.MOE_EINVAL),
+]
+
+
+@pytest.mark.parametrize("what,patch,over,code", NOALLOC_BAD, ids=[w for w, _, _, _ in NOALLOC_BAD])
+def test_noalloc_rejected_on_host(lib, what, patch, code, over):
+    cfg = dict(configs.SMALL["small_top2_rr"], **patch)
+    with pytest.raises(binding.MoeError) as ei:
+        _noalloc_call(cfg, **over)
+    assert ei.value.code == code, what
+
+
+def test_noalloc_limit_is_the_forward_workspace(lib):
+    """A layer is accepted by moe_forward_noalloc iff its forward workspace fits the scratch."""
+    base = configs.SMALL["small_top2_rr"]
+    for n in (1536, 3 * 4096, 3 * 16384, 3 * 65536):
+        cfg = configs.with_overrides(base, n_tokens=n, capacity=n // 24)
+        fits = binding.moe_workspace_size(cfg) <= binding.MOE_NOALLOC_SCRATCH_BYTES
+        if not fits:
+            with pytest.raises(binding.MoeError) as ei:
+                _noalloc_call(cfg)
+            assert ei.value.code == binding.MOE_ESCRATCH
