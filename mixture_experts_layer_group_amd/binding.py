@@ -54,6 +54,13 @@ def load_library(path=LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built: run `python -m mixture_experts_layer_group_amd.build`")
+    # torch ships its own HIP runtime under the same soname as ROCm's: load it first, so that
+    # libmoe.so binds to the runtime that owns torch's streams, events and allocations (loaded
+    # the other way round, the process ends up mixing two runtimes and launches fail)
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     cfgp, metap = ctypes.POINTER(MoeCfg), ctypes.POINTER(MoeMetaC)

@@ -14,7 +14,7 @@
 #include <cstdint>
 #include <cstring>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "moe_internal.h"
 
 namespace {

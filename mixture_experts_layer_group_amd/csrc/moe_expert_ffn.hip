@@ -648,6 +648,54 @@ __device__ __forceinline__ void store_tile(const Job& j, f32x16 (&acc)[T::TN][T:
   }
 }
 
+// Workgroup barrier for LDS hand-offs, written with builtins so that the compiler's wait
+// counters know every LDS and scalar-memory operation has completed at it: s_waitcnt
+// lgkmcnt(0), then s_barrier (no global-memory fence, so loads in flight are not drained).
+__device__ __forceinline__ void lds_barrier_visible() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0); vmcnt and expcnt at their no-wait maxima
+  __builtin_amdgcn_s_barrier();
+}
+
+// One K chunk of the pipelined two-stage loop (chunk kt in stage kt & 1).  Step s multiplies
+// register set s & 1 while the reads of step s + 1 fill the other set.  At the last step, with
+// NEXT (chunk kt + 1 exists), the block waits for chunk kt + 1, passes the barrier (every wave
+// has read chunk kt's stage into registers), refills that stage with chunk kt + 2 (REFILL) and
+// reads chunk kt + 1's first step, so no MFMA waits for a fragment read at a chunk boundary.
+// The waves of tile half wm = 1 refill after their last MFMAs instead, so that each SIMD (one
+// wave of each half) always has a wave issuing MFMAs while the other issues its loads.
+template <class T, bool AKM, bool BKM, bool NEXT, bool REFILL>
+__device__ __forceinline__ void k_chunk(Feed<T>& fd, unsigned char* smem, int kt, int w, int wm,
+                                        int lane, int arow, int brow, int sw,
+                                        bf16x8 (&fa)[2][T::TM], bf16x8 (&fb)[2][T::TN],
+                                        f32x16 (&acc)[T::TN][T::TM]) {
+  constexpr int NS = T::BK / 16, SLOT = T::BM * T::ROW;
+  constexpr int NRD = (T::TM + T::TN) * (AKM || BKM ? 2 : 1);   // wide upper bound
+  constexpr int NMF = T::TM * T::TN;
+  const int st = kt & 1;
+  const unsigned char* S = smem + st * T::STAGE;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    if (s + 1 < NS) {
+      read_step<T, AKM, BKM>(S, S + SLOT, s + 1, arow, brow, lane, sw, fa[(s + 1) & 1],
+                             fb[(s + 1) & 1]);
+    } else if (NEXT) {
+      MOE_WAIT_VMCNT(0);
+      lds_barrier_visible();
+      if (REFILL && !(kGemmStagger && wm == 1))
+        feed_issue<T, AKM, BKM>(fd, smem + st * T::STAGE, w, kt + 2);
+      const unsigned char* Sn = smem + (st ^ 1) * T::STAGE;
+      read_step<T, AKM, BKM>(Sn, Sn + SLOT, 0, arow, brow, lane, sw, fa[0], fb[0]);
+    }
+    mfma_step<T>(fa[s & 1], fb[s & 1], acc);
+    interleave_step<NRD, NMF>();
+    __builtin_amdgcn_sched_barrier(0);
+    if (REFILL && kGemmStagger && s + 1 == NS && wm == 1) {
+      feed_issue<T, AKM, BKM>(fd, smem + st * T::STAGE, w, kt + 2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
 // One tile per block.
 // KM: bit 0 = A is K-major, bit 1 = B is K-major.  DACT: fused activation gradient (-1: none).
 template <int BM, int BN, int WN, int ACT, int BK, int NST, bool OUTF32, int KM, int DACT>
@@ -696,43 +744,25 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
     // step the block waits for chunk kt + 1, passes the barrier (every wave has read chunk
     // kt's stage into registers by then), refills that stage with chunk kt + 2 and reads
     // chunk kt + 1's first step, so no MFMA waits for a fragment read at a chunk boundary.
-    constexpr int NS = BK / 16;
-    static_assert(NS % 2 == 0, "an even number of steps per chunk keeps the register sets aligned");
-    constexpr int NRD = (T::TM + T::TN) * (AKM || BKM ? 2 : 1);   // wide upper bound
-    constexpr int NMF = T::TM * T::TN;
+    static_assert((BK / 16) % 2 == 0,
+                  "an even number of steps per chunk keeps the register sets aligned");
     bf16x8 fa[2][T::TM], fb[2][T::TN];
     feed_issue<T, AKM, BKM>(fd, smem, w, 0);
     MOE_WAIT_VMCNT(0);
-    lds_barrier();
+    lds_barrier_visible();
     if (KT > 1) feed_issue<T, AKM, BKM>(fd, smem + T::STAGE, w, 1);
     read_step<T, AKM, BKM>(smem, smem + SLOT, 0, arow, brow, lane, sw, fa[0], fb[0]);
-    for (int kt = 0; kt < KT; ++kt) {
-      const int st = kt & 1;
-      const unsigned char* S = smem + st * T::STAGE;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        if (s + 1 < NS) {
-          read_step<T, AKM, BKM>(S, S + SLOT, s + 1, arow, brow, lane, sw, fa[(s + 1) & 1],
-                                 fb[(s + 1) & 1]);
-        } else if (kt + 1 < KT) {
-          MOE_WAIT_VMCNT(0);
-          lds_barrier();
-          if (kt + 2 < KT && !(kGemmStagger && wm == 1))
-            feed_issue<T, AKM, BKM>(fd, smem + st * T::STAGE, w, kt + 2);
-          const unsigned char* Sn = smem + (st ^ 1) * T::STAGE;
-          read_step<T, AKM, BKM>(Sn, Sn + SLOT, 0, arow, brow, lane, sw, fa[0], fb[0]);
-        }
-        mfma_step<T>(fa[s & 1], fb[s & 1], acc);
-        interleave_step<NRD, NMF>();
-        __builtin_amdgcn_sched_barrier(0);
-        // the two waves of a SIMD (wm = 0 and 1) refill the stage at different moments, so
-        // that one issues MFMAs while the other issues its DMA
-        if (kGemmStagger && s + 1 == NS && wm == 1 && kt + 2 < KT) {
-          feed_issue<T, AKM, BKM>(fd, smem + st * T::STAGE, w, kt + 2);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
+    // The steady state (chunks with a next chunk and one to refill) runs without a branch
+    // around its LDS reads, so the compiler's waits count exactly the reads in flight; the
+    // last two chunks are peeled.
+    int kt = 0;
+    for (; kt + 2 < KT; ++kt)
+      k_chunk<T, AKM, BKM, true, true>(fd, smem, kt, w, wm, lane, arow, brow, sw, fa, fb, acc);
+    if (kt + 1 < KT) {
+      k_chunk<T, AKM, BKM, true, false>(fd, smem, kt, w, wm, lane, arow, brow, sw, fa, fb, acc);
+      ++kt;
     }
+    k_chunk<T, AKM, BKM, false, false>(fd, smem, kt, w, wm, lane, arow, brow, sw, fa, fb, acc);
   } else if (KT > 0) {
 #pragma unroll
     for (int p = 0; p < NST - 1; ++p) feed_issue<T, AKM, BKM>(fd, smem + p * T::STAGE, w, p);

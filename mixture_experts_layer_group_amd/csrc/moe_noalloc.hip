@@ -6,7 +6,7 @@
 
 #include <mutex>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "moe_internal.h"
 
 namespace {
