@@ -189,16 +189,39 @@ def backward_timing(cfg, x, Wg, W1, W2, bg, u, R, steps):
         ms.append((e0, e1))
     torch.cuda.synchronize()
     t = float(np.median([a.elapsed_time(b) for a, b in ms]))
+    # the training pair: moe_forward_train keeps h (and z) in the workspace, then
+    # moe_backward_saved skips GEMM 1; each call timed on its own
+    y = torch.empty_like(x)
+    aux = torch.empty((4,), dtype=torch.float32, device="cuda")
+    tf, tb = [], []
+    for _ in range(steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        binding.moe_forward_train(cfg, x, Wg, bg, W1, W2, u, y, aux, meta, ws)
+        e[1].record()
+        binding.moe_backward_saved(cfg, x, Wg, bg, W1, W2, u, dy, coefs["coef_aux"],
+                                   coefs["coef_z"], coefs["coef_dev"], out["dx"], out["dWg"],
+                                   out["dbg"], out["dW1"], out["dW2"], meta, ws)
+        e[2].record()
+        tf.append((e[0], e[1]))
+        tb.append((e[1], e[2]))
+    torch.cuda.synchronize()
+    t_tf = float(np.median([a.elapsed_time(b) for a, b in tf]))
+    t_bs = float(np.median([a.elapsed_time(b) for a, b in tb]))
     N, M, H, Es = cfg["n_tokens"], cfg["d_model"], cfg["d_ff"], cfg["n_shared"]
     gl = 2 if cfg["act"] == configs.ACT_SWIGLU else 1
     fwd_ffn = (gl + 1) * 2.0 * M * H * (R + N * Es)
     recompute = gl * 2.0 * M * H * (R + N * Es)
-    del out, ws, dy
+    del out, ws, dy, y, aux
     return {"ms": round(t, 4), "tokens_per_s": round(N / (t * 1e-3), 1), "steps": steps,
             "timing": "median of per-call HIP events",
             "ffn_flops_backward": 2 * fwd_ffn, "ffn_flops_recompute": recompute,
             "tflops_backward_alg": round(2 * fwd_ffn / (t * 1e-3) / 1e12, 2),
-            "tflops_incl_recompute": round((2 * fwd_ffn + recompute) / (t * 1e-3) / 1e12, 2)}
+            "tflops_incl_recompute": round((2 * fwd_ffn + recompute) / (t * 1e-3) / 1e12, 2),
+            "saved": {"backward_ms": round(t_bs, 4), "forward_train_ms": round(t_tf, 4),
+                      "tflops_backward_alg": round(2 * fwd_ffn / (t_bs * 1e-3) / 1e12, 2),
+                      "note": "moe_forward_train then moe_backward_saved (expert activations "
+                              "kept by the forward, GEMM 1 not recomputed)"}}
 
 
 def graph_timing(cfg, xs, ys, Wg, bg, W1, W2, u, aux, meta, ws, steps):

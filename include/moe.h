@@ -39,7 +39,7 @@ extern "C" {
 
 /* 2: gated (SwiGLU) experts; 3: p-norm gates, router z-loss; 4: group-limited routing,
  * device-level balance loss; 5: backward pass; 6: moe_forward_noalloc */
-#define MOE_ABI_VERSION 6
+#define MOE_ABI_VERSION 7
 
 enum moe_status {
   MOE_OK = 0,
@@ -270,6 +270,44 @@ int moe_backward(const moe_cfg* cfg, const void* x, const void* Wg, const float*
                  float coef_z, float coef_dev, void* dx, float* dWg, float* dbg, float* dW1,
                  float* dW2, const moe_meta* meta, void* workspace, size_t workspace_bytes,
                  void* stream);
+
+/*
+ * Training forward: moe_forward run in a moe_backward workspace that keeps, for
+ * moe_backward_saved, the expert activations h and (GELU and SwiGLU layers) their
+ * pre-activations, instead of leaving the backward to recompute expert GEMM 1.  This is the
+ * other side of the trade-off in [GShard] "Memory 与 Communication" (per-device memory):
+ * the activations the backward needs are kept while they fit, and rematerialised only when
+ * they do not (moe_backward).
+ *   arguments as in moe_forward; y, aux_loss and meta are written exactly as moe_forward
+ *   writes them (bit for bit)
+ *   workspace device scratch of at least moe_backward_workspace_size(cfg) bytes, owned by
+ *             the library from this call until the matching moe_backward_saved call
+ * Check order: cfg, workspace (MOE_EINVAL), workspace_bytes against
+ * moe_backward_workspace_size (MOE_EWORKSPACE), then as moe_forward.
+ */
+int moe_forward_train(const moe_cfg* cfg, const void* x, const void* Wg, const float* bg,
+                      const void* W1, const void* W2, const float* u, void* y, float* aux_loss,
+                      const moe_meta* meta, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
+ * moe_backward that takes h and the pre-activations from the workspace of the preceding
+ * moe_forward_train call rather than recomputing expert GEMM 1.  Arguments, outputs, errors
+ * and check order as in moe_backward.  The call must use the same cfg, x, Wg, bg, W1, u and
+ * workspace as that moe_forward_train call, with nothing else run on the workspace in
+ * between (calls on one stream are ordered; across streams the caller orders them).  The
+ * routing, and with it every row index, is still recomputed from x and Wg, so a workspace
+ * that breaks this contract gives wrong gradients but no access outside the buffers.
+ * Results: ReLU layers: every output bit for bit as moe_backward.  GELU and SwiGLU layers:
+ * dW1 bit for bit as moe_backward; dW2, and through the combine weights' gradient dx, dWg
+ * and dbg, use the forward's h = act(z) rounded once from the fp32 accumulators, where
+ * moe_backward recomputes h from the rounded z.
+ */
+int moe_backward_saved(const moe_cfg* cfg, const void* x, const void* Wg, const float* bg,
+                       const void* W1, const void* W2, const float* u, const void* dy,
+                       float coef_aux, float coef_z, float coef_dev, void* dx, float* dWg,
+                       float* dbg, float* dW1, float* dW2, const moe_meta* meta,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Routing only, from caller-given logits [N, E] fp32: softmax, top-k, gate weights, random

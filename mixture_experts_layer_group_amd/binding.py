@@ -80,9 +80,13 @@ def load_library(path=LIB_PATH):
     lib.moe_backward_workspace_size.restype = i32
     lib.moe_backward_workspace_size.argtypes = [cfgp, ctypes.POINTER(sz)]
     f32 = ctypes.c_float
+    bwd = [cfgp, vp, vp, vp, vp, vp, vp, vp, f32, f32, f32, vp, vp, vp, vp, vp, metap, vp, sz, vp]
     lib.moe_backward.restype = i32
-    lib.moe_backward.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, f32, f32, f32, vp, vp, vp, vp,
-                                 vp, metap, vp, sz, vp]
+    lib.moe_backward.argtypes = bwd
+    lib.moe_forward_train.restype = i32
+    lib.moe_forward_train.argtypes = fwd
+    lib.moe_backward_saved.restype = i32
+    lib.moe_backward_saved.argtypes = bwd
     lib.moe_route.restype = i32
     lib.moe_route.argtypes = [cfgp, vp, vp, metap, vp, vp, sz, vp]
     _lib = lib
@@ -168,36 +172,95 @@ def moe_backward_workspace_size(cfg):
     return n.value
 
 
-def moe_backward(cfg, x, Wg, bg, W1, W2, u, dy, coef_aux, coef_z, coef_dev, dx, dWg, dbg, dW1,
-                 dW2, meta, workspace, stream=None):
-    """C ABI moe_backward on torch tensors (see include/moe.h)."""
+def _backward_call(fn, cfg, x, Wg, bg, W1, W2, u, dy, coef_aux, coef_z, coef_dev, dx, dWg,
+                   dbg, dW1, dW2, meta, workspace, stream):
     c = make_cfg(cfg)
     m = meta.as_struct()
-    rc = load_library().moe_backward(
+    rc = getattr(load_library(), fn)(
         ctypes.byref(c), _ptr(x), _ptr(Wg), _ptr(bg), _ptr(W1), _ptr(W2), _ptr(u), _ptr(dy),
         float(coef_aux), float(coef_z), float(coef_dev), _ptr(dx), _ptr(dWg), _ptr(dbg),
         _ptr(dW1), _ptr(dW2), ctypes.byref(m), _ptr(workspace), workspace.numel(),
         _stream(stream))
     if rc:
-        raise MoeError(rc, "moe_backward")
+        raise MoeError(rc, fn)
+
+
+def moe_backward(cfg, x, Wg, bg, W1, W2, u, dy, coef_aux, coef_z, coef_dev, dx, dWg, dbg, dW1,
+                 dW2, meta, workspace, stream=None):
+    """C ABI moe_backward on torch tensors (see include/moe.h)."""
+    _backward_call("moe_backward", cfg, x, Wg, bg, W1, W2, u, dy, coef_aux, coef_z, coef_dev,
+                   dx, dWg, dbg, dW1, dW2, meta, workspace, stream)
+
+
+def moe_backward_saved(cfg, x, Wg, bg, W1, W2, u, dy, coef_aux, coef_z, coef_dev, dx, dWg, dbg,
+                       dW1, dW2, meta, workspace, stream=None):
+    """C ABI moe_backward_saved: the backward on the activations moe_forward_train kept in
+    workspace."""
+    _backward_call("moe_backward_saved", cfg, x, Wg, bg, W1, W2, u, dy, coef_aux, coef_z,
+                   coef_dev, dx, dWg, dbg, dW1, dW2, meta, workspace, stream)
+
+
+def alloc_grads(cfg, x, Wg, W1, W2):
+    """Gradient buffers (torch.empty) of moe_backward: dict(dx, dWg, dbg, dW1, dW2)."""
+    import torch
+    f32 = dict(dtype=torch.float32, device=x.device)
+    return dict(dx=torch.empty_like(x), dWg=torch.empty(tuple(Wg.shape), **f32),
+                dbg=torch.empty((cfg["n_experts"],), **f32),
+                dW1=torch.empty(tuple(W1.shape), **f32), dW2=torch.empty(tuple(W2.shape), **f32))
+
+
+def alloc_backward_workspace(cfg, device="cuda"):
+    import torch
+    return torch.empty(max(1, moe_backward_workspace_size(cfg)), dtype=torch.uint8,
+                       device=device)
 
 
 def backward(cfg, x, Wg, W1, W2, dy, bg=None, u=None, coef_aux=0.0, coef_z=0.0, coef_dev=0.0,
              workspace=None, meta=None, stream=None):
     """Allocate the gradients (torch.empty) and run moe_backward.
     Returns dict(dx, dWg, dbg, dW1, dW2) and the meta."""
+    meta = alloc_meta(cfg, x.device) if meta is None else meta
+    out = alloc_grads(cfg, x, Wg, W1, W2)
+    if workspace is None:
+        workspace = alloc_backward_workspace(cfg, x.device)
+    moe_backward(cfg, x, Wg, bg, W1, W2, u, dy, coef_aux, coef_z, coef_dev, out["dx"],
+                 out["dWg"], out["dbg"], out["dW1"], out["dW2"], meta, workspace, stream)
+    return out, meta
+
+
+def moe_forward_train(cfg, x, Wg, bg, W1, W2, u, y, aux_loss, meta, workspace, stream=None):
+    """C ABI moe_forward_train: moe_forward into a moe_backward workspace that keeps the
+    expert activations for moe_backward_saved."""
+    c = make_cfg(cfg)
+    m = meta.as_struct()
+    rc = load_library().moe_forward_train(
+        ctypes.byref(c), _ptr(x), _ptr(Wg), _ptr(bg), _ptr(W1), _ptr(W2), _ptr(u), _ptr(y),
+        _ptr(aux_loss), ctypes.byref(m), _ptr(workspace), workspace.numel(), _stream(stream))
+    if rc:
+        raise MoeError(rc, "moe_forward_train")
+
+
+def forward_train(cfg, x, Wg, W1, W2, bg=None, u=None, workspace=None, meta=None, y=None,
+                  stream=None):
+    """Allocate outputs and a backward workspace, run moe_forward_train.
+    Returns (y, aux_loss, meta, workspace); pass meta and workspace to backward_saved."""
     import torch
     dev = x.device
     meta = alloc_meta(cfg, dev) if meta is None else meta
-    f32 = dict(dtype=torch.float32, device=dev)
-    out = dict(dx=torch.empty_like(x), dWg=torch.empty(tuple(Wg.shape), **f32),
-               dbg=torch.empty((cfg["n_experts"],), **f32),
-               dW1=torch.empty(tuple(W1.shape), **f32), dW2=torch.empty(tuple(W2.shape), **f32))
-    if workspace is None:
-        workspace = torch.empty(max(1, moe_backward_workspace_size(cfg)), dtype=torch.uint8,
-                                device=dev)
-    moe_backward(cfg, x, Wg, bg, W1, W2, u, dy, coef_aux, coef_z, coef_dev, out["dx"],
-                 out["dWg"], out["dbg"], out["dW1"], out["dW2"], meta, workspace, stream)
+    y = torch.empty_like(x) if y is None else y
+    aux = torch.empty((4,), dtype=torch.float32, device=dev)
+    workspace = alloc_backward_workspace(cfg, dev) if workspace is None else workspace
+    moe_forward_train(cfg, x, Wg, bg, W1, W2, u, y, aux, meta, workspace, stream)
+    return y, aux[:1], meta, workspace
+
+
+def backward_saved(cfg, x, Wg, W1, W2, dy, workspace, meta, bg=None, u=None, coef_aux=0.0,
+                   coef_z=0.0, coef_dev=0.0, stream=None):
+    """Allocate the gradients and run moe_backward_saved on forward_train's workspace.
+    Returns dict(dx, dWg, dbg, dW1, dW2) and the meta."""
+    out = alloc_grads(cfg, x, Wg, W1, W2)
+    moe_backward_saved(cfg, x, Wg, bg, W1, W2, u, dy, coef_aux, coef_z, coef_dev, out["dx"],
+                       out["dWg"], out["dbg"], out["dW1"], out["dW2"], meta, workspace, stream)
     return out, meta
 
 

@@ -237,11 +237,19 @@ int empty_call(const moe_cfg* c, const moe_meta* m, float* aux, hipStream_t s, v
   return rc;
 }
 
-// check_only: run every host check and return without enqueueing anything.
+// Where the training forward keeps GEMM 1's pre-activations (GELU and SwiGLU layers): z1
+// [rows, H1] in compact row order and z1sh [N, Es H1].
+struct TrainOut {
+  void* z1;
+  void* z1sh;
+};
+
+// check_only: run every host check and return without enqueueing anything.  train: also
+// store GEMM 1's pre-activations there (ReLU layers keep h only).
 int forward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* bg,
                  const void* W1, const void* W2, const float* u, void* y, float* aux,
                  const moe_meta* m, void* workspace, size_t wbytes, void* stream,
-                 void* const* ev, bool check_only = false) {
+                 void* const* ev, bool check_only = false, const TrainOut* train = nullptr) {
   Run r;
   r.c = c;
   int rc = make_layout(c, &r.L);
@@ -296,6 +304,12 @@ int forward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* b
                              static_cast<int>((c->n_tokens + BM - 1) / BM), c->n_tokens,
                              static_cast<int>(H)};
     g1.nprob = 2;
+  }
+  if (train && c->act != MOE_ACT_RELU) {
+    g1.p0.zout = train->z1;
+    g1.p0.ldz = H1;
+    g1.p1.zout = train->z1sh;
+    g1.p1.ldz = Es * H1;
   }
   rc = status_of(moe::launch_expert_gemm(g1, r.s));
   if (rc) return rc;
@@ -440,11 +454,13 @@ moe::GemmProblem batched_problem(const void* A, int64_t lda, const void* Bm, int
   return p;
 }
 
+// saved: h (and for GELU / SwiGLU z1) are the training forward's, already in the workspace,
+// and GEMM 1 is not recomputed.  The routing is recomputed either way.
 int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* bg,
                   const void* W1, const void* W2, const float* u, const void* dy,
                   float coef_aux, float coef_z, float coef_dev, void* dx, float* dWg,
                   float* dbg, float* dW1, float* dW2, const moe_meta* m, void* workspace,
-                  size_t wbytes, void* stream) {
+                  size_t wbytes, void* stream, bool saved = false) {
   BwdLayout B;
   int rc = make_bwd_layout(c, &B);
   if (rc) return rc;
@@ -524,7 +540,9 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
   //    ReLU needs no z1: ReLU'(z1) is 1 exactly where h > 0, so GEMM 1 writes h as in the
   //    forward.
   const bool relu = c->act == MOE_ACT_RELU;
-  if (relu) {
+  if (saved) {
+    // kept by the training forward
+  } else if (relu) {
     auto p0 = routed_problem(ws + L.buf, M, W1, M, H1 * M, ws + L.h, H, static_cast<int>(H),
                              static_cast<int>(M), a_rows, L, tiles, ntiles);
     auto p1 = dense_problem(x, M, W1c + E * H1 * M * esz, M, ws + L.hsh, Es * H,
@@ -730,6 +748,30 @@ int moe_backward_workspace_size(const moe_cfg* cfg, size_t* bytes) {
   if (rc) return rc;
   *bytes = B.total;
   return MOE_OK;
+}
+
+int moe_forward_train(const moe_cfg* cfg, const void* x, const void* Wg, const float* bg,
+                      const void* W1, const void* W2, const float* u, void* y, float* aux_loss,
+                      const moe_meta* meta, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  BwdLayout B;
+  const int rc = make_bwd_layout(cfg, &B);
+  if (rc) return rc;
+  if (!workspace || !aligned16(workspace)) return MOE_EINVAL;
+  if (workspace_bytes < B.total) return MOE_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  const TrainOut t{ws + B.z1, ws + B.z1sh};
+  return forward_impl(cfg, x, Wg, bg, W1, W2, u, y, aux_loss, meta, workspace, workspace_bytes,
+                      stream, nullptr, false, &t);
+}
+
+int moe_backward_saved(const moe_cfg* cfg, const void* x, const void* Wg, const float* bg,
+                       const void* W1, const void* W2, const float* u, const void* dy,
+                       float coef_aux, float coef_z, float coef_dev, void* dx, float* dWg,
+                       float* dbg, float* dW1, float* dW2, const moe_meta* meta,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return backward_impl(cfg, x, Wg, bg, W1, W2, u, dy, coef_aux, coef_z, coef_dev, dx, dWg, dbg,
+                       dW1, dW2, meta, workspace, workspace_bytes, stream, true);
 }
 
 int moe_backward(const moe_cfg* cfg, const void* x, const void* Wg, const float* bg,

@@ -88,6 +88,9 @@ struct Job {
   int64_t ldhb;
   float* dwp;      // dot partials of the tile's first row and n-tile (row pitch dwp_ld)
   int dwp_ld;
+  char* Zo;        // pre-activation output at the tile's first row and column (or its gate
+                   // column), or nullptr; the up half of a gated tile is zup bytes later
+  int64_t ldzb;    // bytes
 };
 
 // Load through the constant address space: for tables no kernel of this file writes (tile
@@ -168,6 +171,10 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& g, Job& j, int bid) 
                 : nullptr;
   j.dwp = P.dwp ? P.dwp + static_cast<int64_t>(row0) * P.dwp_ld + nt : nullptr;
   j.dwp_ld = P.dwp_ld;
+  j.ldzb = P.ldz * osz;
+  j.Zo = P.zout ? static_cast<char*>(P.zout) + static_cast<int64_t>(row0) * j.ldzb +
+                      (P.act == kActSwiglu ? brow : c0) * osz
+                : nullptr;
   j.zup = static_cast<int64_t>(P.glu_h) * osz;
   j.K = K;
   j.nrows = nrows;
@@ -527,7 +534,9 @@ __device__ __forceinline__ u32x4 dact_vals(u32x4 d, u32x4 z, u32x4 u, float scal
 // The staging area holds STG bytes; a tile that does not fit goes through it in passes of
 // whole wave-row blocks.  The caller has made the area free (a barrier after its last read);
 // on return every wave's last reads of it are issued but not waited for.
-template <class T, int ACT, int STG, bool F32 = false, int DACT = -1>
+// RAW = 1 stores the accumulators without the activation (gated tiles: the gate halves),
+// RAW = 2 the up halves of a gated tile.
+template <class T, int ACT, int STG, bool F32 = false, int DACT = -1, int RAW = 0>
 __device__ __forceinline__ void store_tile(const Job& j, f32x16 (&acc)[T::TN][T::TM],
                                            unsigned char* stg, int t, int lane, int wm,
                                            int wn) {
@@ -539,7 +548,11 @@ __device__ __forceinline__ void store_tile(const Job& j, f32x16 (&acc)[T::TN][T:
   constexpr int RP = STG / RB < T::BM ? STG / RB : T::BM;  // rows per pass
   static_assert((NCH & (NCH - 1)) == 0, "power-of-two column count");
   static_assert(RP % T::WTM == 0 && T::BM % RP == 0, "passes of whole wave-row blocks");
+  static_assert(RAW == 0 || (!F32 && DACT < 0), "raw pre-activations: bf16 output only");
+  static_assert(RAW < 2 || GLU, "up halves exist in gated tiles only");
   auto out = [&](int jo, int im, int x) {
+    if (RAW == 1) return GLU ? acc[2 * jo][im][x] : acc[jo][im][x];
+    if (RAW == 2) return acc[2 * jo + 1][im][x];
     if (GLU) return swish(acc[2 * jo][im][x]) * acc[2 * jo + 1][im][x];
     return act_fn<ACT>(acc[jo][im][x]);
   };
@@ -698,7 +711,9 @@ __device__ __forceinline__ void k_chunk(Feed<T>& fd, unsigned char* smem, int kt
 
 // One tile per block.
 // KM: bit 0 = A is K-major, bit 1 = B is K-major.  DACT: fused activation gradient (-1: none).
-template <int BM, int BN, int WN, int ACT, int BK, int NST, bool OUTF32, int KM, int DACT>
+// ZOUT: also store the pre-activations (training forward of GEMM 1).
+template <int BM, int BN, int WN, int ACT, int BK, int NST, bool OUTF32, int KM, int DACT,
+          bool ZOUT = false>
 __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
   using T = TileShape<BM, BN, WN, BK, NST>;
   constexpr bool AKM = KM & 1, BKM = (KM >> 1) & 1;
@@ -789,6 +804,21 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
   lds_barrier();
   // fp32 output (the weight-gradient GEMMs): rows of 1 KB, staged in passes of 128 rows
   store_tile<T, ACT, SMEM, OUTF32, DACT>(j, acc, smem, t, lane, wm, wn);
+  if constexpr (ZOUT) {
+    static_assert(!OUTF32 && DACT < 0 && ACT != kActNone, "pre-activations of GEMM 1");
+    // the same staging, once more for the pre-activations (twice for gated tiles: gate
+    // halves, then up halves)
+    Job jz = j;
+    jz.C = j.Zo;
+    jz.ldc = j.ldzb;
+    lds_barrier();
+    store_tile<T, ACT, SMEM, false, -1, 1>(jz, acc, smem, t, lane, wm, wn);
+    if constexpr (GLU) {
+      jz.C = j.Zo + j.zup;
+      lds_barrier();
+      store_tile<T, ACT, SMEM, false, -1, 2>(jz, acc, smem, t, lane, wm, wn);
+    }
+  }
 }
 
 // Thread (ty, tx) accumulates rows 4 ty + i and LDS B columns 4 tx + jj.  Gated problems:
@@ -860,6 +890,11 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs g) {
       o[0] = swish(acc[i][0]) * acc[i][2];
       o[1] = swish(acc[i][1]) * acc[i][3];
       *reinterpret_cast<f32x2*>(j.C + static_cast<int64_t>(r) * j.ldc + tx * 8) = o;
+      if (j.Zo) {   // pre-activations: gate columns, and the up columns zup bytes later
+        char* zr = j.Zo + static_cast<int64_t>(r) * j.ldzb + tx * 8;
+        *reinterpret_cast<f32x2*>(zr) = f32x2{acc[i][0], acc[i][1]};
+        *reinterpret_cast<f32x2*>(zr + j.zup) = f32x2{acc[i][2], acc[i][3]};
+      }
     } else if (DACT >= 0) {   // fused activation gradient: z has C's layout
       const int64_t o = static_cast<int64_t>(r) * j.ldc + tx * 16;
       if (j.dwp) {   // <product row, h row> over this n-tile: the 16 lanes of row r
@@ -897,6 +932,9 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs g) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) o[jj] = apply_act(acc[i][jj], j.act);
       *reinterpret_cast<f32x4*>(j.C + static_cast<int64_t>(r) * j.ldc + tx * 16) = o;
+      if (j.Zo)
+        *reinterpret_cast<f32x4*>(j.Zo + static_cast<int64_t>(r) * j.ldzb + tx * 16) =
+            f32x4{acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
     }
   }
 }
@@ -930,6 +968,12 @@ hipError_t launch_expert_gemm(const GemmArgs& a, hipStream_t s) {
       ((km & 1) && a.p0.a_gather) || (dact && (km != 2 || !a.p0.z)) || dact < 0 || dact > 3 ||
       (a.p0.dwp && (!dact || !a.p0.hdot || !a.p0.tiles)))
     return hipErrorInvalidValue;
+  // pre-activation output: GEMM 1 (row-major operands, bf16 or fp32 output of the input
+  // dtype) with a GELU or SwiGLU activation, on both problems of the launch or neither
+  const bool zout = a.p0.zout != nullptr;
+  if ((a.nprob > 1 && (a.p1.zout != nullptr) != zout) ||
+      (zout && (km != 0 || a.p0.out_f32 || dact || (act != kActGelu && act != kActSwiglu))))
+    return hipErrorInvalidValue;
   const int grid = grid_of(a, gemm_block_n(a.dtype, act));
   if (grid == 0) return hipSuccess;
   const dim3 blk(128 * kGemmWN);
@@ -938,7 +982,14 @@ hipError_t launch_expert_gemm(const GemmArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, kGemmWN, ACTV, kGemmBK, kGemmStages, OUTF, \
                                        KMV, DACTV>),                                      \
                      dim3(grid), blk, 0, s, a)
-    if (a.p0.out_f32) {
+#define MOE_GEMM_LAUNCH_Z(ACTV)                                                            \
+  hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, kGemmWN, ACTV, kGemmBK, kGemmStages, false, \
+                                       0, -1, true>),                                     \
+                     dim3(grid), blk, 0, s, a)
+    if (zout) {
+      if (act == kActGelu) MOE_GEMM_LAUNCH_Z(kActGelu);
+      else MOE_GEMM_LAUNCH_Z(kActSwiglu);
+    } else if (a.p0.out_f32) {
       if (km == 3) MOE_GEMM_LAUNCH(kActNone, true, 3, -1);
       else MOE_GEMM_LAUNCH(kActNone, true, 0, -1);
     } else if (km == 2) {
@@ -956,6 +1007,7 @@ hipError_t launch_expert_gemm(const GemmArgs& a, hipStream_t s) {
       MOE_GEMM_LAUNCH(kActNone, false, 0, -1);
     }
 #undef MOE_GEMM_LAUNCH
+#undef MOE_GEMM_LAUNCH_Z
   } else if (act == kActSwiglu) {
     hipLaunchKernelGGL((gemm_f32_kernel<true, 0, -1>), dim3(grid), dim3(kThreads), 0, s, a);
   } else if (km == 3) {

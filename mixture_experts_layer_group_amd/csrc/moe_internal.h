@@ -127,6 +127,13 @@ struct GemmProblem {
   int64_t ldh;
   float* dwp;
   int dwp_ld;
+  // Pre-activation output (training forward of GEMM 1 with a GELU or SwiGLU activation;
+  // nullptr: none): the tile's accumulators before the activation, rounded to C's dtype, at
+  // zout with pitch ldz and C's column offsets; gated problems write each output's gate
+  // pre-activation at its gate row's column of the stacked [G; U] weight and its up
+  // pre-activation glu_h columns later.
+  void* zout;
+  int64_t ldz;
 };
 
 struct GemmArgs {

@@ -28,7 +28,8 @@ def test_exports_every_declared_symbol(lib):
     declared = binding.header_functions()
     assert {"moe_forward", "moe_route", "moe_workspace_size", "moe_strerror",
             "moe_abi_version", "moe_forward_timed", "moe_backward",
-            "moe_backward_workspace_size"} <= set(declared)
+            "moe_backward_workspace_size", "moe_forward_noalloc", "moe_forward_train",
+            "moe_backward_saved"} <= set(declared)
     out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (moe_\w+)", out))
@@ -123,14 +124,16 @@ def _fake_meta(base=0x10000000, bad=None):
     return binding.Meta(**kw)
 
 
-def _call(cfg, **over):
+def _call(cfg, fn="moe_forward", **over):
+    wsz = (binding.moe_backward_workspace_size if fn == "moe_forward_train"
+           else binding.moe_workspace_size)(cfg)
     a = dict(x=FakeTensor(0x20000000), Wg=FakeTensor(0x21000000), bg=None,
               W1=FakeTensor(0x22000000), W2=FakeTensor(0x23000000), u=FakeTensor(0x24000000),
               y=FakeTensor(0x25000000), aux=FakeTensor(0x26000000), meta=_fake_meta(),
-              ws=FakeTensor(0x27000000, binding.moe_workspace_size(cfg)))
+              ws=FakeTensor(0x27000000, wsz))
     a.update(over)
-    binding.moe_forward(cfg, a["x"], a["Wg"], a["bg"], a["W1"], a["W2"], a["u"], a["y"],
-                        a["aux"], a["meta"], a["ws"], stream=_NoStream())
+    getattr(binding, fn)(cfg, a["x"], a["Wg"], a["bg"], a["W1"], a["W2"], a["u"], a["y"],
+                         a["aux"], a["meta"], a["ws"], stream=_NoStream())
 
 
 class _NoStream:
@@ -155,13 +158,24 @@ INVALID_CALLS = [
 ]
 
 
+@pytest.mark.parametrize("fn", ["moe_forward", "moe_forward_train"])
 @pytest.mark.parametrize("what,over,code", INVALID_CALLS, ids=[w for w, _, _ in INVALID_CALLS])
-def test_invalid_forward_rejected_on_host(lib, what, over, code):
+def test_invalid_forward_rejected_on_host(lib, what, over, code, fn):
     """Each call fails its host checks, so nothing is enqueued (no GPU is touched)."""
     cfg = configs.SMALL["small_top2_rr"]
     with pytest.raises(binding.MoeError) as ei:
-        _call(cfg, **over)
+        _call(cfg, fn, **over)
     assert ei.value.code == code, what
+
+
+def test_train_forward_needs_the_backward_workspace(lib):
+    """moe_forward_train keeps activations in the backward's workspace: a forward-sized one
+    is refused, for every workload (the backward workspace is strictly larger)."""
+    for cfg in list(configs.SMALL.values()) + list(configs.WORKLOADS.values()):
+        ws = FakeTensor(0x27000000, binding.moe_workspace_size(cfg))
+        with pytest.raises(binding.MoeError) as ei:
+            _call(cfg, "moe_forward_train", ws=ws)
+        assert ei.value.code == binding.MOE_EWORKSPACE, cfg["name"]
 
 
 def test_invalid_route_rejected_on_host(lib):
@@ -184,7 +198,7 @@ def test_null_cfg_rejected(lib):
     assert lib.moe_forward(None, *([None] * 9), None, 0, None) == binding.MOE_EINVAL
 
 
-def _bwd_call(cfg, **over):
+def _bwd_call(cfg, fn="moe_backward", **over):
     a = dict(x=FakeTensor(0x20000000), Wg=FakeTensor(0x21000000), bg=None,
              W1=FakeTensor(0x22000000), W2=FakeTensor(0x23000000), u=FakeTensor(0x24000000),
              dy=FakeTensor(0x25000000), coefs=(0.1, 0.01, 0.0), dx=FakeTensor(0x29000000),
@@ -192,7 +206,7 @@ def _bwd_call(cfg, **over):
              dW2=FakeTensor(0x2c000000), meta=_fake_meta(),
              ws=FakeTensor(0x27000000, binding.moe_backward_workspace_size(cfg)))
     a.update(over)
-    binding.moe_backward(cfg, a["x"], a["Wg"], a["bg"], a["W1"], a["W2"], a["u"], a["dy"],
+    getattr(binding, fn)(cfg, a["x"], a["Wg"], a["bg"], a["W1"], a["W2"], a["u"], a["dy"],
                          *a["coefs"], a["dx"], a["dWg"], a["dbg"], a["dW1"], a["dW2"], a["meta"],
                          a["ws"], stream=_NoStream())
 
@@ -211,11 +225,12 @@ INVALID_BWD = [
 ]
 
 
+@pytest.mark.parametrize("fn", ["moe_backward", "moe_backward_saved"])
 @pytest.mark.parametrize("what,over,code", INVALID_BWD, ids=[w for w, _, _ in INVALID_BWD])
-def test_invalid_backward_rejected_on_host(lib, what, over, code):
+def test_invalid_backward_rejected_on_host(lib, what, over, code, fn):
     cfg = configs.SMALL["small_top2_rr"]
     with pytest.raises(binding.MoeError) as ei:
-        _bwd_call(cfg, **over)
+        _bwd_call(cfg, fn, **over)
     assert ei.value.code == code, what
 
 

@@ -28,7 +28,9 @@ def harness():
     return gpu_harness
 
 
-def run_backward(cfg, coefs=COEFS, inp=None, seed=None):
+def run_backward(cfg, coefs=COEFS, inp=None, seed=None, saved=False):
+    """moe_backward, or with saved: moe_forward_train then moe_backward_saved (whose train
+    forward must write y, aux and the routing exactly as moe_forward does)."""
     h = harness()
     inp = synth.make_inputs(cfg, seed) if inp is None else inp
     dev = h.to_device(inp, cfg)
@@ -37,22 +39,36 @@ def run_backward(cfg, coefs=COEFS, inp=None, seed=None):
         dy = torch.from_numpy(dybits.view(np.int16)).cuda().view(torch.bfloat16)
     else:
         dy = torch.from_numpy(dy32).cuda()
-    out, meta = binding.backward(cfg, dev["x"], dev["Wg"], dev["W1"], dev["W2"], dy,
-                                 bg=dev["bg"], u=dev["u"], **coefs)
+    args = (cfg, dev["x"], dev["Wg"], dev["W1"], dev["W2"])
+    if saved:
+        y, aux, meta_f = binding.forward(*args, bg=dev["bg"], u=dev["u"])
+        yt, auxt, meta_t, ws = binding.forward_train(*args, bg=dev["bg"], u=dev["u"])
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16) if y.dtype == torch.bfloat16 else y,
+                           yt.view(torch.int16) if yt.dtype == torch.bfloat16 else yt)
+        assert torch.equal(aux, auxt)
+        mf, mt = meta_f.to_numpy(), meta_t.to_numpy()
+        for f in mf:   # z_loss / dev_loss: one value in a 4-element buffer
+            n = 1 if f in ("z_loss", "dev_loss") else None
+            assert np.array_equal(mf[f][:n], mt[f][:n]), f
+        out, meta = binding.backward_saved(*args, dy, ws, meta_t, bg=dev["bg"], u=dev["u"],
+                                           **coefs)
+    else:
+        out, meta = binding.backward(*args, dy, bg=dev["bg"], u=dev["u"], **coefs)
     torch.cuda.synchronize()
     g = {k: v.float().cpu().numpy() for k, v in out.items()}
     g["meta"] = meta.to_numpy()
     return g, inp, dy32
 
 
-def check(cfg, coefs=COEFS, seed=None):
+def check(cfg, coefs=COEFS, seed=None, saved=False):
     from oracle import moe_backward as mb
     from oracle import moe_oracle as mo
     h = harness()
     name = cfg.get("name", "custom")
     h.say(f"[gpu-bwd] {name}: N={cfg['n_tokens']} E={cfg['n_experts']}+{cfg['n_shared']} "
-          f"k={cfg['top_k']} act={cfg['act']} dtype={cfg['dtype']}")
-    g, inp, dy = run_backward(cfg, coefs, seed=seed)
+          f"k={cfg['top_k']} act={cfg['act']} dtype={cfg['dtype']} saved={saved}")
+    g, inp, dy = run_backward(cfg, coefs, seed=seed, saved=saved)
     logits = g["meta"]["logits"]
     assert h.rel_err(logits, mo.router_logits(inp.x, inp.Wg, inp.bg)) <= h.LOGIT_TOL
     ref = mb.layer_backward(cfg, inp.x, inp.Wg, inp.bg, inp.W1, inp.W2, inp.u, dy,
@@ -161,3 +177,79 @@ def test_workload_backward(name):
     """Full-size layers, every gradient element compared (the oracle runs the whole layer in
     fp64 on the host: about 1 TFLOP for these two)."""
     check(configs.WORKLOADS[name])
+
+
+# ---- moe_forward_train + moe_backward_saved: the backward on the forward's activations
+
+SAVED_KEYS_EQUAL = {0: ("dx", "dWg", "dbg", "dW1", "dW2")}   # ReLU: h is GEMM 1's either way
+
+
+@pytest.mark.parametrize("name", sorted(configs.SMALL) + sorted(EDGE))
+def test_saved_backward(name):
+    """Oracle parity as moe_backward's, and against moe_backward on the same inputs: every
+    gradient bit for bit on ReLU layers, dW1 bit for bit on the others (their dW2 and the
+    combine weights' gradient use the forward's h instead of act(rounded z))."""
+    cfg = dict(configs.SMALL[name] if name in configs.SMALL else EDGE[name], name=name)
+    g, _ = check(cfg, saved=True)
+    g0, _, _ = run_backward(cfg)
+    for key in SAVED_KEYS_EQUAL.get(cfg["act"], ("dW1",)):
+        assert np.array_equal(g[key], g0[key]), key
+    for f in ("topk_idx", "pos", "row", "count", "offset", "stats"):
+        assert np.array_equal(g["meta"][f], g0["meta"][f]), f
+
+
+def test_saved_backward_repeated_and_deterministic():
+    """Two train-forward / saved-backward pairs on one workspace give the same bits."""
+    h = harness()
+    cfg = configs.SMALL["small_swiglu_shared"]
+    inp = synth.make_inputs(cfg)
+    dev = h.to_device(inp, cfg)
+    dy32, dybits = synth.upstream_grad(cfg)
+    dy = torch.from_numpy(dybits.view(np.int16)).cuda().view(torch.bfloat16)
+    args = (cfg, dev["x"], dev["Wg"], dev["W1"], dev["W2"])
+    ws = None
+    outs = []
+    for _ in range(2):
+        _, _, meta, ws = binding.forward_train(*args, bg=dev["bg"], u=dev["u"], workspace=ws)
+        out, _ = binding.backward_saved(*args, dy, ws, meta, bg=dev["bg"], u=dev["u"], **COEFS)
+        torch.cuda.synchronize()
+        outs.append({k: v.float().cpu().numpy() for k, v in out.items()})
+    for key in outs[0]:
+        assert np.array_equal(outs[0][key], outs[1][key]), key
+
+
+def test_saved_backward_empty_batch():
+    cfg = _cfg(n_tokens=0)
+    meta = binding.alloc_meta(cfg)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    dW1 = torch.full((4, 128, 128), 3.0, **f32)
+    dW2 = torch.full((4, 128, 128), 3.0, **f32)
+    dWg = torch.full((4, 128), 3.0, **f32)
+    ws = binding.alloc_backward_workspace(cfg)
+    empty = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
+    aux = torch.empty((4,), **f32)
+    binding.moe_forward_train(cfg, empty, None, None, None, None, None, empty, aux, meta, ws)
+    binding.moe_backward_saved(cfg, empty, None, None, None, None, None, empty, 0.1, 0.1, 0.1,
+                               empty, dWg, None, dW1, dW2, meta, ws)
+    torch.cuda.synchronize()
+    for t in (dWg, dW1, dW2):
+        assert float(t.abs().max()) == 0.0
+
+
+@pytest.mark.parametrize("name", ["gshard_bf16", "switch_bf16"])
+def test_workload_saved_backward(name):
+    """Full-size layers against moe_backward (whose every element test_workload_backward
+    compares with the oracle): ReLU bit for bit; GELU dW1 bit for bit and the rest within
+    the backward's tolerance of it."""
+    h = harness()
+    cfg = configs.WORKLOADS[name]
+    h.say(f"[gpu-bwd] {name}: saved vs recompute at full size")
+    inp = synth.make_inputs(cfg)
+    g, _, _ = run_backward(cfg, inp=inp, saved=True)
+    g0, _, _ = run_backward(cfg, inp=inp)
+    equal = SAVED_KEYS_EQUAL.get(cfg["act"], ("dW1",))
+    for key in ("dx", "dWg", "dbg", "dW1", "dW2"):
+        if key in equal:
+            assert np.array_equal(g[key], g0[key]), key
+        else:
+            assert h.rel_err(g[key], g0[key]) <= G_TOL[cfg["dtype"]], key
