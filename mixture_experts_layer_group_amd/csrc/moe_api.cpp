@@ -13,6 +13,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "moe.h"
 #include "moe_internal.h"
@@ -341,6 +342,62 @@ int forward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* b
 
 // ---------------------------------------------------------------------------- backward
 
+// The backward's second stream.  The weight gradients of the two expert GEMMs depend only on
+// activations the chain has already produced (dW2 on h and dout, dW1 on dz and the dispatched
+// rows), not on the dgrad kernels after them, so they run on this stream beside those
+// kernels: their fp32 tile stores, which leave the MFMA pipes idle, overlap compute-bound
+// work.  One non-blocking, default-priority stream and three timing-free events per device,
+// created on first use and kept until the process ends.  A backward call holds the mutex
+// while it enqueues, so calls from several host threads do not interleave their records.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t ev[3] = {};
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mu;
+SideStream g_side[kMaxDevices];
+
+// The current device's side stream (created if needed); the caller holds g_side_mu.
+int side_stream(SideStream** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_EHIP;
+  SideStream& ss = g_side[dev];
+  if (!ss.s) {
+    SideStream n;
+    if (hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking) != hipSuccess) return MOE_EHIP;
+    for (hipEvent_t& e : n.ev)
+      if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return MOE_EHIP;
+    ss = n;
+  }
+  *out = &ss;
+  return MOE_OK;
+}
+
+// Fork / join of the side stream: fork(i) makes the side stream wait for what the main stream
+// has enqueued so far; the join (at the latest when this object goes out of scope, error
+// paths included) makes the main stream wait for everything enqueued on the side stream.
+struct SideFork {
+  SideStream* ss = nullptr;
+  hipStream_t main = nullptr;
+  bool open = false;
+  int fork(int i) {
+    if (hipEventRecord(ss->ev[i], main) != hipSuccess ||
+        hipStreamWaitEvent(ss->s, ss->ev[i], 0) != hipSuccess)
+      return MOE_EHIP;
+    open = true;
+    return MOE_OK;
+  }
+  int join() {
+    if (!open) return MOE_OK;
+    open = false;
+    if (hipEventRecord(ss->ev[2], ss->s) != hipSuccess ||
+        hipStreamWaitEvent(main, ss->ev[2], 0) != hipSuccess)
+      return MOE_EHIP;
+    return MOE_OK;
+  }
+  ~SideFork() { join(); }
+};
+
 // Workspace of moe_backward: the forward layout (routing buffers, dispatch rows, h, shared h,
 // and the shared-output buffer reused for the shared experts' dx), then the backward's own
 // regions.  Every GEMM reads its operands in place (weights and activations as K-major
@@ -495,6 +552,13 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
   for (const void* p : req)
     if (!p || !aligned16(p)) return MOE_EINVAL;
 
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  SideFork side;   // joined before the lock is released
+  rc = side_stream(&side.ss);
+  if (rc) return rc;
+  side.main = s;
+  const hipStream_t s2 = side.ss->s;
+
   Run r;
   r.c = c;
   r.L = B.F;
@@ -514,12 +578,16 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
   const int a_rows = static_cast<int>(L.rows_alloc);
   const char* W1c = static_cast<const char*>(W1);
   const char* W2c = static_cast<const char*>(W2);
-  auto gemm = [&](const moe::GemmProblem& p0, const moe::GemmProblem* p1) {
+  auto gemm = [&](const moe::GemmProblem& p0, const moe::GemmProblem* p1,
+                  hipStream_t st = nullptr) {
     moe::GemmArgs g{};
     g.dtype = dt; g.p0 = p0; g.nprob = 1;
     if (p1) { g.p1 = *p1; g.nprob = 2; }
-    return status_of(moe::launch_expert_gemm(g, s));
+    return status_of(moe::launch_expert_gemm(g, st ? st : s));
   };
+  const int nsh = static_cast<int>(Es * B.nshared);
+  float* shp2 = reinterpret_cast<float*>(ws + B.shp2);
+  float* shp1 = reinterpret_cast<float*>(ws + B.shp1);
   // batched GEMM entries of the steps below, from the expert offsets
   moe::BwdSetupArgs sa{};
   sa.offset = m->offset;
@@ -571,6 +639,24 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
       if (rc) return rc;
     }
   }
+  // 6a. (side stream, beside steps 3-5) dW2_e [M, H] = dout_e^T h_e; shared q: dy^T hsh_q over
+  //     token ranges into fp32 partials, summed in range order.  Weight gradients are fp32
+  //     batched GEMMs over the experts with K = the expert's kept rows (shared experts: all
+  //     tokens), every operand read in place as a K-major operand.
+  {
+    if ((rc = side.fork(0))) return rc;
+    auto q0 = batched_problem(ws + B.dout, M, ws + L.h, H, dW2, H, static_cast<int>(H),
+                              static_cast<int>(M), static_cast<int>(E), BM, sa.dw2, true);
+    auto q1 = batched_problem(dy, M, ws + L.hsh, Es * H, shp2, H, static_cast<int>(H),
+                              static_cast<int>(M), nsh, BM, sa.dw2 + E, true);
+    q0.a_kmajor = q0.b_kmajor = q1.a_kmajor = q1.b_kmajor = 1;
+    if ((rc = gemm(q0, Es ? &q1 : nullptr, s2))) return rc;
+    for (int64_t q = 0; q < Es; ++q)
+      if ((rc = status_of(moe::launch_split_reduce(shp2 + q * B.nshared * M * H,
+                                                   dW2 + (E + q) * M * H, M * H,
+                                                   static_cast<int>(B.nshared), s2))))
+        return rc;
+  }
   // 3. dz = w (dy W2_e) act'(z1) (routed rows, dy gathered through the row -> token index,
   //    w the slot's gate weight) and (dy W2_{E+q}) act'(z1sh) (shared, output columns q H1):
   //    the GEMM applies the gate weight and the activation gradient in its epilogue and
@@ -599,6 +685,22 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
     rc = status_of(moe::launch_dw_reduce(m->row, dwp, reinterpret_cast<float*>(ws + B.dw),
                                          N * k, static_cast<int>(B.ntn), s));
     if (rc) return rc;
+  }
+  // 6b. (side stream, after 6a) dW1_e [H1, M] = dz1_e^T buf_e; shared q: dz1sh_q^T x over
+  //     token ranges into partials
+  {
+    if ((rc = side.fork(1))) return rc;
+    auto w0 = batched_problem(ws + B.dz1, H1, ws + L.buf, M, dW1, M, static_cast<int>(M),
+                              static_cast<int>(H1), static_cast<int>(E), BM, sa.dw1, true);
+    auto w1 = batched_problem(ws + B.dz1sh, Es * H1, x, M, shp1, M, static_cast<int>(M),
+                              static_cast<int>(H1), nsh, BM, sa.dw1 + E, true);
+    w0.a_kmajor = w0.b_kmajor = w1.a_kmajor = w1.b_kmajor = 1;
+    if ((rc = gemm(w0, Es ? &w1 : nullptr, s2))) return rc;
+    for (int64_t q = 0; q < Es; ++q)
+      if ((rc = status_of(moe::launch_split_reduce(shp1 + q * B.nshared * H1 * M,
+                                                   dW1 + (E + q) * H1 * M, H1 * M,
+                                                   static_cast<int>(B.nshared), s2))))
+        return rc;
   }
   // 4. dx rows = dz W1_e (routed); shared: dz_sh W1_sh over k = (q, h'), whose K-major rows
   //    are the consecutive rows of W1_{E..E+Es-1}
@@ -645,8 +747,7 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
     rc = status_of(moe::launch_dbg(wa, s));
     if (rc) return rc;
   }
-  // 6. weight gradients, fp32: batched GEMMs over the experts with K = the expert's kept rows
-  //    (shared experts: all tokens), every operand read in place as a K-major operand
+  // 6c. dWg, then the join with the side stream
   {
     // dWg [E, M] = dl^T x: token ranges into fp32 partials, then their sum in range order
     float* part = reinterpret_cast<float*>(ws + B.dwgp);
@@ -656,34 +757,8 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
     if ((rc = gemm(p, nullptr))) return rc;
     if ((rc = status_of(moe::launch_split_reduce(part, dWg, E * M, static_cast<int>(B.nsplit), s))))
       return rc;
-    // dW2_e [M, H] = dout_e^T h_e ; shared q: dy^T hsh_q over token ranges into partials
-    const int nsh = static_cast<int>(Es * B.nshared);
-    float* shp2 = reinterpret_cast<float*>(ws + B.shp2);
-    float* shp1 = reinterpret_cast<float*>(ws + B.shp1);
-    auto q0 = batched_problem(ws + B.dout, M, ws + L.h, H, dW2, H, static_cast<int>(H),
-                              static_cast<int>(M), static_cast<int>(E), BM, sa.dw2, true);
-    auto q1 = batched_problem(dy, M, ws + L.hsh, Es * H, shp2, H, static_cast<int>(H),
-                              static_cast<int>(M), nsh, BM, sa.dw2 + E, true);
-    q0.a_kmajor = q0.b_kmajor = q1.a_kmajor = q1.b_kmajor = 1;
-    if ((rc = gemm(q0, Es ? &q1 : nullptr))) return rc;
-    // dW1_e [H1, M] = dz1_e^T buf_e ; shared q: dz1sh_q^T x over token ranges into partials
-    auto w0 = batched_problem(ws + B.dz1, H1, ws + L.buf, M, dW1, M, static_cast<int>(M),
-                              static_cast<int>(H1), static_cast<int>(E), BM, sa.dw1, true);
-    auto w1 = batched_problem(ws + B.dz1sh, Es * H1, x, M, shp1, M, static_cast<int>(M),
-                              static_cast<int>(H1), nsh, BM, sa.dw1 + E, true);
-    w0.a_kmajor = w0.b_kmajor = w1.a_kmajor = w1.b_kmajor = 1;
-    if ((rc = gemm(w0, Es ? &w1 : nullptr))) return rc;
-    for (int64_t q = 0; q < Es; ++q) {   // the shared experts' partials, summed in range order
-      rc = status_of(moe::launch_split_reduce(shp2 + q * B.nshared * M * H, dW2 + (E + q) * M * H,
-                                              M * H, static_cast<int>(B.nshared), s));
-      if (!rc)
-        rc = status_of(moe::launch_split_reduce(shp1 + q * B.nshared * H1 * M,
-                                                dW1 + (E + q) * H1 * M, H1 * M,
-                                                static_cast<int>(B.nshared), s));
-      if (rc) return rc;
-    }
   }
-  return MOE_OK;
+  return side.join();
 }
 
 }  // namespace

@@ -63,14 +63,30 @@ MOE_HD inline TileSpace tile_space(int mt0, int nt0, int mt1, int nt1, int nprob
 //    ceil((T - b) / 8) slots laid out in order, T entries) and holds entry 8 (s - start of bin
 //    b) + b, so each XCD range gets every 8th entry rather than 8 neighbouring ones and an
 //    entry's tiles stay together.
+//  * Other two-problem launches (routed experts + shared experts, whose K can differ): each
+//    XCD range holds its eighth of problem 0's tiles, then its eighth of problem 1's, so
+//    every XCD gets the same share of both.  Problem 1's remainder tiles go to the XCDs
+//    after those that took problem 0's remainder (cyclically), which keeps each XCD's tile
+//    count equal to the number of blocks it receives.
 //  * Inside a problem, group_m m-tiles sweep the n-tiles together (L2 reuse of the weight
 //    tiles across an expert's row tiles and of the row tiles across n-tiles).
 // A bijection from [0, tile_total) onto the tiles of both problems.
 MOE_HD inline bool tile_coord(const TileSpace& s, int bid, int group_m, TileCoord& c) {
-  const int tot0 = s.mt0 * s.nt0, total = tile_total(s);
+  const int tot0 = s.mt0 * s.nt0, total = tile_total(s), tot1 = total - tot0;
   if (bid < 0 || bid >= total) return false;
   const int xcd = bid & 7, loc = bid >> 3, q = total >> 3, r = total & 7;
   int pid = xcd * q + (xcd < r ? xcd : r) + loc;
+  if (s.tpe == 0 && tot0 > 0 && tot1 > 0) {
+    const int q0 = tot0 >> 3, r0 = tot0 & 7, q1 = tot1 >> 3, r1 = tot1 & 7;
+    const int n0 = q0 + (xcd < r0 ? 1 : 0);   // problem 0 tiles of this XCD
+    if (loc < n0) {
+      pid = xcd * q0 + (xcd < r0 ? xcd : r0) + loc;
+    } else {
+      int before = 0;   // XCDs below this one that take one of problem 1's remainder tiles
+      for (int x = 0; x < xcd; ++x) before += ((x - r0 + 8) & 7) < r1 ? 1 : 0;
+      pid = tot0 + xcd * q1 + before + (loc - n0);
+    }
+  }
   if (s.tpe > 0) {
     const int T = total / s.tpe;
     const int sl = pid / s.tpe, rr = pid - sl * s.tpe;

@@ -5,7 +5,8 @@ header is compiled for the host with g++ (tests/tile_map_check.cpp) and checked 
 layer shapes, one- and two-problem launches, both tile shapes: the block -> tile map is a
 bijection, every tile and every batched entry stays inside its own problem, and every
 operand block stays inside its buffer.  Planted mistakes in a copy of the header must each
-make the check fail.
+make the check fail.  Two-problem launches that are not dealt by entries must also give every
+XCD an eighth of each problem's tiles.
 """
 import os
 import shutil
@@ -67,6 +68,11 @@ PLANTED = {
                      "return BatchEntry{n0 * Ep, n0 * M, q * M,"),
     # batched tile rows: the last m-tile of an entry not clipped
     "batch_rows": ("nrows = rows - row0 < BM ? rows - row0 : BM;", "nrows = BM;"),
+    # two-problem ranges: problem 1's remainder tiles given to the same XCDs as problem 0's
+    "second_remainder": ("before += ((x - r0 + 8) & 7) < r1 ? 1 : 0;", "before += x < r1 ? 1 : 0;"),
+    # two-problem ranges: the problems concatenated and cut into eight (unbalanced when their
+    # K differ)
+    "concatenated": ("if (s.tpe == 0 && tot0 > 0 && tot1 > 0) {", "if (false) {"),
 }
 
 

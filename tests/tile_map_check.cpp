@@ -174,8 +174,10 @@ bool check_launch(const Problem& p0, const Problem* p1) {
   std::vector<char> seen((size_t)total, 0);
   bool ok = true;
   moe::TileCoord c;
+  int per_xcd[8][2] = {};
   for (int bid = 0; bid < total; ++bid) {
     if (!moe::tile_coord(sp, bid, kGroupM, c)) return fail(p0.name + ": block inside the grid decoded as none");
+    if (c.prob == 0 || c.prob == 1) per_xcd[bid & 7][c.prob]++;
     const Problem& P = c.prob ? *p1 : p0;
     const int mts = c.prob ? mt1 : mt0, nts = c.prob ? nt1 : nt0;
     if (c.prob < 0 || c.prob >= nprob || c.mt < 0 || c.mt >= mts || c.nt < 0 || c.nt >= nts)
@@ -185,6 +187,15 @@ bool check_launch(const Problem& p0, const Problem* p1) {
     ok &= check_tile(P, c.mt, c.nt);
   }
   if (moe::tile_coord(sp, total, kGroupM, c)) return fail(p0.name + ": block past the grid decoded");
+  // two problems that are not dealt by entries: every XCD (blocks bid with equal bid % 8)
+  // holds an eighth of each problem's tiles, rounded down or up
+  if (p1 && sp.tpe == 0) {
+    const int tot[2] = {mt0 * nt0, mt1 * nt1};
+    for (int x = 0; x < 8; ++x)
+      for (int q = 0; q < 2; ++q)
+        if (per_xcd[x][q] != tot[q] / 8 && per_xcd[x][q] != (tot[q] + 7) / 8)
+          return fail(p0.name + ": an XCD's share of a problem's tiles is unbalanced");
+  }
   ok &= check_disjoint(p0);
   if (p1) ok &= check_disjoint(*p1);
   return ok;
