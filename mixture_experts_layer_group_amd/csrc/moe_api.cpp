@@ -404,7 +404,7 @@ struct SideFork {
 // operands where the contraction runs along their rows), so no transposed copies are kept.
 struct BwdLayout {
   Layout F;
-  size_t z1, dout, wrow, dwp, dz1, dbuf, z1sh, dz1sh, dl, dw, partb, dlp, wgt, dxrt, e2, e1, eh,
+  size_t z1, dout, wrow, dwp, dz1, dbuf, z1sh, dz1sh, dl, dw, partb, dlp, dxrt, e2, e1, eh,
       eg, dwgp, shp2, shp1, total;
   int64_t H1, nchunks, Ep, nsplit, ksplit, nshared, kshared, ntn;
 };
@@ -465,7 +465,6 @@ int make_bwd_layout(const moe_cfg* c, BwdLayout* B) {
   B->dw = take(static_cast<size_t>(N * k) * 4);
   B->partb = take(static_cast<size_t>(B->nchunks * E) * 4);
   B->dlp = take(static_cast<size_t>(N * B->Ep) * es);
-  B->wgt = take(static_cast<size_t>(M * B->Ep) * es);
   B->dxrt = take(static_cast<size_t>(N * M) * es);
   B->e2 = take(static_cast<size_t>(E + Es * B->nshared) * sizeof(moe::BatchEntry));
   B->e1 = take(static_cast<size_t>(E + Es * B->nshared) * sizeof(moe::BatchEntry));
@@ -686,6 +685,25 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
                                          N * k, static_cast<int>(B.ntn), s));
     if (rc) return rc;
   }
+  // 5a. router backward: dl from the combine weights' gradient, then dlp = dl in the layer
+  //     dtype (zero-padded to Ep), the A operand of both router GEMMs below
+  moe::RouterBwdArgs ra{};
+  ra.logits = m->logits; ra.topk_idx = m->topk_idx;
+  ra.dw = reinterpret_cast<const float*>(ws + B.dw);
+  ra.Cg = reinterpret_cast<const int32_t*>(ws + L.Cg);
+  ra.dl = reinterpret_cast<float*>(ws + B.dl);
+  ra.coef_aux = coef_aux; ra.coef_z = coef_z; ra.coef_dev = coef_dev; ra.norm_p = c->norm_p;
+  ra.N = static_cast<int>(N); ra.E = static_cast<int>(E); ra.k = static_cast<int>(k);
+  ra.G = c->n_groups; ra.S = static_cast<int>(L.S); ra.norm = c->gate_norm;
+  ra.n_eg = c->expert_groups;
+  rc = status_of(moe::launch_router_bwd(ra, s));
+  if (rc) return rc;
+  {
+    moe::RouterPrepArgs pa{ra.dl, ws + B.dlp, static_cast<int>(N), static_cast<int>(E),
+                           static_cast<int>(B.Ep), dt};
+    rc = status_of(moe::launch_router_dgrad_prep(pa, s));
+    if (rc) return rc;
+  }
   // 6b. (side stream, after 6a) dW1_e [H1, M] = dz1_e^T buf_e; shared q: dz1sh_q^T x over
   //     token ranges into partials
   {
@@ -703,40 +721,27 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
         return rc;
   }
   // 4. dx rows = dz W1_e (routed); shared: dz_sh W1_sh over k = (q, h'), whose K-major rows
-  //    are the consecutive rows of W1_{E..E+Es-1}
+  //    are the consecutive rows of W1_{E..E+Es-1}.  The router term dxrt = dl Wg reads Wg
+  //    [E, M] in place as a K-major operand (k = e, K = E; dlp's zero padding and the operand
+  //    bounds cover the chunk past E); without shared experts it is this launch's second
+  //    problem, otherwise a launch of its own.
   {
     auto p0 = routed_problem(ws + B.dz1, H1, W1, M, H1 * M, ws + B.dbuf, M,
                              static_cast<int>(M), static_cast<int>(H1), a_rows, L, tiles, ntiles);
     p0.b_kmajor = 1;
-    auto p1 = dense_problem(ws + B.dz1sh, Es * H1, W1c + E * H1 * M * esz, M, ws + L.osh, M,
-                            static_cast<int>(M), static_cast<int>(Es * H1),
-                            static_cast<int>(N), BM);
-    p1.b_kmajor = 1;
-    rc = gemm(p0, Es ? &p1 : nullptr);
+    auto psh = dense_problem(ws + B.dz1sh, Es * H1, W1c + E * H1 * M * esz, M, ws + L.osh, M,
+                             static_cast<int>(M), static_cast<int>(Es * H1),
+                             static_cast<int>(N), BM);
+    psh.b_kmajor = 1;
+    auto prt = dense_problem(ws + B.dlp, B.Ep, Wg, M, ws + B.dxrt, M, static_cast<int>(M),
+                             static_cast<int>(E), static_cast<int>(N), BM);
+    prt.b_kmajor = 1;
+    rc = gemm(p0, Es ? &psh : &prt);
     if (rc) return rc;
+    if (Es && (rc = gemm(prt, nullptr))) return rc;
   }
-  // 5. router backward and dx
+  // 5b. dx = [res] dy + the kept rows' dx + shared + router term; dbg
   {
-    moe::RouterBwdArgs ra{};
-    ra.logits = m->logits; ra.topk_idx = m->topk_idx;
-    ra.dw = reinterpret_cast<const float*>(ws + B.dw);
-    ra.Cg = reinterpret_cast<const int32_t*>(ws + L.Cg);
-    ra.dl = reinterpret_cast<float*>(ws + B.dl);
-    ra.coef_aux = coef_aux; ra.coef_z = coef_z; ra.coef_dev = coef_dev; ra.norm_p = c->norm_p;
-    ra.N = static_cast<int>(N); ra.E = static_cast<int>(E); ra.k = static_cast<int>(k);
-    ra.G = c->n_groups; ra.S = static_cast<int>(L.S); ra.norm = c->gate_norm;
-    ra.n_eg = c->expert_groups;
-    rc = status_of(moe::launch_router_bwd(ra, s));
-    if (rc) return rc;
-    // router term of dx: dxrt = dl Wg as a dense GEMM over the padded expert axis
-    moe::RouterPrepArgs pa{ra.dl, Wg, ws + B.dlp, ws + B.wgt, static_cast<int>(N),
-                           static_cast<int>(E), static_cast<int>(B.Ep), static_cast<int>(M), dt};
-    rc = status_of(moe::launch_router_dgrad_prep(pa, s));
-    if (rc) return rc;
-    rc = gemm(dense_problem(ws + B.dlp, B.Ep, ws + B.wgt, B.Ep, ws + B.dxrt, M,
-                            static_cast<int>(M), static_cast<int>(B.Ep), static_cast<int>(N), BM),
-              nullptr);
-    if (rc) return rc;
     moe::DxArgs da{dy, ws + B.dbuf, Es ? ws + L.osh : nullptr, ws + B.dxrt, m->row, dx,
                    static_cast<int>(N), static_cast<int>(M), static_cast<int>(k), c->residual,
                    dt};

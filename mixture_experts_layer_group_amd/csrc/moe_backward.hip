@@ -333,22 +333,17 @@ __global__ __launch_bounds__(256) void dx_final_kernel(DxArgs a) {
   }
 }
 
-// The router's dgrad operands for the GEMM dxrt = dlp . WgT^T: dlp [N, Ep] = dl in the layer
-// dtype, WgT [M, Ep] = Wg^T, both zero beyond E (Ep = E rounded up to 64).
+// The router's dgrad operand dlp [N, Ep] = dl in the layer dtype, zero beyond E (Ep = E
+// rounded up to 64), the A operand of dxrt = dl Wg (Wg itself is read in place as a K-major
+// operand) and of dWg = dl^T x.
 template <int DT>
 __global__ __launch_bounds__(256) void router_dgrad_prep_kernel(RouterPrepArgs a) {
-  const int64_t nd = static_cast<int64_t>(a.N) * a.Ep, nw = static_cast<int64_t>(a.M) * a.Ep;
-  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < nd + nw;
+  const int64_t nd = static_cast<int64_t>(a.N) * a.Ep;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < nd;
        i += static_cast<int64_t>(gridDim.x) * 256) {
-    if (i < nd) {
-      const int64_t r = i / a.Ep;
-      const int e = static_cast<int>(i - r * a.Ep);
-      st_elem<DT>(a.dlp, i, e < a.E ? a.dl[r * a.E + e] : 0.0f);
-    } else {
-      const int64_t j = i - nd, m = j / a.Ep;
-      const int e = static_cast<int>(j - m * a.Ep);
-      st_elem<DT>(a.wgt, j, e < a.E ? ld_elem<DT>(a.Wg, static_cast<int64_t>(e) * a.M + m) : 0.0f);
-    }
+    const int64_t r = i / a.Ep;
+    const int e = static_cast<int>(i - r * a.Ep);
+    st_elem<DT>(a.dlp, i, e < a.E ? a.dl[r * a.E + e] : 0.0f);
   }
 }
 
@@ -409,7 +404,7 @@ hipError_t launch_split_reduce(const float* part, float* out, int64_t n, int S, 
 }
 
 hipError_t launch_router_dgrad_prep(const RouterPrepArgs& a, hipStream_t s) {
-  const int64_t n = (static_cast<int64_t>(a.N) + a.M) * a.Ep;
+  const int64_t n = static_cast<int64_t>(a.N) * a.Ep;
   if (a.dtype == 1)
     hipLaunchKernelGGL(router_dgrad_prep_kernel<1>, dim3(grid_for(n)), dim3(256), 0, s, a);
   else

@@ -557,6 +557,38 @@ __device__ __forceinline__ void store_tile(const Job& j, f32x16 (&acc)[T::TN][T:
     return act_fn<ACT>(acc[jo][im][x]);
   };
   const int ncch = j.ncols / (F32 ? 4 : 8);   // valid 16-byte columns
+  // Fused activation gradient, in batches of U row chunks per thread: every global load of a
+  // batch (z, u for gated layers, h for the dot partials, the row scale) is issued before the
+  // first of them is used, so a batch waits for one memory round trip, not U; the first
+  // batch's loads are issued before the product is staged, so that round trip overlaps the
+  // staging.  The loads are unconditional (chunks past the tile read its first chunk) and
+  // masked where they are used: a load under a divergent branch, whose other side zeroes
+  // the same registers, has to be waited for before the branch merges.  A half-wave covers
+  // one staged row (NCH = 32 chunks), so the batch bounds are uniform over each half-wave
+  // and its 32 lanes reduce the row's dot partial together.
+  constexpr int U = DACT == kActSwiglu ? 4 : 8;   // gated: three loads per chunk
+  u32x4 zv[U], uv[U], hv[U];
+  float sc[U];
+  const bool hz = j.Hd == j.Z && j.ldhb == j.ldc;   // ReLU: z is h
+  auto dact_load = [&](int i0, int rows) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * T::NT;
+      const int r = i / NCH, c = i - r * NCH;
+      const bool ok = i < rows * NCH && c < ncch;
+      const int64_t o = ok ? static_cast<int64_t>(r) * j.ldc + c * 16 : 0;
+      zv[u] = *reinterpret_cast<const u32x4*>(j.Z + o);
+      if (DACT == kActSwiglu) uv[u] = *reinterpret_cast<const u32x4*>(j.Z + o + j.zup);
+      if (j.dwp && !hz)
+        hv[u] = *reinterpret_cast<const u32x4*>(
+            j.Hd + (ok ? static_cast<int64_t>(r) * j.ldhb + c * 16 : 0));
+      sc[u] = j.rs ? j.rs[i < rows * NCH ? r : 0] : 1.0f;
+    }
+  };
+  if constexpr (DACT >= 0) {
+    static_assert(RP == T::BM && NCH == 32 && !F32, "one pass; one staged row per half-wave");
+    dact_load(t, j.nrows);
+  }
 #pragma unroll
   for (int p = 0; p < T::BM / RP; ++p) {
     if (p > 0) lds_barrier();   // the previous pass has been read out
@@ -592,36 +624,13 @@ __device__ __forceinline__ void store_tile(const Job& j, f32x16 (&acc)[T::TN][T:
     const int64_t poff = static_cast<int64_t>(p * RP) * j.ldc;
     char* C = j.C + poff;
     if constexpr (DACT >= 0) {
-      // Fused activation gradient, in batches of U row chunks per thread: every load of a
-      // batch (z, u for gated layers, h for the dot partials, the row scale) is issued before
-      // the first of them is used, so a batch waits for one memory round trip, not U.  A
-      // half-wave covers one staged row (NCH = 32 chunks), so the batch bounds are uniform
-      // over each half-wave and its 32 lanes reduce the row's dot partial together.
-      static_assert(NCH == 32 && !F32, "one staged row per half-wave");
-      constexpr int U = DACT == kActSwiglu ? 4 : 8;   // gated: three loads per chunk
-      const bool hz = j.Hd == j.Z && j.ldhb == j.ldc;   // ReLU: z is h
-      const char* Zp = j.Z + poff;
-      for (int i0 = t; i0 < rows * NCH; i0 += U * T::NT) {
-        u32x4 sv[U], zv[U], uv[U], hv[U];
-        float sc[U];
+      for (int i0 = t;;) {
+        u32x4 sv[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
+        for (int u = 0; u < U; ++u) {   // staged rows past the tile read row 0
           const int i = i0 + u * T::NT;
-          sv[u] = zv[u] = uv[u] = hv[u] = u32x4{0u, 0u, 0u, 0u};
-          sc[u] = 1.0f;
-          if (i < rows * NCH) {
-            const int r = i / NCH, c = i - r * NCH;
-            sv[u] = *reinterpret_cast<const u32x4*>(stg + r * RB + ((c ^ (r & (NCH - 1))) << 4));
-            if (j.rs) sc[u] = j.rs[p * RP + r];
-            if (c < ncch) {
-              const int64_t o = static_cast<int64_t>(r) * j.ldc + c * 16;
-              zv[u] = *reinterpret_cast<const u32x4*>(Zp + o);
-              if (DACT == kActSwiglu) uv[u] = *reinterpret_cast<const u32x4*>(Zp + o + j.zup);
-              if (j.dwp && !hz)
-                hv[u] = *reinterpret_cast<const u32x4*>(
-                    j.Hd + static_cast<int64_t>(p * RP + r) * j.ldhb + c * 16);
-            }
-          }
+          const int r = i < rows * NCH ? i / NCH : 0, c = i % NCH;
+          sv[u] = *reinterpret_cast<const u32x4*>(stg + r * RB + ((c ^ (r & (NCH - 1))) << 4));
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -630,14 +639,15 @@ __device__ __forceinline__ void store_tile(const Job& j, f32x16 (&acc)[T::TN][T:
           const int r = i / NCH, c = i - r * NCH;
           if (j.dwp) {
             // <product row, h row> over this n-tile (zero past the valid columns)
+            const u32x4 hvu = c < ncch ? (hz ? zv[u] : hv[u]) : u32x4{0u, 0u, 0u, 0u};
             float gv[8], hf[8], part = 0.f;
             unpack_bf16x8(sv[u], gv);
-            unpack_bf16x8(hz ? zv[u] : hv[u], hf);
+            unpack_bf16x8(hvu, hf);
 #pragma unroll
             for (int x = 0; x < 8; ++x) part = fmaf(gv[x], hf[x], part);
             part = group_sum<16>(part);
             part += __shfl_xor(part, 16, 64);
-            if (c == 0) j.dwp[static_cast<int64_t>(p * RP + r) * j.dwp_ld] = part;
+            if (c == 0) j.dwp[static_cast<int64_t>(r) * j.dwp_ld] = part;
           }
           if (c >= ncch) continue;
           const int64_t o = static_cast<int64_t>(r) * j.ldc + c * 16;
@@ -646,17 +656,34 @@ __device__ __forceinline__ void store_tile(const Job& j, f32x16 (&acc)[T::TN][T:
           *reinterpret_cast<u32x4*>(C + o) = dz;
           if (DACT == kActSwiglu) *reinterpret_cast<u32x4*>(C + o + j.zup) = du;
         }
+        i0 += U * T::NT;
+        if (i0 >= rows * NCH) break;
+        dact_load(i0, rows);
       }
       continue;
     }
-    for (int i = t; i < rows * NCH; i += T::NT) {
-      const int r = i / NCH, c = i - r * NCH;
-      if (c >= ncch) continue;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * RB + ((c ^ (r & (NCH - 1))) << 4));
-      // streamed out (non-temporal): h and o are read back by the next kernel only, long
-      // after L2 has turned over (0.7-2% off the whole layer)
-      __builtin_nontemporal_store(
-          v, reinterpret_cast<u32x4*>(C + static_cast<int64_t>(r) * j.ldc + c * 16));
+    // Whole staged rows out, 16 bytes per lane, in batches of 8 chunks per thread: the 8 LDS
+    // reads (unconditional; chunks past the tile read row 0) are issued before the first
+    // store, so a batch waits for one LDS round trip.
+    constexpr int SB = 8;
+    for (int i0 = t; i0 < rows * NCH; i0 += SB * T::NT) {
+      u32x4 v[SB];
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {
+        const int i = i0 + u * T::NT;
+        const int r = i < rows * NCH ? i / NCH : 0, c = i % NCH;
+        v[u] = *reinterpret_cast<const u32x4*>(stg + r * RB + ((c ^ (r & (NCH - 1))) << 4));
+      }
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {
+        const int i = i0 + u * T::NT;
+        const int r = i / NCH, c = i - r * NCH;
+        // streamed out (non-temporal): h and o are read back by the next kernel only, long
+        // after L2 has turned over (0.7-2% off the whole layer)
+        if (i < rows * NCH && c < ncch)
+          __builtin_nontemporal_store(
+              v[u], reinterpret_cast<u32x4*>(C + static_cast<int64_t>(r) * j.ldc + c * 16));
+      }
     }
   }
 }
@@ -676,11 +703,13 @@ __device__ __forceinline__ void lds_barrier_visible() {
 // reads chunk kt + 1's first step, so no MFMA waits for a fragment read at a chunk boundary.
 // The waves of tile half wm = 1 refill after their last MFMAs instead, so that each SIMD (one
 // wave of each half) always has a wave issuing MFMAs while the other issues its loads.
+// The last chunk (!NEXT) multiplies only its first ns 16-deep steps: with K-major operands K
+// need not fill the chunk, and the steps past K would only add products of zeros.
 template <class T, bool AKM, bool BKM, bool NEXT, bool REFILL>
 __device__ __forceinline__ void k_chunk(Feed<T>& fd, unsigned char* smem, int kt, int w, int wm,
                                         int lane, int arow, int brow, int sw,
                                         bf16x8 (&fa)[2][T::TM], bf16x8 (&fb)[2][T::TN],
-                                        f32x16 (&acc)[T::TN][T::TM]) {
+                                        f32x16 (&acc)[T::TN][T::TM], int ns = T::BK / 16) {
   constexpr int NS = T::BK / 16, SLOT = T::BM * T::ROW;
   constexpr int NRD = (T::TM + T::TN) * (AKM || BKM ? 2 : 1);   // wide upper bound
   constexpr int NMF = T::TM * T::TN;
@@ -688,9 +717,11 @@ __device__ __forceinline__ void k_chunk(Feed<T>& fd, unsigned char* smem, int kt
   const unsigned char* S = smem + st * T::STAGE;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
+    if (!NEXT && s >= ns) break;   // uniform over the block
     if (s + 1 < NS) {
-      read_step<T, AKM, BKM>(S, S + SLOT, s + 1, arow, brow, lane, sw, fa[(s + 1) & 1],
-                             fb[(s + 1) & 1]);
+      if (NEXT || s + 1 < ns)
+        read_step<T, AKM, BKM>(S, S + SLOT, s + 1, arow, brow, lane, sw, fa[(s + 1) & 1],
+                               fb[(s + 1) & 1]);
     } else if (NEXT) {
       MOE_WAIT_VMCNT(0);
       lds_barrier_visible();
@@ -777,7 +808,10 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
       k_chunk<T, AKM, BKM, true, false>(fd, smem, kt, w, wm, lane, arow, brow, sw, fa, fb, acc);
       ++kt;
     }
-    k_chunk<T, AKM, BKM, false, false>(fd, smem, kt, w, wm, lane, arow, brow, sw, fa, fb, acc);
+    // steps of the last chunk that hold k < K (all of them unless an operand is K-major)
+    const int ns = (AKM || BKM) ? min(BK / 16, (j.K - kt * BK + 15) / 16) : BK / 16;
+    k_chunk<T, AKM, BKM, false, false>(fd, smem, kt, w, wm, lane, arow, brow, sw, fa, fb, acc,
+                                       ns);
   } else if (KT > 0) {
 #pragma unroll
     for (int p = 0; p < NST - 1; ++p) feed_issue<T, AKM, BKM>(fd, smem + p * T::STAGE, w, p);

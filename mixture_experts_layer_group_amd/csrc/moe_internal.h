@@ -203,9 +203,9 @@ struct DxArgs {            // dx = [res] dy + sum_j dx_rows[row] + dx_shared + r
   int N, M, k, residual, dtype;
 };
 
-struct RouterPrepArgs {    // dlp [N, Ep] = dl, wgt [M, Ep] = Wg^T (layer dtype, zero-padded)
-  const float* dl; const void* Wg; void* dlp; void* wgt;
-  int N, E, Ep, M, dtype;
+struct RouterPrepArgs {    // dlp [N, Ep] = dl in the layer dtype, zero beyond E
+  const float* dl; void* dlp;
+  int N, E, Ep, dtype;
 };
 
 hipError_t launch_act_fwd(const BwdEltArgs& a, int64_t max_elems, hipStream_t s);

@@ -96,7 +96,11 @@ bool check_tile(const Problem& p, int mt, int nt) {
     } else if (p.akm) {
       ok &= check_range(p, "A", aoff + row0, aoff + (K - 1) * p.lda + row0 + nrows, p.a_elems, ctx);
     } else {
-      ok &= check_range(p, "A", aoff + row0 * p.lda, aoff + (row0 + nrows - 1) * p.lda + K,
+      // with a K-major B the K loop runs whole chunks (64 deep, 16 in the fp32 kernel), and a
+      // row-major A row is read to the end of its last chunk
+      const int64_t bk = kBM == 256 ? 64 : 16;
+      const int64_t KA = p.bkm ? (K + bk - 1) / bk * bk : K;
+      ok &= check_range(p, "A", aoff + row0 * p.lda, aoff + (row0 + nrows - 1) * p.lda + KA,
                         p.a_elems, ctx);
     }
     const int64_t bb = e * p.b_stride + boff;
@@ -325,15 +329,18 @@ int check_shape(const Shape& s, const std::vector<int>& cnt) {
   dxs.name = "bwd dx shared";
   dxs.rows = N; dxs.N = M; dxs.K = Es * H1; dxs.lda = Es * H1; dxs.ldb = M; dxs.ldc = M;
   dxs.bkm = true; dxs.a_elems = N * Es * H1; dxs.b_elems = Es * H1 * M; dxs.c_elems = N * M;
-  if (!check_launch(dx, Es ? &dxs : nullptr)) return 0;
-  ++launches;
-  // router dx term: dlp [N, Ep] x Wg^T [M, Ep]
+  // router dx term: dlp [N, Ep] (row-major, K = E of its Ep columns) x Wg [E, M] read K-major;
+  // the dx launch's second problem when there are no shared experts
   Problem rt;
   rt.name = "bwd router dx";
-  rt.rows = N; rt.N = M; rt.K = Ep; rt.lda = Ep; rt.ldb = Ep; rt.ldc = M;
-  rt.a_elems = N * Ep; rt.b_elems = M * Ep; rt.c_elems = N * M;
-  if (!check_launch(rt, nullptr)) return 0;
+  rt.rows = N; rt.N = M; rt.K = E; rt.lda = Ep; rt.ldb = M; rt.ldc = M; rt.bkm = true;
+  rt.a_elems = N * Ep; rt.b_elems = E * M; rt.c_elems = N * M;
+  if (!check_launch(dx, Es ? &dxs : &rt)) return 0;
   ++launches;
+  if (Es) {
+    if (!check_launch(rt, nullptr)) return 0;
+    ++launches;
+  }
   // dWg partials
   Problem wg;
   wg.name = "bwd dWg";
