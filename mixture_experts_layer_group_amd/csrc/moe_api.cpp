@@ -30,6 +30,7 @@ struct Layout {
   // sizes
   int64_t S, nbg, Rmax, rows_alloc, max_tiles;
   int esz, BM;
+  int group_m;   // m-tile group of the routed GEMM launches
 };
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -77,6 +78,7 @@ int make_layout(const moe_cfg* c, Layout* L) {
   L->Rmax = std::min<int64_t>(k * N, G * E * std::min<int64_t>(C, L->S));
   L->rows_alloc = L->Rmax + L->BM;
   L->max_tiles = L->Rmax / L->BM + E + 1;
+  L->group_m = moe::gemm_group_m(c->dtype, std::min<int64_t>(N, G * std::min<int64_t>(C, L->S)));
   // 32-bit limits of the kernels: element indices, and the byte range of a buffer resource
   // (GEMM 1 gathers its rows from the whole of x through one resource; h, o and the shared
   // output are addressed from tile bases inside their buffers)
@@ -312,6 +314,7 @@ int forward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* b
     g1.p1.zout = train->z1sh;
     g1.p1.ldz = Es * H1;
   }
+  g1.group_m = L.group_m;
   rc = status_of(moe::launch_expert_gemm(g1, r.s));
   if (rc) return rc;
   record(ev, 4, r.s);
@@ -331,6 +334,7 @@ int forward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* b
                              static_cast<int>((c->n_tokens + BM - 1) / BM), c->n_tokens, 0};
     g2.nprob = 2;
   }
+  g2.group_m = L.group_m;
   rc = status_of(moe::launch_expert_gemm(g2, r.s));
   if (rc) return rc;
   record(ev, 5, r.s);
@@ -581,6 +585,7 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
                   hipStream_t st = nullptr) {
     moe::GemmArgs g{};
     g.dtype = dt; g.p0 = p0; g.nprob = 1;
+    if (p0.tiles) g.group_m = L.group_m;   // routed launches
     if (p1) { g.p1 = *p1; g.nprob = 2; }
     return status_of(moe::launch_expert_gemm(g, st ? st : s));
   };

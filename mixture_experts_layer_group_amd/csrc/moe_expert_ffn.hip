@@ -123,7 +123,7 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& g, Job& j, int bid) 
                                   (g.p0.dense_rows + BM - 1) / BM,
                                   (g.p1.dense_rows + BM - 1) / BM);
   TileCoord tc;
-  if (!tile_coord(sp, bid, kGemmGroupM, tc)) return false;
+  if (!tile_coord(sp, bid, g.group_m > 0 ? g.group_m : kGemmGroupM, tc)) return false;
   const bool second = tc.prob == 1;
   const int mt = tc.mt, nt = tc.nt;
 
@@ -982,6 +982,12 @@ int grid_of(const GemmArgs& a, int BN) {
 }  // namespace
 
 int gemm_block_m(int dtype) { return dtype == 1 ? 256 : 64; }
+
+int gemm_group_m(int dtype, int64_t max_rows) {
+  const int64_t bm = gemm_block_m(dtype);
+  const int64_t mt = (max_rows + bm - 1) / bm;
+  return static_cast<int>(mt < 1 ? 1 : (mt < kGemmGroupM ? mt : kGemmGroupM));
+}
 
 // bf16: partial last n-tiles are masked; gated tiles write half the columns they compute.
 int gemm_block_n(int dtype, int act) {

@@ -140,6 +140,7 @@ struct GemmArgs {
   GemmProblem p0, p1;
   int nprob;              // 1 or 2 (p1 is always dense)
   int dtype;
+  int group_m;            // m-tiles that sweep the n-tiles together (0: the kernel's default)
 };
 
 // Gather + gate-weighted sum + shared experts + residual, and (block 0) the final aux.
@@ -223,6 +224,10 @@ hipError_t launch_zero(float* p, int64_t n, hipStream_t s);
 
 int gemm_block_m(int dtype);                           // BM of the expert GEMM tiles
 int gemm_block_n(int dtype, int act);                  // output columns per tile
+// m-tile group of a routed launch whose experts hold at most max_rows rows each: one expert's
+// m-tiles when they are fewer than the default group, so that a group's concurrent tiles
+// cover all n-tiles of one expert instead of a few n-tiles of several experts.
+int gemm_group_m(int dtype, int64_t max_rows);
 
 hipError_t launch_router(const RouterArgs& a, hipStream_t s);
 hipError_t launch_gate_scan(const ScanArgs& a, hipStream_t s);

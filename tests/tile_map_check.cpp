@@ -25,6 +25,9 @@ using moe::BatchEntry;
 namespace {
 
 constexpr int kGroupM = 8;
+// m-tile group of the shape's routed launches: one expert's largest m-tile count, at most
+// kGroupM (the launcher's rule); batched and dense launches keep kGroupM
+int g_group_m = kGroupM;
 // tile shape of the launches being checked: 256 x 256 (bf16 kernel) or 64 x 64 (fp32 kernel);
 // a gated GEMM 1 writes half the columns it computes
 int kBM = 256, kBN = 256;
@@ -174,13 +177,14 @@ bool check_launch(const Problem& p0, const Problem* p1) {
   const int mpe1 = p1 ? (int)((p1->rows + kBM - 1) / kBM) : 0;
   const moe::TileSpace sp = moe::tile_space(mt0, nt0, mt1, nt1, nprob, batched, mpe0, mpe1);
   const int total = moe::tile_total(sp);
+  const int gm = p0.routed ? g_group_m : kGroupM;
   // the grid the host launches covers the problems' tile bounds
   std::vector<char> seen((size_t)total, 0);
   bool ok = true;
   moe::TileCoord c;
   int per_xcd[8][2] = {};
   for (int bid = 0; bid < total; ++bid) {
-    if (!moe::tile_coord(sp, bid, kGroupM, c)) return fail(p0.name + ": block inside the grid decoded as none");
+    if (!moe::tile_coord(sp, bid, gm, c)) return fail(p0.name + ": block inside the grid decoded as none");
     if (c.prob == 0 || c.prob == 1) per_xcd[bid & 7][c.prob]++;
     const Problem& P = c.prob ? *p1 : p0;
     const int mts = c.prob ? mt1 : mt0, nts = c.prob ? nt1 : nt0;
@@ -190,7 +194,7 @@ bool check_launch(const Problem& p0, const Problem* p1) {
     if (seen[lin]++) return fail(P.name + ": two blocks decode to one tile");
     ok &= check_tile(P, c.mt, c.nt);
   }
-  if (moe::tile_coord(sp, total, kGroupM, c)) return fail(p0.name + ": block past the grid decoded");
+  if (moe::tile_coord(sp, total, gm, c)) return fail(p0.name + ": block past the grid decoded");
   // two problems that are not dealt by entries: every XCD (blocks bid with equal bid % 8)
   // holds an eighth of each problem's tiles, rounded down or up
   if (p1 && sp.tpe == 0) {
@@ -223,6 +227,13 @@ int check_shape(const Shape& s, const std::vector<int>& cnt) {
   for (int e = 0; e < E; ++e) off[e + 1] = off[e] + cnt[e];
   const int64_t R = off[E];
   if (R > Rmax) return fail("routing keeps more rows than Rmax"), 0;
+  {
+    const int64_t maxr = std::min<int64_t>(N, s.G * std::min<int64_t>(s.C, S));
+    const int64_t mt = (maxr + kBM - 1) / kBM;
+    g_group_m = (int)std::max<int64_t>(1, std::min<int64_t>(kGroupM, mt));
+    for (int e = 0; e < E; ++e)
+      if ((cnt[e] + kBM - 1) / kBM > mt) return fail("an expert holds more m-tiles than the bound"), 0;
+  }
   // device tile list: expert e's rows cut into BM-row pieces, in expert order
   std::vector<moe::TileDesc> tiles;
   for (int e = 0; e < E; ++e)
