@@ -335,6 +335,8 @@ int forward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* b
     g2.nprob = 2;
   }
   g2.group_m = L.group_m;
+  // h larger than the last-level cache (256 MB): plain tile order (see tile_coord)
+  g2.plain = !Es && L.Rmax * H * L.esz > (int64_t{256} << 20);
   rc = status_of(moe::launch_expert_gemm(g2, r.s));
   if (rc) return rc;
   record(ev, 5, r.s);

@@ -28,9 +28,9 @@ struct BatchEntry {
 // The tiles of one launch: problem 0 has mt0 x nt0 tiles (mt0 of a routed problem is the
 // device tile count), problem 1 mt1 x nt1 (0 x 0 when the launch has one problem).
 // tpe > 0: both problems are batched with tpe tiles per entry, and the entries are dealt over
-// the XCD ranges (see tile_coord).
+// the XCD ranges (see tile_coord).  plain: one-problem launch in plain order (see tile_coord).
 struct TileSpace {
-  int mt0, nt0, mt1, nt1, tpe;
+  int mt0, nt0, mt1, nt1, tpe, plain;
 };
 
 struct TileCoord {
@@ -41,10 +41,11 @@ MOE_HD inline int tile_total(const TileSpace& s) { return s.mt0 * s.nt0 + s.mt1 
 
 // nprob: problems in the launch (1 or 2; with 1, mt1 = nt1 = 0); batched: every problem of the
 // launch is batched; mpe0 / mpe1: m-tiles per entry.  Entries are dealt only when every entry
-// of both problems has the same number of tiles and they tile the launch exactly.
+// of both problems has the same number of tiles and they tile the launch exactly.  plain
+// applies to one-problem launches that are not dealt.
 MOE_HD inline TileSpace tile_space(int mt0, int nt0, int mt1, int nt1, int nprob, bool batched,
-                                   int mpe0, int mpe1) {
-  TileSpace s{mt0, nt0, nprob > 1 ? mt1 : 0, nprob > 1 ? nt1 : 0, 0};
+                                   int mpe0, int mpe1, bool plain = false) {
+  TileSpace s{mt0, nt0, nprob > 1 ? mt1 : 0, nprob > 1 ? nt1 : 0, 0, 0};
   if (batched) {
     const int tpe = mpe0 * nt0;
     const bool same = nprob == 1 || mpe1 * nt1 == tpe;
@@ -52,6 +53,7 @@ MOE_HD inline TileSpace tile_space(int mt0, int nt0, int mt1, int nt1, int nprob
     const int T = tpe > 0 ? total / tpe : 0;
     if (same && T > 0 && T * tpe == total) s.tpe = tpe;
   }
+  s.plain = plain && s.tpe == 0 && s.mt1 * s.nt1 == 0 ? 1 : 0;
   return s;
 }
 
@@ -68,6 +70,11 @@ MOE_HD inline TileSpace tile_space(int mt0, int nt0, int mt1, int nt1, int nprob
 //    every XCD gets the same share of both.  Problem 1's remainder tiles go to the XCDs
 //    after those that took problem 0's remainder (cyclically), which keeps each XCD's tile
 //    count equal to the number of blocks it receives.
+//  * Plain order (block b takes slot b) for launches whose row operand does not fit the
+//    last-level cache while the weights are shared: consecutive slots go to the 8 XCDs in
+//    turn, so the XCDs work on the same expert at the same time and share its weight tiles
+//    through that cache, and each XCD keeps whole m-tiles (all their n-tiles at once) in its
+//    L2, reading every row once.
 //  * Inside a problem, group_m m-tiles sweep the n-tiles together (L2 reuse of the weight
 //    tiles across an expert's row tiles and of the row tiles across n-tiles).
 // A bijection from [0, tile_total) onto the tiles of both problems.
@@ -75,7 +82,7 @@ MOE_HD inline bool tile_coord(const TileSpace& s, int bid, int group_m, TileCoor
   const int tot0 = s.mt0 * s.nt0, total = tile_total(s), tot1 = total - tot0;
   if (bid < 0 || bid >= total) return false;
   const int xcd = bid & 7, loc = bid >> 3, q = total >> 3, r = total & 7;
-  int pid = xcd * q + (xcd < r ? xcd : r) + loc;
+  int pid = s.plain ? bid : xcd * q + (xcd < r ? xcd : r) + loc;
   if (s.tpe == 0 && tot0 > 0 && tot1 > 0) {
     const int q0 = tot0 >> 3, r0 = tot0 & 7, q1 = tot1 >> 3, r1 = tot1 & 7;
     const int n0 = q0 + (xcd < r0 ? 1 : 0);   // problem 0 tiles of this XCD

@@ -38,6 +38,7 @@ struct Problem {
   std::vector<moe::TileDesc> tiles;
   std::vector<BatchEntry> entries;
   bool routed = false, batched = false;
+  bool plain = false;      // one-problem launch in plain tile order
   int64_t rows = 0;        // dense: rows; batched: rows of every entry
   int64_t N = 0, K = 0;    // output columns, depth (dense / routed; entries carry their own)
   int64_t lda = 0, ldb = 0, ldc = 0, b_stride = 0;
@@ -175,7 +176,8 @@ bool check_launch(const Problem& p0, const Problem* p1) {
   const bool batched = p0.batched && (!p1 || p1->batched);
   const int mpe0 = (int)((p0.rows + kBM - 1) / kBM);
   const int mpe1 = p1 ? (int)((p1->rows + kBM - 1) / kBM) : 0;
-  const moe::TileSpace sp = moe::tile_space(mt0, nt0, mt1, nt1, nprob, batched, mpe0, mpe1);
+  const moe::TileSpace sp = moe::tile_space(mt0, nt0, mt1, nt1, nprob, batched, mpe0, mpe1,
+                                            p0.plain);
   const int total = moe::tile_total(sp);
   const int gm = p0.routed ? g_group_m : kGroupM;
   // the grid the host launches covers the problems' tile bounds
@@ -261,6 +263,8 @@ int check_shape(const Shape& s, const std::vector<int>& cnt) {
   // ---- forward GEMM 2: o = h W2_e^T (+ shared: o_sh = h_sh [W2_sh..]^T over K segments)
   Problem g2;
   g2.name = "fwd GEMM 2";
+  // the launcher's rule: no shared experts and h larger than 256 MB
+  g2.plain = Es == 0 && Rmax * H * (kBM == 256 ? 2 : 4) > (int64_t(256) << 20);
   g2.routed = true; g2.tiles = tiles;
   g2.N = M; g2.K = H; g2.lda = H; g2.ldb = H; g2.ldc = M; g2.b_stride = M * H;
   g2.a_elems = ra * H; g2.b_elems = (E + Es) * M * H; g2.c_elems = ra * M;
