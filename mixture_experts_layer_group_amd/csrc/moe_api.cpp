@@ -299,6 +299,8 @@ int forward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* b
                            static_cast<int>(H)};
   g1.p0.a_gather = reinterpret_cast<const int32_t*>(ws + L.tokrow);
   g1.nprob = 1;
+  // weights larger than the last-level cache (256 MB): expert-synchronous tile order
+  g1.plain = !Es && E * H1 * M * L.esz > (int64_t{256} << 20) ? 2 : 0;
   if (Es) {
     const char* w1sh = static_cast<const char*>(W1) + E * H1 * M * L.esz;
     g1.p1 = moe::GemmProblem{x, M, w1sh, M, 0, M, 0, ws + L.hsh, Es * H,
@@ -584,9 +586,9 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
   const char* W1c = static_cast<const char*>(W1);
   const char* W2c = static_cast<const char*>(W2);
   auto gemm = [&](const moe::GemmProblem& p0, const moe::GemmProblem* p1,
-                  hipStream_t st = nullptr) {
+                  hipStream_t st = nullptr, int plain = 0) {
     moe::GemmArgs g{};
-    g.dtype = dt; g.p0 = p0; g.nprob = 1;
+    g.dtype = dt; g.p0 = p0; g.nprob = 1; g.plain = plain;
     if (p0.tiles) g.group_m = L.group_m;   // routed launches
     if (p1) { g.p1 = *p1; g.nprob = 2; }
     return status_of(moe::launch_expert_gemm(g, st ? st : s));
@@ -614,6 +616,8 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
   //    ReLU needs no z1: ReLU'(z1) is 1 exactly where h > 0, so GEMM 1 writes h as in the
   //    forward.
   const bool relu = c->act == MOE_ACT_RELU;
+  // the forward GEMM 1's tile order (weights larger than the last-level cache)
+  const int plain1 = !Es && E * H1 * M * L.esz > (int64_t{256} << 20) ? 2 : 0;
   if (saved) {
     // kept by the training forward
   } else if (relu) {
@@ -623,7 +627,7 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
                             static_cast<int>(Es * H), static_cast<int>(M),
                             static_cast<int>(N), BM);
     p0.act = p1.act = moe::kActRelu;
-    rc = gemm(p0, Es ? &p1 : nullptr);
+    rc = gemm(p0, Es ? &p1 : nullptr, nullptr, plain1);
     if (rc) return rc;
   } else {
     auto p0 = routed_problem(ws + L.buf, M, W1, M, H1 * M, ws + B.z1, H1, static_cast<int>(H1),
@@ -631,7 +635,7 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
     auto p1 = dense_problem(x, M, W1c + E * H1 * M * esz, M, ws + B.z1sh, Es * H1,
                             static_cast<int>(Es * H1), static_cast<int>(M),
                             static_cast<int>(N), BM);
-    rc = gemm(p0, Es ? &p1 : nullptr);
+    rc = gemm(p0, Es ? &p1 : nullptr, nullptr, plain1);
     if (rc) return rc;
     moe::BwdEltArgs ea{};
     ea.z = ws + B.z1; ea.h = ws + L.h; ea.rows_ptr = Rdev; ea.nexp = 1;

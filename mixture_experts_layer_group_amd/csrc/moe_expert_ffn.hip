@@ -121,7 +121,7 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& g, Job& j, int bid) 
   const bool batched = g.p0.batch && (g.nprob == 1 || g.p1.batch);
   const TileSpace sp = tile_space(mt0, nt0, mt1, nt1, g.nprob, batched,
                                   (g.p0.dense_rows + BM - 1) / BM,
-                                  (g.p1.dense_rows + BM - 1) / BM, g.plain != 0);
+                                  (g.p1.dense_rows + BM - 1) / BM, g.plain);
   TileCoord tc;
   if (!tile_coord(sp, bid, g.group_m > 0 ? g.group_m : kGemmGroupM, tc)) return false;
   const bool second = tc.prob == 1;

@@ -141,7 +141,7 @@ struct GemmArgs {
   int nprob;              // 1 or 2 (p1 is always dense)
   int dtype;
   int group_m;            // m-tiles that sweep the n-tiles together (0: the kernel's default)
-  int plain;              // one-problem launch in plain block order (tile_coord)
+  int plain;              // one-problem launch order: 0 XCD ranges, 1 plain, 2 expert-synchronous
 };
 
 // Gather + gate-weighted sum + shared experts + residual, and (block 0) the final aux.

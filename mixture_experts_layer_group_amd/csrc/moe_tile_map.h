@@ -28,7 +28,8 @@ struct BatchEntry {
 // The tiles of one launch: problem 0 has mt0 x nt0 tiles (mt0 of a routed problem is the
 // device tile count), problem 1 mt1 x nt1 (0 x 0 when the launch has one problem).
 // tpe > 0: both problems are batched with tpe tiles per entry, and the entries are dealt over
-// the XCD ranges (see tile_coord).  plain: one-problem launch in plain order (see tile_coord).
+// the XCD ranges (see tile_coord).  plain: 0, or the order of a one-problem launch that is not
+// dealt: 1 plain block order, 2 expert-synchronous (see tile_coord).
 struct TileSpace {
   int mt0, nt0, mt1, nt1, tpe, plain;
 };
@@ -41,10 +42,11 @@ MOE_HD inline int tile_total(const TileSpace& s) { return s.mt0 * s.nt0 + s.mt1 
 
 // nprob: problems in the launch (1 or 2; with 1, mt1 = nt1 = 0); batched: every problem of the
 // launch is batched; mpe0 / mpe1: m-tiles per entry.  Entries are dealt only when every entry
-// of both problems has the same number of tiles and they tile the launch exactly.  plain
-// applies to one-problem launches that are not dealt.
+// of both problems has the same number of tiles and they tile the launch exactly.  plain (1 or
+// 2) applies to one-problem launches that are not dealt; 2 needs a multiple of 8 n-tiles and
+// falls back to the XCD ranges otherwise.
 MOE_HD inline TileSpace tile_space(int mt0, int nt0, int mt1, int nt1, int nprob, bool batched,
-                                   int mpe0, int mpe1, bool plain = false) {
+                                   int mpe0, int mpe1, int plain = 0) {
   TileSpace s{mt0, nt0, nprob > 1 ? mt1 : 0, nprob > 1 ? nt1 : 0, 0, 0};
   if (batched) {
     const int tpe = mpe0 * nt0;
@@ -53,7 +55,8 @@ MOE_HD inline TileSpace tile_space(int mt0, int nt0, int mt1, int nt1, int nprob
     const int T = tpe > 0 ? total / tpe : 0;
     if (same && T > 0 && T * tpe == total) s.tpe = tpe;
   }
-  s.plain = plain && s.tpe == 0 && s.mt1 * s.nt1 == 0 ? 1 : 0;
+  s.plain = s.tpe == 0 && s.mt1 * s.nt1 == 0 && (plain == 1 || (plain == 2 && (nt0 & 7) == 0))
+                ? plain : 0;
   return s;
 }
 
@@ -75,6 +78,11 @@ MOE_HD inline TileSpace tile_space(int mt0, int nt0, int mt1, int nt1, int nprob
 //    turn, so the XCDs work on the same expert at the same time and share its weight tiles
 //    through that cache, and each XCD keeps whole m-tiles (all their n-tiles at once) in its
 //    L2, reading every row once.
+//  * Expert-synchronous order for launches whose weights do not fit the last-level cache
+//    while the rows do: XCD x takes n-tiles [x nb, (x + 1) nb) (nb = n-tiles / 8) of every
+//    m-tile, m-tiles in list order, so all XCDs work on the same expert at the same time and
+//    that expert's weights (each n-range read by one XCD) and rows stay in that cache until
+//    the next expert; group_m m-tiles sweep the XCD's nb n-tiles.
 //  * Inside a problem, group_m m-tiles sweep the n-tiles together (L2 reuse of the weight
 //    tiles across an expert's row tiles and of the row tiles across n-tiles).
 // A bijection from [0, tile_total) onto the tiles of both problems.
@@ -82,6 +90,17 @@ MOE_HD inline bool tile_coord(const TileSpace& s, int bid, int group_m, TileCoor
   const int tot0 = s.mt0 * s.nt0, total = tile_total(s), tot1 = total - tot0;
   if (bid < 0 || bid >= total) return false;
   const int xcd = bid & 7, loc = bid >> 3, q = total >> 3, r = total & 7;
+  if (s.plain == 2) {
+    const int nb = s.nt0 >> 3;   // every XCD holds mt0 nb tiles: total / 8 exactly
+    const int per_group = group_m * nb;
+    const int grp = loc / per_group, first = grp * group_m;
+    const int gsz = s.mt0 - first < group_m ? s.mt0 - first : group_m;
+    const int in = loc - grp * per_group;
+    c.prob = 0;
+    c.mt = first + in % gsz;
+    c.nt = xcd * nb + in / gsz;
+    return true;
+  }
   int pid = s.plain ? bid : xcd * q + (xcd < r ? xcd : r) + loc;
   if (s.tpe == 0 && tot0 > 0 && tot1 > 0) {
     const int q0 = tot0 >> 3, r0 = tot0 & 7, q1 = tot1 >> 3, r1 = tot1 & 7;

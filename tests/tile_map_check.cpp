@@ -38,7 +38,7 @@ struct Problem {
   std::vector<moe::TileDesc> tiles;
   std::vector<BatchEntry> entries;
   bool routed = false, batched = false;
-  bool plain = false;      // one-problem launch in plain tile order
+  int plain = 0;           // one-problem launch order: 1 plain, 2 expert-synchronous
   int64_t rows = 0;        // dense: rows; batched: rows of every entry
   int64_t N = 0, K = 0;    // output columns, depth (dense / routed; entries carry their own)
   int64_t lda = 0, ldb = 0, ldc = 0, b_stride = 0;
@@ -249,6 +249,8 @@ int check_shape(const Shape& s, const std::vector<int>& cnt) {
   Problem g1;
   g1.name = "fwd GEMM 1";
   g1.routed = true; g1.tiles = tiles; g1.gather = true;
+  // the launcher's rule: no shared experts and weights larger than 256 MB
+  g1.plain = Es == 0 && E * H1 * M * (kBM == 256 ? 2 : 4) > (int64_t(256) << 20) ? 2 : 0;
   g1.N = H; g1.K = M; g1.lda = M; g1.ldb = M; g1.ldc = H; g1.b_stride = H1 * M;
   g1.gated_b = s.glu; g1.glu_h = s.glu ? (int)H : 0;
   g1.a_elems = N * M; g1.b_elems = (E + Es) * H1 * M; g1.c_elems = ra * H;
@@ -264,7 +266,7 @@ int check_shape(const Shape& s, const std::vector<int>& cnt) {
   Problem g2;
   g2.name = "fwd GEMM 2";
   // the launcher's rule: no shared experts and h larger than 256 MB
-  g2.plain = Es == 0 && Rmax * H * (kBM == 256 ? 2 : 4) > (int64_t(256) << 20);
+  g2.plain = Es == 0 && Rmax * H * (kBM == 256 ? 2 : 4) > (int64_t(256) << 20) ? 1 : 0;
   g2.routed = true; g2.tiles = tiles;
   g2.N = M; g2.K = H; g2.lda = H; g2.ldb = H; g2.ldc = M; g2.b_stride = M * H;
   g2.a_elems = ra * H; g2.b_elems = (E + Es) * M * H; g2.c_elems = ra * M;
