@@ -236,11 +236,13 @@ def test_saved_backward_empty_batch():
         assert float(t.abs().max()) == 0.0
 
 
-@pytest.mark.parametrize("name", ["gshard_bf16", "switch_bf16"])
+@pytest.mark.parametrize("name", ["gshard_bf16", "switch_bf16", "large_expert_bf16"])
 def test_workload_saved_backward(name):
     """Full-size layers against moe_backward (whose every element test_workload_backward
-    compares with the oracle): ReLU bit for bit; GELU dW1 bit for bit and the rest within
-    the backward's tolerance of it."""
+    compares with the oracle on the GShard and Switch layers): ReLU bit for bit; GELU dW1 bit
+    for bit and the rest within the backward's tolerance of it.  On the large-expert layer
+    (too large for the fp64 oracle) the two GEMM 1 launches run the expert-synchronous tile
+    order, the training forward with its pre-activation epilogue and the recompute without."""
     h = harness()
     cfg = configs.WORKLOADS[name]
     h.say(f"[gpu-bwd] {name}: saved vs recompute at full size")
