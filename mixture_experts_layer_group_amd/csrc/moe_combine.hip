@@ -5,7 +5,8 @@
 // the gate-weighted sum of the selected experts' outputs; "Capacity overflow 会跳过 expert
 // computation": a token with no kept slot leaves through the residual, so y_n = x_n
 // bit-exactly (0 + x in fp32 is x).  [Lec16] "共享专家 vs. 路由专家": the shared experts add
-// with weight 1.  Each block gathers 16 tokens; lanes move 16-byte chunks of rows.
+// with weight 1.  Lanes move 16-byte chunks of rows; a block takes as many tokens as make
+// about four chunks per lane, so that each lane issues all its loads at once.
 //
 // Block 0 also finishes the aux loss of [GShard] "Top-2 gating 的四个机制 / Auxiliary loss":
 // aux = (1/G) sum_g E/(k S) sum_e m_{g,e} c_{g,e},  m_{g,e} = P_{g,e} / S, from the per-
@@ -14,17 +15,19 @@
 // sums, and the device-level balance loss of [Lec16] "DeepSeek MoE 的负载均衡" (the
 // expert-level terms grouped by the D expert groups: mean f times summed P per group); all
 // in fp64 with fixed-order reductions (deterministic).
+#include <algorithm>
+
 #include "moe_device.h"
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int kTok = 16;  // tokens per block
+constexpr int kTokMax = 64;  // tokens per block at most (short rows)
+constexpr int kU = 4;        // chunks per lane and round
 
 // Every o row, x row and shared-expert row is read exactly once and y is written once, so
-// they bypass the caches' retention (non-temporal): on the shared+routed layer this raises
-// the pass from 4.9 to 5.8 TB/s.
+// they bypass the caches' retention (non-temporal).
 template <class V>
 __device__ __forceinline__ V ld_stream(const V* p) {
   return __builtin_nontemporal_load(p);
@@ -82,14 +85,15 @@ __device__ void aux_final(const CombineArgs& a) {
   }
 }
 
-template <int DT>
+// KT = top-k (compile time, so that the slot loops are straight-line code).
+template <int DT, int KT>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
-  __shared__ int rows_s[kTok][kMaxTopK];
-  __shared__ float w_s[kTok][kMaxTopK];
+  __shared__ int rows_s[kTokMax][kMaxTopK];
+  __shared__ float w_s[kTokMax][kMaxTopK];
   const int t = threadIdx.x;
-  const int tok0 = blockIdx.x * kTok;
-  const int nt = min(kTok, a.N - tok0);
-  const int k = a.k;
+  const int tok0 = blockIdx.x * a.tpb;
+  const int nt = min(a.tpb, a.N - tok0);
+  constexpr int k = KT;
   if (blockIdx.x == 0) aux_final(a);
   for (int i = t; i < nt * k; i += 256) {
     const int tl = i / k, jj = i - tl * k;
@@ -118,27 +122,38 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
       for (int q = 0; q < 4; ++q) acc[q] = fmaf(wgt, __uint_as_float(v[q]), acc[q]);
     }
   };
-  // U chunks per thread per round, every load of the round issued before its stores.
-  constexpr int U = 2;
+  // U chunks per lane per round, every load of the round issued before its stores.  The
+  // loads are unconditional, so that none waits for the one before it (a load under a
+  // per-lane branch is waited for where the branch merges): a chunk past the block re-reads
+  // its last chunk, and a dropped slot's expert row is read through a buffer resource at an
+  // offset past its range, which returns zeros without a memory access (and is not used).
+  // The range is checked dword by dword against the record count (2^31 - 1 here): every
+  // expert row lies below 2^31 - 1 bytes from o (the workspace layout checks it), and the
+  // dropped-slot offset has bit 31 set, so each dword of its access is past the range.
+  constexpr int U = kU;
+  constexpr uint32_t kNoRow = 0x80000000u;
+  typedef __amdgpu_buffer_rsrc_t rsrc_t;
+  const rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(ob), static_cast<short>(0),
+                                                         0x7fffffff, 0x00020000);
   const int total = nt * ch;
   for (int base = t; base < total; base += 256 * U) {
-    u32x4 vo[U][kMaxTopK], vs[U], vx[U];
+    u32x4 vo[U][KT], vs[U], vx[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int idx = base + u * 256;
-      if (idx < total) {
-        const int tl = idx / ch, c = idx - tl * ch;
-        const size_t n = static_cast<size_t>(tok0 + tl);
+      const int idx = base + u * 256 < total ? base + u * 256 : total - 1;
+      const int tl = idx / ch, c = idx - tl * ch;
+      const size_t n = static_cast<size_t>(tok0 + tl);
+      const char* xrow = xb + n * rowbytes + c * 16;
 #pragma unroll
-        for (int jj = 0; jj < kMaxTopK; ++jj) {
-          if (jj < k) {
-            const int r = rows_s[tl][jj];
-            if (r >= 0) vo[u][jj] = ld_stream(reinterpret_cast<const u32x4*>(ob + static_cast<size_t>(r) * rowbytes + c * 16));
-          }
-        }
-        if (sb) vs[u] = ld_stream(reinterpret_cast<const u32x4*>(sb + n * rowbytes + c * 16));
-        if (a.residual) vx[u] = ld_stream(reinterpret_cast<const u32x4*>(xb + n * rowbytes + c * 16));
+      for (int jj = 0; jj < KT; ++jj) {
+        const int r = rows_s[tl][jj];
+        const uint32_t off = r >= 0 ? static_cast<uint32_t>(r) * static_cast<uint32_t>(rowbytes) +
+                                          static_cast<uint32_t>(c) * 16u
+                                    : kNoRow;
+        vo[u][jj] = __builtin_amdgcn_raw_buffer_load_b128(orsrc, off, 0, 2);   // nt
       }
+      if (sb) vs[u] = ld_stream(reinterpret_cast<const u32x4*>(sb + n * rowbytes + c * 16));
+      if (a.residual) vx[u] = ld_stream(reinterpret_cast<const u32x4*>(xrow));
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -150,8 +165,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 #pragma unroll
       for (int q = 0; q < EPC; ++q) acc[q] = 0.f;
 #pragma unroll
-      for (int jj = 0; jj < kMaxTopK; ++jj)
-        if (jj < k && rows_s[tl][jj] >= 0) add(acc, vo[u][jj], w_s[tl][jj]);
+      for (int jj = 0; jj < KT; ++jj)
+        if (rows_s[tl][jj] >= 0) add(acc, vo[u][jj], w_s[tl][jj]);
       if (sb) add(acc, vs[u], 1.0f);
       if (a.residual) add(acc, vx[u], 1.0f);
       u32x4 out;
@@ -171,13 +186,27 @@ __global__ __launch_bounds__(256) void aux_only_kernel(CombineArgs a) { aux_fina
 
 }  // namespace
 
-hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
-  const int grid = (a.N + kTok - 1) / kTok;
+hipError_t launch_combine(const CombineArgs& args, hipStream_t s) {
+  if (args.k < 1 || args.k > kMaxTopK || args.M <= 0) return hipErrorInvalidValue;
+  // One round of kU chunks per lane covers the block's tokens (whole rows, at least one),
+  // and a short batch still spreads over one block per CU.
+  CombineArgs a = args;
+  const int ch = a.M / (a.dtype == 1 ? 8 : 4);
+  a.tpb = std::max(1, std::min({kTokMax, 256 * kU / ch, a.N / 256}));
+  const int grid = (a.N + a.tpb - 1) / a.tpb;
   if (grid == 0) return hipSuccess;
-  if (a.dtype == 1)
-    hipLaunchKernelGGL(combine_kernel<1>, dim3(grid), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(combine_kernel<0>, dim3(grid), dim3(256), 0, s, a);
+#define MOE_COMBINE_K(KV)                                                                  \
+  case KV:                                                                                  \
+    if (a.dtype == 1)                                                                       \
+      hipLaunchKernelGGL((combine_kernel<1, KV>), dim3(grid), dim3(256), 0, s, a);         \
+    else                                                                                    \
+      hipLaunchKernelGGL((combine_kernel<0, KV>), dim3(grid), dim3(256), 0, s, a);         \
+    break;
+  switch (a.k) {
+    MOE_COMBINE_K(1) MOE_COMBINE_K(2) MOE_COMBINE_K(3) MOE_COMBINE_K(4)
+    MOE_COMBINE_K(5) MOE_COMBINE_K(6) MOE_COMBINE_K(7) MOE_COMBINE_K(8)
+  }
+#undef MOE_COMBINE_K
   return hipGetLastError();
 }
 

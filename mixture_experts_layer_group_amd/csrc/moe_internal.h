@@ -161,6 +161,7 @@ struct CombineArgs {
   int nblocks;
   int n_eg;               // expert groups of the device-level loss
   int N, M, k, residual, dtype, G, E, S;
+  int tpb;                // tokens per combine block (set by launch_combine)
 };
 
 struct EmptyArgs {         // N == 0: zero the small outputs (aux, z_loss, dev_loss nullable)
