@@ -6,7 +6,8 @@
 // computation": a token with no kept slot leaves through the residual, so y_n = x_n
 // bit-exactly (0 + x in fp32 is x).  [Lec16] "共享专家 vs. 路由专家": the shared experts add
 // with weight 1.  Lanes move 16-byte chunks of rows; a block takes as many tokens as make
-// about four chunks per lane, so that each lane issues all its loads at once.
+// one round of two (short rows) or four chunks per lane, so that each lane issues all its
+// loads at once.
 //
 // Block 0 also finishes the aux loss of [GShard] "Top-2 gating 的四个机制 / Auxiliary loss":
 // aux = (1/G) sum_g E/(k S) sum_e m_{g,e} c_{g,e},  m_{g,e} = P_{g,e} / S, from the per-
@@ -24,7 +25,6 @@ namespace moe {
 namespace {
 
 constexpr int kTokMax = 64;  // tokens per block at most (short rows)
-constexpr int kU = 4;        // chunks per lane and round
 
 // Every o row, x row and shared-expert row is read exactly once and y is written once, so
 // they bypass the caches' retention (non-temporal).
@@ -85,8 +85,9 @@ __device__ void aux_final(const CombineArgs& a) {
   }
 }
 
-// KT = top-k (compile time, so that the slot loops are straight-line code).
-template <int DT, int KT>
+// KT = top-k (compile time, so that the slot loops are straight-line code); U = chunks per
+// lane and round.
+template <int DT, int KT, int U>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   __shared__ int rows_s[kTokMax][kMaxTopK];
   __shared__ float w_s[kTokMax][kMaxTopK];
@@ -130,7 +131,6 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   // The range is checked dword by dword against the record count (2^31 - 1 here): every
   // expert row lies below 2^31 - 1 bytes from o (the workspace layout checks it), and the
   // dropped-slot offset has bit 31 set, so each dword of its access is past the range.
-  constexpr int U = kU;
   constexpr uint32_t kNoRow = 0x80000000u;
   typedef __amdgpu_buffer_rsrc_t rsrc_t;
   const rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(ob), static_cast<short>(0),
@@ -188,19 +188,25 @@ __global__ __launch_bounds__(256) void aux_only_kernel(CombineArgs a) { aux_fina
 
 hipError_t launch_combine(const CombineArgs& args, hipStream_t s) {
   if (args.k < 1 || args.k > kMaxTopK || args.M <= 0) return hipErrorInvalidValue;
-  // One round of kU chunks per lane covers the block's tokens (whole rows, at least one),
-  // and a short batch still spreads over one block per CU.
+  // One round of U chunks per lane covers the block's tokens (whole rows, at least one), and
+  // a short batch still spreads over one block per CU.  Rows of up to 128 chunks take two
+  // chunks per lane (more blocks), longer rows four (more loads in flight per lane).
   CombineArgs a = args;
   const int ch = a.M / (a.dtype == 1 ? 8 : 4);
-  a.tpb = std::max(1, std::min({kTokMax, 256 * kU / ch, a.N / 256}));
+  const int u = ch <= 128 ? 2 : 4;
+  a.tpb = std::max(1, std::min({kTokMax, 256 * u / ch, a.N / 256}));
   const int grid = (a.N + a.tpb - 1) / a.tpb;
   if (grid == 0) return hipSuccess;
 #define MOE_COMBINE_K(KV)                                                                  \
   case KV:                                                                                  \
-    if (a.dtype == 1)                                                                       \
-      hipLaunchKernelGGL((combine_kernel<1, KV>), dim3(grid), dim3(256), 0, s, a);         \
+    if (a.dtype == 1 && u == 2)                                                             \
+      hipLaunchKernelGGL((combine_kernel<1, KV, 2>), dim3(grid), dim3(256), 0, s, a);      \
+    else if (a.dtype == 1)                                                                  \
+      hipLaunchKernelGGL((combine_kernel<1, KV, 4>), dim3(grid), dim3(256), 0, s, a);      \
+    else if (u == 2)                                                                        \
+      hipLaunchKernelGGL((combine_kernel<0, KV, 2>), dim3(grid), dim3(256), 0, s, a);      \
     else                                                                                    \
-      hipLaunchKernelGGL((combine_kernel<0, KV>), dim3(grid), dim3(256), 0, s, a);         \
+      hipLaunchKernelGGL((combine_kernel<0, KV, 4>), dim3(grid), dim3(256), 0, s, a);      \
     break;
   switch (a.k) {
     MOE_COMBINE_K(1) MOE_COMBINE_K(2) MOE_COMBINE_K(3) MOE_COMBINE_K(4)
