@@ -759,7 +759,11 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
   if (!decode_tile<BM, OUTN, 2>(g, j, blockIdx.x)) return;
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wm = w / WN, wn = w % WN;
+  // Waves w and w + 4 share a SIMD: the second half's column blocks are rotated by WN / 2, so
+  // that a tile whose valid columns end half-way still has one multiplying wave per SIMD.
+  const int wm = w / WN, wn = (w % WN) ^ ((wm & 1) * (WN / 2));
+  // A wave whose rows or columns all lie past the tile's valid block multiplies nothing.
+  const bool live = wm * T::WTM < j.nrows && wn * (OUTN / WN) < j.ncols;
   Feed<T> fd;
   feed_init<T, GLU, AKM, BKM>(j, w, lane, fd);
 
@@ -797,21 +801,31 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
     MOE_WAIT_VMCNT(0);
     lds_barrier_visible();
     if (KT > 1) feed_issue<T, AKM, BKM>(fd, smem + T::STAGE, w, 1);
-    read_step<T, AKM, BKM>(smem, smem + SLOT, 0, arow, brow, lane, sw, fa[0], fb[0]);
-    // The steady state (chunks with a next chunk and one to refill) runs without a branch
-    // around its LDS reads, so the compiler's waits count exactly the reads in flight; the
-    // last two chunks are peeled.
-    int kt = 0;
-    for (; kt + 2 < KT; ++kt)
-      k_chunk<T, AKM, BKM, true, true>(fd, smem, kt, w, wm, lane, arow, brow, sw, fa, fb, acc);
-    if (kt + 1 < KT) {
-      k_chunk<T, AKM, BKM, true, false>(fd, smem, kt, w, wm, lane, arow, brow, sw, fa, fb, acc);
-      ++kt;
+    if (live) {
+      read_step<T, AKM, BKM>(smem, smem + SLOT, 0, arow, brow, lane, sw, fa[0], fb[0]);
+      // The steady state (chunks with a next chunk and one to refill) runs without a branch
+      // around its LDS reads, so the compiler's waits count exactly the reads in flight; the
+      // last two chunks are peeled.
+      int kt = 0;
+      for (; kt + 2 < KT; ++kt)
+        k_chunk<T, AKM, BKM, true, true>(fd, smem, kt, w, wm, lane, arow, brow, sw, fa, fb, acc);
+      if (kt + 1 < KT) {
+        k_chunk<T, AKM, BKM, true, false>(fd, smem, kt, w, wm, lane, arow, brow, sw, fa, fb,
+                                          acc);
+        ++kt;
+      }
+      // steps of the last chunk that hold k < K (all of them unless an operand is K-major)
+      const int ns = (AKM || BKM) ? min(BK / 16, (j.K - kt * BK + 15) / 16) : BK / 16;
+      k_chunk<T, AKM, BKM, false, false>(fd, smem, kt, w, wm, lane, arow, brow, sw, fa, fb, acc,
+                                         ns);
+    } else {
+      // the same loads and barriers as k_chunk, in the same order, without the MFMAs
+      for (int kt = 0; kt + 1 < KT; ++kt) {
+        MOE_WAIT_VMCNT(0);
+        lds_barrier_visible();
+        if (kt + 2 < KT) feed_issue<T, AKM, BKM>(fd, smem + (kt & 1) * T::STAGE, w, kt + 2);
+      }
     }
-    // steps of the last chunk that hold k < K (all of them unless an operand is K-major)
-    const int ns = (AKM || BKM) ? min(BK / 16, (j.K - kt * BK + 15) / 16) : BK / 16;
-    k_chunk<T, AKM, BKM, false, false>(fd, smem, kt, w, wm, lane, arow, brow, sw, fa, fb, acc,
-                                       ns);
   } else if (KT > 0) {
 #pragma unroll
     for (int p = 0; p < NST - 1; ++p) feed_issue<T, AKM, BKM>(fd, smem + p * T::STAGE, w, p);
@@ -821,16 +835,18 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_bf16_kernel(GemmArgs g) {
       lds_barrier();
       const int sf = st == 0 ? NST - 1 : st - 1;  // (kt + NST - 1) % NST
       feed_issue<T, AKM, BKM>(fd, smem + sf * T::STAGE, w, kt + NST - 1);
-      mma_chunk<T, AKM, BKM>(smem + st * T::STAGE, smem + st * T::STAGE + SLOT, arow, brow, lane,
-                             sw, acc);
+      if (live)
+        mma_chunk<T, AKM, BKM>(smem + st * T::STAGE, smem + st * T::STAGE + SLOT, arow, brow,
+                               lane, sw, acc);
       st = st == NST - 1 ? 0 : st + 1;
     }
 #pragma unroll
     for (int i = 0; i < NST - 1; ++i) {  // the last NST - 1 chunks: nothing left to issue
       wait_chunk(NST - 2 - i);
       lds_barrier();
-      mma_chunk<T, AKM, BKM>(smem + st * T::STAGE, smem + st * T::STAGE + SLOT, arow, brow, lane,
-                             sw, acc);
+      if (live)
+        mma_chunk<T, AKM, BKM>(smem + st * T::STAGE, smem + st * T::STAGE + SLOT, arow, brow,
+                               lane, sw, acc);
       st = st == NST - 1 ? 0 : st + 1;
     }
   }
