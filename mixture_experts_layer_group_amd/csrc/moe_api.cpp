@@ -247,6 +247,12 @@ struct TrainOut {
   void* z1sh;
 };
 
+// Tile order of GEMM 1 (forward, and the backward's recompute): 2 = expert-synchronous when
+// there are no shared experts and the weights of min(E, 8) experts exceed 256 MB, else 0.
+int esync_gemm1(int64_t E, int64_t Es, int64_t H1, int64_t M, int64_t esz) {
+  return !Es && std::min<int64_t>(E, 8) * H1 * M * esz > (int64_t{256} << 20) ? 2 : 0;
+}
+
 // check_only: run every host check and return without enqueueing anything.  train: also
 // store GEMM 1's pre-activations there (ReLU layers keep h only).
 int forward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* bg,
@@ -299,8 +305,10 @@ int forward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* b
                            static_cast<int>(H)};
   g1.p0.a_gather = reinterpret_cast<const int32_t*>(ws + L.tokrow);
   g1.nprob = 1;
-  // weights larger than the last-level cache (256 MB): expert-synchronous tile order
-  g1.plain = !Es && E * H1 * M * L.esz > (int64_t{256} << 20) ? 2 : 0;
+  // Expert-synchronous tile order when the weights of the 8 experts that the XCD ranges run
+  // at once (one per XCD) overflow the 256 MB last-level cache; otherwise the XCD ranges read
+  // every weight and every gathered row once.
+  g1.plain = esync_gemm1(E, Es, H1, M, L.esz);
   if (Es) {
     const char* w1sh = static_cast<const char*>(W1) + E * H1 * M * L.esz;
     g1.p1 = moe::GemmProblem{x, M, w1sh, M, 0, M, 0, ws + L.hsh, Es * H,
@@ -617,7 +625,7 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
   //    forward.
   const bool relu = c->act == MOE_ACT_RELU;
   // the forward GEMM 1's tile order (weights larger than the last-level cache)
-  const int plain1 = !Es && E * H1 * M * L.esz > (int64_t{256} << 20) ? 2 : 0;
+  const int plain1 = esync_gemm1(E, Es, H1, M, L.esz);
   if (saved) {
     // kept by the training forward
   } else if (relu) {

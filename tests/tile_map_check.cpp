@@ -249,8 +249,11 @@ int check_shape(const Shape& s, const std::vector<int>& cnt) {
   Problem g1;
   g1.name = "fwd GEMM 1";
   g1.routed = true; g1.tiles = tiles; g1.gather = true;
-  // the launcher's rule: no shared experts and weights larger than 256 MB
-  g1.plain = Es == 0 && E * H1 * M * (kBM == 256 ? 2 : 4) > (int64_t(256) << 20) ? 2 : 0;
+  // the launcher's rule: no shared experts and the weights of min(E, 8) experts (one per
+  // XCD under the XCD ranges) larger than 256 MB
+  g1.plain = Es == 0 &&
+                     std::min<int64_t>(E, 8) * H1 * M * (kBM == 256 ? 2 : 4) > (int64_t(256) << 20)
+                 ? 2 : 0;
   g1.N = H; g1.K = M; g1.lda = M; g1.ldb = M; g1.ldc = H; g1.b_stride = H1 * M;
   g1.gated_b = s.glu; g1.glu_h = s.glu ? (int)H : 0;
   g1.a_elems = N * M; g1.b_elems = (E + Es) * H1 * M; g1.c_elems = ra * H;
