@@ -115,6 +115,12 @@ EDGE = {
                                    zipf_s=0.5),
     "grouped_one_group": _cfg(n_experts=16, top_k=4, capacity=100, expert_groups=4,
                               topk_groups=1, act=2),
+    # rows of more than 1024 16-byte chunks: one token per combine block and several load
+    # rounds per lane; GEMM 1 over K = 9216 with a half-filled n-tile (d_ff = 128)
+    "wide_rows_bf16": _cfg(n_tokens=300, d_model=9216, d_ff=128, n_experts=4, capacity=60,
+                           act=1, n_groups=2),
+    "wide_rows_fp32": _cfg(dtype=0, n_tokens=200, d_model=4160, d_ff=64, n_experts=3,
+                           top_k=2, capacity=90, act=1),
 }
 
 
