@@ -60,6 +60,10 @@ constexpr bool kGemmPipelined = MOE_GEMM_PIPELINED;
 #define MOE_GEMM_STAGGER 1
 #endif
 constexpr bool kGemmStagger = MOE_GEMM_STAGGER;
+// fp32 output tiles (weight gradients) staged per wave instead of per block
+#ifndef MOE_GEMM_F32_WAVE_STAGING
+#define MOE_GEMM_F32_WAVE_STAGING 1
+#endif
 
 struct Job {
   const char* A;   // first row of the tile (bytes)
@@ -556,6 +560,46 @@ __device__ __forceinline__ void store_tile(const Job& j, f32x16 (&acc)[T::TN][T:
     if (GLU) return swish(acc[2 * jo][im][x]) * acc[2 * jo + 1][im][x];
     return act_fn<ACT>(acc[jo][im][x]);
   };
+#if MOE_GEMM_F32_WAVE_STAGING
+  if constexpr (F32 && DACT < 0 && RAW == 0) {
+    // fp32 tiles (the weight gradients): each wave stages its own 128 x 32 blocks, one column
+    // block jo at a time, in a private 16 KB region of the staging area and writes them back
+    // as whole 128-byte row segments, so no block barrier holds any wave and all eight waves
+    // stage at once.  Region rows are 128 bytes with their 16-byte columns XOR ((r >> 1) & 7):
+    // the writes (16 rows x one column per 16 lanes) and the reads (2 rows x 8 columns) are
+    // conflict-free.  A wave reads back only what it wrote, and its LDS operations complete
+    // in order, so the stores' use of each read is the only wait.
+    constexpr int RR = 128;   // bytes per region row: 32 fp32 columns
+    static_assert(STG >= T::NW * T::WTM * RR, "a private staging region per wave");
+    unsigned char* reg = stg + (t >> 6) * (T::WTM * RR);
+#pragma unroll
+    for (int jo = 0; jo < T::TN; ++jo) {
+#pragma unroll
+      for (int im = 0; im < T::TM; ++im) {
+        const int r = 32 * im + (lane & 31);
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const int sg = 2 * qd + (lane >> 5);   // 16-byte column of the region row
+          f32x4 v;
+#pragma unroll
+          for (int x = 0; x < 4; ++x) v[x] = acc[jo][im][4 * qd + x];
+          *reinterpret_cast<f32x4*>(reg + r * RR + ((sg ^ ((r >> 1) & 7)) << 4)) = v;
+        }
+      }
+      const int c0 = wn * (T::BN / T::WN) + 32 * jo;   // tile column of the block's column 0
+#pragma unroll
+      for (int q = 0; q < T::WTM / 8; ++q) {
+        const int r = 8 * q + (lane >> 3), sg = lane & 7;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(reg + r * RR + ((sg ^ ((r >> 1) & 7)) << 4));
+        const int row = wm * T::WTM + r, col = c0 + 4 * sg;
+        if (row < j.nrows && col < j.ncols)
+          __builtin_nontemporal_store(
+              v, reinterpret_cast<f32x4*>(j.C + static_cast<int64_t>(row) * j.ldc + col * 4));
+      }
+    }
+    return;
+  }
+#endif
   const int ncch = j.ncols / (F32 ? 4 : 8);   // valid 16-byte columns
   // Fused activation gradient, in batches of U row chunks per thread: every global load of a
   // batch (z, u for gated layers, h for the dot partials, the row scale) is issued before the
