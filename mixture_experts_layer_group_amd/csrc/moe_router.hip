@@ -5,13 +5,16 @@
 // the balance loss, the top-k weights and the top-k expert ids.  [Lec16] "MoE Kernel 优化":
 // the gating work (softmax, top-k, dispatch bookkeeping) runs fused in one kernel.
 //
-// One block = 1024 threads (16 waves) = 64 consecutive tokens of one group.
+// One block = 64 consecutive tokens of one group, on 1024 threads (16 waves, one block per
+// CU), or, for bf16 launches with more blocks than CUs and E <= 128, on 512 threads (8
+// waves) within 80 KB of LDS, so that two blocks share a CU and one's epilogue runs beside
+// the other's GEMM phase.
 //  1. GEMM on waves 0..3: x[64, M] . Wg[E, M]^T.  bf16: both operands stream global -> LDS
-//     directly (buffer_load ... lds) through 3-4 stages of 256- or 128-byte row chunks
+//     directly (buffer_load ... lds) through 2-4 stages of 256- or 128-byte row chunks
 //     (XOR-swizzled 16-byte columns) into v_mfma_f32_32x32x16_bf16 tiles, fp32
 //     accumulation.  fp32: plain FMA through an LDS staging area (fp32 MFMA and fp32
 //     vector peaks are equal on this chip).
-//  2. Epilogue, 16 lanes per token (all 16 waves): + bg, logits out, row max and sum of exp
+//  2. Epilogue, 16 (or 8) lanes per token (all waves): + bg, logits out, row max and sum of exp
 //     (fp32), top-k on the logits (ties to the lower expert index), gate weights (sum or
 //     p-norm), the random-routing decision in fp64, LDS histograms of selections and
 //     active slots per rank, the per-expert column sums of the softmax probabilities
@@ -25,12 +28,16 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 1024;       // 16 waves: all of them share the per-token epilogue
+// Launches with more router blocks than the chip has CUs (bf16, E <= 128): 8 waves and at
+// most 80 KB of LDS per block, so that two blocks share a CU and one block's epilogue runs
+// beside the other's GEMM phase.
+constexpr int kThreadsPair = 512;
+constexpr int kChipCUs = 256;
 constexpr int kGemmThreads = 256;    // the GEMM phase runs on waves 0..3
-constexpr int kLanesPerToken = kThreads / kRouteTokens;
 constexpr int kRowBytes = 256;  // bytes of K per LDS row per chunk
 
 }  // namespace
-__host__ __device__ int router_lds_stage_bytes(int dt, int epad);
+__host__ __device__ int router_lds_stage_bytes(int dt, int epad, int nt);
 namespace {
 
 __device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 7); }
@@ -64,13 +71,15 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // LDS layout of the bf16 router GEMM for EPAD padded experts and top-k <= 8: stages of
-// x[64] + Wg[EPAD] rows of ROWB bytes, within 160 KB together with the histograms.
-template <int EPAD>
+// x[64] + Wg[EPAD] rows of ROWB bytes, within LDSB bytes together with the histograms
+// (256-byte rows unless fewer than two such stages fit).
+template <int EPAD, int LDSB>
 struct RouterPipe {
-  static constexpr int kRowB = EPAD >= 256 ? 128 : 256;
-  static constexpr int kStage = (kRouteTokens + EPAD) * kRowB;
   static constexpr int kHist = EPAD * (1 + kMaxTopK) * 4;
-  static constexpr int kFit = (160 * 1024 - kHist) / kStage;
+  static constexpr int kRowB =
+      EPAD >= 256 || (LDSB - kHist) / ((kRouteTokens + EPAD) * 256) < 2 ? 128 : 256;
+  static constexpr int kStage = (kRouteTokens + EPAD) * kRowB;
+  static constexpr int kFit = (LDSB - kHist) / kStage;
   static constexpr int kStages = kFit >= 4 ? 4 : kFit;
   static constexpr int kXq = kRouteTokens * kRowB / 1024 / 4;  // x loads per wave per chunk
   static constexpr int kWq = EPAD * kRowB / 1024 / 4;          // Wg loads per wave per chunk
@@ -91,10 +100,10 @@ __device__ __forceinline__ int rswz(int r) {
 // several chunks are in flight while one is multiplied.  The 16-byte columns of each row are
 // XOR-permuted (rswz, applied on the global side) so fragment reads are conflict-free.  Rows
 // of x past the block's tokens and rows of Wg past E read as zeros (buffer bounds).
-template <int EPAD>
+template <int EPAD, int LDSB>
 __device__ void router_gemm_bf16(const RouterArgs& a, unsigned char* smem, float* lg, int ls,
                                  int tok0, int nt) {
-  using P = RouterPipe<EPAD>;
+  using P = RouterPipe<EPAD, LDSB>;
   constexpr int NST = P::kStages, STAGE = P::kStage, XQ = P::kXq, WQ = P::kWq;
   constexpr int ROWB = P::kRowB, CPR = ROWB / 16;
   constexpr int NTILE = 2 * (EPAD / 32);   // 2 token tiles x EPAD/32 expert tiles
@@ -249,9 +258,10 @@ __device__ void router_gemm_f32(const RouterArgs& a, unsigned char* stage, float
     if (i < ne) lg[tl * ls + eg + 4 * i] = acc[i];
 }
 
-template <int DT, int EPAD>
-__global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
+template <int DT, int EPAD, int NT>
+__global__ __launch_bounds__(NT, NT == kThreads ? 1 : 2) void router_kernel(RouterArgs a) {
   constexpr int epad = EPAD;
+  constexpr int LDSB = (NT == kThreads ? 160 : 80) * 1024;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int t = threadIdx.x;
   const int b = blockIdx.x;
@@ -261,23 +271,23 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
   const int E = a.E, k = a.k;
   const int ls = epad + 1;
   float* lg = reinterpret_cast<float*>(smem);
-  int* hsel = reinterpret_cast<int*>(smem + router_lds_stage_bytes(DT, epad));
+  int* hsel = reinterpret_cast<int*>(smem + router_lds_stage_bytes(DT, epad, NT));
   int* hact = hsel + epad;
-  for (int i = t; i < epad * (1 + k); i += kThreads) hsel[i] = 0;
+  for (int i = t; i < epad * (1 + k); i += NT) hsel[i] = 0;
 
   if (a.logits_in) {
-    for (int idx = t; idx < kRouteTokens * E; idx += kThreads) {
+    for (int idx = t; idx < kRouteTokens * E; idx += NT) {
       const int r = idx / E, e = idx - r * E;
       lg[r * ls + e] = r < nt ? a.logits_in[static_cast<size_t>(tok0 + r) * E + e] : 0.f;
     }
     __syncthreads();
   } else {
     if (DT == 1)
-      router_gemm_bf16<EPAD>(a, smem, lg, ls, tok0, nt);
+      router_gemm_bf16<EPAD, LDSB>(a, smem, lg, ls, tok0, nt);
     else
       router_gemm_f32(a, smem, lg, ls, tok0, nt, epad);
     __syncthreads();
-    for (int idx = t; idx < nt * E; idx += kThreads) {
+    for (int idx = t; idx < nt * E; idx += NT) {
       const int r = idx / E, e = idx - r * E;
       float v = lg[r * ls + e];
       if (a.bg) v += a.bg[e];
@@ -287,14 +297,14 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
     __syncthreads();
   }
 
-  // ---- per token: L = 16 consecutive lanes share one row of logits
-  constexpr int L = kLanesPerToken;
+  // ---- per token: L = 16 (or 8) consecutive lanes share one row of logits
+  constexpr int L = NT / kRouteTokens;
   const int tl = t / L, q = t % L;
   const bool valid = tl < nt;
   const int n = tok0 + tl;
   float* row = lg + tl * ls;
 
-  static_assert(L == 16, "one token per 16-lane DPP row");
+  static_assert(L == 16 || L == 8, "one token per 16- or 8-lane DPP group");
   // The lane's logits (experts q + L i) stay in registers for the max, the sum and top-k.
   constexpr int NV = EPAD / L;
   float rv[NV];
@@ -316,13 +326,14 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
 
   // Group-limited routing ([Lec16] "DeepSeek V3 MoE (670B)"): the E experts form n_eg
   // contiguous groups; a group scores its best logit, and the topk_eg best groups (ties to
-  // the lower index) stay open.  Lane q scores groups q and q + L.
-  uint32_t taken = 0;  // bit i <-> expert q + L i excluded (E <= 256 -> i < 16)
+  // the lower index) stay open.  Lane q scores groups q + L h (up to 32 groups).
+  uint32_t taken = 0;  // bit i <-> expert q + L i excluded (E <= 256 -> i < 32)
   if (a.n_eg > 1) {
     const int D = a.n_eg, gs = E / D;
-    float gv[2];
+    constexpr int NG = 32 / L;
+    float gv[NG];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < NG; ++h) {
       const int d = q + h * L;
       float v = -INFINITY;
       if (d < D)
@@ -337,7 +348,7 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
       float bv = -INFINITY;
       int bd = 0x7fffffff;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < NG; ++h) {
         const int d = q + h * L;
         if (d < D && !((open >> d) & 1u) && (gv[h] > bv || (gv[h] == bv && d < bd))) {
           bv = gv[h];
@@ -453,7 +464,7 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
 
   // Column sums of the probabilities: SPC consecutive lanes per expert, each summing every
   // SPC-th row in fp64, then a fixed butterfly over those lanes (deterministic).
-  constexpr int SPC = kThreads / EPAD;
+  constexpr int SPC = NT / EPAD;
   {
     const int e = t / SPC, part = t % SPC;
     double s = 0.0;
@@ -471,7 +482,7 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
       a.sel[o] = hsel[e];
     }
   }
-  for (int idx = t; idx < k * E; idx += kThreads) {
+  for (int idx = t; idx < k * E; idx += NT) {
     const int j = idx / E, e = idx - j * E;
     a.ahist[((static_cast<size_t>(g) * k + j) * E + e) * a.nbg + bi] = hact[j * epad + e];
   }
@@ -486,16 +497,17 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
   }
 }
 
-template <int DT, int EPAD>
+template <int DT, int EPAD, int NT>
 hipError_t launch_router_t(const RouterArgs& a, hipStream_t s, int grid) {
-  const size_t lds = router_lds_stage_bytes(DT, EPAD) + static_cast<size_t>(EPAD) * (1 + a.k) * 4;
+  const size_t lds =
+      router_lds_stage_bytes(DT, EPAD, NT) + static_cast<size_t>(EPAD) * (1 + a.k) * 4;
   static const bool attr = [] {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(&router_kernel<DT, EPAD>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&router_kernel<DT, EPAD, NT>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     return true;
   }();
   (void)attr;
-  hipLaunchKernelGGL((router_kernel<DT, EPAD>), dim3(grid), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL((router_kernel<DT, EPAD, NT>), dim3(grid), dim3(NT), lds, s, a);
   return hipGetLastError();
 }
 
@@ -503,12 +515,14 @@ hipError_t launch_router_t(const RouterArgs& a, hipStream_t s, int grid) {
 
 // LDS bytes before the histograms: the bf16 pipeline stages (or the fp32 staging area),
 // never less than the logits tile [64][epad + 1] floats that aliases them.
-__host__ __device__ int router_lds_stage_bytes(int dt, int epad) {
+__host__ __device__ int router_lds_stage_bytes(int dt, int epad, int nt) {
   int b = router_stage_bytes(epad);
-  if (dt == 1) {
-    const int rowb = epad >= 256 ? 128 : 256;
+  if (dt == 1) {   // the layout of RouterPipe<epad, budget>
+    const int budget = (nt == kThreads ? 160 : 80) * 1024;
+    const int hist = epad * (1 + kMaxTopK) * 4;
+    const int rowb = epad >= 256 || (budget - hist) / ((kRouteTokens + epad) * 256) < 2 ? 128 : 256;
     const int stage = (kRouteTokens + epad) * rowb;
-    const int fit = (160 * 1024 - epad * (1 + kMaxTopK) * 4) / stage;
+    const int fit = (budget - hist) / stage;
     b = (fit >= 4 ? 4 : fit) * stage;
   }
   const int lgb = kRouteTokens * (epad + 1) * 4;
@@ -521,15 +535,21 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
   if (grid == 0) return hipSuccess;
   const int e = epad <= 32 ? 32 : epad <= 64 ? 64 : epad <= 128 ? 128 : 256;
   if (a.dtype == 1) {
-    if (e == 32) return launch_router_t<1, 32>(a, s, grid);
-    if (e == 64) return launch_router_t<1, 64>(a, s, grid);
-    if (e == 128) return launch_router_t<1, 128>(a, s, grid);
-    return launch_router_t<1, 256>(a, s, grid);
+    // more router blocks than CUs: two blocks of 8 waves per CU
+    if (grid > kChipCUs && e <= 128) {
+      if (e == 32) return launch_router_t<1, 32, kThreadsPair>(a, s, grid);
+      if (e == 64) return launch_router_t<1, 64, kThreadsPair>(a, s, grid);
+      return launch_router_t<1, 128, kThreadsPair>(a, s, grid);
+    }
+    if (e == 32) return launch_router_t<1, 32, kThreads>(a, s, grid);
+    if (e == 64) return launch_router_t<1, 64, kThreads>(a, s, grid);
+    if (e == 128) return launch_router_t<1, 128, kThreads>(a, s, grid);
+    return launch_router_t<1, 256, kThreads>(a, s, grid);
   }
-  if (e == 32) return launch_router_t<0, 32>(a, s, grid);
-  if (e == 64) return launch_router_t<0, 64>(a, s, grid);
-  if (e == 128) return launch_router_t<0, 128>(a, s, grid);
-  return launch_router_t<0, 256>(a, s, grid);
+  if (e == 32) return launch_router_t<0, 32, kThreads>(a, s, grid);
+  if (e == 64) return launch_router_t<0, 64, kThreads>(a, s, grid);
+  if (e == 128) return launch_router_t<0, 128, kThreads>(a, s, grid);
+  return launch_router_t<0, 256, kThreads>(a, s, grid);
 }
 
 }  // namespace moe

@@ -121,6 +121,12 @@ EDGE = {
                            act=1, n_groups=2),
     "wide_rows_fp32": _cfg(dtype=0, n_tokens=200, d_model=4160, d_ff=64, n_experts=3,
                            top_k=2, capacity=90, act=1),
+    # more 64-token router blocks than the chip has CUs: the router's two-blocks-per-CU form
+    # (8 lanes per token), with 32 expert groups (four per lane) and with random routing
+    "pair_router_grouped": _cfg(n_tokens=16640, n_experts=128, top_k=4, capacity=700,
+                                expert_groups=32, topk_groups=4, act=2, zipf_s=0.7),
+    "pair_router_random": _cfg(n_tokens=16448, n_groups=4, n_experts=64, top_k=2,
+                               capacity=150, random_routing=1, act=1),
 }
 
 
