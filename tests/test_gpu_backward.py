@@ -155,6 +155,55 @@ def test_backward_deterministic():
         assert np.array_equal(a[key], b[key]), key
 
 
+def test_backward_from_two_threads_on_two_streams():
+    """Backward calls from two host threads, each on its own stream with its own workspace,
+    share the library's second stream (their enqueueing takes turns); every result equals the
+    sequential one bit for bit."""
+    import threading
+    h = harness()
+    prepared = []
+    for name in ("small_shared_top3", "small_swiglu_shared"):
+        cfg = configs.SMALL[name]
+        inp = synth.make_inputs(cfg)
+        dev = h.to_device(inp, cfg)
+        dy32, dybits = synth.upstream_grad(cfg)
+        dy = (torch.from_numpy(dybits.view(np.int16)).cuda().view(torch.bfloat16)
+              if dybits is not None else torch.from_numpy(dy32).cuda())
+        prepared.append((cfg, dev, dy))
+
+    def call(cfg, dev, dy, stream=None):
+        out, _ = binding.backward(cfg, dev["x"], dev["Wg"], dev["W1"], dev["W2"], dy,
+                                  bg=dev["bg"], u=dev["u"], stream=stream, **COEFS)
+        return out
+
+    ref = [call(*p) for p in prepared]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in prepared]
+    results = [[] for _ in prepared]
+    errors = []
+
+    def work(i):
+        try:
+            with torch.cuda.stream(streams[i]):
+                for _ in range(4):
+                    results[i].append(call(*prepared[i], stream=streams[i]))
+        except Exception as e:   # reported on the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(prepared))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i, outs in enumerate(results):
+        assert len(outs) == 4
+        for out in outs:
+            for key in ("dx", "dWg", "dbg", "dW1", "dW2"):
+                assert torch.equal(out[key].float(), ref[i][key].float()), (i, key)
+
+
 def test_backward_empty_batch():
     cfg = _cfg(n_tokens=0)
     meta = binding.alloc_meta(cfg)
