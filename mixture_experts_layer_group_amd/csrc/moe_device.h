@@ -29,36 +29,46 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
 }
 
-// erf(x) by Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26:
-// erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2), t = 1 / (1 + p x),
-// x >= 0, odd extension; |error| <= 1.5e-7.  One reciprocal and one exponential (hardware
-// v_rcp_f32 / v_exp_f32) instead of a general-purpose erf in the GEMM epilogues.
-__device__ __forceinline__ float erf_as7126(float x) {
-  const float ax = fabsf(x);
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
-  float p = fmaf(1.061405429f, t, -1.453152027f);
-  p = fmaf(p, t, 1.421413741f);
-  p = fmaf(p, t, -0.284496736f);
-  p = fmaf(p, t, 0.254829592f);
-  const float y = fmaf(-p * t, __expf(-ax * ax), 1.0f);
-  return copysignf(y, x);
+// erfc by Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26:
+// erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2), t = 1 / (1 + p x), x >= 0,
+// |error| <= 1.5e-7.  At x = |z| / sqrt 2 this gives the normal tail
+// Phi(-|z|) = erfc(|z| / sqrt 2) / 2 = (a1 t + ... + a5 t^5) / 2 exp(-z^2 / 2), which both
+// GELU and its derivative need: the 1 / sqrt 2 is folded into p and the 1/2 into the a_i.
+// az = |z|, e = exp(-z^2 / 2).  One hardware reciprocal (v_rcp_f32).
+__device__ __forceinline__ float normal_tail_as7126(float az, float e) {
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.70710678118654752440f, az, 1.0f));
+  float p = fmaf(0.5f * 1.061405429f, t, 0.5f * -1.453152027f);
+  p = fmaf(p, t, 0.5f * 1.421413741f);
+  p = fmaf(p, t, 0.5f * -0.284496736f);
+  p = fmaf(p, t, 0.5f * 0.254829592f);
+  return p * t * e;
 }
 
-// GELU in its erf form, 0.5 z (1 + erf(z / sqrt 2)).
+// exp(-z^2 / 2) as one v_exp_f32 (a power of two) of z^2 (-log2(e) / 2).
+__device__ __forceinline__ float exp_neg_half_sq(float z) {
+  return __builtin_amdgcn_exp2f(z * z * -0.72134752044448170368f);
+}
+
+// GELU in its erf form, z Phi(z) = 0.5 z (1 + erf(z / sqrt 2)), written for both signs at
+// once: z Phi(z) = max(z, 0) - |z| Phi(-|z|).
 __device__ __forceinline__ float gelu_erf(float z) {
-  return 0.5f * z * (1.0f + erf_as7126(z * 0.70710678118654752440f));
+  const float az = fabsf(z);
+  return fmaf(-az, normal_tail_as7126(az, exp_neg_half_sq(z)), fmaxf(z, 0.0f));
+}
+
+// GELU'(z) = Phi(z) + z phi(z), phi(z) = exp(-z^2 / 2) / sqrt(2 pi): the density's exponential
+// is the one the tail uses.
+__device__ __forceinline__ float gelu_grad(float z) {
+  const float e = exp_neg_half_sq(z);
+  const float q = normal_tail_as7126(fabsf(z), e);
+  const float Phi = z > 0.0f ? 1.0f - q : q;
+  return fmaf(z * 0.39894228040143267794f, e, Phi);
 }
 
 // Swish with beta = 1: z * sigmoid(z) = z / (1 + exp(-z)) (exp(-z) = inf for very negative z
 // gives -0).
 __device__ __forceinline__ float swish(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
-}
-
-// GELU'(z) = Phi(z) + z phi(z), Phi(z) = (1 + erf(z / sqrt 2)) / 2, phi the normal density.
-__device__ __forceinline__ float gelu_grad(float z) {
-  const float Phi = 0.5f * (1.0f + erf_as7126(z * 0.70710678118654752440f));
-  return Phi + z * 0.39894228040143267794f * __expf(-0.5f * z * z);
 }
 
 // d/dz z sigmoid(z) = sigmoid(z) (1 + z (1 - sigmoid(z))).
