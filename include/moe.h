@@ -21,8 +21,8 @@
  *     asynchronously on it; outputs are valid once the stream has been synchronised.
  *   - The library allocates no device memory and keeps no pointer after returning; calls
  *     with distinct workspaces may run concurrently.  Its only state: moe_forward_noalloc's
- *     static scratch array (one per GPU, see there), and the second stream of the backward
- *     calls (one per GPU, see moe_backward).
+ *     static scratch array (one per GPU, see there), and the two side streams of the
+ *     backward calls (per GPU, see moe_backward).
  *   - Return value: MOE_OK (0) or a negative MOE_E* code.  All argument checks run on the
  *     host before anything is enqueued; a call that fails them enqueues nothing and writes
  *     nothing.  MOE_EHIP reports a launch error (hipGetLastError) after enqueueing.
@@ -249,12 +249,12 @@ int moe_backward_workspace_size(const moe_cfg* cfg, size_t* bytes);
  * Transformer"; [Lec16] "DeepSeek V3 MoE (670B)" for the gated form), the gate
  * normalisation and the softmax.  The routing and the expert activations are recomputed
  * from the inputs (the results match a moe_forward of the same inputs bit for bit).
- * Streams: the weight-gradient GEMMs run on a second stream of the current GPU, forked from
- * `stream` and joined back into it before the call returns, so every output is ordered on
- * `stream` as usual.  The library creates that stream and three events on the first
- * backward call on a GPU and keeps them until the process ends; backward calls from several
- * host threads take turns while they enqueue, and their second-stream work runs in the order
- * of the calls.
+ * Streams: the two weight-gradient GEMMs run on two side streams of the current GPU, each
+ * forked from `stream` once its inputs are enqueued and joined back into it before the call
+ * returns, so every output is ordered on `stream` as usual.  The library creates those
+ * streams and four events on the first backward call on a GPU and keeps them until the
+ * process ends; backward calls from several host threads take turns while they enqueue, and
+ * their side-stream work runs in the order of the calls.
  *   x, Wg, bg, W1, W2, u   as in moe_forward
  *   dy        [N, M] T      upstream gradient of y
  *   coef_*    host floats (finite) weighting the three auxiliary losses

@@ -358,29 +358,31 @@ int forward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* b
 
 // ---------------------------------------------------------------------------- backward
 
-// The backward's second stream.  The weight gradients of the two expert GEMMs depend only on
+// The backward's side streams.  The weight gradients of the two expert GEMMs depend only on
 // activations the chain has already produced (dW2 on h and dout, dW1 on dz and the dispatched
-// rows), not on the dgrad kernels after them, so they run on this stream beside those
-// kernels: their fp32 tile stores, which leave the MFMA pipes idle, overlap compute-bound
-// work.  One non-blocking, default-priority stream and three timing-free events per device,
-// created on first use and kept until the process ends.  A backward call holds the mutex
-// while it enqueues, so calls from several host threads do not interleave their records.
+// rows), not on the dgrad kernels after them, so each runs on a stream of its own beside
+// those kernels, from the moment its inputs exist: their fp32 tile stores, which leave the
+// MFMA pipes idle, overlap compute-bound work.  Two non-blocking, default-priority streams and
+// four timing-free events per device, created on first use and kept until the process ends.
+// A backward call holds the mutex while it enqueues, so calls from several host threads do
+// not interleave their records.
 struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t ev[3] = {};
+  hipStream_t s[2] = {};
+  hipEvent_t ev[4] = {};
 };
 constexpr int kMaxDevices = 64;
 std::mutex g_side_mu;
 SideStream g_side[kMaxDevices];
 
-// The current device's side stream (created if needed); the caller holds g_side_mu.
+// The current device's side streams (created if needed); the caller holds g_side_mu.
 int side_stream(SideStream** out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_EHIP;
   SideStream& ss = g_side[dev];
-  if (!ss.s) {
+  if (!ss.s[0]) {
     SideStream n;
-    if (hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking) != hipSuccess) return MOE_EHIP;
+    for (hipStream_t& st : n.s)
+      if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return MOE_EHIP;
     for (hipEvent_t& e : n.ev)
       if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return MOE_EHIP;
     ss = n;
@@ -389,27 +391,30 @@ int side_stream(SideStream** out) {
   return MOE_OK;
 }
 
-// Fork / join of the side stream: fork(i) makes the side stream wait for what the main stream
+// Fork / join of the side streams: fork(i) makes side stream i wait for what the main stream
 // has enqueued so far; the join (at the latest when this object goes out of scope, error
-// paths included) makes the main stream wait for everything enqueued on the side stream.
+// paths included) makes the main stream wait for everything enqueued on both.
 struct SideFork {
   SideStream* ss = nullptr;
   hipStream_t main = nullptr;
-  bool open = false;
+  bool open[2] = {false, false};
   int fork(int i) {
     if (hipEventRecord(ss->ev[i], main) != hipSuccess ||
-        hipStreamWaitEvent(ss->s, ss->ev[i], 0) != hipSuccess)
+        hipStreamWaitEvent(ss->s[i], ss->ev[i], 0) != hipSuccess)
       return MOE_EHIP;
-    open = true;
+    open[i] = true;
     return MOE_OK;
   }
   int join() {
-    if (!open) return MOE_OK;
-    open = false;
-    if (hipEventRecord(ss->ev[2], ss->s) != hipSuccess ||
-        hipStreamWaitEvent(main, ss->ev[2], 0) != hipSuccess)
-      return MOE_EHIP;
-    return MOE_OK;
+    int rc = MOE_OK;
+    for (int i = 0; i < 2; ++i) {
+      if (!open[i]) continue;
+      open[i] = false;
+      if (hipEventRecord(ss->ev[2 + i], ss->s[i]) != hipSuccess ||
+          hipStreamWaitEvent(main, ss->ev[2 + i], 0) != hipSuccess)
+        rc = MOE_EHIP;
+    }
+    return rc;
   }
   ~SideFork() { join(); }
 };
@@ -572,7 +577,7 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
   rc = side_stream(&side.ss);
   if (rc) return rc;
   side.main = s;
-  const hipStream_t s2 = side.ss->s;
+  const hipStream_t s2 = side.ss->s[0], s3 = side.ss->s[1];
 
   Run r;
   r.c = c;
@@ -657,10 +662,10 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
       if (rc) return rc;
     }
   }
-  // 6a. (side stream, beside steps 3-5) dW2_e [M, H] = dout_e^T h_e; shared q: dy^T hsh_q over
-  //     token ranges into fp32 partials, summed in range order.  Weight gradients are fp32
-  //     batched GEMMs over the experts with K = the expert's kept rows (shared experts: all
-  //     tokens), every operand read in place as a K-major operand.
+  // 6a. (first side stream, beside steps 3-5) dW2_e [M, H] = dout_e^T h_e; shared q: dy^T hsh_q
+  //     over token ranges into fp32 partials, summed in range order.  Weight gradients are
+  //     fp32 batched GEMMs over the experts with K = the expert's kept rows (shared experts:
+  //     all tokens), every operand read in place as a K-major operand.
   {
     if ((rc = side.fork(0))) return rc;
     auto q0 = batched_problem(ws + B.dout, M, ws + L.h, H, dW2, H, static_cast<int>(H),
@@ -699,6 +704,24 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
     p1.z = relu ? ws + L.hsh : ws + B.z1sh;
     rc = gemm(p0, Es ? &p1 : nullptr);
     if (rc) return rc;
+  }
+  // 6b. (second side stream, forked as soon as dz exists) dW1_e [H1, M] = dz1_e^T buf_e;
+  //     shared q: dz1sh_q^T x over token ranges into partials
+  {
+    if ((rc = side.fork(1))) return rc;
+    auto w0 = batched_problem(ws + B.dz1, H1, ws + L.buf, M, dW1, M, static_cast<int>(M),
+                              static_cast<int>(H1), static_cast<int>(E), BM, sa.dw1, true);
+    auto w1 = batched_problem(ws + B.dz1sh, Es * H1, x, M, shp1, M, static_cast<int>(M),
+                              static_cast<int>(H1), nsh, BM, sa.dw1 + E, true);
+    w0.a_kmajor = w0.b_kmajor = w1.a_kmajor = w1.b_kmajor = 1;
+    if ((rc = gemm(w0, Es ? &w1 : nullptr, s3))) return rc;
+    for (int64_t q = 0; q < Es; ++q)
+      if ((rc = status_of(moe::launch_split_reduce(shp1 + q * B.nshared * H1 * M,
+                                                   dW1 + (E + q) * H1 * M, H1 * M,
+                                                   static_cast<int>(B.nshared), s3))))
+        return rc;
+  }
+  {
     // dw_nj = sum of the row's n-tile partials (0 for dropped slots)
     rc = status_of(moe::launch_dw_reduce(m->row, dwp, reinterpret_cast<float*>(ws + B.dw),
                                          N * k, static_cast<int>(B.ntn), s));
@@ -722,22 +745,6 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
                            static_cast<int>(B.Ep), dt};
     rc = status_of(moe::launch_router_dgrad_prep(pa, s));
     if (rc) return rc;
-  }
-  // 6b. (side stream, after 6a) dW1_e [H1, M] = dz1_e^T buf_e; shared q: dz1sh_q^T x over
-  //     token ranges into partials
-  {
-    if ((rc = side.fork(1))) return rc;
-    auto w0 = batched_problem(ws + B.dz1, H1, ws + L.buf, M, dW1, M, static_cast<int>(M),
-                              static_cast<int>(H1), static_cast<int>(E), BM, sa.dw1, true);
-    auto w1 = batched_problem(ws + B.dz1sh, Es * H1, x, M, shp1, M, static_cast<int>(M),
-                              static_cast<int>(H1), nsh, BM, sa.dw1 + E, true);
-    w0.a_kmajor = w0.b_kmajor = w1.a_kmajor = w1.b_kmajor = 1;
-    if ((rc = gemm(w0, Es ? &w1 : nullptr, s2))) return rc;
-    for (int64_t q = 0; q < Es; ++q)
-      if ((rc = status_of(moe::launch_split_reduce(shp1 + q * B.nshared * H1 * M,
-                                                   dW1 + (E + q) * H1 * M, H1 * M,
-                                                   static_cast<int>(B.nshared), s2))))
-        return rc;
   }
   // 4. dx rows = dz W1_e (routed); shared: dz_sh W1_sh over k = (q, h'), whose K-major rows
   //    are the consecutive rows of W1_{E..E+Es-1}.  The router term dxrt = dl Wg reads Wg
@@ -771,7 +778,7 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
     rc = status_of(moe::launch_dbg(wa, s));
     if (rc) return rc;
   }
-  // 6c. dWg, then the join with the side stream
+  // 6c. dWg, then the join with the side streams
   {
     // dWg [E, M] = dl^T x: token ranges into fp32 partials, then their sum in range order
     float* part = reinterpret_cast<float*>(ws + B.dwgp);
