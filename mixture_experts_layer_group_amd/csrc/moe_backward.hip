@@ -142,12 +142,16 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(RouterBwdArgs a) {
   se = wave_sum(se);
   const float lse = mx + logf(se);
 
-  // gradient of the selected probabilities through the normalisation
+  // gradient of the selected probabilities through the normalisation: with w_j = ps_j / D,
+  // D = (sum_i ps_i^P)^(1/P) (sum: P = 1), dps_i = (dw_i - w_i^(P-1) sum_j w_j dw_j) / D.
+  // Written this way the two terms cancel exactly where the weights do not depend on the
+  // logits; a single selected expert under either normalisation has weight 1 whatever the
+  // logits, so it passes no gradient at all (the difference of two separately rounded
+  // quotients would leak dw's size times the rounding into dl).
   float dps[kMaxTopK];
   int sel[kMaxTopK];
   {
     float ps[kMaxTopK], dw[kMaxTopK];
-    float s = 0.0f, D = 0.0f;
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) {
       sel[j] = -1;
@@ -156,22 +160,27 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(RouterBwdArgs a) {
         sel[j] = a.topk_idx[static_cast<int64_t>(n) * k + j];
         ps[j] = expf(l[sel[j]] - mx) / se;
         dw[j] = a.dw[static_cast<int64_t>(n) * k + j];
-        s += dw[j] * ps[j];
       }
     }
     if (a.norm == 0) {
 #pragma unroll
       for (int j = 0; j < kMaxTopK; ++j) dps[j] = dw[j];
-    } else {
+    } else if (k > 1) {
       const float P = a.norm == 1 ? 1.0f : a.norm_p;
+      float D = 0.0f;
 #pragma unroll
       for (int j = 0; j < kMaxTopK; ++j)
         if (j < k) D += a.norm == 1 ? ps[j] : powf(ps[j], P);
       if (a.norm == 2) D = powf(D, 1.0f / P);
-      const float c = a.norm == 1 ? s / (D * D) : s * powf(D, -1.0f - P);
+      float w[kMaxTopK], t = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j) {
+        w[j] = j < k ? ps[j] / D : 0.0f;
+        t = fmaf(w[j], dw[j], t);
+      }
 #pragma unroll
       for (int j = 0; j < kMaxTopK; ++j)
-        if (j < k) dps[j] = dw[j] / D - (a.norm == 1 ? 1.0f : powf(ps[j], P - 1.0f)) * c;
+        if (j < k) dps[j] = (dw[j] - (a.norm == 1 ? t : powf(w[j], P - 1.0f) * t)) / D;
     }
   }
   const int g = n / a.S;

@@ -119,6 +119,13 @@ EDGE = {
     "one_token": _cfg(n_tokens=1, capacity=1),
     "bare_pnorm_topk8": _cfg(n_experts=16, top_k=8, capacity=64, residual=0, gate_norm=2,
                              norm_p=2.0, expert_groups=4, topk_groups=2),
+    # one selected expert under a normalisation: its weight is 1 whatever the logits, so the
+    # router gradient is the balance and z losses' alone (small next to dw)
+    "top1_sum_norm": _cfg(n_experts=5, top_k=1, capacity=72, gate_norm=1, act=2,
+                          n_groups=4, n_tokens=1356),
+    "top1_pnorm_fp32_shared": _cfg(dtype=0, n_experts=6, top_k=1, capacity=137, gate_norm=2,
+                                   norm_p=3.0, n_shared=2, d_model=192, d_ff=64, act=1,
+                                   n_groups=4, n_tokens=1652, expert_groups=2, topk_groups=1),
 }
 
 
