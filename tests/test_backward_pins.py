@@ -204,7 +204,7 @@ def test_planted_backward_mistakes_are_caught(name, monkeypatch):
     assert caught, f"mutant {name} passed every finite-difference check"
 
 
-# ---- the acceptance bound of the GPU test's ReLU dW1 comparison (tests/relu_slack.py)
+# ---- the acceptance bounds of the GPU test's ReLU dW1 and dx comparisons (tests/relu_slack.py)
 
 def _relu_flip_case(threshold, monkeypatch):
     """dW1 of the oracle whose ReLU' is 1 only for z > threshold (every decision at
@@ -215,27 +215,32 @@ def _relu_flip_case(threshold, monkeypatch):
     inp = synth.make_inputs(cfg)
     dy, _ = synth.upstream_grad(cfg)
     ref = mb.layer_backward(cfg, inp.x, inp.Wg, inp.bg, inp.W1, inp.W2, inp.u, dy)
-    slack, n_amb = relu_slack.relu_decision_slack(cfg, inp, ref["routing"], dy)
+    slack, slack_dx, n_amb = relu_slack.relu_slacks(cfg, inp, ref["routing"], dy)
     orig = mb.act_grad
     monkeypatch.setattr(mb, "act_grad", lambda z, act: (np.asarray(z) > threshold).astype(
         np.float64) if act == 0 else orig(z, act))
     flipped = mb.layer_backward(cfg, inp.x, inp.Wg, inp.bg, inp.W1, inp.W2, inp.u, dy)
-    return ref["dW1"], flipped["dW1"], slack, n_amb
+    return ([(ref["dW1"], flipped["dW1"], slack), (ref["dx"], flipped["dx"], slack_dx)],
+            n_amb)
 
 
 def test_relu_slack_accepts_flips_of_ambiguous_decisions(monkeypatch):
     """Flipping every ReLU decision with |z| below the ambiguity threshold stays inside the
-    bound, and there are such decisions in the layer (so the case is not vacuous)."""
+    dW1 and dx bounds, and there are such decisions in the layer (so the case is not
+    vacuous)."""
     import relu_slack
-    a, b, slack, n_amb = _relu_flip_case(0.5 * relu_slack.RELU_DELTA, monkeypatch)
-    d = np.abs(a - b)
-    assert n_amb > 0 and d.max() > 0
-    assert (d <= slack + 1e-12 * np.abs(a).max()).all()
+    pairs, n_amb = _relu_flip_case(0.5 * relu_slack.RELU_DELTA, monkeypatch)
+    assert n_amb > 0
+    for a, b, slack in pairs:
+        d = np.abs(a - b)
+        assert d.max() > 0
+        assert (d <= slack + 1e-12 * np.abs(a).max()).all()
 
 
 def test_relu_slack_rejects_flips_beyond_it(monkeypatch):
     """Planted mistake: ReLU' cut at z > 1e-2 (decisions far outside the fp32 accumulation
-    error) moves dW1 beyond the bound plus the bf16 tolerance."""
-    a, b, slack, _ = _relu_flip_case(1e-2, monkeypatch)
-    excess = np.abs(a - b) - 1.02 * slack
-    assert excess.max() / np.abs(a).max() > 2e-2
+    error) moves dW1 and dx beyond the bound plus the bf16 tolerance."""
+    pairs, _ = _relu_flip_case(1e-2, monkeypatch)
+    for a, b, slack in pairs:
+        excess = np.abs(a - b) - 1.02 * slack
+        assert excess.max() / np.abs(a).max() > 2e-2
