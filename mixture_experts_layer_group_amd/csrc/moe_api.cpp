@@ -643,24 +643,23 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
     rc = gemm(p0, Es ? &p1 : nullptr, nullptr, plain1);
     if (rc) return rc;
   } else {
-    auto p0 = routed_problem(ws + L.buf, M, W1, M, H1 * M, ws + B.z1, H1, static_cast<int>(H1),
+    // the training forward's GEMM 1: h from the fp32 accumulators through the forward's own
+    // activation epilogue, and the pre-activations z1 beside it, so that the recomputed h is
+    // the forward's bit for bit (an activation applied to the rounded z1 afterwards would not
+    // be)
+    auto p0 = routed_problem(ws + L.buf, M, W1, M, H1 * M, ws + L.h, H, static_cast<int>(H),
                              static_cast<int>(M), a_rows, L, tiles, ntiles);
-    auto p1 = dense_problem(x, M, W1c + E * H1 * M * esz, M, ws + B.z1sh, Es * H1,
-                            static_cast<int>(Es * H1), static_cast<int>(M),
+    auto p1 = dense_problem(x, M, W1c + E * H1 * M * esz, M, ws + L.hsh, Es * H,
+                            static_cast<int>(Es * H), static_cast<int>(M),
                             static_cast<int>(N), BM);
+    p0.act = p1.act = c->act;
+    p0.glu_h = p1.glu_h = static_cast<int>(H);
+    p0.zout = ws + B.z1;
+    p0.ldz = H1;
+    p1.zout = ws + B.z1sh;
+    p1.ldz = Es * H1;
     rc = gemm(p0, Es ? &p1 : nullptr, nullptr, plain1);
     if (rc) return rc;
-    moe::BwdEltArgs ea{};
-    ea.z = ws + B.z1; ea.h = ws + L.h; ea.rows_ptr = Rdev; ea.nexp = 1;
-    ea.H = static_cast<int>(H); ea.act = c->act; ea.dtype = dt;
-    rc = status_of(moe::launch_act_fwd(ea, L.Rmax * H, s));
-    if (rc) return rc;
-    if (Es) {
-      ea.z = ws + B.z1sh; ea.h = ws + L.hsh; ea.rows_ptr = nullptr;
-      ea.rows = static_cast<int>(N); ea.nexp = static_cast<int>(Es);
-      rc = status_of(moe::launch_act_fwd(ea, N * Es * H, s));
-      if (rc) return rc;
-    }
   }
   // 6a. (first side stream, beside steps 3-5) dW2_e [M, H] = dout_e^T h_e; shared q: dy^T hsh_q
   //     over token ranges into fp32 partials, summed in range order.  Weight gradients are

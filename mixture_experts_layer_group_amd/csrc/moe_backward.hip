@@ -20,21 +20,11 @@ namespace moe {
 namespace {
 
 template <int DT>
-__device__ __forceinline__ float ld_elem(const void* p, int64_t i) {
-  if (DT == 1) return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
-  return static_cast<const float*>(p)[i];
-}
-
-template <int DT>
 __device__ __forceinline__ void st_elem(void* p, int64_t i, float v) {
   if (DT == 1)
     static_cast<uint16_t*>(p)[i] = f32_to_bf16(v);
   else
     static_cast<float*>(p)[i] = v;
-}
-
-__device__ __forceinline__ int rows_of(const BwdEltArgs& a) {
-  return a.rows_ptr ? *a.rows_ptr : a.rows;
 }
 
 // 16-byte vectors of the layer dtype: 8 bf16 or 4 fp32 values.
@@ -62,39 +52,6 @@ struct Vec {
     *reinterpret_cast<u32x4*>(static_cast<char*>(p) + i * (DT == 1 ? 2 : 4)) = w;
   }
 };
-
-// h = act(z) from the pre-activations: per row, nexp blocks of H1 inputs -> H outputs
-// (gated: h = Swish(g) * u with g, u the two halves of the block); 16 bytes per thread.
-template <int DT>
-__global__ __launch_bounds__(256) void act_fwd_kernel(BwdEltArgs a) {
-  constexpr int V = Vec<DT>::N;
-  const int rows = rows_of(a);
-  const int64_t W = static_cast<int64_t>(a.nexp) * a.H;
-  const int64_t total = static_cast<int64_t>(rows) * W / V;
-  const int H1 = a.act == kActSwiglu ? 2 * a.H : a.H;
-  for (int64_t iv = blockIdx.x * 256ll + threadIdx.x; iv < total; iv += static_cast<int64_t>(gridDim.x) * 256) {
-    const int64_t i = iv * V;
-    const int64_t r = i / W;
-    const int c = static_cast<int>(i - r * W);
-    const int q = c / a.H, cc = c - q * a.H;
-    const int64_t zi = r * a.nexp * H1 + static_cast<int64_t>(q) * H1 + cc;
-    Vec<DT> z, h;
-    z.load(a.z, zi);
-    if (a.act == kActSwiglu) {
-      Vec<DT> u;
-      u.load(a.z, zi + a.H);
-#pragma unroll
-      for (int x = 0; x < V; ++x) h.v[x] = swish(z.v[x]) * u.v[x];
-    } else if (a.act == kActGelu) {
-#pragma unroll
-      for (int x = 0; x < V; ++x) h.v[x] = gelu_erf(z.v[x]);
-    } else {
-#pragma unroll
-      for (int x = 0; x < V; ++x) h.v[x] = fmaxf(z.v[x], 0.0f);
-    }
-    h.store(a.h, i);
-  }
-}
 
 // One block: the batched GEMM entries of the weight gradients, which read the compact
 // buffers, x and dl in place as K-major operands (K = rows of the expert, or tokens).
@@ -367,15 +324,6 @@ int grid_for(int64_t n) {
 }
 
 }  // namespace
-
-hipError_t launch_act_fwd(const BwdEltArgs& a, int64_t max_elems, hipStream_t s) {
-  if (max_elems == 0) return hipSuccess;
-  if (a.dtype == 1)
-    hipLaunchKernelGGL(act_fwd_kernel<1>, dim3(grid_for(max_elems)), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(act_fwd_kernel<0>, dim3(grid_for(max_elems)), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
 
 hipError_t launch_bwd_setup(const BwdSetupArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(bwd_setup_kernel, dim3(1), dim3(256), 0, s, a);

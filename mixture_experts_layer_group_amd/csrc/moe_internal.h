@@ -171,13 +171,6 @@ struct EmptyArgs {         // N == 0: zero the small outputs (aux, z_loss, dev_l
 
 // ---- backward pass (moe_backward.hip)
 
-struct BwdEltArgs {        // elementwise activation over rows (the backward's recompute)
-  const void* z;           // [rows, nexp * H1] pre-activations (H1 = 2H for gated experts)
-  void* h;                 // [rows, nexp * H] activations
-  const int32_t* rows_ptr; // device row count (nullptr: rows)
-  int rows, nexp, H, act, dtype;
-};
-
 
 struct BwdSetupArgs {      // batched GEMM entries of the backward (built on the device)
   const int32_t* offset;   // [E+1] expert offsets of the compact buffer
@@ -211,7 +204,6 @@ struct RouterPrepArgs {    // dlp [N, Ep] = dl in the layer dtype, zero beyond E
   int N, E, Ep, dtype;
 };
 
-hipError_t launch_act_fwd(const BwdEltArgs& a, int64_t max_elems, hipStream_t s);
 hipError_t launch_bwd_setup(const BwdSetupArgs& a, hipStream_t s);
 hipError_t launch_router_bwd(const RouterBwdArgs& a, hipStream_t s);
 hipError_t launch_dbg(const DwgArgs& a, hipStream_t s);
