@@ -146,6 +146,15 @@ def z_loss_grad(l, p, coef_z):
     return coef_z * 2.0 * lse * p / N
 
 
+def router_backward(cfg, p, idx, lr, dw, coef_aux=0.0, coef_z=0.0, coef_dev=0.0):
+    """dL/dl [N, E] from the combine weights' gradient dw [N, k]: through the gate weights
+    (gate_weight_grad), plus the balance losses, then the softmax, plus the z-loss.  p: the
+    softmax probabilities, idx: the selection, lr: the logits (float64)."""
+    dp = gate_weight_grad(p, idx, cfg["gate_norm"], cfg.get("norm_p", 1.0), dw)
+    dp += balance_grad(cfg, idx, coef_aux, coef_dev)
+    return softmax_grad(p, dp) + z_loss_grad(lr, p, coef_z)
+
+
 def layer_backward(cfg, x, Wg, bg, W1, W2, u, dy, coef_aux=0.0, coef_z=0.0, coef_dev=0.0,
                    logits=None, exact=False):
     """Gradients of L (module docstring) with respect to x, Wg, bg, W1, W2.
@@ -192,10 +201,7 @@ def layer_backward(cfg, x, Wg, bg, W1, W2, u, dy, coef_aux=0.0, coef_z=0.0, coef
         dW1[E + q] += dW1e
         dW2[E + q] += dW2e
 
-    # router: gate weights, balance losses, softmax, z-loss
-    dp = gate_weight_grad(p, idx, cfg["gate_norm"], cfg.get("norm_p", 1.0), dw)
-    dp += balance_grad(cfg, idx, coef_aux, coef_dev)
-    dl = softmax_grad(p, dp) + z_loss_grad(lr, p, coef_z)
+    dl = router_backward(cfg, p, idx, lr, dw, coef_aux, coef_z, coef_dev)
     dWg = dl.T @ x
     dbg = dl.sum(axis=0)
     dx += dl @ np.asarray(Wg, np.float64)

@@ -244,3 +244,42 @@ def test_relu_slack_rejects_flips_beyond_it(monkeypatch):
     for a, b, slack in pairs:
         excess = np.abs(a - b) - 1.02 * slack
         assert excess.max() / np.abs(a).max() > 2e-2
+
+
+# ---- the rounded-dw router reference of the GPU test's bf16 dWg / dbg (tests/router_ref.py)
+
+def _router_ref_case(name):
+    from mixture_experts_layer_group_amd import configs, synth
+    from oracle import moe_oracle as mo
+    cfg = configs.SMALL[name]
+    inp = synth.make_inputs(cfg)
+    dy, _ = synth.upstream_grad(cfg)
+    logits = np.asarray(mo.router_logits(inp.x, inp.Wg, inp.bg), np.float32)
+    ref = mb.layer_backward(cfg, inp.x, inp.Wg, inp.bg, inp.W1, inp.W2, inp.u, dy,
+                            logits=logits, **COEFS)
+    return cfg, inp, dy, logits, ref
+
+
+@pytest.mark.parametrize("name", ["small_shared_top3", "small_swiglu_shared", "small_top2_rr"])
+def test_router_ref_unrounded_is_the_oracle(name):
+    """Without the rounding the reference's dw, dWg and dbg are the oracle's own (so its row
+    bookkeeping, activations and chain are the oracle's)."""
+    import router_ref
+    cfg, inp, dy, logits, ref = _router_ref_case(name)
+    dw = router_ref.dw_of(cfg, inp, ref["routing"], dy, rounded=False)
+    assert np.abs(dw - ref["dw"]).max() <= 1e-12 * np.abs(ref["dw"]).max()
+    dWg, dbg, _ = router_ref.router_grads(cfg, inp, ref["routing"], dy, logits, COEFS,
+                                          rounded=False)
+    assert np.abs(dWg - ref["dWg"]).max() <= 1e-12 * np.abs(ref["dWg"]).max()
+    assert np.abs(dbg - ref["dbg"]).max() <= 1e-12 * np.abs(ref["dWg"]).max()
+
+
+@pytest.mark.parametrize("name", ["small_shared_top3", "small_swiglu_shared"])
+def test_router_ref_rounding_moves_dw_by_bf16_amounts(name):
+    """The rounded dw differs from the exact one (the reference is not the plain oracle), by
+    bf16-sized amounts."""
+    import router_ref
+    cfg, inp, dy, logits, ref = _router_ref_case(name)
+    dw = router_ref.dw_of(cfg, inp, ref["routing"], dy)
+    d = np.abs(dw - ref["dw"]).max() / np.abs(ref["dw"]).max()
+    assert 0.0 < d <= 2e-2

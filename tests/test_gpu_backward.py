@@ -11,6 +11,7 @@ import pytest
 from mixture_experts_layer_group_amd import binding, configs, synth
 
 import relu_slack
+import router_ref
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -78,14 +79,20 @@ def check(cfg, coefs=COEFS, seed=None, saved=False):
         assert np.array_equal(np.asarray(g["meta"][f]).astype(np.int64),
                               np.asarray(r[f]).astype(np.int64)), f
     tol = G_TOL[cfg["dtype"]]
-    errs = {}
-    for key in ("dWg", "dW2"):
-        errs[key] = h.rel_err(g[key], ref[key])
+    errs = {"dW2": h.rel_err(g["dW2"], ref["dW2"])}
+    # dWg and dbg: bf16 layers against the oracle's router chain on the dw of bf16-rounded
+    # activations (tests/router_ref.py), fp32 layers against the oracle as it is
+    if cfg["dtype"] == 1:
+        rWg, rbg, rdl = router_ref.router_grads(cfg, inp, r, dy, logits, coefs)
+    else:
+        rWg, rbg, rdl = ref["dWg"], ref["dbg"], ref["dlogits"]
+    errs["dWg"] = h.rel_err(g["dWg"], rWg)
+    errs["dWg_plain"] = h.rel_err(g["dWg"], ref["dWg"])
     # dbg sums dl over the tokens, so its error is bounded relative to the sum of the terms'
     # magnitudes; the terms cancel (exactly for one expert, whose softmax has no gradient, and
     # in opposite pairs for two), which a bound relative to max |dbg| alone would measure
-    scale = np.abs(ref["dlogits"]).sum(axis=0).max()
-    errs["dbg"] = float(np.abs(g["dbg"] - ref["dbg"]).max() / (scale if scale > 0 else 1.0))
+    scale = np.abs(rdl).sum(axis=0).max()
+    errs["dbg"] = float(np.abs(g["dbg"] - rbg).max() / (scale if scale > 0 else 1.0))
     errs["dbg_plain"] = h.rel_err(g["dbg"], ref["dbg"])
     # dx and dW1 go through ReLU' decisions that either side may take at |z| near 0: every
     # element within the tolerance plus what those decisions can move it
@@ -135,6 +142,13 @@ EDGE = {
     "top1_pnorm_fp32_shared": _cfg(dtype=0, n_experts=6, top_k=1, capacity=137, gate_norm=2,
                                    norm_p=3.0, n_shared=2, d_model=192, d_ff=64, act=1,
                                    n_groups=4, n_tokens=1652, expert_groups=2, topk_groups=1),
+    # bf16 layers whose router gradient rests on a few tokens' dw (checked against the
+    # rounded-activation reference of tests/router_ref.py)
+    "one_token_all_experts": _cfg(n_tokens=1, d_model=384, d_ff=256, n_experts=3, top_k=3,
+                                  capacity=1, act=1, gate_norm=0, zipf_s=4.0, seed=922),
+    "capacity_one_top1_shared": _cfg(n_tokens=127, d_model=384, d_ff=256, n_experts=3,
+                                     n_shared=3, top_k=1, capacity=1, act=2, gate_norm=0,
+                                     seed=1002),
 }
 
 
@@ -330,3 +344,14 @@ def test_workload_saved_backward(name):
 def test_random_seed_backward(i):
     import random_layers
     check(random_layers.random_cfg(i))
+
+
+@pytest.mark.parametrize("name", ["small_shared_top3", "small_swiglu_shared", "small_top1_zipf"])
+def test_recompute_equals_kept_activations(name):
+    """moe_backward recomputes GEMM 1 through the training forward's own epilogue, so its
+    activations, and with them every gradient, equal moe_backward_saved's bit for bit."""
+    cfg = configs.SMALL[name]
+    a, _, _ = run_backward(cfg)
+    b, _, _ = run_backward(cfg, saved=True)
+    for key in ("dx", "dWg", "dbg", "dW1", "dW2"):
+        assert np.array_equal(a[key], b[key]), key
