@@ -625,7 +625,7 @@ int backward_impl(const moe_cfg* c, const void* x, const void* Wg, const float* 
   sa.kshared = static_cast<int>(B.kshared);
   rc = status_of(moe::launch_bwd_setup(sa, s));
   if (rc) return rc;
-  // 2. pre-activations z1 = buf W1_e^T (routed) and x W1_sh^T (shared), then h = act(z1).
+  // 2. h = act(z1) with z1 = buf W1_e^T (routed) and x W1_sh^T (shared), and z1 beside it.
   //    ReLU needs no z1: ReLU'(z1) is 1 exactly where h > 0, so GEMM 1 writes h as in the
   //    forward.
   const bool relu = c->act == MOE_ACT_RELU;
