@@ -11,8 +11,9 @@
 // give every block its base, and moe_permute adds the in-block prefix.
 //
 // One block per (group, expert), one wave per rank j: every wave loads its rank's block
-// histogram (up to 512 blocks at once, so the loads overlap), the k totals n_j meet in LDS,
-// and each wave then runs the base recurrence over the ranks below it and writes its scan.
+// histogram and its share of the blocks' probability sums and selection counts (up to 512
+// blocks of each at once, so the loads overlap), the k totals n_j meet in LDS, and each wave
+// then runs the base recurrence over the ranks below it and writes its scan.
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -32,31 +33,38 @@ __global__ __launch_bounds__(kMaxTopK * kWave) void gate_scan_kernel(ScanArgs a)
   const int g = blockIdx.x / E, e = blockIdx.x - g * E;
   if (blockIdx.x == 0 && threadIdx.x == 0) a.stats[2] = 0;  // counted by the dispatch kernel
 
-  // aux partials: probabilities and selections over the group's blocks, split over the waves
+  // aux partials: probabilities and selections over the group's blocks, split over the waves,
+  // and n_j: active rank-j slots of the expert in the group.  Each round issues all of its
+  // loads (kChunks of each array per lane) before the first is used; the sums run in block
+  // order per lane as before.
   const size_t pe = (static_cast<size_t>(g) * E + e) * nbg;
-  double ps = 0.0;
-  int cs = 0;
-  for (int b = threadIdx.x; b < nbg; b += k * kWave) {
-    ps += a.psum[pe + b];
-    cs += a.sel[pe + b];
-  }
-  ps = wave_sum(ps);
-  cs = wave_sum(cs);
-
-  // n_j: active rank-j slots of the expert in the group
   const size_t o = ((static_cast<size_t>(g) * k + j) * E + e) * nbg;
   const int32_t* __restrict__ h = a.ahist + o;
+  const int stride = k * kWave;
+  double ps = 0.0;
+  int cs = 0;
   int v[kChunks];
   int tot = 0;
-  for (int b0 = 0; b0 < nbg; b0 += kPass) {
+  for (int b0 = 0, p0 = threadIdx.x; b0 < nbg || p0 < nbg; b0 += kPass, p0 += kChunks * stride) {
+    double pv[kChunks];
+    int sv[kChunks];
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
       const int b = b0 + c * kWave + lane;
       v[c] = b < nbg ? h[b] : 0;
+      const int bp = p0 + c * stride;
+      pv[c] = bp < nbg ? a.psum[pe + bp] : 0.0;
+      sv[c] = bp < nbg ? a.sel[pe + bp] : 0;
     }
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) tot += v[c];
+    for (int c = 0; c < kChunks; ++c) {
+      tot += v[c];
+      ps += pv[c];
+      cs += sv[c];
+    }
   }
+  ps = wave_sum(ps);
+  cs = wave_sum(cs);
   tot = wave_sum(tot);
   if (lane == 0) {
     tot_s[j] = tot;
