@@ -1,5 +1,5 @@
-"""Reference router-side gradients of bf16 layers (dWg, dbg), shared by the GPU backward tests
-and the CPU tests that pin it.
+"""Reference router-side gradients (dWg, dbg) of the GPU backward tests, shared with the CPU
+tests that pin them.
 
 The combine weights' gradient dw_nj = <dy_n W2_e, h_row> is formed on the device from the
 hidden activation h and the product dy W2_e, both in the layer's dtype (the layer keeps its
@@ -13,6 +13,10 @@ every other step the oracle's.
 import numpy as np
 
 from mixture_experts_layer_group_amd import synth
+
+# fp32 layers: the router gradients' allowance beyond the tolerance, in units of the terms'
+# magnitude scale (four fp32 rounding units)
+FP32_UNITS = 2.0 ** -22
 from oracle import moe_backward as mb
 from oracle import moe_oracle as mo
 
@@ -54,3 +58,56 @@ def router_grads(cfg, inp, r, dy, logits, coefs, rounded=True):
     dl = mb.router_backward(cfg, r["p"], r["topk_idx"], lr, dw_of(cfg, inp, r, dy, rounded),
                             **coefs)
     return dl.T @ np.asarray(inp.x, np.float64), dl.sum(axis=0), dl
+
+
+def magnitude_scale(cfg, inp, r, dy, logits, coefs):
+    """Elementwise magnitudes (dWg [E, M], dbg [E]) of the terms the router gradients are made
+    of: dw's products |(dy W2_e)_h| |h_h| summed, carried through the gate normalisation and
+    the softmax with the absolute values of their coefficients, plus the balance and z-loss
+    terms' magnitudes.  An fp32 result is accurate to a small multiple of the rounding unit
+    relative to this scale, not to its own size: on a layer whose router gradient rests on one
+    token, the dot products behind dw cancel, and their accumulation order alone moves dWg by
+    that cancellation times the rounding unit."""
+    N, E, k = cfg["n_tokens"], cfg["n_experts"], cfg["top_k"]
+    M = np.shape(inp.x)[1]
+    if N == 0:
+        return np.zeros((E, M)), np.zeros(E)
+    x = np.asarray(inp.x, np.float64)
+    dy = np.asarray(dy, np.float64)
+    kept = r["pos"] >= 0
+    b = np.zeros((N, k))
+    for e in range(E):
+        w1 = np.asarray(inp.W1[e], np.float64)
+        w2 = np.asarray(inp.W2[e], np.float64)
+        for j in range(k):
+            rows = np.nonzero(kept[:, j] & (r["topk_idx"][:, j] == e))[0]
+            if rows.size == 0:
+                continue
+            z = x[rows] @ w1.T
+            if cfg["act"] == mo.ACT_SWIGLU:
+                H = w1.shape[0] // 2
+                h = mo.swish(z[:, :H]) * z[:, H:]
+            else:
+                h = mo.activation(z, cfg["act"])
+            b[rows, j] = (np.abs(dy[rows] @ w2) * np.abs(h)).sum(axis=1)
+    p = np.asarray(r["p"], np.float64)
+    idx = np.asarray(r["topk_idx"], np.int64)
+    ps = np.take_along_axis(p, idx, axis=1)
+    norm = cfg["gate_norm"]
+    if norm == 0:
+        bps = b
+    elif k == 1:
+        bps = np.zeros_like(b)
+    else:
+        P = 1.0 if norm == 1 else float(cfg.get("norm_p", 1.0))
+        D = (ps ** P).sum(axis=1, keepdims=True) ** (1.0 / P)
+        w = ps / D
+        bps = (b + w ** (P - 1.0) * (w * b).sum(axis=1, keepdims=True)) / D
+    bp = np.zeros((N, E))
+    for j in range(k):
+        np.add.at(bp, (np.arange(N), idx[:, j]), bps[:, j])
+    bp += np.abs(mb.balance_grad(cfg, idx, coefs.get("coef_aux", 0.0), coefs.get("coef_dev", 0.0)))
+    lr = np.asarray(logits, np.float32).astype(np.float64)
+    bl = p * (bp + (p * bp).sum(axis=1, keepdims=True)) + np.abs(
+        mb.z_loss_grad(lr, p, coefs.get("coef_z", 0.0)))
+    return bl.T @ np.abs(x), bl.sum(axis=0)

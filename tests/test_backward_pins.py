@@ -283,3 +283,40 @@ def test_router_ref_rounding_moves_dw_by_bf16_amounts(name):
     dw = router_ref.dw_of(cfg, inp, ref["routing"], dy)
     d = np.abs(dw - ref["dw"]).max() / np.abs(ref["dw"]).max()
     assert 0.0 < d <= 2e-2
+
+
+# ---- the fp32 router-gradient allowance of the GPU test (tests/router_ref.magnitude_scale)
+
+def _fp32_router_cases():
+    from mixture_experts_layer_group_amd import configs
+    return [n for n, c in configs.SMALL.items() if c["dtype"] == 0]
+
+
+@pytest.mark.parametrize("name", _fp32_router_cases())
+def test_magnitude_scale_bounds_the_gradients(name):
+    """The magnitudes of the terms bound the router gradients they form, element by element."""
+    import router_ref
+    cfg, inp, dy, logits, ref = _router_ref_case(name)
+    mWg, mbg = router_ref.magnitude_scale(cfg, inp, ref["routing"], dy, logits, COEFS)
+    assert np.all(mWg >= np.abs(ref["dWg"]) * (1 - 1e-12))
+    assert np.all(mbg >= np.abs(ref["dbg"]) * (1 - 1e-12))
+
+
+@pytest.mark.parametrize("name", _fp32_router_cases())
+def test_fp32_router_check_detects_dw_errors(name):
+    """Planted mistake: dw off by 1e-4 relative (random signs) fails the fp32 criterion (1e-5
+    of max |dWg| beyond FP32_UNITS of the magnitude scale); the oracle itself passes it."""
+    import router_ref
+    cfg, inp, dy, logits, ref = _router_ref_case(name)
+    r = ref["routing"]
+    mWg, _ = router_ref.magnitude_scale(cfg, inp, r, dy, logits, COEFS)
+
+    def err(dw):
+        dl = mb.router_backward(cfg, r["p"], r["topk_idx"], np.asarray(logits, np.float64), dw,
+                                **COEFS)
+        d = np.abs(dl.T @ np.asarray(inp.x, np.float64) - ref["dWg"]).max()
+        return (d - router_ref.FP32_UNITS * mWg.max()) / np.abs(ref["dWg"]).max()
+
+    rng = np.random.default_rng(1)
+    assert err(ref["dw"]) <= 1e-5
+    assert err(ref["dw"] * (1 + 1e-4 * rng.choice([-1.0, 1.0], size=ref["dw"].shape))) > 1e-5
