@@ -427,6 +427,49 @@ def measure(name, args, ev, headline):
     return out
 
 
+def library_gemm_timing(reps=10):
+    """torch.matmul in bf16 (contiguous operands, so the library sees plain row-major GEMMs) on
+    the large-expert layer's two GEMMs as dense problems (32768 rows = 16384 tokens x top-2)
+    and on GShard's two expert GEMMs as a batch of 64 experts padded to 512 rows each (its mean
+    of 16384 x 2 / 64 rows, so no expert is dropped only if the routing is exactly even).  The
+    median of reps launches, timed with events on torch's current stream."""
+    import torch
+    shapes = {
+        "large_expert_gemm1_dense": (1, 32768, 4096, 14336),
+        "large_expert_gemm2_dense": (1, 32768, 14336, 4096),
+        "gshard_gemm1_batched_padded": (64, 512, 1024, 4096),
+        "gshard_gemm2_batched_padded": (64, 512, 4096, 1024),
+    }
+    try:
+        blas = str(torch.backends.cuda.preferred_blas_library())
+    except Exception:   # older torch: the library choice is not exposed
+        blas = "default"
+    res = {"blas": blas, "torch": torch.__version__}
+    g = torch.Generator(device="cuda").manual_seed(7)
+    for name, (b, m, k, n) in shapes.items():
+        a = torch.randn(b, m, k, device="cuda", dtype=torch.bfloat16, generator=g)
+        w = torch.randn(b, k, n, device="cuda", dtype=torch.bfloat16, generator=g).contiguous()
+        if b == 1:
+            a, w = a[0], w[0]
+        c = torch.matmul(a, w)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            torch.matmul(a, w, out=c)
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = float(np.median(ts))
+        tf = 2.0 * b * m * k * n / (ms * 1e-3) / 1e12
+        res[name] = {"shape": [b, m, k, n], "ms": round(ms, 4), "TFLOPs": round(tf, 1),
+                     "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 3)}
+        del a, w, c
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -442,6 +485,10 @@ def main():
                     help="headline forward steps replayed from HIP graphs (0: skip)")
     ap.add_argument("--backward-steps", type=int, default=10,
                     help="timed moe_backward calls per layer (0: skip)")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="also time torch's bf16 matmul (the ROCm BLAS library) on the dense "
+                         "large-expert GEMM shapes and on GShard's expert GEMMs padded to 512 "
+                         "rows per expert, for comparison with the expert GEMM")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run 3 device-to-device copies of 1 GiB (the known-size kernel "
                          "that scales the HBM byte counters) and exit")
@@ -520,6 +567,8 @@ def main():
     for key in ("graph", "backward"):
         if key in head:
             out[key] = head[key]
+    if args.library_gemm:
+        out["library_gemm"] = library_gemm_timing()
     if out["cpu_baseline"] is None:
         del out["cpu_baseline"]
     out["configs"] = rest
