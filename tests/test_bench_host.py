@@ -29,11 +29,13 @@ def test_more_than_one_gpu_is_refused(args, env):
     assert p.stdout == ""
 
 
-def test_no_gpu_is_an_error_not_a_fallback():
+@pytest.mark.parametrize("extra", [(), ("--library-gemm",)])
+def test_no_gpu_is_an_error_not_a_fallback(extra):
+    """Also with the library comparison asked for: nothing runs on the CPU in its place."""
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
-    p = _run("--steps", "1", "--warmup", "0")
+    p = _run("--steps", "1", "--warmup", "0", *extra)
     assert p.returncode == 1
     assert "needs a GPU" in p.stderr
     assert p.stdout == ""
